@@ -1,0 +1,175 @@
+/*
+ * losa.h -- C ABI of liblosa.so: LoSA per-denoising-step attention on MI355X.
+ *
+ * LoSA (Locality Aware Sparse Attention for Block-Wise Diffusion Language
+ * Models, arXiv 2604.12056) runs, at each denoising step of a block of B
+ * tokens and for one attention layer:
+ *   1. a locality score per block token: the mean squared change of its
+ *      query since the previous step (gist.science pt summary, section
+ *      "3. Metodologia", step 1; fr summary, "Pruning par Localité");
+ *   2. the |A| most-changed tokens form the active set, the rest are stable
+ *      (same passages);
+ *   3. QUEST page selection for the active tokens only (pt step 3; fr
+ *      "Calcul Sparse pour les Tokens Actifs");
+ *   4. the union of their selected pages, the only prefix KV that is read
+ *      (fr "Réduction de l'Union KV"; hf.space abstract);
+ *   5. prefix attention of the active tokens over that union, giving the
+ *      prefix output o_p and log-normaliser L_p (agifrontier tutorial,
+ *      section on the LoSA workflow);
+ *   6. stable tokens reuse the cached (o_p, L_p) (pt step 2);
+ *   7. dense attention of all block tokens over the block itself (tutorial,
+ *      workflow section; pt step 4);
+ *   8. an online-softmax (log-sum-exp) merge of prefix and block parts, the
+ *      new statistics kept for the next step (pt step 4);
+ *   and the first step of every block is a forced dense prefix pass
+ *   (tutorial, section on limitations).
+ *
+ * Reading of what the pages leave open (QUEST is named, not defined there):
+ * pages are 16 consecutive tokens of one KV head; a page's metadata is the
+ * element-wise min and max of its keys; a query's bound for a page is
+ * sum_i max(q_i*min_i, q_i*max_i); every active query keeps the
+ * budget_tokens/16 pages of largest bound (all pages when that covers the
+ * prefix); the union is taken per KV head over the G*|A| active rows of its
+ * query-head group (G = n_qhead / n_kvhead); every active row attends over
+ * the whole union; scores are per (query head, token), so each query head
+ * has its own active set.
+ *
+ * Canonical index arithmetic (reproduced bit for bit; see each call):
+ *   locality e = fp32 chain over i ascending of fl(acc + fl(d_i*d_i)),
+ *     d_i = fl(q_t,i - q_prev,i), acc from +0; reported score = e / d;
+ *   active set: |A| largest e, equal scores to the lower token, ascending;
+ *   page bound U = fp32 chain over i ascending of fl(acc + fl(q_i*s_i)),
+ *     s_i = max_i if q_i >= 0 else min_i, acc from +0 (for bf16 inputs every
+ *     product is exact, so a fused multiply-add gives the same bits);
+ *   top-k: k largest U, -0 equal to +0, equal bounds to the lower page;
+ *   page indices are local to their sequence and lists are ascending.
+ * Values (o_p, L_p, outputs) are fp32 arithmetic on the device: scores,
+ * exponentials, the log-sum-exp merge; bf16 outputs are rounded to nearest
+ * even.  The natural logarithm is used for L_p.
+ *
+ * Memory.  Every array argument is a device pointer (hipMalloc or
+ * equivalent) owned by the caller, 16-byte aligned.  The library allocates,
+ * frees and synchronises nothing and keeps no state between calls; the
+ * workspace is scratch owned by the caller and must not be shared by calls
+ * that may run concurrently.  All work is enqueued on `stream` (a
+ * hipStream_t; NULL is the default stream).  Calls return after enqueueing.
+ *
+ * Layouts (row-major, innermost last; T = kv_tokens):
+ *   q_t, q_prev, out       [n_seq][B][n_qhead][head_dim]      dtype
+ *   k_blk, v_blk           [n_seq][B][n_kvhead][head_dim]     dtype
+ *   k_cache, v_cache       [n_kvhead][T][head_dim]            dtype
+ *       sequence s holds tokens kv_off[s] .. kv_off[s]+prefix_len[s]-1;
+ *       kv_off[s] is a multiple of page_size; sequences may not overlap.
+ *   kv_off, prefix_len     [n_seq] int32 (device)
+ *   op_cache               [n_seq][n_qhead][B][head_dim]      fp32 (o_p)
+ *   lp_cache               [n_seq][n_qhead][B]                fp32 (L_p)
+ *   page_meta              opaque, losa_page_meta_bytes() bytes
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued;
+ * a failed check returns its status and enqueues nothing.  A failed launch
+ * returns LOSA_ERR_HIP.  Asynchronous device faults surface at the caller's
+ * next synchronisation.  prefix_len[s] must lie in [0, max_prefix_len] and
+ * kv_off[s] + prefix_len[s] <= kv_tokens; kernels clamp out-of-range values
+ * into the cache instead of reading past it, so the results for such a
+ * sequence are unspecified but memory-safe.  Inputs must be finite.
+ */
+#ifndef LOSA_H_
+#define LOSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum losa_status {
+    LOSA_OK = 0,
+    LOSA_ERR_INVALID_ARG = 1, /* a null/misaligned pointer or an inconsistent shape */
+    LOSA_ERR_UNSUPPORTED = 2, /* a legal shape this build has no kernel for */
+    LOSA_ERR_WORKSPACE = 3,   /* workspace smaller than losa_workspace_bytes() */
+    LOSA_ERR_HIP = 4          /* a HIP launch failed */
+} losa_status;
+
+typedef enum losa_dtype { LOSA_F32 = 0, LOSA_BF16 = 1 } losa_dtype;
+
+typedef struct losa_shape {
+    int32_t n_seq;          /* sequences in the batch, >= 1 */
+    int32_t block;          /* B: tokens per block, 1..64 */
+    int32_t n_qhead;        /* query heads, a multiple of n_kvhead */
+    int32_t n_kvhead;       /* KV heads, >= 1 */
+    int32_t head_dim;       /* 64 or 128 */
+    int32_t page_size;      /* 16 */
+    int32_t budget_tokens;  /* per-query prefix budget in tokens, a positive multiple of page_size */
+    int32_t n_active;       /* |A|: active tokens per query head, 0..block */
+    int32_t max_prefix_len; /* upper bound of prefix_len[], 0..kv_tokens; sizes the grids */
+    int32_t dtype;          /* losa_dtype of q, k, v and out */
+    int64_t kv_tokens;      /* T: tokens per KV head in k_cache/v_cache, a multiple of page_size */
+    float softmax_scale;    /* > 0, or 0 for 1/sqrt(head_dim) */
+    uint32_t flags;         /* must be 0 */
+} losa_shape;
+
+/* Optional device outputs of losa_step (each pointer may be NULL). */
+typedef struct losa_debug {
+    float *locality;     /* [n_seq][n_qhead][B] locality score e/d */
+    int32_t *active;     /* [n_seq][n_qhead][n_active] active tokens, ascending */
+    int32_t *page_sel;   /* [n_seq][n_qhead][n_active][k], k = budget_tokens/page_size:
+                            each active row's pages, ascending, -1 past the prefix's pages */
+    int32_t *union_idx;  /* [n_seq][n_kvhead][union_cap] union of a KV head's pages, ascending */
+    int32_t *union_cnt;  /* [n_seq][n_kvhead] union sizes */
+    int32_t union_cap;   /* capacity of each union_idx row; >= losa_union_capacity() */
+} losa_debug;
+
+/* Human-readable name of a status code (static string). */
+const char *losa_status_string(int status);
+
+/* Bytes of the page metadata for this shape's cache (0 if the shape is invalid). */
+size_t losa_page_meta_bytes(const losa_shape *shape);
+
+/* Workspace bytes that losa_step and losa_dense_first_step need (0 if invalid). */
+size_t losa_workspace_bytes(const losa_shape *shape);
+
+/* Largest possible union per (sequence, KV head): min(pages of the longest
+ * prefix, G * n_active * budget_tokens/page_size); -1 if the shape is invalid. */
+int32_t losa_union_capacity(const losa_shape *shape);
+
+/*
+ * Page metadata for QUEST selection (reading above): for every page of every
+ * sequence and KV head, the element-wise minimum and maximum of the keys of
+ * its tokens that lie below prefix_len[s].  Run once per committed block
+ * (the prefix does not change between the denoising steps of a block).
+ * Writes page_meta (losa_page_meta_bytes(shape) bytes, library layout).
+ */
+int losa_build_page_meta(const losa_shape *shape, const void *k_cache, const int32_t *kv_off,
+                         const int32_t *prefix_len, void *page_meta, void *stream);
+
+/*
+ * Forced dense first step of a block (agifrontier tutorial, limitations
+ * section): every block token of every query head attends over its whole
+ * prefix; (o_p, L_p) of every token are written to op_cache/lp_cache
+ * (prefix_len 0 gives o_p = 0, L_p = -inf); then dense in-block attention
+ * and the merge write `out`.
+ */
+int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *k_blk,
+                          const void *v_blk, const void *k_cache, const void *v_cache,
+                          const int32_t *kv_off, const int32_t *prefix_len, float *op_cache,
+                          float *lp_cache, void *out, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * One LoSA step (steps 1-8 above).  q_prev is the previous step's q_t.  Only
+ * the (o_p, L_p) of active (query head, token) rows are recomputed, over the
+ * union of their KV head's selected pages, and overwrite the cache; stable
+ * rows read the cache unchanged.  `out` is written for every token.
+ * n_active = 0 reads no prefix KV at all.  debug may be NULL.
+ */
+int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, const void *k_blk,
+              const void *v_blk, const void *k_cache, const void *v_cache, const void *page_meta,
+              const int32_t *kv_off, const int32_t *prefix_len, float *op_cache, float *lp_cache,
+              void *out, const losa_debug *debug, void *workspace, size_t workspace_bytes,
+              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOSA_H_ */

@@ -59,6 +59,8 @@ def load(path: str = LIB_PATH):
                                 _I, _I, _I]
     lib.oracle_dense_first_step.argtypes = [_S, _F, _F, _F, _F, _F, _I, _I, _D, _D, _F]
     lib.oracle_naive_sparse_step.argtypes = [_S, _F, _F, _F, _F, _F, _F, _F, _I, _I, _D, _D, _F]
+    lib.oracle_dense_row.argtypes = [_S, c_int, c_int, c_int, _F, _F, _F, _F, _F, _I, _I, _D, _D,
+                                     _F]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -209,6 +211,20 @@ class Oracle:
                              _i(ucnt))
         return dict(out=out, locality=loc, active=act[..., :A], page_sel=psel[..., :A, :k],
                     union_idx=uidx, union_cnt=ucnt)
+
+    def dense_row(self, q_t, k_blk, v_blk, s, h, t):
+        """One (sequence, head, token) row of the dense first step: (o_p, L_p, out row).
+        Does not touch the (o_p, L_p) cache."""
+        c = self.cfg
+        op = np.zeros(c.head_dim, np.float64)
+        lp = np.zeros(1, np.float64)
+        out = np.zeros(c.head_dim, np.float32)
+        sh = self.shape()
+        self.lib.oracle_dense_row(ctypes.byref(sh), int(s), int(h), int(t), _f(_f32(q_t)),
+                                  _f(_f32(k_blk)), _f(_f32(v_blk)), _f(self.k_cache),
+                                  _f(self.v_cache), _i(self.kv_off), _i(self.prefix_len), _d(op),
+                                  _d(lp), _f(out))
+        return op, float(lp[0]), out
 
     def naive_sparse_step(self, q_t, k_blk, v_blk):
         c = self.cfg

@@ -465,3 +465,34 @@ void oracle_naive_sparse_step(const oracle_shape *sh, const float *q_t, const fl
     free(o);
     suffix_and_merge(sh, q_t, k_blk, v_blk, op_cache, lp_cache, out);
 }
+
+/* One row of the dense first step, for sampled checks at sizes where the full
+ * step is slow: (o_p, L_p) of query head h, token t of sequence s over its
+ * whole prefix, then that row's dense in-block attention and merge. */
+void oracle_dense_row(const oracle_shape *sh, int s, int h, int t, const float *q_t,
+                      const float *k_blk, const float *v_blk, const float *k_cache,
+                      const float *v_cache, const int32_t *kv_off, const int32_t *prefix_len,
+                      double *op, double *lp, float *out_row) {
+    const int B = sh->block, H = sh->n_qhead, Hk = sh->n_kvhead, d = sh->head_dim;
+    const int G = H / Hk, g = h / G;
+    const int64_t np_ = n_pages_of(sh, prefix_len[s]);
+    int32_t *all = (int32_t *)malloc(sizeof(int32_t) * (size_t)(np_ + 1));
+    for (int64_t p = 0; p < np_; ++p) all[p] = (int32_t)p;
+    const float *q = q_t + (((int64_t)s * B + t) * H + h) * d;
+    prefix_attend(sh, s, g, q, k_cache, v_cache, kv_off, prefix_len, all, np_, op, lp);
+    free(all);
+    const float **keys = (const float **)malloc(sizeof(float *) * (size_t)B);
+    const float **vals = (const float **)malloc(sizeof(float *) * (size_t)B);
+    double *s_buf = (double *)malloc(sizeof(double) * (size_t)B);
+    double *os = (double *)malloc(sizeof(double) * (size_t)d);
+    double *o = (double *)malloc(sizeof(double) * (size_t)d);
+    for (int u = 0; u < B; ++u) {
+        keys[u] = k_blk + (((int64_t)s * B + u) * Hk + g) * d;
+        vals[u] = v_blk + (((int64_t)s * B + u) * Hk + g) * d;
+    }
+    double ls;
+    attend(q, keys, vals, B, d, scale_of(sh), s_buf, os, &ls);
+    merge(op, *lp, os, ls, d, o);
+    for (int i = 0; i < d; ++i) out_row[i] = store_out(sh, o[i]);
+    free(keys); free(vals); free(s_buf); free(os); free(o);
+}

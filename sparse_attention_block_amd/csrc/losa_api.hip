@@ -1,0 +1,221 @@
+// C-ABI entry points of liblosa.so: argument checks (host only, before any HIP
+// call), workspace carve-up and the launch sequence of each call.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "losa_internal.h"
+
+using namespace losa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxPagesSupported = 262144;  // LDS bitmap of the union merge (32 KiB)
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const losa_shape *sh) {
+    if (!sh) return LOSA_ERR_INVALID_ARG;
+    if (sh->n_seq < 1 || sh->block < 1 || sh->n_qhead < 1 || sh->n_kvhead < 1)
+        return LOSA_ERR_INVALID_ARG;
+    if (sh->n_qhead % sh->n_kvhead) return LOSA_ERR_INVALID_ARG;
+    if (sh->page_size <= 0 || sh->head_dim <= 0) return LOSA_ERR_INVALID_ARG;
+    if (sh->dtype != LOSA_F32 && sh->dtype != LOSA_BF16) return LOSA_ERR_INVALID_ARG;
+    if (sh->budget_tokens < sh->page_size || sh->budget_tokens % sh->page_size)
+        return LOSA_ERR_INVALID_ARG;
+    if (sh->n_active < 0 || sh->n_active > sh->block) return LOSA_ERR_INVALID_ARG;
+    if (sh->kv_tokens < sh->page_size || sh->kv_tokens % sh->page_size) return LOSA_ERR_INVALID_ARG;
+    if (sh->max_prefix_len < 0 || sh->max_prefix_len > sh->kv_tokens) return LOSA_ERR_INVALID_ARG;
+    if (!(sh->softmax_scale >= 0.0f) || isinf(sh->softmax_scale)) return LOSA_ERR_INVALID_ARG;
+    if (sh->flags != 0) return LOSA_ERR_INVALID_ARG;
+    if (sh->page_size != kPage) return LOSA_ERR_UNSUPPORTED;
+    if (sh->head_dim != 64 && sh->head_dim != 128) return LOSA_ERR_UNSUPPORTED;
+    if (sh->block > 64) return LOSA_ERR_UNSUPPORTED;
+    if ((int64_t)(sh->n_qhead / sh->n_kvhead) * sh->block > kMaxRows) return LOSA_ERR_UNSUPPORTED;
+    if ((sh->max_prefix_len + kPage - 1) / kPage > kMaxPagesSupported) return LOSA_ERR_UNSUPPORTED;
+    if (sh->kv_tokens / kPage > (int64_t)1 << 30) return LOSA_ERR_UNSUPPORTED;
+    return LOSA_OK;
+}
+
+Dims make_dims(const losa_shape *sh) {
+    Dims D;
+    D.S = sh->n_seq;
+    D.B = sh->block;
+    D.Hq = sh->n_qhead;
+    D.Hk = sh->n_kvhead;
+    D.G = D.Hq / D.Hk;
+    D.d = sh->head_dim;
+    D.A = sh->n_active;
+    D.k = sh->budget_tokens / kPage;
+    D.bf16 = sh->dtype == LOSA_BF16;
+    D.max_pages = (sh->max_prefix_len + kPage - 1) / kPage;
+    D.T = sh->kv_tokens;
+    D.n_tiles_total = (D.T / kPage + kTile - 1) / kTile;
+    D.n_tiles_grid = (D.max_pages + kTile - 1) / kTile + 1;
+    D.kk = D.k < kTile ? D.k : kTile;
+    D.R = D.G * D.A;
+    D.Rd = D.G * D.B;
+    D.R16 = (D.Rd + 15) / 16 * 16;
+    const int64_t rk = (int64_t)D.R * D.k;
+    int64_t cap = rk < D.max_pages ? rk : D.max_pages;
+    D.union_cap = cap > 0 ? static_cast<int>(cap) : 1;
+    D.n_chunks_sparse = (D.union_cap + kSparseChunk - 1) / kSparseChunk;
+    D.n_chunks_dense = D.max_pages > 0 ? (D.max_pages + kDenseChunk - 1) / kDenseChunk : 1;
+    const float scale = sh->softmax_scale > 0.0f ? sh->softmax_scale
+                                                 : 1.0f / sqrtf(static_cast<float>(D.d));
+    D.scale_log2 = scale * 1.44269504088896340736f;
+    return D;
+}
+
+// Carve the workspace; with base == nullptr only the total size is computed.
+size_t carve(const Dims &D, char *base, Work *W) {
+    const size_t sT = D.bf16 ? 2 : 4;
+    const size_t SG = (size_t)D.S * D.Hk;
+    const size_t R1 = D.R > 0 ? D.R : 1;
+    const size_t A1 = D.A > 0 ? D.A : 1;
+    const size_t part_rows =
+        std::max((size_t)D.n_chunks_sparse * R1, (size_t)D.n_chunks_dense * D.Rd);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char *p = base ? base + off : nullptr;
+        off += align_up(bytes);
+        return p;
+    };
+    Work w;
+    w.counters = reinterpret_cast<int32_t *>(take(SG * 4));
+    w.active = reinterpret_cast<int32_t *>(take((size_t)D.S * D.Hq * A1 * 4));
+    w.qrows = take(SG * D.R16 * D.d * sT);
+    w.qsel = reinterpret_cast<float *>(take(SG * R1 * D.d * 8));
+    w.cand = reinterpret_cast<uint64_t *>(take(SG * R1 * D.n_tiles_grid * D.kk * 8));
+    w.union_idx = reinterpret_cast<int32_t *>(take(SG * D.union_cap * 4));
+    w.union_cnt = reinterpret_cast<int32_t *>(take(SG * 4));
+    w.part_acc = reinterpret_cast<float *>(take(SG * part_rows * D.d * 4));
+    w.part_ml = reinterpret_cast<float *>(take(SG * part_rows * 2 * 4));
+    if (W) *W = w;
+    return off;
+}
+
+size_t meta_bytes(const Dims &D) {
+    const size_t sT = D.bf16 ? 2 : 4;
+    return (size_t)D.Hk * D.n_tiles_total * kTile * D.d * 2 * sT;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LOSA_OK : LOSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *losa_status_string(int status) {
+    switch (status) {
+        case LOSA_OK: return "ok";
+        case LOSA_ERR_INVALID_ARG: return "invalid argument";
+        case LOSA_ERR_UNSUPPORTED: return "unsupported shape";
+        case LOSA_ERR_WORKSPACE: return "workspace too small";
+        case LOSA_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t losa_page_meta_bytes(const losa_shape *shape) {
+    if (check_shape(shape) != LOSA_OK) return 0;
+    return meta_bytes(make_dims(shape));
+}
+
+size_t losa_workspace_bytes(const losa_shape *shape) {
+    if (check_shape(shape) != LOSA_OK) return 0;
+    return carve(make_dims(shape), nullptr, nullptr);
+}
+
+int32_t losa_union_capacity(const losa_shape *shape) {
+    if (check_shape(shape) != LOSA_OK) return -1;
+    return make_dims(shape).union_cap;
+}
+
+int losa_build_page_meta(const losa_shape *shape, const void *k_cache, const int32_t *kv_off,
+                         const int32_t *prefix_len, void *page_meta, void *stream) {
+    int st = check_shape(shape);
+    if (st != LOSA_OK) return st;
+    if (!k_cache || !kv_off || !prefix_len || !page_meta) return LOSA_ERR_INVALID_ARG;
+    if (!aligned(k_cache, 16) || !aligned(page_meta, 16) || !aligned(kv_off, 4) ||
+        !aligned(prefix_len, 4))
+        return LOSA_ERR_INVALID_ARG;
+    const Dims D = make_dims(shape);
+    return hip_status(launch_page_meta(D, k_cache, kv_off, prefix_len, page_meta,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *k_blk,
+                          const void *v_blk, const void *k_cache, const void *v_cache,
+                          const int32_t *kv_off, const int32_t *prefix_len, float *op_cache,
+                          float *lp_cache, void *out, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+    int st = check_shape(shape);
+    if (st != LOSA_OK) return st;
+    const void *p16[] = {q_t, k_blk, v_blk, k_cache, v_cache, op_cache, out, workspace};
+    for (const void *p : p16)
+        if (!p || !aligned(p, 16)) return LOSA_ERR_INVALID_ARG;
+    if (!kv_off || !prefix_len || !lp_cache || !aligned(kv_off, 4) || !aligned(prefix_len, 4) ||
+        !aligned(lp_cache, 4))
+        return LOSA_ERR_INVALID_ARG;
+    const Dims D = make_dims(shape);
+    Work W;
+    const size_t need = carve(D, static_cast<char *>(workspace), &W);
+    if (workspace_bytes < need) return LOSA_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_prepare(D, true, q_t, nullptr, W, nullptr, nullptr, nullptr, s);
+    if (e == hipSuccess) e = launch_prefix(D, true, k_cache, v_cache, kv_off, prefix_len, W, s);
+    if (e == hipSuccess)
+        e = launch_finish(D, true, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache,
+                          out, s);
+    return hip_status(e);
+}
+
+int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, const void *k_blk,
+              const void *v_blk, const void *k_cache, const void *v_cache, const void *page_meta,
+              const int32_t *kv_off, const int32_t *prefix_len, float *op_cache, float *lp_cache,
+              void *out, const losa_debug *debug, void *workspace, size_t workspace_bytes,
+              void *stream) {
+    int st = check_shape(shape);
+    if (st != LOSA_OK) return st;
+    const void *p16[] = {q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, op_cache, out,
+                         workspace};
+    for (const void *p : p16)
+        if (!p || !aligned(p, 16)) return LOSA_ERR_INVALID_ARG;
+    if (!kv_off || !prefix_len || !lp_cache || !aligned(kv_off, 4) || !aligned(prefix_len, 4) ||
+        !aligned(lp_cache, 4))
+        return LOSA_ERR_INVALID_ARG;
+    const Dims D = make_dims(shape);
+    losa_debug dbg;
+    memset(&dbg, 0, sizeof dbg);
+    if (debug) {
+        dbg = *debug;
+        const void *pd[] = {dbg.locality, dbg.active, dbg.page_sel, dbg.union_idx, dbg.union_cnt};
+        for (const void *p : pd)
+            if (p && !aligned(p, 4)) return LOSA_ERR_INVALID_ARG;
+        if (dbg.union_idx && dbg.union_cap < D.union_cap) return LOSA_ERR_INVALID_ARG;
+    }
+    Work W;
+    const size_t need = carve(D, static_cast<char *>(workspace), &W);
+    if (workspace_bytes < need) return LOSA_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (D.R > 0 && select_lds_bytes(D) > 60 * 1024) return LOSA_ERR_UNSUPPORTED;
+    hipError_t e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active,
+                                  dbg.union_cnt, s);
+    if (D.R > 0) {
+        if (e == hipSuccess)
+            e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, dbg.union_idx,
+                              dbg.union_cnt, dbg.union_cap, s);
+        if (e == hipSuccess) e = launch_prefix(D, false, k_cache, v_cache, kv_off, prefix_len, W, s);
+    }
+    if (e == hipSuccess)
+        e = launch_finish(D, false, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache,
+                          out, s);
+    return hip_status(e);
+}
+
+}  // extern "C"

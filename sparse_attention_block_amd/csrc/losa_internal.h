@@ -1,0 +1,117 @@
+// Internal declarations of liblosa.so: problem dimensions, the carve-up of the
+// caller's workspace, kernel launchers and small device helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "losa.h"
+
+namespace losa {
+
+constexpr int kPage = 16;        // tokens per page
+constexpr int kTile = 64;        // pages per metadata tile: one page per lane of a wave
+constexpr int kSparseChunk = 8;  // union pages per prefix workgroup (sparse step)
+constexpr int kDenseChunk = 32;  // prefix pages per prefix workgroup (dense first step)
+constexpr int kMaxRows = 256;    // G * B stacked rows per KV head at most
+
+// Everything a kernel needs to know about the problem, by value.
+struct Dims {
+    int S, B, Hq, Hk, G, d, A, k;     // k = budget pages per row
+    int bf16;                         // 1: bf16 storage, 0: fp32
+    int max_pages;                    // pages of the longest prefix
+    int64_t T;                        // kv_tokens
+    int64_t n_tiles_total;            // metadata tiles per KV head over the whole cache
+    int n_tiles_grid;                 // tiles a sequence can touch (grid x of selection)
+    int kk;                           // candidates kept per (tile, row) = min(k, 64)
+    int union_cap;                    // min(max_pages, G*A*k)
+    int R;                            // stacked active rows per KV head = G*A
+    int Rd;                           // stacked dense rows per KV head = G*B
+    int R16;                          // Rd rounded up to 16
+    int n_chunks_sparse, n_chunks_dense;
+    float scale_log2;                 // softmax scale * log2(e)
+};
+
+// Device views into the workspace (all carved from one caller buffer).
+struct Work {
+    int32_t *counters;   // [S][Hk] arrival counters of the selection kernel
+    int32_t *active;     // [S][Hq][max(A,1)]
+    void *qrows;         // [S][Hk][R16][d] storage type: stacked query rows
+    float *qsel;         // [S][Hk][max(R,1)][d][2] (max(q,0), min(q,0)) selection operands
+    uint64_t *cand;      // [S][Hk][R][n_tiles_grid][kk] tile candidates
+    int32_t *union_idx;  // [S][Hk][union_cap]
+    int32_t *union_cnt;  // [S][Hk]
+    float *part_acc;     // [S][Hk][n_chunks][rows][d]
+    float *part_ml;      // [S][Hk][n_chunks][rows][2] (running max in log2 units, sum)
+};
+
+// Launchers (one per translation unit); each returns the hipGetLastError code.
+hipError_t launch_page_meta(const Dims &D, const void *k_cache, const int32_t *kv_off,
+                            const int32_t *prefix_len, void *meta, hipStream_t st);
+hipError_t launch_prepare(const Dims &D, bool dense, const void *q_t, const void *q_prev,
+                          const Work &W, float *dbg_locality, int32_t *dbg_active,
+                          int32_t *dbg_union_cnt, hipStream_t st);
+hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
+                         const int32_t *prefix_len, const Work &W, int32_t *dbg_page_sel,
+                         int32_t *dbg_union_idx, int32_t *dbg_union_cnt, int dbg_union_cap,
+                         hipStream_t st);
+size_t select_lds_bytes(const Dims &D);  // dynamic LDS of the selection kernel
+hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const void *v_cache,
+                         const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
+                         hipStream_t st);
+hipError_t launch_finish(const Dims &D, bool dense, const void *q_t, const void *k_blk,
+                         const void *v_blk, const int32_t *kv_off, const int32_t *prefix_len,
+                         const Work &W, float *op_cache, float *lp_cache, void *out,
+                         hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Device helpers.
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even bf16 (finite inputs; NaN maps to a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Order-preserving map of an fp32 value to uint32 (-0 treated as +0); 0 is
+// below every finite value and serves as "no candidate".
+__device__ __forceinline__ uint32_t ord_key(float f) {
+    uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Sequence geometry with out-of-range values clamped into the cache.
+struct SeqGeom {
+    int64_t off;   // first cache token
+    int len;       // prefix tokens
+    int pages;     // ceil(len / 16)
+    int64_t gp0;   // first global page
+};
+
+__device__ __forceinline__ SeqGeom seq_geom(const Dims &D, const int32_t *kv_off,
+                                            const int32_t *prefix_len, int s) {
+    SeqGeom g;
+    int64_t off = kv_off[s];
+    int len = prefix_len[s];
+    if (off < 0) off = 0;
+    off = off / kPage * kPage;
+    if (off > D.T) off = D.T;
+    if (len < 0) len = 0;
+    if (len > D.max_pages * kPage) len = D.max_pages * kPage;
+    if (off + len > D.T) len = static_cast<int>(D.T - off);
+    g.off = off;
+    g.len = len;
+    g.pages = (len + kPage - 1) / kPage;
+    g.gp0 = off / kPage;
+    return g;
+}
+
+}  // namespace losa

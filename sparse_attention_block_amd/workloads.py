@@ -203,6 +203,23 @@ def make_layer(cfg: Config, layer: int = 0, n_steps: Optional[int] = None,
     return lay
 
 
+def make_cache_state(cfg: Config, layer: int = 0, stream: int = 20):
+    """A seeded (o_p, L_p) cache state: the prefix statistics a previous step left
+    behind, for starting a step without running the dense pass first.
+    o_p ~ N(0, 0.3); L_p = log(L) + N(0, 0.5) (-inf where the prefix is empty)."""
+    rng = _rng(cfg.cfg_id, layer, stream)
+    S, Hq, B, d = cfg.n_seq, cfg.n_qhead, cfg.block, cfg.head_dim
+    op = _normal(rng, (S, Hq, B, d), 0.3)
+    lp = _normal(rng, (S, Hq, B), 0.5)
+    for s, L in enumerate(cfg.prefix_lens):
+        if L > 0:
+            lp[s] += np.float32(np.log(L))
+        else:
+            lp[s] = -np.inf
+            op[s] = 0.0
+    return op, lp
+
+
 # ---------------------------------------------------------------------------
 # The five workloads.
 

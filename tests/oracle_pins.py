@@ -305,6 +305,24 @@ def pin_dense_first_step_equals_attention(lib):
                         assert abs(orc.lp[s, h, t] - lp) < 1e-9
 
 
+def pin_dense_row_equals_attention(lib):
+    cfg = W.small_case(45, n_seq=2, n_qhead=4, n_kvhead=2, head_dim=32, dtype="bf16",
+                       prefix_lens=(150, 0), n_steps=1)
+    lay = W.make_layer(cfg)
+    orc = new_oracle(lib, lay)
+    scale = 1 / math.sqrt(cfg.head_dim)
+    for (s, h, t) in [(0, 0, 0), (0, 3, 15), (1, 2, 7), (0, 1, 9)]:
+        op, lp, out = orc.dense_row(lay.q[0], lay.k_blk[0], lay.v_blk[0], s, h, t)
+        o, _ = _dense_reference(lay, 0, s, h, t, scale)
+        bf16_nearest(out, o, f"dense row {s} {h} {t}")
+        g = h // cfg.group
+        L, off = int(lay.prefix_len[s]), int(lay.kv_off[s])
+        o_p, l_p = sdpa64(lay.q[0][s, t, h], lay.k_cache[g, off:off + L],
+                          lay.v_cache[g, off:off + L], scale)
+        close(op, o_p, 1e-9, 1e-12, "dense row o_p")
+        assert (lp == l_p == -math.inf) or abs(lp - l_p) < 1e-9
+
+
 def pin_all_active_full_budget_is_dense(lib):
     """|A| = B and a budget covering the prefix: a LoSA step is dense attention."""
     for cid, (dtype, lens) in enumerate([("bf16", (96, 40)), ("f32", (64,))]):
@@ -395,6 +413,7 @@ ALL_PINS = [
     pin_page_meta, pin_locality_value, pin_locality_planted_drift, pin_active_set_order_and_ties,
     pin_page_bound_is_box_maximum, pin_topk_and_union, pin_needles_rank_high,
     pin_sparse_prefix_equals_sdpa, pin_dense_first_step_equals_attention,
+    pin_dense_row_equals_attention,
     pin_all_active_full_budget_is_dense, pin_stable_reuse_and_merge, pin_mixed_step_rows,
     pin_naive_sparse_per_query,
 ]

@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports what include/losa.h declares, sizes its
+buffers, and rejects bad arguments on the host before anything is enqueued
+(no GPU needed: every call below fails validation before its first HIP call)."""
+import ctypes
+
+import pytest
+
+from sparse_attention_block_amd import binding as L
+from sparse_attention_block_amd import workloads as W
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def shape_of(cfg, **kw):
+    _, lens, T = W.prefix_layout(cfg.prefix_lens, cfg.page_size)
+    args = dict(n_seq=cfg.n_seq, block=cfg.block, n_qhead=cfg.n_qhead, n_kvhead=cfg.n_kvhead,
+                head_dim=cfg.head_dim, budget_tokens=cfg.budget, n_active=cfg.n_active,
+                max_prefix_len=int(max(lens)), dtype=cfg.dtype, kv_tokens=T)
+    args.update(kw)
+    return L.make_shape(**args)
+
+
+CONFIGS = [W.tiny_f32(), W.gqa_16k(), W.long_64k(128, 4), W.long_64k(256, 8), W.ragged_batch(),
+           W.trace_128k(0), W.trace_128k(20)]
+
+
+def test_exports_every_header_symbol(lib):
+    names = L.header_functions()
+    assert set(names) >= {"losa_build_page_meta", "losa_step", "losa_dense_first_step",
+                          "losa_status_string", "losa_page_meta_bytes", "losa_workspace_bytes",
+                          "losa_union_capacity"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert L.status_string(L.LOSA_OK) == "ok"
+    assert "workspace" in L.status_string(L.LOSA_ERR_WORKSPACE)
+    assert L.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_sizes(cfg):
+    sh = shape_of(cfg)
+    _, lens, T = W.prefix_layout(cfg.prefix_lens, cfg.page_size)
+    max_pages = (int(max(lens)) + 15) // 16
+    cap = min(max_pages, cfg.group * cfg.n_active * (cfg.budget // 16))
+    assert L.union_capacity(sh) == max(cap, 1)
+    s_t = 2 if cfg.dtype == "bf16" else 4
+    tiles = (T // 16 + 63) // 64
+    assert L.page_meta_bytes(sh) == cfg.n_kvhead * tiles * 64 * cfg.head_dim * 2 * s_t
+    ws = L.workspace_bytes(sh)
+    assert 0 < ws < 1 << 31
+
+
+BAD_SHAPES = [
+    (dict(n_qhead=6, n_kvhead=4), L.LOSA_ERR_INVALID_ARG),
+    (dict(budget_tokens=40), L.LOSA_ERR_INVALID_ARG),
+    (dict(budget_tokens=0), L.LOSA_ERR_INVALID_ARG),
+    (dict(n_active=17), L.LOSA_ERR_INVALID_ARG),
+    (dict(n_active=-1), L.LOSA_ERR_INVALID_ARG),
+    (dict(head_dim=96), L.LOSA_ERR_UNSUPPORTED),
+    (dict(page_size=32, budget_tokens=64), L.LOSA_ERR_UNSUPPORTED),
+    (dict(dtype=7), L.LOSA_ERR_INVALID_ARG),
+    (dict(flags=1), L.LOSA_ERR_INVALID_ARG),
+    (dict(max_prefix_len=2048), L.LOSA_ERR_INVALID_ARG),
+    (dict(softmax_scale=-1.0), L.LOSA_ERR_INVALID_ARG),
+    (dict(kv_tokens=1000), L.LOSA_ERR_INVALID_ARG),
+    (dict(n_seq=0), L.LOSA_ERR_INVALID_ARG),
+    (dict(block=65, n_active=4), L.LOSA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_SHAPES, ids=[str(k) for k, _ in BAD_SHAPES])
+def test_bad_shape_rejected(lib, kw, status):
+    sh = shape_of(W.tiny_f32(), **kw)
+    assert L.workspace_bytes(sh) == 0 and L.page_meta_bytes(sh) == 0
+    assert L.union_capacity(sh) == -1
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    r = lib.losa_step(ctypes.byref(sh), *([fake] * 12), None, fake, 1 << 30, None)
+    assert r == status
+    r = lib.losa_dense_first_step(ctypes.byref(sh), *([fake] * 11), 1 << 30, None)
+    assert r == status
+    r = lib.losa_build_page_meta(ctypes.byref(sh), fake, fake, fake, fake, None)
+    assert r == status
+
+
+def test_pointer_and_workspace_checks(lib):
+    sh = shape_of(W.gqa_16k())
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    need = L.workspace_bytes(sh)
+    args = [fake] * 12
+    # null and misaligned tensors
+    for i in range(12):
+        bad = list(args)
+        bad[i] = None
+        assert lib.losa_step(ctypes.byref(sh), *bad, None, fake, need, None) == L.LOSA_ERR_INVALID_ARG
+        if i not in (7, 8, 10):  # kv_off, prefix_len, lp_cache need only 4-byte alignment
+            bad[i] = odd
+            assert lib.losa_step(ctypes.byref(sh), *bad, None, fake, need, None) == \
+                L.LOSA_ERR_INVALID_ARG
+    assert lib.losa_step(ctypes.byref(sh), *args, None, None, need, None) == L.LOSA_ERR_INVALID_ARG
+    # workspace one byte short
+    assert lib.losa_step(ctypes.byref(sh), *args, None, fake, need - 1, None) == L.LOSA_ERR_WORKSPACE
+    assert lib.losa_dense_first_step(ctypes.byref(sh), *([fake] * 11), need - 1, None) == \
+        L.LOSA_ERR_WORKSPACE
+    # debug union list shorter than the union capacity
+    dbg = L.LosaDebug(None, None, None, fake, None, L.union_capacity(sh) - 1)
+    assert lib.losa_step(ctypes.byref(sh), *args, ctypes.byref(dbg), fake, need, None) == \
+        L.LOSA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    cfg = W.tiny_f32()
+    sh = shape_of(cfg)
+    t = torch.zeros(1 << 16)
+    with pytest.raises(ValueError):
+        L.losa_build_page_meta(sh, t, torch.zeros(1, dtype=torch.int32),
+                               torch.zeros(1, dtype=torch.int32), torch.zeros(16, dtype=torch.uint8))

@@ -1,0 +1,214 @@
+"""HIP path (through the C ABI) against the CPU oracle on seeded inputs.
+
+Indices (locality scores, active sets, per-row pages, unions) must match bit
+for bit; outputs and the (o_p, L_p) cache within the tolerances of
+gpu_support.TOL.  Sizes run from a few pages (several tiles, ragged tails,
+empty prefixes) up to the 64K, ragged-batch and 128K-trace workloads.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_support import Pair, assert_close, host, say
+from sparse_attention_block_amd import binding as L
+from sparse_attention_block_amd import workloads as W
+from sparse_attention_block_amd.build import SELFTEST_LIB
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+
+
+# ---------------------------------------------------------------------------
+# builtins the kernels rely on
+
+def _selftest():
+    lib = ctypes.CDLL(SELFTEST_LIB)
+    lib.losa_selftest_bound_step.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_void_p]
+    lib.losa_selftest_mfma.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 4
+    return lib
+
+
+def test_bound_step_is_round_to_nearest_even_sum():
+    """The page-bound step of the selection kernel, fma(q+, max, acc) then
+    fma(q-, min, acc) on bf16 operands, adds q*max (q >= 0) or q*min (q < 0) to
+    acc with one IEEE round-to-nearest-even (inputs kept to a small exponent
+    spread so that the float64 reference sum is exact)."""
+    say("[bound step] probe")
+    rng = np.random.default_rng(3)
+    n = 1 << 20
+    q = W.round_bf16(rng.standard_normal(n).astype(np.float32) * 2.0 ** rng.integers(-6, 6, n))
+    x = W.round_bf16(rng.standard_normal(n).astype(np.float32))
+    y = W.round_bf16(rng.standard_normal(n).astype(np.float32))
+    acc = (rng.standard_normal(n) * 2.0 ** rng.integers(-8, 8, n)).astype(np.float32)
+    # ties: acc with an odd last bit plus exactly half an ulp
+    m = n // 8
+    acc[:m] = (1.0 + (2 * rng.integers(0, 1 << 10, m) + 1) * 2.0 ** -23).astype(np.float32)
+    q[:m] = 2.0 ** -12
+    x[:m] = 2.0 ** -12 * np.where(rng.random(m) < 0.5, 1.0, -1.0)
+    y[:m] = x[:m]
+    qp = np.where(q >= 0, q, 0).astype(np.float32)
+    qn = np.where(q >= 0, 0, q).astype(np.float32)
+    meta = ((x.view(np.uint32) >> 16) | (y.view(np.uint32) & 0xFFFF0000)).astype(np.uint32)
+    sel = np.where(q >= 0, x, y).astype(np.float64)
+    ref = (acc.astype(np.float64) + q.astype(np.float64) * sel).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a).cuda()
+    tens = [dev(a) for a in (acc, qp, qn, meta)]
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    lib = _selftest()
+    assert lib.losa_selftest_bound_step(*[t.data_ptr() for t in tens], out.data_ptr(), n,
+                                        torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    # compare values (a zero's sign is not part of the ranking key)
+    bad = ~((got == ref) & ~(np.isnan(got)))
+    assert not bad.any(), f"{int(bad.sum())} mismatches, e.g. {np.argwhere(bad)[:3].ravel().tolist()}"
+
+
+@pytest.mark.parametrize("K", [32, 16])
+def test_mfma_lane_layout(K):
+    say(f"[mfma] probe K={K}")
+    rng = np.random.default_rng(K)
+    A = W.round_bf16(rng.standard_normal((16, K)).astype(np.float32))
+    B = W.round_bf16(rng.standard_normal((K, 16)).astype(np.float32))
+    bits = lambda a: torch.from_numpy((a.view(np.uint32) >> 16).astype(np.int16)).cuda()
+    Ad, Bd = bits(A), bits(B)
+    D = torch.zeros(256, dtype=torch.float32, device="cuda")
+    lib = _selftest()
+    assert lib.losa_selftest_mfma(K, Ad.data_ptr(), Bd.data_ptr(), D.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    ref = A.astype(np.float64) @ B.astype(np.float64)
+    np.testing.assert_allclose(D.cpu().numpy().reshape(16, 16), ref, rtol=1e-5, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# small shapes: several tiles, ragged tails, edge cases
+
+SMALL = [
+    # (name, kwargs)
+    ("f32_d64_B16_A4_b64_L1024", dict(dtype="f32", head_dim=64, block=16, n_active=4, budget=64,
+                                     prefix_lens=(1024,))),
+    ("bf16_d128_B16_A4_b64_ragged", dict(dtype="bf16", head_dim=128, block=16, n_active=4,
+                                         budget=64, prefix_lens=(1000, 48, 16, 0), n_kvhead=2,
+                                         n_qhead=8)),
+    ("bf16_d64_B32_A8_b128_L2000", dict(dtype="bf16", head_dim=64, block=32, n_active=8,
+                                        budget=128, prefix_lens=(2000, 333), n_kvhead=2,
+                                        n_qhead=8)),
+    ("bf16_d128_B16_A1_b16", dict(dtype="bf16", head_dim=128, block=16, n_active=1, budget=16,
+                                  prefix_lens=(4096 + 40,), n_kvhead=2, n_qhead=8)),
+    ("bf16_d128_B16_A2_b256", dict(dtype="bf16", head_dim=128, block=16, n_active=2, budget=256,
+                                   prefix_lens=(5000,), n_kvhead=2, n_qhead=8)),
+    ("bf16_d128_B16_AB_bL", dict(dtype="bf16", head_dim=128, block=16, n_active=16, budget=1024,
+                                 prefix_lens=(1024, 700), n_kvhead=2, n_qhead=8)),
+    ("bf16_d128_B32_AB_b64", dict(dtype="bf16", head_dim=128, block=32, n_active=32, budget=64,
+                                  prefix_lens=(3000,), n_kvhead=1, n_qhead=4)),
+    ("bf16_d128_B16_A0", dict(dtype="bf16", head_dim=128, block=16, n_active=0, budget=128,
+                              prefix_lens=(1024,), n_kvhead=2, n_qhead=8, n_drift=3)),
+    ("f32_d128_B32_A8_b256", dict(dtype="f32", head_dim=128, block=32, n_active=8, budget=256,
+                                  prefix_lens=(1500, 48), n_kvhead=2, n_qhead=8)),
+    ("f32_d64_B16_A16_bL", dict(dtype="f32", head_dim=64, block=16, n_active=16, budget=2048,
+                                prefix_lens=(1000,), n_kvhead=1, n_qhead=4)),
+    ("bf16_d64_B16_A4_b64_L16", dict(dtype="bf16", head_dim=64, block=16, n_active=4, budget=64,
+                                     prefix_lens=(16, 48, 0), n_kvhead=1, n_qhead=4)),
+    ("bf16_d128_G8_A4_b128", dict(dtype="bf16", head_dim=128, block=16, n_active=4, budget=128,
+                                  prefix_lens=(9000,), n_kvhead=1, n_qhead=8)),
+    ("bf16_d128_B64_A8_b64", dict(dtype="bf16", head_dim=128, block=64, n_active=8, budget=64,
+                                  prefix_lens=(2048,), n_kvhead=2, n_qhead=4)),
+    ("bf16_d128_seq_offsets", dict(dtype="bf16", head_dim=128, block=16, n_active=3, budget=48,
+                                   prefix_lens=(1040, 17, 2064, 999, 1), n_kvhead=2, n_qhead=4,
+                                   needles=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[n for n, _ in SMALL])
+def test_small_trace(name, kw):
+    kw = dict(kw)
+    cid = 200 + [n for n, _ in SMALL].index(name)
+    cfg = W.small_case(cid, n_steps=3, **kw)
+    lay = W.make_layer(cfg)
+    p = Pair(lay, name)
+    p.dense(0)
+    for step in (1, 2):
+        p.sparse(step)
+
+
+def test_tiny_f32_workload():
+    cfg = W.tiny_f32()
+    p = Pair(W.make_layer(cfg), cfg.name)
+    p.dense(0)
+    r = p.sparse(1)
+    # the drifting tokens are the active ones in every head
+    for h in range(cfg.n_qhead):
+        assert r["res"]["active"][0, h].tolist() == p.lay.drift_tokens[1][0].tolist()
+
+
+def test_gqa_16k_workload():
+    cfg = W.gqa_16k()
+    p = Pair(W.make_layer(cfg), cfg.name)
+    p.dense(0)
+    for step in range(1, cfg.n_steps):
+        p.sparse(step)
+
+
+def test_determinism_and_lost_cache_recovery():
+    cfg = W.gqa_16k().replace(prefix_lens=(4096,), cfg_id=77, name="det")
+    p = Pair(W.make_layer(cfg, n_steps=3), "determinism")
+    p.dense(0)
+    op0, lp0 = p.gpu.op_cache.clone(), p.gpu.lp_cache.clone()
+    a = p.gpu.step(p.q[1], p.q[0], p.kb[1], p.vb[1]).clone()
+    op1 = p.gpu.op_cache.clone()
+    p.gpu.op_cache.copy_(op0)
+    p.gpu.lp_cache.copy_(lp0)
+    b = p.gpu.step(p.q[1], p.q[0], p.kb[1], p.vb[1]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(op1, p.gpu.op_cache)
+    # lose the cache, recover with one dense pass
+    p.gpu.op_cache.zero_()
+    p.gpu.lp_cache.fill_(float("-inf"))
+    p.dense(0)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (the long-context configuration the benchmark times)
+
+@pytest.mark.parametrize("budget,n_active", [(128, 4), (256, 8), (128, 2)])
+def test_long_64k(budget, n_active):
+    cfg = W.long_64k(budget, n_active)
+    lay = W.make_layer(cfg, n_steps=4)
+    p = Pair(lay, cfg.name)
+    p.dense(0, sample_rows=12)
+    op, lp = W.make_cache_state(cfg)
+    p.set_cache(op, lp)
+    for step in (1, 2, 3):
+        p.sparse(step)
+
+
+def test_ragged_batch():
+    cfg = W.ragged_batch()
+    lay = W.make_layer(cfg, n_steps=3)
+    p = Pair(lay, cfg.name)
+    p.dense(0, sample_rows=12)
+    op, lp = W.make_cache_state(cfg)
+    p.set_cache(op, lp)
+    for step in (1, 2):
+        p.sparse(step)
+
+
+@pytest.mark.parametrize("layer", [0, 4, 20, 35])
+def test_trace_128k_layer(layer):
+    cfg = W.trace_128k(layer)
+    lay = W.make_layer(cfg, layer=layer, n_steps=2)
+    p = Pair(lay, cfg.name)
+    p.dense(0, sample_rows=6)
+    op, lp = W.make_cache_state(cfg, layer)
+    p.set_cache(op, lp)
+    p.sparse(1)
