@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of LoSA per-denoising-step attention on one MI355X.
+
+Workload: the long-context layer shape (prefix L = 65536 tokens, block B = 16,
+32 query / 8 KV heads, head_dim 128, bf16, budget 128 tokens, |A| = 4, needle
+pages, 8 denoising steps per block).  One bench step = one block: a forced
+dense first step and 7 LoSA steps, for each of --layers independent layers
+run in model order (step-major, layer-minor), so a layer's metadata and KV are
+not re-read from the on-die cache between its steps (16 layers x ~24 MiB of
+sparse-step traffic exceed the 256 MB MALL).  The page metadata of the fixed
+prefix is built before timing (it changes once per committed block).
+
+Prints one JSON line: value = attention microseconds per (layer, denoising
+step), amortised over the block (dense first step included); plus per-kernel
+durations from HIP events the library records between its launches inside the
+timed region, the roofline of the dominant kernel, and the CPU oracle timed on
+one layer-block of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention us per block-step + HBM GB/s, 64K ctx, B=16, budget 128"
+PEAK_HBM_GBPS = 8000.0
+STEPS_PER_BLOCK = 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        self.hip = ctypes.CDLL(path or "libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.made = []
+
+    # timing-only events: no system-scope fence (cache writeback/invalidate) on record
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE) == 0
+        self.made.append(ev.value)
+        return ev.value
+
+    def record(self, ev: int, stream: int):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
+
+    def ms(self, e0: int, e1: int) -> float:
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(e0),
+                                            ctypes.c_void_p(e1)) == 0
+        return float(out.value)
+
+    def destroy_all(self):
+        for ev in self.made:
+            self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+        self.made = []
+
+
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_attention_block_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_tag: str, digest: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken
+    on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel_tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, lay):
+    """The oracle, as it stands, on one layer-block of the same workload."""
+    from oracle import Oracle
+
+    orc = Oracle(cfg, lay.kv_off, lay.prefix_len, lay.kv_tokens, lay.k_cache, lay.v_cache)
+    orc.page_meta()
+    t0 = time.perf_counter()
+    orc.dense_first_step(lay.q[0], lay.k_blk[0], lay.v_blk[0])
+    for t in range(1, STEPS_PER_BLOCK):
+        orc.step(lay.q[t], lay.q[t - 1], lay.k_blk[t], lay.v_blk[t])
+    sec = time.perf_counter() - t0
+    return {"value": sec * 1e6 / STEPS_PER_BLOCK, "unit": "us per block-step", "cores": 1,
+            "kind": "oracle",
+            "sample": f"one layer, one {STEPS_PER_BLOCK}-step block (1 dense + "
+                      f"{STEPS_PER_BLOCK - 1} LoSA steps) of the same 64K workload, single thread, "
+                      f"{sec:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5, help="timed blocks")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed blocks")
+    ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--budget", type=int, default=128)
+    ap.add_argument("--active", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-events", action="store_true",
+                    help="time without the per-kernel stage events")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the LoSA step is measured on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_attention_block_amd import binding as L
+    from sparse_attention_block_amd import workloads as W
+    from sparse_attention_block_amd.layer import LayerState, to_device
+
+    L.load()
+    torch.cuda.set_device(0)
+    cfg = W.long_64k(args.budget, args.active)
+    log(f"[bench] generating {cfg.name}")
+    lay = W.make_layer(cfg, n_steps=STEPS_PER_BLOCK)
+    dev = lambda x: to_device(x, cfg.dtype)
+    base = LayerState.from_layer(lay)
+    layers = [base]
+    for _ in range(args.layers - 1):
+        layers.append(LayerState(n_seq=cfg.n_seq, block=cfg.block, n_qhead=cfg.n_qhead,
+                                 n_kvhead=cfg.n_kvhead, head_dim=cfg.head_dim,
+                                 budget_tokens=cfg.budget, n_active=cfg.n_active, dtype=cfg.dtype,
+                                 k_cache=base.k_cache.clone(), v_cache=base.v_cache.clone(),
+                                 kv_off=lay.kv_off, prefix_len=lay.prefix_len))
+    for ls in layers:
+        ls.build_page_meta()
+    q = [dev(x) for x in lay.q]
+    kb = [dev(x) for x in lay.k_blk]
+    vb = [dev(x) for x in lay.v_blk]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = HipEvents()
+
+    # union sizes of every LoSA step (identical across the replicated layers)
+    union_cnt = []
+    dbg = L.Debug.alloc(base.shape)
+    base.dense_first_step(q[0], kb[0], vb[0])
+    for t in range(1, STEPS_PER_BLOCK):
+        base.step(q[t], q[t - 1], kb[t], vb[t], debug=dbg)
+        torch.cuda.synchronize()
+        union_cnt.append(dbg.union_cnt.cpu().numpy().copy())
+    union_pages = np.array([u.sum() for u in union_cnt], dtype=np.float64)  # per step, all KV heads
+
+    # one prepared call per (step, layer): checks and marshalling happen here, once
+    calls = {}
+    for t in range(STEPS_PER_BLOCK):
+        for li, ls in enumerate(layers):
+            calls[(t, li)] = (ls.prepare_dense_first_step(q[0], kb[0], vb[0]) if t == 0 else
+                              ls.prepare_step(q[t], q[t - 1], kb[t], vb[t]))
+
+    def run_block(events):
+        """One block for every layer; events[(t, l)] = stage events or None."""
+        for t in range(STEPS_PER_BLOCK):
+            for li in range(len(layers)):
+                c = calls[(t, li)]
+                c.set_events(events[(t, li)] if events is not None else None)
+                c()
+
+    def new_events():
+        return {(t, li): [hip.create() for _ in range(L.LOSA_STAGE_EVENTS)]
+                for t in range(STEPS_PER_BLOCK) for li in range(len(layers))}
+
+    log(f"[bench] warmup {args.warmup} blocks x {len(layers)} layers")
+    for _ in range(args.warmup):
+        run_block(None)
+    torch.cuda.synchronize()
+
+    use_events = not args.no_events
+    ev_blocks = [new_events() for _ in range(args.steps)] if use_events else None
+    e_start, e_stop = hip.create(), hip.create()
+    log(f"[bench] timing {args.steps} blocks")
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    hip.record(e_start, stream)
+    for k in range(args.steps):
+        run_block(ev_blocks[k] if use_events else None)
+    hip.record(e_stop, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = hip.ms(e_start, e_stop)
+
+    n_calls = args.steps * STEPS_PER_BLOCK * len(layers)
+    value_us = total_ms * 1e3 / n_calls
+    ms_per_step = total_ms / args.steps
+
+    # per-stage durations from the library's events
+    stages = {"dense": {"prepare": [], "prefix": [], "finish": [], "total": []},
+              "sparse": {"prepare": [], "select": [], "prefix": [], "finish": [], "total": []}}
+    if use_events:
+        for evs in ev_blocks:
+            for (t, li), e in evs.items():
+                d = [hip.ms(e[i], e[i + 1]) * 1e3 for i in range(4)]
+                tot = hip.ms(e[0], e[4]) * 1e3
+                if t == 0:
+                    stages["dense"]["prepare"].append(d[0])
+                    stages["dense"]["prefix"].append(d[2])
+                    stages["dense"]["finish"].append(d[3])
+                    stages["dense"]["total"].append(tot)
+                else:
+                    stages["sparse"]["prepare"].append(d[0])
+                    stages["sparse"]["select"].append(d[1])
+                    stages["sparse"]["prefix"].append(d[2])
+                    stages["sparse"]["finish"].append(d[3])
+                    stages["sparse"]["total"].append(tot)
+    mean = lambda xs: float(np.mean(xs)) if xs else None
+
+    # algorithmic bytes (bf16 storage)
+    sT = 2
+    Hk, d, P, L_ = cfg.n_kvhead, cfg.head_dim, cfg.page_size, cfg.prefix_lens[0]
+    n_pages = (L_ + P - 1) // P
+    kv_page_bytes = P * d * 2 * sT
+    union_bytes = float(union_pages.mean()) * kv_page_bytes
+    meta_bytes = Hk * n_pages * 2 * d * sT
+    dense_kv_bytes = Hk * L_ * 2 * d * sT
+    S, B, Hq = cfg.n_seq, cfg.block, cfg.n_qhead
+    small_bytes = (2 * S * B * Hq * d * sT + 2 * S * B * Hk * d * sT + S * Hq * B * (d + 1) * 4
+                   + S * Hq * cfg.n_active * (d + 1) * 4 + S * B * Hq * d * sT)
+    sparse_step_bytes = meta_bytes + union_bytes + small_bytes
+    dense_step_bytes = dense_kv_bytes + 2 * S * B * Hq * d * sT + 2 * S * B * Hk * d * sT \
+        + S * Hq * B * (d + 1) * 4
+    block_bytes = dense_step_bytes + (STEPS_PER_BLOCK - 1) * sparse_step_bytes
+    hbm_gbps = block_bytes / (value_us * STEPS_PER_BLOCK * 1e-6) / 1e9
+
+    kernels = {}
+    if use_events:
+        spec = {
+            "sparse_prefix": (stages["sparse"]["prefix"], union_bytes, STEPS_PER_BLOCK - 1),
+            "page_select": (stages["sparse"]["select"], meta_bytes, STEPS_PER_BLOCK - 1),
+            "dense_prefix": (stages["dense"]["prefix"], dense_kv_bytes, 1),
+            "sparse_prepare": (stages["sparse"]["prepare"], 0, STEPS_PER_BLOCK - 1),
+            "sparse_finish": (stages["sparse"]["finish"], 0, STEPS_PER_BLOCK - 1),
+            "dense_prepare": (stages["dense"]["prepare"], 0, 1),
+            "dense_finish": (stages["dense"]["finish"], 0, 1),
+        }
+        for name, (xs, nbytes, per_block) in spec.items():
+            us = mean(xs)
+            kernels[name] = {"avg_us": us, "launches_per_layer_block": per_block,
+                             "us_per_layer_block": us * per_block if us else None}
+            if nbytes:
+                gbps = nbytes / (us * 1e-6) / 1e9
+                kernels[name].update({"bytes_per_launch": nbytes, "achieved_gbps": gbps,
+                                      "frac_of_peak": gbps / PEAK_HBM_GBPS})
+    dominant = max((k for k in kernels if "bytes_per_launch" in kernels[k]),
+                   key=lambda k: kernels[k]["us_per_layer_block"], default=None)
+    digests = {"sparse_prefix": source_digest("prefix.hip"), "dense_prefix": source_digest("prefix.hip"),
+               "page_select": source_digest("select.hip")}
+
+    def roofline(name):
+        if name is None:
+            return None
+        k = kernels[name]
+        return {"kernel": name, "bound": "hbm", "achieved": k["achieved_gbps"],
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k["frac_of_peak"],
+                "traffic": traffic_from_profile(name, digests[name]),
+                "bytes_per_launch": k["bytes_per_launch"], "avg_launch_us": k["avg_us"]}
+
+    sparse_us = mean(stages["sparse"]["total"]) if use_events else None
+    dense_us = mean(stages["dense"]["total"]) if use_events else None
+    rec = {
+        "metric": METRIC,
+        "value": value_us,
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "prefix_len": L_, "block": B, "n_qhead": Hq,
+                   "n_kvhead": Hk, "head_dim": d, "page_size": P, "budget_tokens": cfg.budget,
+                   "n_active": cfg.n_active, "steps_per_block": STEPS_PER_BLOCK,
+                   "layers": len(layers), "step": "one block of 8 denoising steps "
+                   "(1 dense + 7 LoSA) for every layer"},
+        "hbm_gbps": hbm_gbps,
+        "sparse_step_us": sparse_us,
+        "dense_step_us": dense_us,
+        "speedup_vs_dense": (dense_us / sparse_us) if (sparse_us and dense_us) else None,
+        "union_pages_per_kv_head": float(union_pages.mean()) / (cfg.n_seq * Hk),
+        "density": float(union_pages.mean()) / (cfg.n_seq * Hk * n_pages),
+        "roofline": roofline(dominant),
+        "roofline_sparse_prefix": roofline("sparse_prefix") if use_events else None,
+        "kernels": kernels,
+        "wall_s": wall,
+    }
+    hip.destroy_all()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on one layer-block")
+        rec["cpu_baseline"] = cpu_baseline(cfg, lay)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

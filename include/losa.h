@@ -109,7 +109,11 @@ typedef struct losa_shape {
     uint32_t flags;         /* must be 0 */
 } losa_shape;
 
-/* Optional device outputs of losa_step (each pointer may be NULL). */
+/* Number of events in losa_debug.stage_events. */
+#define LOSA_STAGE_EVENTS 5
+
+/* Optional outputs of losa_step / losa_dense_first_step (each pointer may be
+ * NULL; the dense call uses only stage_events). */
 typedef struct losa_debug {
     float *locality;     /* [n_seq][n_qhead][B] locality score e/d */
     int32_t *active;     /* [n_seq][n_qhead][n_active] active tokens, ascending */
@@ -118,6 +122,11 @@ typedef struct losa_debug {
     int32_t *union_idx;  /* [n_seq][n_kvhead][union_cap] union of a KV head's pages, ascending */
     int32_t *union_cnt;  /* [n_seq][n_kvhead] union sizes */
     int32_t union_cap;   /* capacity of each union_idx row; >= losa_union_capacity() */
+    void **stage_events; /* profiling: LOSA_STAGE_EVENTS caller-created hipEvent_t, recorded
+                            on the stream before the first kernel (0) and after the
+                            prepare (1), page-selection (2), prefix-attention (3) and
+                            finishing (4) kernels; a skipped stage records at the same
+                            point as the one before it */
 } losa_debug;
 
 /* Human-readable name of a status code (static string). */
@@ -153,8 +162,8 @@ int losa_build_page_meta(const losa_shape *shape, const void *k_cache, const int
 int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *k_blk,
                           const void *v_blk, const void *k_cache, const void *v_cache,
                           const int32_t *kv_off, const int32_t *prefix_len, float *op_cache,
-                          float *lp_cache, void *out, void *workspace, size_t workspace_bytes,
-                          void *stream);
+                          float *lp_cache, void *out, const losa_debug *debug, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /*
  * One LoSA step (steps 1-8 above).  q_prev is the previous step's q_t.  Only

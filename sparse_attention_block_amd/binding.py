@@ -46,7 +46,11 @@ class LosaDebug(ctypes.Structure):
     _fields_ = [
         ("locality", c_void_p), ("active", c_void_p), ("page_sel", c_void_p),
         ("union_idx", c_void_p), ("union_cnt", c_void_p), ("union_cap", c_int32),
+        ("stage_events", POINTER(c_void_p)),
     ]
+
+
+LOSA_STAGE_EVENTS = 5
 
 
 _lib = None
@@ -71,7 +75,8 @@ def load(path: str = LIB_PATH):
     lib.losa_union_capacity.restype = c_int32
     lib.losa_build_page_meta.argtypes = [S, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.losa_build_page_meta.restype = c_int
-    lib.losa_dense_first_step.argtypes = [S] + [c_void_p] * 11 + [c_size_t, c_void_p]
+    lib.losa_dense_first_step.argtypes = [S] + [c_void_p] * 10 + [POINTER(LosaDebug), c_void_p,
+                                                                   c_size_t, c_void_p]
     lib.losa_dense_first_step.restype = c_int
     lib.losa_step.argtypes = [S] + [c_void_p] * 12 + [POINTER(LosaDebug), c_void_p, c_size_t,
                                                        c_void_p]
@@ -168,7 +173,7 @@ def losa_build_page_meta(shape, k_cache, kv_off, prefix_len, page_meta, stream=N
 
 
 def losa_dense_first_step(shape, q_t, k_blk, v_blk, k_cache, v_cache, kv_off, prefix_len,
-                          op_cache, lp_cache, out, workspace, stream=None):
+                          op_cache, lp_cache, out, workspace, debug=None, stream=None):
     n, dt = _sizes(shape), _torch_dtype(shape)
     ws_need = workspace_bytes(shape)
     args = [
@@ -180,9 +185,10 @@ def losa_dense_first_step(shape, q_t, k_blk, v_blk, k_cache, v_cache, kv_off, pr
         _check(op_cache, "op_cache", torch.float32, n["op"]),
         _check(lp_cache, "lp_cache", torch.float32, n["lp"]),
         _check(out, "out", dt, n["q"]),
-        _check(workspace, "workspace", torch.uint8, ws_need),
     ]
-    _raise(load().losa_dense_first_step(ctypes.byref(shape), *args, workspace.numel(),
+    dbg = ctypes.byref(debug.struct(shape)) if debug is not None else None
+    ws = _check(workspace, "workspace", torch.uint8, ws_need)
+    _raise(load().losa_dense_first_step(ctypes.byref(shape), *args, dbg, ws, workspace.numel(),
                                         _stream(stream)), "losa_dense_first_step")
 
 
@@ -195,6 +201,7 @@ class Debug:
     page_sel: Optional[torch.Tensor] = None
     union_idx: Optional[torch.Tensor] = None
     union_cnt: Optional[torch.Tensor] = None
+    stage_events: Optional[list] = None   # LOSA_STAGE_EVENTS raw hipEvent_t handles (ints)
 
     @staticmethod
     def alloc(shape: LosaShape, device="cuda") -> "Debug":
@@ -212,13 +219,19 @@ class Debug:
         S, B, Hq, Hk, A = shape.n_seq, shape.block, shape.n_qhead, shape.n_kvhead, shape.n_active
         k = shape.budget_tokens // shape.page_size
         cap = self.union_idx.shape[-1] if self.union_idx is not None else 0
+        ev = None
+        if self.stage_events is not None:
+            if len(self.stage_events) != LOSA_STAGE_EVENTS:
+                raise ValueError(f"stage_events needs {LOSA_STAGE_EVENTS} events")
+            self._ev_array = (c_void_p * LOSA_STAGE_EVENTS)(*self.stage_events)
+            ev = ctypes.cast(self._ev_array, POINTER(c_void_p))
         return LosaDebug(
             _check(self.locality, "debug.locality", torch.float32, S * Hq * B, True),
             _check(self.active, "debug.active", torch.int32, S * Hq * A, True),
             _check(self.page_sel, "debug.page_sel", torch.int32, S * Hq * A * k, True),
             _check(self.union_idx, "debug.union_idx", torch.int32, S * Hk * cap, True),
             _check(self.union_cnt, "debug.union_cnt", torch.int32, S * Hk, True),
-            cap)
+            cap, ev)
 
 
 def losa_step(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off, prefix_len,
@@ -240,3 +253,75 @@ def losa_step(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_
     ws = _check(workspace, "workspace", torch.uint8, ws_need)
     _raise(load().losa_step(ctypes.byref(shape), *args, dbg, ws, workspace.numel(),
                             _stream(stream)), "losa_step")
+
+
+# ---------------------------------------------------------------------------
+# prepared calls: checks and marshalling done once, then a bare C call
+
+class PreparedCall:
+    """A call of one entry point with fixed, already checked arguments.
+
+    ``set_events`` swaps the profiling events recorded between the library's
+    launches (a list of LOSA_STAGE_EVENTS raw hipEvent_t handles, or None)."""
+
+    def __init__(self, fn, head, dbg: LosaDebug, tail, what: str):
+        self._fn, self._head, self._dbg, self._tail, self._what = fn, head, dbg, tail, what
+        self._args = (*head, ctypes.byref(dbg), *tail)
+        self._ev = None
+
+    def set_events(self, events):
+        if events is None:
+            self._dbg.stage_events = None
+            self._ev = None
+        else:
+            self._ev = (c_void_p * LOSA_STAGE_EVENTS)(*events)
+            self._dbg.stage_events = ctypes.cast(self._ev, POINTER(c_void_p))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != LOSA_OK:
+            raise LosaError(st, self._what)
+
+
+def prepare_dense_first_step(shape, q_t, k_blk, v_blk, k_cache, v_cache, kv_off, prefix_len,
+                             op_cache, lp_cache, out, workspace, stream=None) -> PreparedCall:
+    n, dt = _sizes(shape), _torch_dtype(shape)
+    head = [ctypes.byref(shape),
+            _check(q_t, "q_t", dt, n["q"]), _check(k_blk, "k_blk", dt, n["blk"]),
+            _check(v_blk, "v_blk", dt, n["blk"]), _check(k_cache, "k_cache", dt, n["cache"]),
+            _check(v_cache, "v_cache", dt, n["cache"]),
+            _check(kv_off, "kv_off", torch.int32, shape.n_seq),
+            _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+            _check(op_cache, "op_cache", torch.float32, n["op"]),
+            _check(lp_cache, "lp_cache", torch.float32, n["lp"]),
+            _check(out, "out", dt, n["q"])]
+    tail = [_check(workspace, "workspace", torch.uint8, workspace_bytes(shape)),
+            c_size_t(workspace.numel()), _stream(stream)]
+    keep = (q_t, k_blk, v_blk, k_cache, v_cache, kv_off, prefix_len, op_cache, lp_cache, out,
+            workspace)
+    call = PreparedCall(load().losa_dense_first_step, head, LosaDebug(), tail,
+                        "losa_dense_first_step")
+    call._keep = keep
+    return call
+
+
+def prepare_step(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off,
+                 prefix_len, op_cache, lp_cache, out, workspace, stream=None) -> PreparedCall:
+    n, dt = _sizes(shape), _torch_dtype(shape)
+    head = [ctypes.byref(shape),
+            _check(q_t, "q_t", dt, n["q"]), _check(q_prev, "q_prev", dt, n["q"]),
+            _check(k_blk, "k_blk", dt, n["blk"]), _check(v_blk, "v_blk", dt, n["blk"]),
+            _check(k_cache, "k_cache", dt, n["cache"]), _check(v_cache, "v_cache", dt, n["cache"]),
+            _check(page_meta, "page_meta", torch.uint8, page_meta_bytes(shape)),
+            _check(kv_off, "kv_off", torch.int32, shape.n_seq),
+            _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+            _check(op_cache, "op_cache", torch.float32, n["op"]),
+            _check(lp_cache, "lp_cache", torch.float32, n["lp"]),
+            _check(out, "out", dt, n["q"])]
+    tail = [_check(workspace, "workspace", torch.uint8, workspace_bytes(shape)),
+            c_size_t(workspace.numel()), _stream(stream)]
+    keep = (q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off, prefix_len, op_cache,
+            lp_cache, out, workspace)
+    call = PreparedCall(load().losa_step, head, LosaDebug(), tail, "losa_step")
+    call._keep = keep
+    return call

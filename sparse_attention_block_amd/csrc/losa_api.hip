@@ -41,6 +41,11 @@ int check_shape(const losa_shape *sh) {
     return LOSA_OK;
 }
 
+size_t meta_main_bytes(const Dims &D) {
+    const size_t sT = D.bf16 ? 2 : 4;
+    return (size_t)D.Hk * D.n_tiles_total * kTile * D.d * 2 * sT;
+}
+
 Dims make_dims(const losa_shape *sh) {
     Dims D;
     D.S = sh->n_seq;
@@ -53,11 +58,13 @@ Dims make_dims(const losa_shape *sh) {
     D.k = sh->budget_tokens / kPage;
     D.bf16 = sh->dtype == LOSA_BF16;
     D.max_pages = (sh->max_prefix_len + kPage - 1) / kPage;
+    D.hb_stride = (std::max(D.max_pages, 1) + 3) / 4 * 4;
     D.T = sh->kv_tokens;
     D.n_tiles_total = (D.T / kPage + kTile - 1) / kTile;
+    D.meta_main_bytes = static_cast<int64_t>(meta_main_bytes(D));
     D.n_tiles_grid = (D.max_pages + kTile - 1) / kTile + 1;
-    D.kk = D.k < kTile ? D.k : kTile;
     D.R = D.G * D.A;
+    D.Rs16 = (D.R + 15) / 16 * 16;
     D.Rd = D.G * D.B;
     D.R16 = (D.Rd + 15) / 16 * 16;
     const int64_t rk = (int64_t)D.R * D.k;
@@ -89,8 +96,12 @@ size_t carve(const Dims &D, char *base, Work *W) {
     w.counters = reinterpret_cast<int32_t *>(take(SG * 4));
     w.active = reinterpret_cast<int32_t *>(take((size_t)D.S * D.Hq * A1 * 4));
     w.qrows = take(SG * D.R16 * D.d * sT);
-    w.qsel = reinterpret_cast<float *>(take(SG * R1 * D.d * 8));
-    w.cand = reinterpret_cast<uint64_t *>(take(SG * R1 * D.n_tiles_grid * D.kk * 8));
+    w.qsel16 = reinterpret_cast<uint32_t *>(take(SG * D.Rs16 * D.d * 4));
+    w.qsel32 = reinterpret_cast<float *>(take(SG * R1 * D.d * 8));
+    w.qabs = reinterpret_cast<float *>(take(SG * R1 * 4));
+    w.hbound = reinterpret_cast<float *>(take(SG * R1 * D.hb_stride * 4));
+    w.tmax = reinterpret_cast<float *>(take(SG * R1 * D.n_tiles_grid * 4));
+    w.psel = reinterpret_cast<int32_t *>(take(SG * R1 * D.k * 4));
     w.union_idx = reinterpret_cast<int32_t *>(take(SG * D.union_cap * 4));
     w.union_cnt = reinterpret_cast<int32_t *>(take(SG * 4));
     w.part_acc = reinterpret_cast<float *>(take(SG * part_rows * D.d * 4));
@@ -100,11 +111,16 @@ size_t carve(const Dims &D, char *base, Work *W) {
 }
 
 size_t meta_bytes(const Dims &D) {
-    const size_t sT = D.bf16 ? 2 : 4;
-    return (size_t)D.Hk * D.n_tiles_total * kTile * D.d * 2 * sT;
+    return meta_main_bytes(D) + (size_t)D.Hk * D.n_tiles_total * kTile * 4;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LOSA_OK : LOSA_ERR_HIP; }
+
+// Profiling hook: record the caller's stage event i, if any.
+hipError_t mark(void **events, int i, hipStream_t s) {
+    if (!events || !events[i]) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+}
 
 }  // namespace
 
@@ -152,8 +168,8 @@ int losa_build_page_meta(const losa_shape *shape, const void *k_cache, const int
 int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *k_blk,
                           const void *v_blk, const void *k_cache, const void *v_cache,
                           const int32_t *kv_off, const int32_t *prefix_len, float *op_cache,
-                          float *lp_cache, void *out, void *workspace, size_t workspace_bytes,
-                          void *stream) {
+                          float *lp_cache, void *out, const losa_debug *debug, void *workspace,
+                          size_t workspace_bytes, void *stream) {
     int st = check_shape(shape);
     if (st != LOSA_OK) return st;
     const void *p16[] = {q_t, k_blk, v_blk, k_cache, v_cache, op_cache, out, workspace};
@@ -167,11 +183,17 @@ int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *
     const size_t need = carve(D, static_cast<char *>(workspace), &W);
     if (workspace_bytes < need) return LOSA_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_prepare(D, true, q_t, nullptr, W, nullptr, nullptr, nullptr, s);
+    void **ev = debug ? debug->stage_events : nullptr;
+    hipError_t e = mark(ev, 0, s);
+    if (e == hipSuccess) e = launch_prepare(D, true, q_t, nullptr, W, nullptr, nullptr, nullptr, s);
+    if (e == hipSuccess) e = mark(ev, 1, s);
+    if (e == hipSuccess) e = mark(ev, 2, s);
     if (e == hipSuccess) e = launch_prefix(D, true, k_cache, v_cache, kv_off, prefix_len, W, s);
+    if (e == hipSuccess) e = mark(ev, 3, s);
     if (e == hipSuccess)
         e = launch_finish(D, true, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache,
                           out, s);
+    if (e == hipSuccess) e = mark(ev, 4, s);
     return hip_status(e);
 }
 
@@ -202,19 +224,25 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
     Work W;
     const size_t need = carve(D, static_cast<char *>(workspace), &W);
     if (workspace_bytes < need) return LOSA_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     if (D.R > 0 && select_lds_bytes(D) > 60 * 1024) return LOSA_ERR_UNSUPPORTED;
-    hipError_t e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active,
-                                  dbg.union_cnt, s);
-    if (D.R > 0) {
-        if (e == hipSuccess)
-            e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, dbg.union_idx,
-                              dbg.union_cnt, dbg.union_cap, s);
-        if (e == hipSuccess) e = launch_prefix(D, false, k_cache, v_cache, kv_off, prefix_len, W, s);
-    }
+    if (D.R > 0 && D.k > kMaxK && D.k < D.max_pages) return LOSA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void **ev = dbg.stage_events;
+    hipError_t e = mark(ev, 0, s);
+    if (e == hipSuccess)
+        e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active, dbg.union_cnt, s);
+    if (e == hipSuccess) e = mark(ev, 1, s);
+    if (D.R > 0 && e == hipSuccess)
+        e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, dbg.union_idx,
+                          dbg.union_cnt, dbg.union_cap, s);
+    if (e == hipSuccess) e = mark(ev, 2, s);
+    if (D.R > 0 && e == hipSuccess)
+        e = launch_prefix(D, false, k_cache, v_cache, kv_off, prefix_len, W, s);
+    if (e == hipSuccess) e = mark(ev, 3, s);
     if (e == hipSuccess)
         e = launch_finish(D, false, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache,
                           out, s);
+    if (e == hipSuccess) e = mark(ev, 4, s);
     return hip_status(e);
 }
 

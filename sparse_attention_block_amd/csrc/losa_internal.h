@@ -9,23 +9,32 @@
 
 namespace losa {
 
-constexpr int kPage = 16;        // tokens per page
-constexpr int kTile = 64;        // pages per metadata tile: one page per lane of a wave
-constexpr int kSparseChunk = 8;  // union pages per prefix workgroup (sparse step)
-constexpr int kDenseChunk = 32;  // prefix pages per prefix workgroup (dense first step)
-constexpr int kMaxRows = 256;    // G * B stacked rows per KV head at most
+constexpr int kPage = 16;         // tokens per page
+constexpr int kTile = 64;         // pages per metadata tile: one page per lane of a wave
+constexpr int kSparseChunk = 4;   // union pages per prefix workgroup (sparse step): 1 per wave
+constexpr int kDenseChunk = 64;   // prefix pages per prefix workgroup (dense first step)
+constexpr int kMaxRows = 256;     // G * B stacked rows per KV head at most
+constexpr int kMaxK = 64;         // pages per row the exact selection keeps in one register
+
+// Relative error bound between the MFMA-accumulated page bound and the exact
+// fp32 chain (both sides together), and an absolute floor for flushed
+// subnormal products: |U_mfma - U_chain| <= kBoundRel * sum_i |q_i| * max|k| + kBoundAbs.
+constexpr float kBoundRel = 1.0f / 4096.0f;
+constexpr float kBoundAbs = 1.0e-30f;
 
 // Everything a kernel needs to know about the problem, by value.
 struct Dims {
     int S, B, Hq, Hk, G, d, A, k;     // k = budget pages per row
     int bf16;                         // 1: bf16 storage, 0: fp32
     int max_pages;                    // pages of the longest prefix
+    int hb_stride;                    // row stride of the upper-bound buffer (max_pages, 4-aligned)
     int64_t T;                        // kv_tokens
     int64_t n_tiles_total;            // metadata tiles per KV head over the whole cache
-    int n_tiles_grid;                 // tiles a sequence can touch (grid x of selection)
-    int kk;                           // candidates kept per (tile, row) = min(k, 64)
+    int64_t meta_main_bytes;          // bytes of the min/max part of the page metadata
+    int n_tiles_grid;                 // tiles a sequence can touch
     int union_cap;                    // min(max_pages, G*A*k)
     int R;                            // stacked active rows per KV head = G*A
+    int Rs16;                         // R rounded up to 16 (selection MFMA row tiles)
     int Rd;                           // stacked dense rows per KV head = G*B
     int R16;                          // Rd rounded up to 16
     int n_chunks_sparse, n_chunks_dense;
@@ -34,11 +43,15 @@ struct Dims {
 
 // Device views into the workspace (all carved from one caller buffer).
 struct Work {
-    int32_t *counters;   // [S][Hk] arrival counters of the selection kernel
+    int32_t *counters;   // [S][Hk] arrival counters
     int32_t *active;     // [S][Hq][max(A,1)]
-    void *qrows;         // [S][Hk][R16][d] storage type: stacked query rows
-    float *qsel;         // [S][Hk][max(R,1)][d][2] (max(q,0), min(q,0)) selection operands
-    uint64_t *cand;      // [S][Hk][R][n_tiles_grid][kk] tile candidates
+    void *qrows;         // [S][Hk][R16][d] storage type: stacked query rows (attention)
+    uint32_t *qsel16;    // [S][Hk][Rs16][d] bf16 pairs (max(q,0) | min(q,0) << 16): MFMA operand
+    float *qsel32;       // [S][Hk][max(R,1)][d][2] fp32 (max(q,0), min(q,0)): exact chain operand
+    float *qabs;         // [S][Hk][max(R,1)] upper bound of sum_i |q_i|
+    float *hbound;       // [S][Hk][max(R,1)][hb_stride] upper bound of each page's exact bound
+    float *tmax;         // [S][Hk][max(R,1)][n_tiles_grid] per tile: max lower bound
+    int32_t *psel;       // [S][Hk][max(R,1)][k] each active row's selected pages
     int32_t *union_idx;  // [S][Hk][union_cap]
     int32_t *union_cnt;  // [S][Hk]
     float *part_acc;     // [S][Hk][n_chunks][rows][d]
@@ -55,7 +68,7 @@ hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
                          const int32_t *prefix_len, const Work &W, int32_t *dbg_page_sel,
                          int32_t *dbg_union_idx, int32_t *dbg_union_cnt, int dbg_union_cap,
                          hipStream_t st);
-size_t select_lds_bytes(const Dims &D);  // dynamic LDS of the selection kernel
+size_t select_lds_bytes(const Dims &D);  // dynamic LDS of the exact-selection kernel
 hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const void *v_cache,
                          const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
                          hipStream_t st);

@@ -10,6 +10,10 @@
 // one chunk with one fully coalesced 1 KiB load:
 //   bf16: chunk = 4 dimensions, one dword per dimension = (max | min << 16)
 //   fp32: chunk = 2 dimensions, (max_0, min_0, max_1, min_1)
+// That chunk is also exactly the B operand a lane supplies to
+// v_mfma_f32_16x16x32_bf16 for 8 consecutive k-slots (max_i, min_i pairs).
+// After the min/max part follows, per KV head and global page, the largest
+// |key| element of the page (fp32), which bounds the error of MFMA scoring.
 #include "losa_internal.h"
 
 namespace losa {
@@ -22,8 +26,11 @@ __global__ __launch_bounds__(256) void k_page_meta(Dims D, const T *__restrict__
     constexpr bool BF = sizeof(T) == 2;
     constexpr int DPC = BF ? 4 : 2;       // dimensions per 16-byte chunk
     constexpr int NCH = DIM / DPC;
+    __shared__ uint32_t s_amax[kTile];
     const int g = blockIdx.y, s = blockIdx.z;
     const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
+    if (threadIdx.x < kTile) s_amax[threadIdx.x] = 0u;
+    __syncthreads();
     for (int item = threadIdx.x; item < kTile * NCH; item += blockDim.x) {
         const int pl = blockIdx.x * kTile + (item % kTile);
         const int c = item / kTile;
@@ -47,6 +54,10 @@ __global__ __launch_bounds__(256) void k_page_meta(Dims D, const T *__restrict__
                 mx[e] = fmaxf(mx[e], v);
             }
         }
+        float am = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPC; ++e) am = fmaxf(am, fmaxf(fabsf(mn[e]), fabsf(mx[e])));
+        atomicMax(&s_amax[item % kTile], __float_as_uint(am));  // non-negative: bits order as values
         const int64_t gp = sg.gp0 + pl;
         const int64_t tile = gp / kTile;
         const int lane = static_cast<int>(gp % kTile);
@@ -66,6 +77,14 @@ __global__ __launch_bounds__(256) void k_page_meta(Dims D, const T *__restrict__
         uint4 *dst = reinterpret_cast<uint4 *>(meta) +
                      ((size_t)(g * D.n_tiles_total + tile) * NCH + c) * kTile + lane;
         *dst = u;
+    }
+    __syncthreads();
+    if (threadIdx.x < kTile) {
+        const int pl = blockIdx.x * kTile + threadIdx.x;
+        if (pl < sg.pages) {
+            float *aux = reinterpret_cast<float *>(reinterpret_cast<char *>(meta) + D.meta_main_bytes);
+            aux[(size_t)g * D.n_tiles_total * kTile + sg.gp0 + pl] = __uint_as_float(s_amax[threadIdx.x]);
+        }
     }
 }
 

@@ -39,6 +39,35 @@ __device__ __forceinline__ float shfl_sum32(float v) {
     return v;
 }
 
+// K and V of one page in the register layouts of the two MFMAs.
+template <int DIM>
+struct PageRegs {
+    static constexpr int KSTEPS = DIM / 32;
+    static constexpr int DPL = DIM / 16;
+    uint4 k[KSTEPS];         // token l%16, dims 32*kk + 8*(l/16) .. +7
+    uint32_t v[4][DPL / 2];  // tokens 4*(l/16) + j, dims DPL*(l%16) .. +DPL-1
+    int valid;               // tokens of the page below the prefix length
+
+    __device__ __forceinline__ void load(const uint16_t *kc, const uint16_t *vc, size_t base,
+                                         int valid_, int l16, int lg) {
+        valid = valid_;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            k[kk] = *reinterpret_cast<const uint4 *>(kc + base + (size_t)l16 * DIM + 32 * kk + 8 * lg);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint16_t *src = vc + base + (size_t)(4 * lg + j) * DIM + DPL * l16;
+            if constexpr (DPL == 8) {
+                const uint4 v4 = *reinterpret_cast<const uint4 *>(src);
+                v[j][0] = v4.x; v[j][1] = v4.y; v[j][2] = v4.z; v[j][3] = v4.w;
+            } else {
+                const uint2 v2 = *reinterpret_cast<const uint2 *>(src);
+                v[j][0] = v2.x; v[j][1] = v2.y;
+            }
+        }
+    }
+};
+
 template <int DIM, int RTW>
 __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
                                                      const uint16_t *__restrict__ kc,
@@ -55,24 +84,25 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
     const int sgi = blockIdx.x % ng;
     const int chunk = blockIdx.x / ng;
     const int s = sgi / D.Hk, g = sgi % D.Hk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
     const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
     const int cp = dense ? kDenseChunk : kSparseChunk;
-    const int n_items = dense ? sg.pages : W.union_cnt[sgi];
     const int first = chunk * cp;
-    if (first >= n_items) return;
-    const int n_here = min(cp, n_items - first);
     const int rows = dense ? D.Rd : D.R;
     const int nch = dense ? D.n_chunks_dense : D.n_chunks_sparse;
     const int n_rt = (rows + 15) / 16;
     const int WPG = n_rt < 4 ? n_rt : 4;
     const int n_pg = 4 / WPG;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pg = w / WPG, wr = w % WPG;
-    const int l16 = lane & 15, lg = lane >> 4;
-    const int32_t *uidx = W.union_idx + (size_t)sgi * D.union_cap;
 
+    // Requested together: the union size, this chunk's page ids (lane i: page
+    // first + i), and the Q operands.
+    const int n_items = dense ? sg.pages : W.union_cnt[sgi];
+    const int my_pos = first + lane;
+    int my_page = my_pos;
+    if (!dense) my_page = (lane < cp && my_pos < D.union_cap) ? W.union_idx[(size_t)sgi * D.union_cap + my_pos] : 0;
     // Q operands (B of QK^T): lane l holds row l%16, dims 32*kk + 8*(l/16) .. +7.
     uint4 qop[RTW][KSTEPS];
     const uint16_t *qr = static_cast<const uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
@@ -88,6 +118,8 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
                 qop[i][kk] = make_uint4(0, 0, 0, 0);
         }
     }
+    if (first >= n_items) return;
+    const int n_here = min(cp, n_items - first);
 
     float4_t oacc[RTW][DPL];
     float m_run[RTW], l_run[RTW];
@@ -99,42 +131,31 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
         for (int e = 0; e < DPL; ++e) oacc[i][e] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    if (pg < n_pg) {
+    auto page_of = [&](int it) { return __builtin_amdgcn_readlane(my_page, it); };
+    auto base_of = [&](int p) { return ((size_t)g * D.T + sg.off + (size_t)p * kPage) * DIM; };
+    if (pg < n_pg && pg < n_here) {
+        PageRegs<DIM> cur, nxt;
+        {
+            const int p = page_of(pg);
+            cur.load(kc, vc, base_of(p), min(kPage, sg.len - p * kPage), l16, lg);
+        }
         for (int it = pg; it < n_here; it += n_pg) {
-            const int pos = first + it;
-            const int p = dense ? pos : uidx[pos];
-            const int valid = min(kPage, sg.len - p * kPage);
-            const size_t base = ((size_t)g * D.T + sg.off + (size_t)p * kPage) * DIM;
-            uint4 kop[KSTEPS];
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk)
-                kop[kk] = *reinterpret_cast<const uint4 *>(kc + base + (size_t)l16 * DIM + 32 * kk +
-                                                           8 * lg);
-            // V rows: tokens 4*lg + j, dims DPL*l16 .. +DPL-1.
-            uint32_t vw[4][DPL / 2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tok = 4 * lg + j;
-                const uint16_t *src = vc + base + (size_t)tok * DIM + DPL * l16;
-                if constexpr (DPL == 8) {
-                    const uint4 v4 = *reinterpret_cast<const uint4 *>(src);
-                    vw[j][0] = v4.x; vw[j][1] = v4.y; vw[j][2] = v4.z; vw[j][3] = v4.w;
-                } else {
-                    const uint2 v2 = *reinterpret_cast<const uint2 *>(src);
-                    vw[j][0] = v2.x; vw[j][1] = v2.y;
-                }
-                if (tok >= valid) {
-#pragma unroll
-                    for (int q = 0; q < DPL / 2; ++q) vw[j][q] = 0u;
-                }
+            const int itn = it + n_pg;
+            if (itn < n_here) {
+                const int pn = page_of(itn);
+                nxt.load(kc, vc, base_of(pn), min(kPage, sg.len - pn * kPage), l16, lg);
             }
-            // V^T operands: for output dim DPL*m + e, tokens 4*lg .. 4*lg+3.
+            const int valid = cur.valid;
+            // V^T operands: output dim DPL*m + e, tokens 4*lg .. 4*lg+3 (masked past the prefix)
             short4_t vop[DPL];
 #pragma unroll
             for (int e = 0; e < DPL; ++e) {
                 const int q = e >> 1, sh = (e & 1) * 16;
-                vop[e] = short4_t{static_cast<short>(vw[0][q] >> sh), static_cast<short>(vw[1][q] >> sh),
-                                  static_cast<short>(vw[2][q] >> sh), static_cast<short>(vw[3][q] >> sh)};
+                short vv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    vv[j] = (4 * lg + j < valid) ? static_cast<short>(cur.v[j][q] >> sh) : short(0);
+                vop[e] = short4_t{vv[0], vv[1], vv[2], vv[3]};
             }
 #pragma unroll
             for (int i = 0; i < RTW; ++i) {
@@ -144,8 +165,8 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
 #pragma unroll
                 for (int kk = 0; kk < KSTEPS; ++kk)
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, kop[kk]), __builtin_bit_cast(bf16x8_t, qop[i][kk]),
-                        sacc, 0, 0, 0);
+                        __builtin_bit_cast(bf16x8_t, cur.k[kk]),
+                        __builtin_bit_cast(bf16x8_t, qop[i][kk]), sacc, 0, 0, 0);
                 float sv[4];
                 float mp = -__builtin_huge_valf();
 #pragma unroll
@@ -174,6 +195,7 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
                     oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[e], pop, oacc[i][e], 0, 0, 0);
                 }
             }
+            cur = nxt;
         }
     }
 #pragma unroll

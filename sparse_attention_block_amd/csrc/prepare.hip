@@ -7,10 +7,11 @@
 //  * the |A| largest scores per query head form the active set, equal scores
 //    going to the lower token (same passage; fr summary, "Sélection des
 //    Tokens Actifs");
-//  * the active rows' queries, stacked per KV head (row r = j*|A| + a for
-//    query head j of the group and active slot a) so a KV page is read once
-//    for all of them, in the storage type for attention and as the fp32
-//    selection operands (max(q,0), min(q,0)) of the page bound;
+//  * the active rows' queries stacked per KV head (row r = j*|A| + a for query
+//    head j of the group and active slot a), so that a KV page is read once
+//    for all of them: in the storage type for attention, as bf16 pairs
+//    (max(q,0), min(q,0)) for the MFMA page scoring, as fp32 pairs for the
+//    exact page-bound chain, and an upper bound of sum_i |q_i| per row;
 //  * the dense first step stacks all G*B rows instead (r = j*B + t).
 // The module is compiled with -ffp-contract=off, so a*b+c stays two roundings.
 #include "losa_internal.h"
@@ -23,6 +24,58 @@ __device__ __forceinline__ float ld(const T *p, int i) {
     else return reinterpret_cast<const float *>(p)[i];
 }
 
+// Squared-change chain of one (head, token) row, loads issued before the chain.
+template <typename T, int DIM>
+__device__ __forceinline__ float locality_chain(const T *a, const T *b) {
+    float acc = 0.0f;
+    if constexpr (sizeof(T) == 2) {
+        constexpr int N = DIM / 8;  // uint4 = 8 bf16
+        uint4 va[N], vb[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            va[i] = reinterpret_cast<const uint4 *>(a)[i];
+            vb[i] = reinterpret_cast<const uint4 *>(b)[i];
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const uint32_t xa[4] = {va[i].x, va[i].y, va[i].z, va[i].w};
+            const uint32_t xb[4] = {vb[i].x, vb[i].y, vb[i].z, vb[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float d0 = bf16_lo(xa[e]) - bf16_lo(xb[e]);
+                const float s0 = d0 * d0;
+                acc = acc + s0;
+                const float d1 = bf16_hi(xa[e]) - bf16_hi(xb[e]);
+                const float s1 = d1 * d1;
+                acc = acc + s1;
+            }
+        }
+    } else {
+        constexpr int SEG = 64;  // floats per batch of loads
+#pragma unroll
+        for (int s0 = 0; s0 < DIM; s0 += SEG) {
+            float4 va[SEG / 4], vb[SEG / 4];
+#pragma unroll
+            for (int i = 0; i < SEG / 4; ++i) {
+                va[i] = reinterpret_cast<const float4 *>(a + s0)[i];
+                vb[i] = reinterpret_cast<const float4 *>(b + s0)[i];
+            }
+#pragma unroll
+            for (int i = 0; i < SEG / 4; ++i) {
+                const float xa[4] = {va[i].x, va[i].y, va[i].z, va[i].w};
+                const float xb[4] = {vb[i].x, vb[i].y, vb[i].z, vb[i].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float dl = xa[e] - xb[e];
+                    const float sq = dl * dl;
+                    acc = acc + sq;
+                }
+            }
+        }
+    }
+    return acc;
+}
+
 template <typename T, int DIM>
 __global__ __launch_bounds__(256) void k_prepare(Dims D, int dense, const T *__restrict__ q_t,
                                                  const T *__restrict__ q_prev, Work W,
@@ -30,6 +83,8 @@ __global__ __launch_bounds__(256) void k_prepare(Dims D, int dense, const T *__r
                                                  int32_t *__restrict__ dbg_act,
                                                  int32_t *__restrict__ dbg_ucnt) {
     constexpr bool BF = sizeof(T) == 2;
+    constexpr int CH = 8;            // dimensions per work item when stacking rows
+    constexpr int NCHK = DIM / CH;   // 8 or 16 items per row
     __shared__ float e_s[kMaxRows];
     __shared__ int sel_s[kMaxRows];
     __shared__ int act_s[kMaxRows];
@@ -45,15 +100,8 @@ __global__ __launch_bounds__(256) void k_prepare(Dims D, int dense, const T *__r
     if (!dense) {
         for (int i = threadIdx.x; i < G * B; i += blockDim.x) {
             const int j = i / B, t = i % B, h = g * G + j;
-            const T *a = q_t + ((size_t)(s * B + t) * Hq + h) * DIM;
-            const T *b = q_prev + ((size_t)(s * B + t) * Hq + h) * DIM;
-            float acc = 0.0f;
-#pragma unroll 8
-            for (int x = 0; x < DIM; ++x) {
-                const float dl = ld(a, x) - ld(b, x);
-                const float sq = dl * dl;
-                acc = acc + sq;
-            }
+            const size_t off = ((size_t)(s * B + t) * Hq + h) * DIM;
+            const float acc = locality_chain<T, DIM>(q_t + off, q_prev + off);
             e_s[i] = acc;
             if (dbg_loc) dbg_loc[((size_t)s * Hq + h) * B + t] = acc / static_cast<float>(DIM);
         }
@@ -83,29 +131,62 @@ __global__ __launch_bounds__(256) void k_prepare(Dims D, int dense, const T *__r
     } else {
         rows = G * B;
     }
-    // Stacked query rows.
+    // Stacked rows, CH dimensions per work item; the NCHK consecutive lanes of
+    // a row reduce sum |q| with shuffles, so every pass covers whole rows.
     T *qr = static_cast<T *>(W.qrows) + (size_t)sg * D.R16 * DIM;
-    float *qs = W.qsel + (size_t)sg * (D.R > 0 ? D.R : 1) * DIM * 2;
-    for (int idx = threadIdx.x; idx < D.R16 * DIM; idx += blockDim.x) {
-        const int r = idx / DIM, x = idx % DIM;
-        if (r >= rows) {
-            if constexpr (BF) reinterpret_cast<uint16_t *>(qr)[idx] = 0;
-            else reinterpret_cast<float *>(qr)[idx] = 0.0f;
-            continue;
+    const int R1 = D.R > 0 ? D.R : 1;
+    uint32_t *q16 = W.qsel16 + (size_t)sg * D.Rs16 * DIM;
+    float *q32 = W.qsel32 + (size_t)sg * R1 * DIM * 2;
+    const int pad_rows = dense ? D.R16 : (D.R16 > D.Rs16 ? D.R16 : D.Rs16);
+    const int n_items = ((pad_rows * NCHK + 255) / 256) * 256;
+    for (int item = threadIdx.x; item < n_items; item += blockDim.x) {
+        const int r = item / NCHK, c = item % NCHK;
+        float v[CH];
+        const bool live = r < rows;
+        if (live) {
+            int j, t;
+            if (dense) { j = r / B; t = r % B; }
+            else { j = r / A; t = act_s[r]; }
+            const T *src = q_t + ((size_t)(s * B + t) * Hq + g * G + j) * DIM + c * CH;
+#pragma unroll
+            for (int e = 0; e < CH; ++e) v[e] = ld(src, e);
+        } else {
+#pragma unroll
+            for (int e = 0; e < CH; ++e) v[e] = 0.0f;
         }
-        int j, t;
-        if (dense) { j = r / B; t = r % B; }
-        else { j = r / A; t = act_s[r]; }
-        const int h = g * G + j;
-        const T *src = q_t + ((size_t)(s * B + t) * Hq + h) * DIM + x;
-        qr[idx] = *src;
+        if (r < D.R16) {
+            T *dst = qr + (size_t)r * DIM + c * CH;
+#pragma unroll
+            for (int e = 0; e < CH; ++e) {
+                if constexpr (BF) reinterpret_cast<uint16_t *>(dst)[e] = f32_to_bf16(v[e]);
+                else reinterpret_cast<float *>(dst)[e] = v[e];
+            }
+        }
         if (!dense) {
-            // Selection operands (q+, q-): q+ = q, q- = 0 when q >= 0 (also for -0),
-            // else q+ = 0, q- = q.
-            const float q = ld(src, 0);
-            const bool pos = q >= 0.0f;
-            qs[2 * idx] = pos ? q : 0.0f;
-            qs[2 * idx + 1] = pos ? 0.0f : q;
+            // (q+, q-): q+ = q, q- = 0 when q >= 0 (-0 included), else q+ = 0, q- = q.
+            float ab = 0.0f;
+            if (r < D.Rs16) {
+                uint32_t *d16 = q16 + (size_t)r * DIM + c * CH;
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    const bool pos = v[e] >= 0.0f;
+                    const uint32_t hb = __float_as_uint(v[e]) >> 16;  // exact for bf16 values
+                    d16[e] = BF ? (pos ? hb : (hb << 16)) : 0u;
+                }
+            }
+            if (live) {
+                float *d32 = q32 + ((size_t)r * DIM + c * CH) * 2;
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    const bool pos = v[e] >= 0.0f;
+                    d32[2 * e] = pos ? v[e] : 0.0f;
+                    d32[2 * e + 1] = pos ? 0.0f : v[e];
+                    ab += fabsf(v[e]);
+                }
+            }
+#pragma unroll
+            for (int o = 1; o < NCHK; o <<= 1) ab += __shfl_xor(ab, o);
+            if (live && c == 0) W.qabs[(size_t)sg * R1 + r] = ab * (1.0f + 1.0f / 256.0f);
         }
     }
 }

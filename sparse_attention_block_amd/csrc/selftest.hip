@@ -2,6 +2,9 @@
 // called only by the GPU tests (not part of the LoSA computation).
 //  * one page-bound step, fma(q+, max, acc) then fma(q-, min, acc) with bf16
 //    operands, must equal the IEEE round-to-nearest-even sum acc + q*sel;
+//  * a plain copy kernel (HBM traffic calibration of the profiler counters,
+//    and the bandwidth a short streaming kernel reaches) and an empty kernel
+//    (the launch floor);
 //  * the operand/result lane layouts assumed for v_mfma_f32_16x16x32_bf16
 //    and v_mfma_f32_16x16x16_bf16: lane l supplies row (or column) l%16 and
 //    k-elements K*(l/16) .. K*(l/16)+K-1, and holds result rows
@@ -51,7 +54,29 @@ __global__ void k_mfma(int K, const uint16_t *A, const uint16_t *B, float *D) {
     for (int j = 0; j < 4; ++j) D[(4 * kb + j) * 16 + r] = d[j];
 }
 
+// dst[i] = src[i] for n16 16-byte elements, grid-stride.
+__global__ __launch_bounds__(256) void k_copy(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                              size_t n16) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16;
+         i += (size_t)gridDim.x * blockDim.x)
+        dst[i] = src[i];
+}
+
+__global__ void k_empty() {}
+
 extern "C" {
+
+int losa_selftest_copy(const void *src, void *dst, size_t bytes, int blocks, void *stream) {
+    if (bytes % 16 || blocks <= 0) return 1;
+    hipLaunchKernelGGL(k_copy, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int losa_selftest_empty(void *stream) {
+    hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 int losa_selftest_bound_step(const float *acc, const float *qp, const float *qn,
                              const uint32_t *meta, float *out, int n, void *stream) {

@@ -61,12 +61,26 @@ class LayerState:
         L.losa_build_page_meta(self.shape, self.k_cache, self.kv_off, self.prefix_len,
                                self.page_meta, stream)
 
-    def dense_first_step(self, q_t, k_blk, v_blk, out=None, stream=None):
+    def dense_first_step(self, q_t, k_blk, v_blk, out=None, debug: Optional[L.Debug] = None,
+                         stream=None):
         out = self.out if out is None else out
         L.losa_dense_first_step(self.shape, q_t, k_blk, v_blk, self.k_cache, self.v_cache,
                                 self.kv_off, self.prefix_len, self.op_cache, self.lp_cache, out,
-                                self.workspace, stream)
+                                self.workspace, debug, stream)
         return out
+
+    def prepare_dense_first_step(self, q_t, k_blk, v_blk, out=None, stream=None):
+        out = self.out if out is None else out
+        return L.prepare_dense_first_step(self.shape, q_t, k_blk, v_blk, self.k_cache,
+                                          self.v_cache, self.kv_off, self.prefix_len,
+                                          self.op_cache, self.lp_cache, out, self.workspace,
+                                          stream)
+
+    def prepare_step(self, q_t, q_prev, k_blk, v_blk, out=None, stream=None):
+        out = self.out if out is None else out
+        return L.prepare_step(self.shape, q_t, q_prev, k_blk, v_blk, self.k_cache, self.v_cache,
+                              self.page_meta, self.kv_off, self.prefix_len, self.op_cache,
+                              self.lp_cache, out, self.workspace, stream)
 
     def step(self, q_t, q_prev, k_blk, v_blk, debug: Optional[L.Debug] = None, out=None,
              stream=None):

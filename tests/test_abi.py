@@ -51,7 +51,8 @@ def test_sizes(cfg):
     assert L.union_capacity(sh) == max(cap, 1)
     s_t = 2 if cfg.dtype == "bf16" else 4
     tiles = (T // 16 + 63) // 64
-    assert L.page_meta_bytes(sh) == cfg.n_kvhead * tiles * 64 * cfg.head_dim * 2 * s_t
+    # min/max pairs per (page, dimension), then one fp32 max |key| per page
+    assert L.page_meta_bytes(sh) == cfg.n_kvhead * tiles * 64 * (cfg.head_dim * 2 * s_t + 4)
     ws = L.workspace_bytes(sh)
     assert 0 < ws < 1 << 31
 
@@ -82,7 +83,7 @@ def test_bad_shape_rejected(lib, kw, status):
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
     r = lib.losa_step(ctypes.byref(sh), *([fake] * 12), None, fake, 1 << 30, None)
     assert r == status
-    r = lib.losa_dense_first_step(ctypes.byref(sh), *([fake] * 11), 1 << 30, None)
+    r = lib.losa_dense_first_step(ctypes.byref(sh), *([fake] * 10), None, fake, 1 << 30, None)
     assert r == status
     r = lib.losa_build_page_meta(ctypes.byref(sh), fake, fake, fake, fake, None)
     assert r == status
@@ -106,10 +107,10 @@ def test_pointer_and_workspace_checks(lib):
     assert lib.losa_step(ctypes.byref(sh), *args, None, None, need, None) == L.LOSA_ERR_INVALID_ARG
     # workspace one byte short
     assert lib.losa_step(ctypes.byref(sh), *args, None, fake, need - 1, None) == L.LOSA_ERR_WORKSPACE
-    assert lib.losa_dense_first_step(ctypes.byref(sh), *([fake] * 11), need - 1, None) == \
-        L.LOSA_ERR_WORKSPACE
+    assert lib.losa_dense_first_step(ctypes.byref(sh), *([fake] * 10), None, fake, need - 1,
+                                     None) == L.LOSA_ERR_WORKSPACE
     # debug union list shorter than the union capacity
-    dbg = L.LosaDebug(None, None, None, fake, None, L.union_capacity(sh) - 1)
+    dbg = L.LosaDebug(None, None, None, fake, None, L.union_capacity(sh) - 1, None)
     assert lib.losa_step(ctypes.byref(sh), *args, ctypes.byref(dbg), fake, need, None) == \
         L.LOSA_ERR_INVALID_ARG
 
