@@ -10,10 +10,11 @@
 //    and attended densely);
 //  * the online-softmax merge L = log(e^L_p + e^L_s),
 //    out = e^(L_p-L) o_p + e^(L_s-L) o_s, rounded to the storage type.
-// The reads that depend on no other read (block keys, queries, the active
-// list, the union size) are requested together; one wave per candidate row
-// reduces the partial maxima and sums, and the partial outputs and block
-// values are read in unrolled batches.  All arithmetic is fp32; scores and
+// One thread per output element.  The reads that depend on no other read
+// (block keys and values, queries, the active list, the union size, the
+// cached statistics) are requested together; a token's prefix partials are
+// requested next, in batches of 32 chunks, and the first batch is in flight
+// while the block scores are computed.  All arithmetic is fp32; scores and
 // log-normalisers are in log2 units inside.
 #include "losa_internal.h"
 
@@ -25,22 +26,39 @@ __device__ __forceinline__ float ldv(const T *p, size_t i) {
     else return reinterpret_cast<const float *>(p)[i];
 }
 
-constexpr int kFinishThreads = 512;
-constexpr int kFinishWaves = kFinishThreads / 64;
+constexpr int kFinishMaxThreads = 256;
+constexpr int kVReg = 16;    // block values per thread held in registers (the rest re-read)
+constexpr int kPartBatch = 24;  // prefix partials per thread requested together (each
+                                // wave keeps at most 63 vector loads in flight)
 
-__device__ __forceinline__ float wave_max_f(float v) {
+// running combination of prefix partials (log2 units): max, sum, weighted output
+struct PartAcc {
+    float mx = -__builtin_huge_valf(), ls = 0.0f, oa = 0.0f;
+    // entries i < n of m, l, a (arrays of kPartBatch)
+    __device__ __forceinline__ void add(const float *m, const float *l, const float *a, int n) {
+        float bm = -__builtin_huge_valf();
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-__device__ __forceinline__ float wave_sum_f(float v) {
+        for (int i = 0; i < kPartBatch; ++i)
+            if (i < n) bm = fmaxf(bm, m[i]);
+        const float nm = fmaxf(mx, bm);
+        if (nm == -__builtin_huge_valf()) return;
+        const float sc = __builtin_amdgcn_exp2f(mx - nm);
+        ls *= sc;
+        oa *= sc;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
+        for (int i = 0; i < kPartBatch; ++i) {
+            if (i < n) {
+                const float w = __builtin_amdgcn_exp2f(m[i] - nm);
+                ls = fmaf(w, l[i], ls);
+                oa = fmaf(w, a[i], oa);
+            }
+        }
+        mx = nm;
+    }
+};
 
 template <typename T, int DIM>
-__global__ __launch_bounds__(kFinishThreads) void k_finish(
+__global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     Dims D, int dense, int TG, const T *__restrict__ q_t, const T *__restrict__ k_blk,
     const T *__restrict__ v_blk, const int32_t *__restrict__ kv_off,
     const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ active,
@@ -55,67 +73,156 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(
     const int nt = min(TG, B - t0);
     const int g = h / G, j = h % G;
     const int sgi = s * D.Hk + g;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int t = tid / DIM, x = tid % DIM;  // this thread's output element
+    const bool live = t < nt;
+    const int tok = t0 + t;
     const int nch = dense ? D.n_chunks_dense : D.n_chunks_sparse;
     const int rows = dense ? D.Rd : D.R;
-    // candidate prefix rows: the |A| stacked rows of this head (sparse) or this
-    // group's tokens (dense); rho indexes them
-    const int NR = dense ? nt : D.A;
+    // prefix rows: stacked row row0 + rho; on the dense step row rho is token
+    // t0 + rho, on a sparse step active slot rho of head h
     const int row0 = dense ? j * B + t0 : j * D.A;
 
-    // LDS: at most 64*129 + 16*128 + 16*64 + 16 + 4*64 words (< 48 KiB)
+    // LDS: at most 64*129 + 4*128 + 4*64 + 4 + 64 words + 64*DIM bf16 (< 49 KiB)
+    constexpr bool BF = sizeof(T) == 2;
     float *kb = sm;                        // [B][DIM + 1]
     float *qs = kb + B * (DIM + 1);        // [TG][DIM]
     float *ps = qs + TG * DIM;             // [TG][B] scores, then softmax weights
     float *ls2 = ps + TG * B;              // [TG] L_s (log2 units)
-    float *rst = ls2 + TG;                 // [NR][3] per candidate row: max, 1/sum, L_p (log2)
-    int *act = reinterpret_cast<int *>(rst + 3 * NR);  // [NR] token of candidate row (sparse)
+    int *act = reinterpret_cast<int *>(ls2 + TG);  // [A] token of each active slot (sparse)
+    const int vb_words = (B * (DIM + 1) + TG * DIM + TG * B + TG + (D.A > 0 ? D.A : 1) + 3) & ~3;
+    uint16_t *vb = reinterpret_cast<uint16_t *>(sm + vb_words);  // [B][DIM] (bf16), 16-byte aligned
 
-    // the number of prefix chunks that wrote partials (uniform scalar load,
-    // requested before the block loads so that its latency overlaps them)
-    int nchu;
+    // -- 1. every read that depends on no other read ---------------------------
+    int nchu;  // prefix chunks that wrote partials
     {
         const int cp = dense ? kDenseChunk : kSparseChunk;
-        int n_items;
-        if (dense) n_items = seq_geom(D, kv_off, prefix_len, s).pages;
-        else n_items = union_cnt[sgi];
+        const int n_items = dense ? seq_geom(D, kv_off, prefix_len, s).pages : union_cnt[sgi];
         nchu = (n_items + cp - 1) / cp;
     }
-    for (int idx = tid; idx < B * DIM; idx += blockDim.x) {
-        const int u = idx / DIM, x = idx % DIM;
-        kb[u * (DIM + 1) + x] = ldv(k_blk, ((size_t)(s * B + u) * D.Hk + g) * DIM + x);
+    // Block keys (and values, bf16) and the queries as 16-byte vectors, every
+    // address clamped into its tensor so that no load is conditional: all of
+    // them are in flight before the first is used.
+    constexpr int EV = 16 / sizeof(T);             // elements per vector
+    constexpr int KPT = 64 * DIM / EV / kFinishMaxThreads;  // vectors per thread (B <= 64)
+    const int nkv = B * DIM / EV;
+    uint4 kr[KPT], vr4[BF ? KPT : 1];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int idx = min(tid + i * nthr, nkv - 1);
+        const size_t off = ((size_t)(s * B + idx * EV / DIM) * D.Hk + g) * DIM + (idx * EV) % DIM;
+        kr[i] = *reinterpret_cast<const uint4 *>(k_blk + off);
+        if constexpr (BF) vr4[i] = *reinterpret_cast<const uint4 *>(v_blk + off);
     }
-    for (int idx = tid; idx < nt * DIM; idx += blockDim.x) {
-        const int t = idx / DIM, x = idx % DIM;
-        qs[t * DIM + x] = ldv(q_t, ((size_t)(s * B + t0 + t) * D.Hq + h) * DIM + x);
+    const int nq = nt * DIM / EV;
+    const int qi = min(tid, nq - 1);
+    const uint4 qv4 = *reinterpret_cast<const uint4 *>(
+        q_t + ((size_t)(s * B + t0 + qi * EV / DIM) * D.Hq + h) * DIM + (qi * EV) % DIM);
+    const int av_ = dense || D.A == 0 ? 0 : active[((size_t)s * D.Hq + h) * D.A + min(tid, D.A - 1)];
+    // fp32 storage: this thread's column of the block values, from global memory
+    const T *vcol = v_blk + ((size_t)s * B * D.Hk + g) * DIM + x;
+    const size_t vs = (size_t)D.Hk * DIM;
+    float vr[BF ? 1 : kVReg];
+    if constexpr (!BF) {
+#pragma unroll
+        for (int u = 0; u < kVReg; ++u) vr[u] = ldv(vcol, min(u, B - 1) * vs);
     }
-    if (!dense && tid < NR) act[tid] = active[((size_t)s * D.Hq + h) * D.A + tid];
-    // per candidate row, one wave reduces the chunk maxima and sums
-    for (int rho = wave; rho < NR; rho += kFinishWaves) {
-        const float *ml = part_ml + ((size_t)sgi * nch * rows + row0 + rho) * 2;
-        const size_t cs = (size_t)rows * 2;
-        float mx = -__builtin_huge_valf();
-        for (int c = lane; c < nchu; c += 64) mx = fmaxf(mx, ml[c * cs]);
-        mx = wave_max_f(mx);
-        float ls = 0.0f;
-        for (int c = lane; c < nchu; c += 64)
-            ls = fmaf(__builtin_amdgcn_exp2f(ml[c * cs] - mx), ml[c * cs + 1], ls);
-        ls = wave_sum_f(ls);
-        if (lane == 0) {
-            rst[3 * rho] = mx;
-            rst[3 * rho + 1] = nchu > 0 ? 1.0f / ls : 0.0f;
-            rst[3 * rho + 2] = nchu > 0 ? mx + __log2f(ls) : -__builtin_huge_valf();
+    const size_t crow = ((size_t)s * D.Hq + h) * B + tok;
+    // cached statistics of the token (used if its row is stable); clamped row
+    const size_t crow_c = ((size_t)s * D.Hq + h) * B + min(tok, B - 1);
+    const float opc = op_cache[crow_c * DIM + x];
+    const float lpc = lp_cache[crow_c];
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
+    auto unpack = [](const uint4 &w, float *f) {
+        if constexpr (BF) {
+            const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[2 * e] = bf16_lo(a[e]);
+                f[2 * e + 1] = bf16_hi(a[e]);
+            }
+        } else {
+            f[0] = __uint_as_float(w.x);
+            f[1] = __uint_as_float(w.y);
+            f[2] = __uint_as_float(w.z);
+            f[3] = __uint_as_float(w.w);
         }
+    };
+    // LDS stores at the same clamped indexes (threads past the end rewrite the
+    // last vector with its own value), so that no store -- and no load feeding
+    // it -- sits in a branch
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int idx = min(tid + i * nthr, nkv - 1);
+        float f[EV];
+        unpack(kr[i], f);
+        float *dst = kb + (idx * EV / DIM) * (DIM + 1) + (idx * EV) % DIM;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) dst[e] = f[e];
+        if constexpr (BF) *reinterpret_cast<uint4 *>(vb + idx * EV) = vr4[i];
     }
+    {
+        float f[EV];
+        unpack(qv4, f);
+#pragma unroll
+        for (int e = 0; e < EV; ++e) qs[qi * EV + e] = f[e];
+    }
+    if (!dense && D.A > 0) act[min(tid, D.A - 1)] = av_;
     __syncthreads();
 
-    // block scores q.k (scaled, log2 units)
-    for (int pr = tid; pr < nt * B; pr += blockDim.x) {
-        const int t = pr / B, u = pr % B;
-        float dot = 0.0f;
-#pragma unroll 8
-        for (int x = 0; x < DIM; ++x) dot = fmaf(qs[t * DIM + x], kb[u * (DIM + 1) + x], dot);
-        ps[t * B + u] = dot * D.scale_log2;
+    // -- 2. this token's prefix row; its first batch of partials is requested
+    //       before the block scores are computed -------------------------------
+    int rho = -1;
+    if (live) {
+        if (dense) {
+            rho = t;
+        } else {
+            for (int a = 0; a < D.A; ++a)
+                if (act[a] == tok) rho = a;
+        }
+    }
+    const size_t pr0 = (size_t)sgi * nch * rows + row0 + (rho < 0 ? 0 : rho);
+    const float *mlp = part_ml + pr0 * 2;
+    const float *acp = part_acc + pr0 * DIM + x;
+    const size_t cs = (size_t)rows * 2, as = (size_t)rows * DIM;
+    const int n0 = rho >= 0 ? min(nchu, kPartBatch) : 0;
+    float mv[kPartBatch], lv[kPartBatch], av[kPartBatch];
+    // rho is uniform over a wave (a wave holds one token); the chunk index is
+    // clamped so that no load is conditional, and entries past n0 are ignored
+    auto load_parts = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < kPartBatch; ++i) {
+            const int c = min(c0 + i, nchu - 1);
+            const float2 v = *reinterpret_cast<const float2 *>(mlp + c * cs);
+            mv[i] = v.x;
+            lv[i] = v.y;
+            av[i] = acp[c * as];
+        }
+    };
+    if (n0 > 0) load_parts(0);
+    __builtin_amdgcn_sched_barrier(0);  // the partials stay in flight during the block scores
+
+    // block scores q.k (scaled, log2 units): 8 threads per (token, key) pair
+    {
+        constexpr int SEG = DIM / 8;
+        const int n_pairs = nt * B;
+        const int iters = (n_pairs * 8 + nthr - 1) / nthr;
+        for (int it = 0; it < iters; ++it) {
+            const int idx = it * nthr + tid;
+            const int pr = idx >> 3, part = idx & 7;
+            float dot = 0.0f;
+            if (pr < n_pairs) {
+                const int tt = pr / B, u = pr % B;
+                const float *qp = qs + tt * DIM + part * SEG;
+                const float *kp = kb + u * (DIM + 1) + part * SEG;
+#pragma unroll
+                for (int i = 0; i < SEG; ++i) dot = fmaf(qp[i], kp[i], dot);
+            }
+            dot += __shfl_xor(dot, 1);
+            dot += __shfl_xor(dot, 2);
+            dot += __shfl_xor(dot, 4);
+            if (pr < n_pairs && part == 0) ps[pr] = dot * D.scale_log2;
+        }
     }
     __syncthreads();
     if (tid < nt) {
@@ -132,78 +239,77 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(
         ls2[tid] = m + __log2f(l);
     }
     __syncthreads();
+    if (!live) return;
 
-    // outputs: one thread per (token, dimension)
-    for (int item = tid; item < nt * DIM; item += blockDim.x) {
-        const int t = item / DIM, x = item % DIM;
-        const int tok = t0 + t;
-        const size_t crow = ((size_t)s * D.Hq + h) * B + tok;
-        int rho = -1;
-        if (dense) {
-            rho = t;
-        } else {
-            for (int a = 0; a < NR; ++a)
-                if (act[a] == tok) rho = a;
-        }
-        float op, lp2;
-        if (rho >= 0) {
-            // chunk weights exp2(m_c - max) / sum, applied to the partial outputs
-            const float mx = rst[3 * rho], inv = rst[3 * rho + 1];
-            lp2 = rst[3 * rho + 2];
-            const float *acc = part_acc + ((size_t)sgi * nch * rows + row0 + rho) * DIM + x;
-            const float *ml = part_ml + ((size_t)sgi * nch * rows + row0 + rho) * 2;
-            const size_t as = (size_t)rows * DIM, cs = (size_t)rows * 2;
-            op = 0.0f;
-#pragma unroll 16
-            for (int c = 0; c < nchu; ++c)
-                op = fmaf(__builtin_amdgcn_exp2f(ml[c * cs] - mx), acc[c * as], op);
-            op *= inv;
-            op_cache[crow * DIM + x] = op;
-            if (x == 0) lp_cache[crow] = lp2 * kLn2;
-        } else {
-            op = op_cache[crow * DIM + x];
-            lp2 = lp_cache[crow] * kLog2e;
-        }
-        const T *vcol = v_blk + ((size_t)s * B * D.Hk + g) * DIM + x;
-        const size_t vs = (size_t)D.Hk * DIM;
-        float os = 0.0f;
-#pragma unroll 16
-        for (int u = 0; u < B; ++u) os = fmaf(ps[t * B + u], ldv(vcol, u * vs), os);
-        float v;
-        if (lp2 == -__builtin_huge_valf()) {
-            v = os;
-        } else {
-            const float M = fmaxf(lp2, ls2[t]);
-            const float ep = __builtin_amdgcn_exp2f(lp2 - M), es = __builtin_amdgcn_exp2f(ls2[t] - M);
-            v = (ep * op + es * os) / (ep + es);
-        }
-        T *o = out + ((size_t)(s * B + tok) * D.Hq + h) * DIM + x;
-        if constexpr (sizeof(T) == 2) *reinterpret_cast<uint16_t *>(o) = f32_to_bf16(v);
-        else *reinterpret_cast<float *>(o) = v;
+    // -- 3. output ---------------------------------------------------------------
+    float os = 0.0f;
+    if constexpr (BF) {
+        for (int u = 0; u < B; ++u) os = fmaf(ps[t * B + u], bf16_to_f32(vb[u * DIM + x]), os);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kVReg; ++u)
+            if (u < B) os = fmaf(ps[t * B + u], vr[u], os);
+        for (int u = kVReg; u < B; ++u) os = fmaf(ps[t * B + u], ldv(vcol, u * vs), os);
     }
+    float op, lp2;
+    if (rho >= 0) {
+        PartAcc pa;
+        pa.add(mv, lv, av, n0);
+        for (int c0 = kPartBatch; c0 < nchu; c0 += kPartBatch) {
+            load_parts(c0);
+            pa.add(mv, lv, av, min(kPartBatch, nchu - c0));
+        }
+        if (nchu > 0) {
+            op = pa.oa / pa.ls;
+            lp2 = pa.mx + __log2f(pa.ls);
+        } else {
+            op = 0.0f;
+            lp2 = -__builtin_huge_valf();
+        }
+        op_cache[crow * DIM + x] = op;
+        if (x == 0) lp_cache[crow] = lp2 * kLn2;
+    } else {
+        op = opc;
+        lp2 = lpc * kLog2e;
+    }
+    float v;
+    if (lp2 == -__builtin_huge_valf()) {
+        v = os;
+    } else {
+        const float M = fmaxf(lp2, ls2[t]);
+        const float ep = __builtin_amdgcn_exp2f(lp2 - M), es = __builtin_amdgcn_exp2f(ls2[t] - M);
+        v = (ep * op + es * os) / (ep + es);
+    }
+    T *o = out + ((size_t)(s * B + tok) * D.Hq + h) * DIM + x;
+    if constexpr (sizeof(T) == 2) *reinterpret_cast<uint16_t *>(o) = f32_to_bf16(v);
+    else *reinterpret_cast<float *>(o) = v;
 }
 
-size_t finish_lds_bytes(const Dims &D, bool dense, int TG) {
-    const int NR = dense ? TG : D.A;
-    return ((size_t)D.B * (D.d + 1) + (size_t)TG * D.d + (size_t)TG * D.B + TG + 4 * (size_t)NR) * 4;
+size_t finish_lds_bytes(const Dims &D, int TG) {
+    const size_t words = ((size_t)D.B * (D.d + 1) + (size_t)TG * D.d + (size_t)TG * D.B + TG +
+                          (size_t)(D.A > 0 ? D.A : 1) + 3) & ~(size_t)3;
+    return words * 4 + (D.bf16 ? (size_t)D.B * D.d * 2 : 0);
 }
 
-int finish_group(const Dims &D, bool dense) {
-    // tokens per workgroup: on the dense step every row combines one partial
-    // per prefix chunk, so the groups are small
-    return dense ? (D.B < 2 ? D.B : 2) : (D.B < 16 ? D.B : 16);
+// Tokens per workgroup: one output element per thread, 256 threads; the
+// workgroup count (B / TG) * Hq * S then exceeds the CU count for the shapes
+// of a long-context layer.
+int finish_group(const Dims &D) {
+    const int tg = kFinishMaxThreads / D.d;
+    return D.B < tg ? D.B : tg;
 }
 
 hipError_t launch_finish(const Dims &D, bool dense, const void *q_t, const void *k_blk,
                          const void *v_blk, const int32_t *kv_off, const int32_t *prefix_len,
                          const Work &W, float *op_cache, float *lp_cache, void *out,
                          hipStream_t st) {
-    const int TG = finish_group(D, dense);
+    const int TG = finish_group(D);
     dim3 grid((D.B + TG - 1) / TG, D.Hq, D.S);
-    const size_t lds = finish_lds_bytes(D, dense, TG);
+    const size_t lds = finish_lds_bytes(D, TG);
+    const int threads = TG * D.d;
     const int dn = dense ? 1 : 0;
 #define LAUNCH_F(T, DIMV)                                                                        \
-    hipLaunchKernelGGL((k_finish<T, DIMV>), grid, dim3(kFinishThreads), lds, st, D, dn, TG,      \
+    hipLaunchKernelGGL((k_finish<T, DIMV>), grid, dim3(threads), lds, st, D, dn, TG,      \
                        static_cast<const T *>(q_t), static_cast<const T *>(k_blk),               \
                        static_cast<const T *>(v_blk), kv_off, prefix_len, W.active, W.union_cnt, \
                        W.part_ml, W.part_acc, op_cache, lp_cache, static_cast<T *>(out))

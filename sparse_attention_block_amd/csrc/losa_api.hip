@@ -12,7 +12,7 @@ using namespace losa;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxPagesSupported = 262144;  // LDS bitmap of the union merge (32 KiB)
+constexpr int kMaxPagesSupported = kMaxBitmapWords * 32;  // LDS bitmap of the union (32 KiB)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -93,7 +93,6 @@ size_t carve(const Dims &D, char *base, Work *W) {
         return p;
     };
     Work w;
-    w.counters = reinterpret_cast<int32_t *>(take(SG * 4));
     w.active = reinterpret_cast<int32_t *>(take((size_t)D.S * D.Hq * A1 * 4));
     w.qrows = take(SG * D.R16 * D.d * sT);
     w.qsel16 = reinterpret_cast<uint32_t *>(take(SG * D.Rs16 * D.d * 4));
@@ -102,7 +101,6 @@ size_t carve(const Dims &D, char *base, Work *W) {
     w.hbound = reinterpret_cast<float *>(take(SG * R1 * D.hb_stride * 4));
     w.tmax = reinterpret_cast<float *>(take(SG * R1 * D.n_tiles_grid * 4));
     w.psel = reinterpret_cast<int32_t *>(take(SG * R1 * D.k * 4));
-    w.union_idx = reinterpret_cast<int32_t *>(take(SG * D.union_cap * 4));
     w.union_cnt = reinterpret_cast<int32_t *>(take(SG * 4));
     w.part_acc = reinterpret_cast<float *>(take(SG * part_rows * D.d * 4));
     w.part_ml = reinterpret_cast<float *>(take(SG * part_rows * 2 * 4));
@@ -188,7 +186,8 @@ int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *
     if (e == hipSuccess) e = launch_prepare(D, true, q_t, nullptr, W, nullptr, nullptr, nullptr, s);
     if (e == hipSuccess) e = mark(ev, 1, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
-    if (e == hipSuccess) e = launch_prefix(D, true, k_cache, v_cache, kv_off, prefix_len, W, s);
+    if (e == hipSuccess)
+        e = launch_prefix(D, true, k_cache, v_cache, kv_off, prefix_len, W, nullptr, nullptr, 0, s);
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (e == hipSuccess)
         e = launch_finish(D, true, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache,
@@ -233,11 +232,11 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
         e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active, dbg.union_cnt, s);
     if (e == hipSuccess) e = mark(ev, 1, s);
     if (D.R > 0 && e == hipSuccess)
-        e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, dbg.union_idx,
-                          dbg.union_cnt, dbg.union_cap, s);
+        e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
     if (D.R > 0 && e == hipSuccess)
-        e = launch_prefix(D, false, k_cache, v_cache, kv_off, prefix_len, W, s);
+        e = launch_prefix(D, false, k_cache, v_cache, kv_off, prefix_len, W, dbg.union_idx,
+                          dbg.union_cnt, dbg.union_cap, s);
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (e == hipSuccess)
         e = launch_finish(D, false, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache,

@@ -12,6 +12,7 @@ namespace losa {
 constexpr int kPage = 16;         // tokens per page
 constexpr int kTile = 64;         // pages per metadata tile: one page per lane of a wave
 constexpr int kSparseChunk = 4;   // union pages per prefix workgroup (sparse step): 1 per wave
+constexpr int kMaxBitmapWords = 8192;  // union bitmap in LDS: 262144 pages
 constexpr int kDenseChunk = 64;   // prefix pages per prefix workgroup (dense first step)
 constexpr int kMaxRows = 256;     // G * B stacked rows per KV head at most
 constexpr int kMaxK = 64;         // pages per row the exact selection keeps in one register
@@ -43,7 +44,6 @@ struct Dims {
 
 // Device views into the workspace (all carved from one caller buffer).
 struct Work {
-    int32_t *counters;   // [S][Hk] arrival counters
     int32_t *active;     // [S][Hq][max(A,1)]
     void *qrows;         // [S][Hk][R16][d] storage type: stacked query rows (attention)
     uint32_t *qsel16;    // [S][Hk][Rs16][d] bf16 pairs (max(q,0) | min(q,0) << 16): MFMA operand
@@ -52,8 +52,7 @@ struct Work {
     float *hbound;       // [S][Hk][max(R,1)][hb_stride] upper bound of each page's exact bound
     float *tmax;         // [S][Hk][max(R,1)][n_tiles_grid] per tile: max lower bound
     int32_t *psel;       // [S][Hk][max(R,1)][k] each active row's selected pages
-    int32_t *union_idx;  // [S][Hk][union_cap]
-    int32_t *union_cnt;  // [S][Hk]
+    int32_t *union_cnt;  // [S][Hk] union size, written by the sparse prefix kernel
     float *part_acc;     // [S][Hk][n_chunks][rows][d]
     float *part_ml;      // [S][Hk][n_chunks][rows][2] (running max in log2 units, sum)
 };
@@ -66,11 +65,13 @@ hipError_t launch_prepare(const Dims &D, bool dense, const void *q_t, const void
                           int32_t *dbg_union_cnt, hipStream_t st);
 hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
                          const int32_t *prefix_len, const Work &W, int32_t *dbg_page_sel,
-                         int32_t *dbg_union_idx, int32_t *dbg_union_cnt, int dbg_union_cap,
                          hipStream_t st);
 size_t select_lds_bytes(const Dims &D);  // dynamic LDS of the exact-selection kernel
+// Sparse step: the union of the rows' pages is built here (the dbg_union_*
+// outputs are optional).
 hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const void *v_cache,
                          const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
+                         int32_t *dbg_union_idx, int32_t *dbg_union_cnt, int dbg_union_cap,
                          hipStream_t st);
 hipError_t launch_finish(const Dims &D, bool dense, const void *q_t, const void *k_blk,
                          const void *v_blk, const int32_t *kv_off, const int32_t *prefix_len,

@@ -68,16 +68,74 @@ struct PageRegs {
     }
 };
 
+// Union of the selected pages of one (sequence, KV head) -- the rows' lists
+// psel[0 .. n_sel), -1 for none -- as a bitmap in LDS (bm: ceil(pages/32)
+// words), compacted in ascending page order.  The pages at union positions
+// [first, first + cp) go to pg_out; with dbg_idx, every position is written
+// there too.  Returns the union size.  Called by all 256 threads.
+__device__ int union_slice(const int32_t *__restrict__ psel, int n_sel, int pages, bool all_pages,
+                           int first, int cp, uint32_t *bm, int *wsum, int *pg_out,
+                           int32_t *dbg_idx, int dbg_cap) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (all_pages) {
+        if (tid < cp) pg_out[tid] = first + tid;
+        if (dbg_idx)
+            for (int i = tid; i < min(pages, dbg_cap); i += 256) dbg_idx[i] = i;
+        __syncthreads();
+        return pages;
+    }
+    const int words = (pages + 31) / 32;
+    for (int i = tid; i < words; i += 256) bm[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n_sel; i += 256) {
+        const int pg = psel[i];
+        if (pg >= 0) atomicOr(&bm[pg >> 5], 1u << (pg & 31));
+    }
+    __syncthreads();
+    const int wpt = (words + 255) / 256;
+    const int w0 = min(tid * wpt, words), w1 = min(w0 + wpt, words);
+    int cnt = 0;
+    for (int i = w0; i < w1; ++i) cnt += __popc(bm[i]);
+    int incl = cnt;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int pos = incl - cnt, total = 0;
+    for (int q = 0; q < 4; ++q) {
+        if (q < w) pos += wsum[q];
+        total += wsum[q];
+    }
+    for (int i = w0; i < w1; ++i) {
+        uint32_t b = bm[i];
+        while (b) {
+            const int pg = i * 32 + __ffs(b) - 1;
+            b &= b - 1u;
+            if (pos >= first && pos < first + cp) pg_out[pos - first] = pg;
+            if (dbg_idx && pos < dbg_cap) dbg_idx[pos] = pg;
+            ++pos;
+        }
+    }
+    __syncthreads();
+    return total;
+}
+
 template <int DIM, int RTW>
 __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
                                                      const uint16_t *__restrict__ kc,
                                                      const uint16_t *__restrict__ vc,
                                                      const int32_t *__restrict__ kv_off,
                                                      const int32_t *__restrict__ prefix_len,
-                                                     Work W) {
+                                                     Work W, int32_t *dbg_uidx, int32_t *dbg_ucnt,
+                                                     int dbg_cap) {
     constexpr int KSTEPS = DIM / 32;  // QK^T k-steps of 32 dims
     constexpr int DPL = DIM / 16;     // V dims per lane = PV MFMAs per page
-    __shared__ float s_acc[4][16][DIM];
+    constexpr int RAW = 4 * 16 * DIM > kMaxBitmapWords ? 4 * 16 * DIM : kMaxBitmapWords;
+    __shared__ float s_raw[RAW];  // the union bitmap first, then the page groups' outputs
+    __shared__ int s_wsum[4], s_pg[kSparseChunk];
+    auto s_acc = reinterpret_cast<float (*)[16][DIM]>(s_raw);
     __shared__ float s_ml[4][16][2];
 
     const int ng = D.S * D.Hk;
@@ -97,13 +155,8 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
     const int n_pg = 4 / WPG;
     const int pg = w / WPG, wr = w % WPG;
 
-    // Requested together: the union size, this chunk's page ids (lane i: page
-    // first + i), and the Q operands.
-    const int n_items = dense ? sg.pages : W.union_cnt[sgi];
-    const int my_pos = first + lane;
-    int my_page = my_pos;
-    if (!dense) my_page = (lane < cp && my_pos < D.union_cap) ? W.union_idx[(size_t)sgi * D.union_cap + my_pos] : 0;
-    // Q operands (B of QK^T): lane l holds row l%16, dims 32*kk + 8*(l/16) .. +7.
+    // Q operands (B of QK^T): lane l holds row l%16, dims 32*kk + 8*(l/16) .. +7;
+    // requested before the union is built.
     uint4 qop[RTW][KSTEPS];
     const uint16_t *qr = static_cast<const uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
 #pragma unroll
@@ -117,6 +170,22 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
             else
                 qop[i][kk] = make_uint4(0, 0, 0, 0);
         }
+    }
+    // this chunk's pages (lane i: union position first + i)
+    int n_items, my_page = first + lane;
+    if (dense) {
+        n_items = sg.pages;
+    } else {
+        const int R1 = D.R > 0 ? D.R : 1;
+        n_items = union_slice(W.psel + (size_t)sgi * R1 * D.k, D.R * D.k, sg.pages, D.k >= sg.pages,
+                              first, cp, reinterpret_cast<uint32_t *>(s_raw), s_wsum, s_pg,
+                              chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
+                              dbg_cap);
+        if (chunk == 0 && tid == 0) {
+            W.union_cnt[sgi] = min(n_items, D.union_cap);
+            if (dbg_ucnt) dbg_ucnt[sgi] = n_items;
+        }
+        my_page = lane < cp ? s_pg[lane] : 0;
     }
     if (first >= n_items) return;
     const int n_here = min(cp, n_items - first);
@@ -267,8 +336,11 @@ template <int DIM>
 __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, int dense, const float *__restrict__ kc,
                                                     const float *__restrict__ vc,
                                                     const int32_t *__restrict__ kv_off,
-                                                    const int32_t *__restrict__ prefix_len, Work W) {
+                                                    const int32_t *__restrict__ prefix_len, Work W,
+                                                    int32_t *dbg_uidx, int32_t *dbg_ucnt, int dbg_cap) {
     constexpr int DPT = DIM / 16;
+    __shared__ uint32_t s_bm[kMaxBitmapWords];
+    __shared__ int s_wsum[4], s_pg[kSparseChunk];
     __shared__ float q_s[16][DIM];
     __shared__ float k_s[16][DIM + 1];
     __shared__ float v_s[16][DIM];
@@ -279,8 +351,21 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, int dense, const flo
     const int s = sgi / D.Hk, g = sgi % D.Hk;
     const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
     const int cp = dense ? kDenseChunk : kSparseChunk;
-    const int n_items = dense ? sg.pages : W.union_cnt[sgi];
     const int first = chunk * cp;
+    int n_items;
+    if (dense) {
+        n_items = sg.pages;
+    } else {
+        const int R1 = D.R > 0 ? D.R : 1;
+        n_items = union_slice(W.psel + (size_t)sgi * R1 * D.k, D.R * D.k, sg.pages, D.k >= sg.pages,
+                              first, cp, s_bm, s_wsum, s_pg,
+                              chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
+                              dbg_cap);
+        if (chunk == 0 && threadIdx.x == 0) {
+            W.union_cnt[sgi] = min(n_items, D.union_cap);
+            if (dbg_ucnt) dbg_ucnt[sgi] = n_items;
+        }
+    }
     if (first >= n_items) return;
     const int n_here = min(cp, n_items - first);
     const int rows = dense ? D.Rd : D.R;
@@ -288,7 +373,6 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, int dense, const flo
     const int n_rt = (rows + 15) / 16;
     const int tid = threadIdx.x, r16 = tid / 16, j16 = tid % 16;
     const float *qr = static_cast<const float *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
-    const int32_t *uidx = W.union_idx + (size_t)sgi * D.union_cap;
 
     for (int rt = 0; rt < n_rt; ++rt) {
         __syncthreads();
@@ -298,7 +382,7 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, int dense, const flo
         for (int x = 0; x < DPT; ++x) acc[x] = 0.0f;
         for (int it = 0; it < n_here; ++it) {
             const int pos = first + it;
-            const int p = dense ? pos : uidx[pos];
+            const int p = dense ? pos : s_pg[it];
             const int valid = min(kPage, sg.len - p * kPage);
             const size_t base = ((size_t)g * D.T + sg.off + (size_t)p * kPage) * DIM;
             __syncthreads();
@@ -345,7 +429,7 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, int dense, const flo
 
 hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const void *v_cache,
                          const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
-                         hipStream_t st) {
+                         int32_t *dbg_uidx, int32_t *dbg_ucnt, int dbg_cap, hipStream_t st) {
     const int nch = dense ? D.n_chunks_dense : D.n_chunks_sparse;
     dim3 grid(nch * D.S * D.Hk);
     const int dn = dense ? 1 : 0;
@@ -357,7 +441,7 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const v
         const int rtw = n_rt <= 4 ? 1 : (n_rt <= 8 ? 2 : 4);
 #define LAUNCH_P(DIMV, RTWV)                                                                    \
     hipLaunchKernelGGL((k_prefix_bf16<DIMV, RTWV>), grid, dim3(256), 0, st, D, dn, k, v, kv_off, \
-                       prefix_len, W)
+                       prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap)
         if (D.d == 128) {
             if (rtw == 1) LAUNCH_P(128, 1);
             else if (rtw == 2) LAUNCH_P(128, 2);
@@ -373,10 +457,10 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const v
         auto *v = static_cast<const float *>(v_cache);
         if (D.d == 128)
             hipLaunchKernelGGL((k_prefix_f32<128>), grid, dim3(256), 0, st, D, dn, k, v, kv_off,
-                               prefix_len, W);
+                               prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap);
         else
             hipLaunchKernelGGL((k_prefix_f32<64>), grid, dim3(256), 0, st, D, dn, k, v, kv_off,
-                               prefix_len, W);
+                               prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap);
     }
     return hipGetLastError();
 }

@@ -36,6 +36,7 @@ __device__ __forceinline__ float locality_chain(const T *a, const T *b) {
             va[i] = reinterpret_cast<const uint4 *>(a)[i];
             vb[i] = reinterpret_cast<const uint4 *>(b)[i];
         }
+        __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the chain starts
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const uint32_t xa[4] = {va[i].x, va[i].y, va[i].z, va[i].w};
@@ -92,9 +93,8 @@ __global__ __launch_bounds__(256) void k_prepare(Dims D, int dense, const T *__r
     const int G = D.G, B = D.B, A = D.A, Hq = D.Hq;
     const int sg = s * D.Hk + g;
     if (threadIdx.x == 0) {
-        W.counters[sg] = 0;
         W.union_cnt[sg] = 0;
-        if (dbg_ucnt) dbg_ucnt[sg] = 0;  // the selection kernel overwrites it when |A| > 0
+        if (dbg_ucnt) dbg_ucnt[sg] = 0;  // the sparse prefix kernel overwrites them when |A| > 0
     }
     int rows;
     if (!dense) {
@@ -132,61 +132,91 @@ __global__ __launch_bounds__(256) void k_prepare(Dims D, int dense, const T *__r
         rows = G * B;
     }
     // Stacked rows, CH dimensions per work item; the NCHK consecutive lanes of
-    // a row reduce sum |q| with shuffles, so every pass covers whole rows.
+    // a row reduce sum |q| with shuffles, so every pass covers whole rows.  The
+    // loads of up to kPasses passes are issued before any of them is used.
     T *qr = static_cast<T *>(W.qrows) + (size_t)sg * D.R16 * DIM;
     const int R1 = D.R > 0 ? D.R : 1;
     uint32_t *q16 = W.qsel16 + (size_t)sg * D.Rs16 * DIM;
     float *q32 = W.qsel32 + (size_t)sg * R1 * DIM * 2;
-    const int pad_rows = dense ? D.R16 : (D.R16 > D.Rs16 ? D.R16 : D.Rs16);
-    const int n_items = ((pad_rows * NCHK + 255) / 256) * 256;
-    for (int item = threadIdx.x; item < n_items; item += blockDim.x) {
-        const int r = item / NCHK, c = item % NCHK;
-        float v[CH];
-        const bool live = r < rows;
-        if (live) {
+    const int pad_rows = dense ? D.R16 : D.Rs16;
+    const int n_items = rows > 0 ? ((pad_rows * NCHK + 255) / 256) * 256 : 0;
+    constexpr int kPasses = 4;
+    for (int i0 = 0; i0 < n_items; i0 += kPasses * 256) {
+        // CH consecutive dimensions of one row per item, as 16-byte vectors read
+        // from a clamped row (always in bounds), zeroed past the live rows
+        constexpr int NV = CH * sizeof(T) / 16;
+        uint4 raw[kPasses][NV];
+#pragma unroll
+        for (int pi = 0; pi < kPasses; ++pi) {
+            const int item = i0 + pi * 256 + threadIdx.x;
+            const int r = min(item / NCHK, rows - 1), c = item % NCHK;
             int j, t;
             if (dense) { j = r / B; t = r % B; }
             else { j = r / A; t = act_s[r]; }
-            const T *src = q_t + ((size_t)(s * B + t) * Hq + g * G + j) * DIM + c * CH;
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                q_t + ((size_t)(s * B + t) * Hq + g * G + j) * DIM + c * CH);
 #pragma unroll
-            for (int e = 0; e < CH; ++e) v[e] = ld(src, e);
-        } else {
-#pragma unroll
-            for (int e = 0; e < CH; ++e) v[e] = 0.0f;
+            for (int e = 0; e < NV; ++e) raw[pi][e] = src[e];
         }
-        if (r < D.R16) {
-            T *dst = qr + (size_t)r * DIM + c * CH;
+        float v[kPasses][CH];
 #pragma unroll
-            for (int e = 0; e < CH; ++e) {
-                if constexpr (BF) reinterpret_cast<uint16_t *>(dst)[e] = f32_to_bf16(v[e]);
-                else reinterpret_cast<float *>(dst)[e] = v[e];
-            }
-        }
-        if (!dense) {
-            // (q+, q-): q+ = q, q- = 0 when q >= 0 (-0 included), else q+ = 0, q- = q.
-            float ab = 0.0f;
-            if (r < D.Rs16) {
-                uint32_t *d16 = q16 + (size_t)r * DIM + c * CH;
+        for (int pi = 0; pi < kPasses; ++pi) {
+            const int item = i0 + pi * 256 + threadIdx.x;
+            const bool ok = item < n_items && item / NCHK < rows;
 #pragma unroll
-                for (int e = 0; e < CH; ++e) {
-                    const bool pos = v[e] >= 0.0f;
-                    const uint32_t hb = __float_as_uint(v[e]) >> 16;  // exact for bf16 values
-                    d16[e] = BF ? (pos ? hb : (hb << 16)) : 0u;
+            for (int e = 0; e < NV; ++e) {
+                const uint32_t w[4] = {raw[pi][e].x, raw[pi][e].y, raw[pi][e].z, raw[pi][e].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if constexpr (BF) {
+                        v[pi][e * 8 + 2 * q] = ok ? bf16_lo(w[q]) : 0.0f;
+                        v[pi][e * 8 + 2 * q + 1] = ok ? bf16_hi(w[q]) : 0.0f;
+                    } else {
+                        v[pi][e * 4 + q] = ok ? __uint_as_float(w[q]) : 0.0f;
+                    }
                 }
             }
-            if (live) {
-                float *d32 = q32 + ((size_t)r * DIM + c * CH) * 2;
+        }
+#pragma unroll
+        for (int pi = 0; pi < kPasses; ++pi) {
+            const int item = i0 + pi * 256 + threadIdx.x;
+            if (i0 + pi * 256 >= n_items) break;  // uniform over the workgroup
+            const int r = item / NCHK, c = item % NCHK;
+            const bool live = r < rows;
+            if (r < pad_rows) {
+                T *dst = qr + (size_t)r * DIM + c * CH;
 #pragma unroll
                 for (int e = 0; e < CH; ++e) {
-                    const bool pos = v[e] >= 0.0f;
-                    d32[2 * e] = pos ? v[e] : 0.0f;
-                    d32[2 * e + 1] = pos ? 0.0f : v[e];
-                    ab += fabsf(v[e]);
+                    if constexpr (BF) reinterpret_cast<uint16_t *>(dst)[e] = f32_to_bf16(v[pi][e]);
+                    else reinterpret_cast<float *>(dst)[e] = v[pi][e];
                 }
             }
+            if (!dense) {
+                // (q+, q-): q+ = q, q- = 0 when q >= 0 (-0 included), else q+ = 0, q- = q.
+                float ab = 0.0f;
+                if (r < D.Rs16) {
+                    uint32_t *d16 = q16 + (size_t)r * DIM + c * CH;
 #pragma unroll
-            for (int o = 1; o < NCHK; o <<= 1) ab += __shfl_xor(ab, o);
-            if (live && c == 0) W.qabs[(size_t)sg * R1 + r] = ab * (1.0f + 1.0f / 256.0f);
+                    for (int e = 0; e < CH; ++e) {
+                        const bool pos = v[pi][e] >= 0.0f;
+                        const uint32_t hb = __float_as_uint(v[pi][e]) >> 16;  // exact for bf16 values
+                        d16[e] = BF ? (pos ? hb : (hb << 16)) : 0u;
+                    }
+                }
+                if (live) {
+                    float *d32 = q32 + ((size_t)r * DIM + c * CH) * 2;
+#pragma unroll
+                    for (int e = 0; e < CH; ++e) {
+                        const bool pos = v[pi][e] >= 0.0f;
+                        d32[2 * e] = pos ? v[pi][e] : 0.0f;
+                        d32[2 * e + 1] = pos ? 0.0f : v[pi][e];
+                        ab += fabsf(v[pi][e]);
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < NCHK; o <<= 1) ab += __shfl_xor(ab, o);
+                if (live && c == 0) W.qabs[(size_t)sg * R1 + r] = ab * (1.0f + 1.0f / 256.0f);
+            }
         }
     }
 }

@@ -26,8 +26,8 @@
 // it; those candidate pages (typically a little more than k) get the exact
 // fp32 chain -- two IEEE fused multiply-adds per dimension, q+ * max then
 // q- * min, one of them an exact zero and the products exact for bf16 -- and
-// the exact top-k is taken on keys (score bits, page).  The union is a bitmap
-// in LDS compacted into an ascending list.
+// the exact top-k is taken on keys (score bits, page).  Each row's pages go to
+// the workspace; the prefix kernel builds their union.
 #include "losa_internal.h"
 
 namespace losa {
@@ -119,21 +119,31 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
             amax[cb] = aux[in_tile];
         }
         const uint32_t *q16 = W.qsel16 + (size_t)sgi * D.Rs16 * DIM;
+        constexpr int KS = DIM / 16;
+        // row operands of row tile rt (row rt*16 + l16, dims 16*kk + 4*lg .. +3 as
+        // (q+, q-) pairs) and the sum |q| bounds of the lane's output rows;
+        // clamped indexes, masked where used
+        uint4 aop[KS];
+        float qa[4];
+        auto load_rows = [&](int rt) {
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+                aop[kk] = *reinterpret_cast<const uint4 *>(q16 + (size_t)(rt * 16 + l16) * DIM +
+                                                           16 * kk + 4 * lg);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qa[j] = qabs[min(rt * 16 + 4 * lg + j, R1 - 1)];
+        };
+        load_rows(0);
         // the whole tile's page operands, requested at once:
         // page cb*16 + l16, metadata chunk 4*kk + lg (dims 16kk + 4lg .. +3)
-        constexpr int KS = DIM / 16;
         uint4 bop[KS][4];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) bop[kk][cb] = mt[(size_t)(4 * kk + lg) * kTile + cb * 16 + l16];
-        for (int rt = 0; rt < D.Rs16 / 16; ++rt) {
-            // row operands: row rt*16 + l16, dims 16*kk + 4*lg .. +3 as (q+, q-) pairs
-            uint4 aop[KS];
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk)
-                aop[kk] = *reinterpret_cast<const uint4 *>(q16 + (size_t)(rt * 16 + l16) * DIM +
-                                                           16 * kk + 4 * lg);
+        __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
+        const int n_rt = D.Rs16 / 16;
+        for (int rt = 0; rt < n_rt; ++rt) {
             float4_t acc[4];
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) acc[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -144,16 +154,20 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
                     acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8_t, aop[kk]), __builtin_bit_cast(bf16x8_t, bop[kk][cb]),
                         acc[cb], 0, 0, 0);
+            float qcur[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qcur[j] = qa[j];
+            if (rt + 1 < n_rt) load_rows(rt + 1);  // in flight during this tile's epilogue
             // lane holds rows rt*16 + 4*lg + j of pages cb*16 + l16
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = rt * 16 + 4 * lg + j;
-                const float qa = r < R ? qabs[r] : 0.0f;
+                const float qa_j = r < R ? qcur[j] : 0.0f;
                 uint32_t lmax = 0u;
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) {
                     const bool valid = r < R && pl[cb] >= 0 && pl[cb] < sg.pages;
-                    const float e = kBoundRel * qa * amax[cb] + kBoundAbs;
+                    const float e = kBoundRel * qa_j * amax[cb] + kBoundAbs;
                     const float u = acc[cb][j];
                     if (valid) {
                         hb[(size_t)r * D.hb_stride + pl[cb]] = u + e;
@@ -190,20 +204,22 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2: exact top-k per row over the candidates, and the union.
+// Phase 2: exact top-k per row over the candidates.
 
 struct SelectDbg {
     int32_t *page_sel;   // [S][Hq][A][k]
-    int32_t *union_idx;  // [S][Hk][cap]
-    int32_t *union_cnt;  // [S][Hk]
-    int cap;
 };
 
 // The exact chain for global page gp (contract of include/losa.h); the page's
-// metadata chunks are loaded before the chain starts.
+// metadata chunks are loaded before the chain starts.  bf16: qw holds the
+// row's bf16 query values (word w = dimensions 2w, 2w+1); per dimension one
+// fused multiply-add with max_i (q >= 0, -0 included) or min_i (q < 0) -- the
+// same value as the pair q+ * max then q- * min, whose other product is an
+// exact zero.  fp32: qw holds (max(q,0), min(q,0)) per dimension, each product
+// rounded, then added.
 template <int DIM, bool BF>
 __device__ __forceinline__ float exact_bound(const uint4 *meta, const Dims &D, int g, int64_t gp,
-                                             const float *q) {
+                                             const uint32_t *qw) {
     constexpr int DPC = BF ? 4 : 2;
     constexpr int NCH = DIM / DPC;
     const uint4 *m = meta + (size_t)(g * D.n_tiles_total + gp / kTile) * NCH * kTile + gp % kTile;
@@ -219,13 +235,14 @@ __device__ __forceinline__ float exact_bound(const uint4 *meta, const Dims &D, i
             const uint4 m4 = mv[c];
             const int cc = c0 + c;
             if constexpr (BF) {
+                const uint2 q2 = *reinterpret_cast<const uint2 *>(qw + 2 * cc);
+                const float qd[4] = {bf16_lo(q2.x), bf16_hi(q2.x), bf16_lo(q2.y), bf16_hi(q2.y)};
                 const uint32_t wd[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc = __builtin_fmaf(q[2 * (4 * cc + e)], bf16_lo(wd[e]), acc);
-                    acc = __builtin_fmaf(q[2 * (4 * cc + e) + 1], bf16_hi(wd[e]), acc);
-                }
+                for (int e = 0; e < 4; ++e)
+                    acc = __builtin_fmaf(qd[e], qd[e] >= 0.0f ? bf16_lo(wd[e]) : bf16_hi(wd[e]), acc);
             } else {
+                const float *q = reinterpret_cast<const float *>(qw);
                 const float p0 = q[4 * cc + 0] * __uint_as_float(m4.x);
                 acc = acc + p0;
                 const float p1 = q[4 * cc + 1] * __uint_as_float(m4.y);
@@ -244,11 +261,11 @@ template <int DIM, bool BF>
 __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__ meta,
                                                const int32_t *__restrict__ kv_off,
                                                const int32_t *__restrict__ prefix_len, Work W,
+                                               const void *__restrict__ qrows,
                                                const float *__restrict__ qsel32,
                                                const float *__restrict__ hbound,
                                                const float *__restrict__ tmax, SelectDbg dbg) {
     extern __shared__ uint32_t smem[];
-    __shared__ int s_last;
     const int ng = D.S * D.Hk;
     const int sgi = blockIdx.x % ng;
     const int r = blockIdx.x / ng;
@@ -258,10 +275,9 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
     const int R = D.R, R1 = R > 0 ? R : 1, k = D.k;
     const int h = g * D.G + r / D.A, a = r % D.A;
     const bool all_pages = k >= sg.pages;
-    const int bm_words = (D.max_pages + 31) / 32;
-    uint32_t *bitmap = smem;
-    volatile int32_t *pend = reinterpret_cast<int32_t *>(smem + bm_words);
-    float *qw = reinterpret_cast<float *>(smem + bm_words + 128);
+    uint64_t *mk = reinterpret_cast<uint64_t *>(smem);  // [128] keys being merged
+    volatile int32_t *pend = reinterpret_cast<int32_t *>(smem + 256);  // [128] candidate pages
+    uint32_t *qw = smem + 384;                                          // the row's chain operands
     int32_t *psel = W.psel + ((size_t)sgi * R1 + r) * k;
 
     if (all_pages) {
@@ -273,57 +289,59 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         const int n_t = static_cast<int>((sg.gp0 + sg.pages - 1) / kTile - tile0 + 1);
         const float *tm = tmax + ((size_t)sgi * R1 + r) * D.n_tiles_grid;
         const float *hb = hbound + ((size_t)sgi * R1 + r) * D.hb_stride;
-        const float *qg = qsel32 + ((size_t)sgi * R1 + r) * DIM * 2;
-        // the row's chain operands, staged in LDS (read as broadcasts)
-        for (int i = lane; i < 2 * DIM; i += 64) qw[i] = qg[i];
-        const float *q = qw;
-        // loads of the tile maxima (up to 4 per lane) and of the first 4096 upper
-        // ends are issued together
-        constexpr int TMR = 4;
-        uint32_t tmk[TMR];
+        // Requested together: the row's chain operands, the tile maxima of the
+        // first 256 tiles and the first 4096 upper ends.  Indexes are clamped
+        // into the buffers; lanes past the end are masked where the values
+        // are used.
+        constexpr int QPL = BF ? DIM / 128 : 2 * DIM / 64;  // operand words per lane (0: half a wave)
+        uint32_t qv[QPL > 0 ? QPL : 1];
+        if constexpr (BF) {
+            const uint32_t *qg = reinterpret_cast<const uint32_t *>(
+                static_cast<const uint16_t *>(qrows) + ((size_t)sgi * D.R16 + r) * DIM);
+            qv[0] = qg[lane % (DIM / 2)];
+        } else {
+            const float *qg = qsel32 + ((size_t)sgi * R1 + r) * DIM * 2;
 #pragma unroll
-        for (int i = 0; i < TMR; ++i) {
-            const int x = lane + 64 * i;
-            tmk[i] = x < n_t ? ord_key(tm[x]) : 0u;
+            for (int i = 0; i < QPL; ++i) qv[i] = __float_as_uint(qg[lane + 64 * i]);
         }
+        constexpr int TMR = 4;
+        float tmv[TMR];
+#pragma unroll
+        for (int i = 0; i < TMR; ++i) tmv[i] = tm[min(lane + 64 * i, n_t - 1)];
         float4 hv[16];
         // upper ends of pages base + 256*jj + 4*lane + e, jj < 16, e < 4
         auto load_h = [&](int base) {
-            const int lim = sg.pages - base - 4 * lane;  // valid while 256*jj + e < lim
-            const float *hp = hb + base + 4 * lane;
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                if (256 * jj + 3 < lim) {
-                    hv[jj] = *reinterpret_cast<const float4 *>(hp + 256 * jj);
-                } else {
-                    hv[jj].x = 256 * jj + 0 < lim ? hp[256 * jj + 0] : -__builtin_huge_valf();
-                    hv[jj].y = 256 * jj + 1 < lim ? hp[256 * jj + 1] : -__builtin_huge_valf();
-                    hv[jj].z = 256 * jj + 2 < lim ? hp[256 * jj + 2] : -__builtin_huge_valf();
-                    hv[jj].w = 256 * jj + 3 < lim ? hp[256 * jj + 3] : -__builtin_huge_valf();
-                }
-            }
+            for (int jj = 0; jj < 16; ++jj)
+                hv[jj] = *reinterpret_cast<const float4 *>(
+                    hb + min(base + 256 * jj + 4 * lane, D.hb_stride - 4));
         };
         load_h(0);
-        // 1. threshold: the k-th largest tile maximum of the lower ends
+        __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
+        if constexpr (BF) {
+            if (lane < DIM / 2) qw[lane] = qv[0];
+        } else {
+#pragma unroll
+            for (int i = 0; i < QPL; ++i) qw[lane + 64 * i] = qv[i];
+        }
+        // 1. threshold: each lane's maximum over its tiles (lane, lane + 64, ...)
+        // of the lower ends; the k-th largest of these 64 values is reached by
+        // k distinct pages, so it is at most the k-th largest exact bound.
+        uint32_t gm = 0u;
+#pragma unroll
+        for (int i = 0; i < TMR; ++i)
+            if (lane + 64 * i < n_t) gm = max(gm, ord_key(tmv[i]));
+        for (int x = lane + 64 * TMR; x < n_t; x += 64) gm = max(gm, ord_key(tm[x]));
         uint32_t lam = 0u;  // below every finite key: all pages qualify
-        if (n_t >= k) {
-            uint64_t taken = 0ull;  // per lane: which of its tiles were extracted
+        if (min(n_t, 64) >= k) {
             for (int e = 0; e < k; ++e) {
-                uint32_t best = 0u;
-                int bi = -1;
-                for (int i = 0, x = lane; x < n_t; ++i, x += 64) {
-                    const uint32_t v = i < TMR ? tmk[i] : ord_key(tm[x]);
-                    if (!((taken >> i) & 1ull) && (bi < 0 || v > best)) {
-                        best = v;
-                        bi = i;
-                    }
-                }
-                const uint32_t m = wave_max_u32(best);
-                const uint64_t own = __ballot(bi >= 0 && best == m);
-                if (lane == __ffsll(static_cast<unsigned long long>(own)) - 1) taken |= 1ull << bi;
+                const uint32_t m = wave_max_u32(gm);
+                const uint64_t own = __ballot(gm == m);
+                if (lane == __ffsll(static_cast<unsigned long long>(own)) - 1) gm = 0u;
                 lam = m;
             }
         }
+        __syncthreads();  // qw visible to the chains
         // 2. candidates: upper end >= threshold; exact chain in batches of 64
         uint64_t lst = 0ull;  // lane e < k: e-th best (score key << 32 | ~page)
         int npend = 0;
@@ -342,19 +360,26 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                 }
             }
             const bool last_batch = base + 4096 >= sg.pages;
-            for (int bit = 0; bit < 64; ++bit) {
-                const bool c = (cmask >> bit) & 1ull;
+            // append each lane's candidates, lowest bit first, while any lane has some
+            for (;;) {
+                const bool c = cmask != 0ull;
                 const uint64_t bal = __ballot(c);
-                if (c) pend[npend + lanes_below(bal, lane)] = base + 256 * (bit >> 2) + 4 * lane + (bit & 3);
-                npend += __popcll(bal);
-                const bool last = last_batch && bit == 63;
+                if (bal) {
+                    const int bit = c ? __ffsll(static_cast<unsigned long long>(cmask)) - 1 : 0;
+                    if (c) {
+                        pend[npend + lanes_below(bal, lane)] = base + 256 * (bit >> 2) + 4 * lane + (bit & 3);
+                        cmask &= cmask - 1ull;
+                    }
+                    npend += __popcll(bal);
+                }
+                const bool last = last_batch && bal == 0ull;
                 while (npend >= 64 || (last && npend > 0)) {
                     __builtin_amdgcn_wave_barrier();
                     const int n = npend < 64 ? npend : 64;
                     uint64_t cand = 0ull;
                     if (lane < n) {
                         const int pc = pend[lane];
-                        const float u = exact_bound<DIM, BF>(meta, D, g, sg.gp0 + pc, q);
+                        const float u = exact_bound<DIM, BF>(meta, D, g, sg.gp0 + pc, qw);
                         cand = (static_cast<uint64_t>(ord_key(u)) << 32) |
                                static_cast<uint32_t>(~static_cast<uint32_t>(pc));
                     }
@@ -364,18 +389,30 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                     __builtin_amdgcn_wave_barrier();
                     if (lane < rest) pend[lane] = moved;
                     npend = rest;
-                    // merge: top-k of (candidates, current list)
-                    uint64_t av = cand, bv = lane < k ? lst : 0ull, nl = 0ull;
-                    for (int e = 0; e < k; ++e) {
-                        const uint64_t loc = av > bv ? av : bv;
-                        const uint64_t m = wave_max_u64(loc);
-                        if (m == 0ull) break;
-                        if (lane == e) nl = m;
-                        if (av == m) av = 0ull;
-                        else if (bv == m) bv = 0ull;
+                    // merge: rank every key of (batch, current list) among all of
+                    // them (keys are distinct: one per page); rank e < k -> lane e
+                    const int nlst = __popcll(__ballot(lane < k && lst != 0ull));
+                    if (lane < n) mk[lane] = cand;
+                    if (lane < nlst) mk[n + lane] = lst;
+                    __syncthreads();
+                    const int tot = n + nlst;
+                    const uint64_t x0 = lane < tot ? mk[lane] : 0ull;
+                    const uint64_t x1 = lane + 64 < tot ? mk[lane + 64] : 0ull;
+                    int r0 = 0, r1 = 0;
+#pragma unroll 4
+                    for (int i = 0; i < tot; ++i) {
+                        const uint64_t y = mk[i];
+                        r0 += y > x0;
+                        r1 += y > x1;
                     }
-                    lst = nl;
+                    __syncthreads();
+                    if (lane < tot && r0 < k) mk[r0] = x0;
+                    if (lane + 64 < tot && r1 < k) mk[r1] = x1;
+                    __syncthreads();
+                    lst = lane < min(tot, k) ? mk[lane] : 0ull;
+                    __syncthreads();
                 }
+                if (bal == 0ull) break;
             }
         }
         // 3. the row's pages (k of them: every page of the exact top-k is a candidate)
@@ -389,82 +426,24 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
             if (lane < k) dst[rank] = has ? page : -1;
         }
     }
-
-    // Arrival: the last row of this (sequence, KV head) builds the union.
-    __threadfence();
-    __syncthreads();
-    if (lane == 0) s_last = atomicAdd(&W.counters[sgi], 1) == R - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const int words = (sg.pages + 31) / 32;
-    for (int i = lane; i < words; i += 64) {
-        if (all_pages) {
-            const int rem = sg.pages - i * 32;
-            bitmap[i] = rem >= 32 ? 0xffffffffu : ((1u << rem) - 1u);
-        } else {
-            bitmap[i] = 0u;
-        }
-    }
-    __syncthreads();
-    if (!all_pages) {
-        const int32_t *ps = W.psel + (size_t)sgi * R1 * k;
-        for (int i = lane; i < R * k; i += 64) {
-            const int pg = ps[i];
-            if (pg >= 0) atomicOr(&bitmap[pg >> 5], 1u << (pg & 31));
-        }
-    }
-    __syncthreads();
-    const int wpt = (words + 63) / 64;
-    const int w0 = min(lane * wpt, words), w1 = min(w0 + wpt, words);
-    int cnt = 0;
-    for (int i = w0; i < w1; ++i) cnt += __popc(bitmap[i]);
-    int incl = cnt;
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
-    }
-    int pos = incl - cnt;
-    const int total = __shfl(incl, 63);
-    int32_t *uo = W.union_idx + (size_t)sgi * D.union_cap;
-    for (int i = w0; i < w1; ++i) {
-        uint32_t b = bitmap[i];
-        while (b) {
-            const int bit = __ffs(b) - 1;
-            b &= b - 1;
-            const int pg = i * 32 + bit;
-            if (pos < D.union_cap) uo[pos] = pg;
-            if (dbg.union_idx && pos < dbg.cap) dbg.union_idx[(size_t)sgi * dbg.cap + pos] = pg;
-            ++pos;
-        }
-    }
-    if (lane == 0) {
-        W.union_cnt[sgi] = min(total, D.union_cap);
-        if (dbg.union_cnt) dbg.union_cnt[sgi] = total;
-        W.counters[sgi] = 0;  // ready for the next kernel that counts arrivals
-    }
 }
 
-size_t select_lds_bytes(const Dims &D) {
-    const size_t bm_words = (D.max_pages + 31) / 32;
-    return (bm_words + 128 + 2 * (size_t)D.d) * 4;
-}
+size_t select_lds_bytes(const Dims &D) { return (384 + 2 * (size_t)D.d) * 4; }
 
 hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
                          const int32_t *prefix_len, const Work &W, int32_t *dbg_page_sel,
-                         int32_t *dbg_union_idx, int32_t *dbg_union_cnt, int dbg_union_cap,
                          hipStream_t st) {
     const int ng = D.S * D.Hk;
     const dim3 grid1(((D.n_tiles_grid + 3) / 4) * ng);
     const size_t lds = select_lds_bytes(D);
-    SelectDbg dbg{dbg_page_sel, dbg_union_idx, dbg_union_cnt, dbg_union_cap};
+    SelectDbg dbg{dbg_page_sel};
     auto *m = static_cast<const uint4 *>(meta);
 #define LAUNCH_S(DIMV, BFV)                                                                       \
     do {                                                                                          \
         hipLaunchKernelGGL((k_score<DIMV, BFV>), grid1, dim3(256), 0, st, D, m, kv_off,           \
                            prefix_len, W);                                                        \
         hipLaunchKernelGGL((k_select<DIMV, BFV>), dim3(ng * D.R), dim3(64), lds, st, D, m, kv_off, \
-                           prefix_len, W, W.qsel32, W.hbound, W.tmax, dbg);                       \
+                           prefix_len, W, W.qrows, W.qsel32, W.hbound, W.tmax, dbg);                       \
     } while (0)
     if (D.bf16) {
         if (D.d == 128) LAUNCH_S(128, true);
