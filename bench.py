@@ -20,7 +20,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -80,23 +79,17 @@ class HipEvents:
         self.made = []
 
 
-def source_digest(*names) -> str:
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "sparse_attention_block_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def traffic_from_profile(kernel_tag: str):
+    """HBM bytes per launch from the committed rocprofv3 counter passes, if they were
+    taken on the current kernel sources (else None)."""
+    from sparse_attention_block_amd.profiling import KERNEL_TAGS, source_digest
 
-
-def traffic_from_profile(kernel_tag: str, digest: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken
-    on the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"counters_{kernel_tag}.json")
-    if not os.path.exists(path):
+    if kernel_tag not in KERNEL_TAGS or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_digest") != digest:
+    if rec.get("source_digest") != source_digest(KERNEL_TAGS[kernel_tag][1]):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -130,6 +123,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="time without the per-kernel stage events")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="launch one plain copy kernel of MIB MiB before timing (reference "
+                         "dispatch for profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -195,6 +191,20 @@ def main():
         return {(t, li): [hip.create() for _ in range(L.LOSA_STAGE_EVENTS)]
                 for t in range(STEPS_PER_BLOCK) for li in range(len(layers))}
 
+    if args.copy_calibration:
+        from sparse_attention_block_amd.build import SELFTEST_LIB
+        st = ctypes.CDLL(SELFTEST_LIB)
+        st.losa_selftest_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_int, ctypes.c_void_p]
+        nb = args.copy_calibration << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        assert st.losa_selftest_copy(src.data_ptr(), dst.data_ptr(), nb, 4096, stream) == 0
+        torch.cuda.synchronize()
+        assert bool(torch.equal(src, dst))
+        del src, dst
+        log(f"[bench] copy calibration: {args.copy_calibration} MiB read + written once")
     log(f"[bench] warmup {args.warmup} blocks x {len(layers)} layers")
     for _ in range(args.warmup):
         run_block(None)
@@ -218,25 +228,17 @@ def main():
     value_us = total_ms * 1e3 / n_calls
     ms_per_step = total_ms / args.steps
 
-    # per-stage durations from the library's events
-    stages = {"dense": {"prepare": [], "prefix": [], "finish": [], "total": []},
-              "sparse": {"prepare": [], "select": [], "prefix": [], "finish": [], "total": []}}
+    # per-kernel durations from the library's stage events (one kernel per stage)
+    names = ["prepare", "score", "select", "prefix", "finish"]
+    stages = {"dense": {n: [] for n in names + ["total"]},
+              "sparse": {n: [] for n in names + ["total"]}}
     if use_events:
         for evs in ev_blocks:
             for (t, li), e in evs.items():
-                d = [hip.ms(e[i], e[i + 1]) * 1e3 for i in range(4)]
-                tot = hip.ms(e[0], e[4]) * 1e3
-                if t == 0:
-                    stages["dense"]["prepare"].append(d[0])
-                    stages["dense"]["prefix"].append(d[2])
-                    stages["dense"]["finish"].append(d[3])
-                    stages["dense"]["total"].append(tot)
-                else:
-                    stages["sparse"]["prepare"].append(d[0])
-                    stages["sparse"]["select"].append(d[1])
-                    stages["sparse"]["prefix"].append(d[2])
-                    stages["sparse"]["finish"].append(d[3])
-                    stages["sparse"]["total"].append(tot)
+                kind = "dense" if t == 0 else "sparse"
+                for i, n in enumerate(names):
+                    stages[kind][n].append(hip.ms(e[i], e[i + 1]) * 1e3)
+                stages[kind]["total"].append(hip.ms(e[0], e[5]) * 1e3)
     mean = lambda xs: float(np.mean(xs)) if xs else None
 
     # algorithmic bytes (bf16 storage)
@@ -258,9 +260,11 @@ def main():
 
     kernels = {}
     if use_events:
+        # name: (event durations, algorithmic HBM bytes per launch or 0, launches per block)
         spec = {
             "sparse_prefix": (stages["sparse"]["prefix"], union_bytes, STEPS_PER_BLOCK - 1),
-            "page_select": (stages["sparse"]["select"], meta_bytes, STEPS_PER_BLOCK - 1),
+            "page_score": (stages["sparse"]["score"], meta_bytes, STEPS_PER_BLOCK - 1),
+            "page_select": (stages["sparse"]["select"], 0, STEPS_PER_BLOCK - 1),
             "dense_prefix": (stages["dense"]["prefix"], dense_kv_bytes, 1),
             "sparse_prepare": (stages["sparse"]["prepare"], 0, STEPS_PER_BLOCK - 1),
             "sparse_finish": (stages["sparse"]["finish"], 0, STEPS_PER_BLOCK - 1),
@@ -277,8 +281,6 @@ def main():
                                       "frac_of_peak": gbps / PEAK_HBM_GBPS})
     dominant = max((k for k in kernels if "bytes_per_launch" in kernels[k]),
                    key=lambda k: kernels[k]["us_per_layer_block"], default=None)
-    digests = {"sparse_prefix": source_digest("prefix.hip"), "dense_prefix": source_digest("prefix.hip"),
-               "page_select": source_digest("select.hip")}
 
     def roofline(name):
         if name is None:
@@ -286,7 +288,7 @@ def main():
         k = kernels[name]
         return {"kernel": name, "bound": "hbm", "achieved": k["achieved_gbps"],
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k["frac_of_peak"],
-                "traffic": traffic_from_profile(name, digests[name]),
+                "traffic": traffic_from_profile(name),
                 "bytes_per_launch": k["bytes_per_launch"], "avg_launch_us": k["avg_us"]}
 
     sparse_us = mean(stages["sparse"]["total"]) if use_events else None

@@ -110,7 +110,7 @@ typedef struct losa_shape {
 } losa_shape;
 
 /* Number of events in losa_debug.stage_events. */
-#define LOSA_STAGE_EVENTS 5
+#define LOSA_STAGE_EVENTS 6
 
 /* Optional outputs of losa_step / losa_dense_first_step (each pointer may be
  * NULL; the dense call uses only stage_events). */
@@ -124,9 +124,9 @@ typedef struct losa_debug {
     int32_t union_cap;   /* capacity of each union_idx row; >= losa_union_capacity() */
     void **stage_events; /* profiling: LOSA_STAGE_EVENTS caller-created hipEvent_t, recorded
                             on the stream before the first kernel (0) and after the
-                            prepare (1), page-selection (2), prefix-attention (3) and
-                            finishing (4) kernels; a skipped stage records at the same
-                            point as the one before it */
+                            prepare (1), page-scoring (2), page-selection (3),
+                            prefix-attention (4) and finishing (5) kernels; a skipped
+                            stage records at the same point as the one before it */
 } losa_debug;
 
 /* Human-readable name of a status code (static string). */

@@ -50,7 +50,7 @@ class LosaDebug(ctypes.Structure):
     ]
 
 
-LOSA_STAGE_EVENTS = 5
+LOSA_STAGE_EVENTS = 6
 
 
 _lib = None

@@ -57,14 +57,15 @@ struct PartAcc {
     }
 };
 
-template <typename T, int DIM>
+template <typename T, int DIM, bool DENSE>
 __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
-    Dims D, int dense, int TG, const T *__restrict__ q_t, const T *__restrict__ k_blk,
+    Dims D, int TG, const T *__restrict__ q_t, const T *__restrict__ k_blk,
     const T *__restrict__ v_blk, const int32_t *__restrict__ kv_off,
     const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ active,
     const int32_t *__restrict__ union_cnt, const float *__restrict__ part_ml,
     const float *__restrict__ part_acc, float *__restrict__ op_cache,
     float *__restrict__ lp_cache, T *__restrict__ out) {
+    constexpr bool dense = DENSE;
     constexpr float kLn2 = 0.69314718055994530942f;
     constexpr float kLog2e = 1.44269504088896340736f;
     extern __shared__ float sm[];
@@ -307,19 +308,24 @@ hipError_t launch_finish(const Dims &D, bool dense, const void *q_t, const void 
     dim3 grid((D.B + TG - 1) / TG, D.Hq, D.S);
     const size_t lds = finish_lds_bytes(D, TG);
     const int threads = TG * D.d;
-    const int dn = dense ? 1 : 0;
-#define LAUNCH_F(T, DIMV)                                                                        \
-    hipLaunchKernelGGL((k_finish<T, DIMV>), grid, dim3(threads), lds, st, D, dn, TG,      \
+#define LAUNCH_F(T, DIMV, DN)                                                                     \
+    hipLaunchKernelGGL((k_finish<T, DIMV, DN>), grid, dim3(threads), lds, st, D, TG,             \
                        static_cast<const T *>(q_t), static_cast<const T *>(k_blk),               \
                        static_cast<const T *>(v_blk), kv_off, prefix_len, W.active, W.union_cnt, \
                        W.part_ml, W.part_acc, op_cache, lp_cache, static_cast<T *>(out))
+#define PICK_F(T, DIMV)                          \
+    do {                                         \
+        if (dense) LAUNCH_F(T, DIMV, true);      \
+        else LAUNCH_F(T, DIMV, false);           \
+    } while (0)
     if (D.bf16) {
-        if (D.d == 128) LAUNCH_F(uint16_t, 128);
-        else LAUNCH_F(uint16_t, 64);
+        if (D.d == 128) PICK_F(uint16_t, 128);
+        else PICK_F(uint16_t, 64);
     } else {
-        if (D.d == 128) LAUNCH_F(float, 128);
-        else LAUNCH_F(float, 64);
+        if (D.d == 128) PICK_F(float, 128);
+        else PICK_F(float, 64);
     }
+#undef PICK_F
 #undef LAUNCH_F
     return hipGetLastError();
 }

@@ -186,13 +186,14 @@ int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *
     if (e == hipSuccess) e = launch_prepare(D, true, q_t, nullptr, W, nullptr, nullptr, nullptr, s);
     if (e == hipSuccess) e = mark(ev, 1, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
+    if (e == hipSuccess) e = mark(ev, 3, s);
     if (e == hipSuccess)
         e = launch_prefix(D, true, k_cache, v_cache, kv_off, prefix_len, W, nullptr, nullptr, 0, s);
-    if (e == hipSuccess) e = mark(ev, 3, s);
+    if (e == hipSuccess) e = mark(ev, 4, s);
     if (e == hipSuccess)
         e = launch_finish(D, true, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache,
                           out, s);
-    if (e == hipSuccess) e = mark(ev, 4, s);
+    if (e == hipSuccess) e = mark(ev, 5, s);
     return hip_status(e);
 }
 
@@ -231,17 +232,19 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
     if (e == hipSuccess)
         e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active, dbg.union_cnt, s);
     if (e == hipSuccess) e = mark(ev, 1, s);
+    if (D.R > 0 && e == hipSuccess) e = launch_score(D, page_meta, kv_off, prefix_len, W, s);
+    if (e == hipSuccess) e = mark(ev, 2, s);
     if (D.R > 0 && e == hipSuccess)
         e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, s);
-    if (e == hipSuccess) e = mark(ev, 2, s);
+    if (e == hipSuccess) e = mark(ev, 3, s);
     if (D.R > 0 && e == hipSuccess)
         e = launch_prefix(D, false, k_cache, v_cache, kv_off, prefix_len, W, dbg.union_idx,
                           dbg.union_cnt, dbg.union_cap, s);
-    if (e == hipSuccess) e = mark(ev, 3, s);
+    if (e == hipSuccess) e = mark(ev, 4, s);
     if (e == hipSuccess)
         e = launch_finish(D, false, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache,
                           out, s);
-    if (e == hipSuccess) e = mark(ev, 4, s);
+    if (e == hipSuccess) e = mark(ev, 5, s);
     return hip_status(e);
 }
 

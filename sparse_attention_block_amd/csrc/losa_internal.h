@@ -63,6 +63,8 @@ hipError_t launch_page_meta(const Dims &D, const void *k_cache, const int32_t *k
 hipError_t launch_prepare(const Dims &D, bool dense, const void *q_t, const void *q_prev,
                           const Work &W, float *dbg_locality, int32_t *dbg_active,
                           int32_t *dbg_union_cnt, hipStream_t st);
+hipError_t launch_score(const Dims &D, const void *meta, const int32_t *kv_off,
+                        const int32_t *prefix_len, const Work &W, hipStream_t st);
 hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
                          const int32_t *prefix_len, const Work &W, int32_t *dbg_page_sel,
                          hipStream_t st);

@@ -122,14 +122,15 @@ __device__ int union_slice(const int32_t *__restrict__ psel, int n_sel, int page
     return total;
 }
 
-template <int DIM, int RTW>
-__global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
+template <int DIM, int RTW, bool DENSE>
+__global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
                                                      const uint16_t *__restrict__ kc,
                                                      const uint16_t *__restrict__ vc,
                                                      const int32_t *__restrict__ kv_off,
                                                      const int32_t *__restrict__ prefix_len,
                                                      Work W, int32_t *dbg_uidx, int32_t *dbg_ucnt,
                                                      int dbg_cap) {
+    constexpr bool dense = DENSE;
     constexpr int KSTEPS = DIM / 32;  // QK^T k-steps of 32 dims
     constexpr int DPL = DIM / 16;     // V dims per lane = PV MFMAs per page
     constexpr int RAW = 4 * 16 * DIM > kMaxBitmapWords ? 4 * 16 * DIM : kMaxBitmapWords;
@@ -332,12 +333,13 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D, int dense,
     }
 }
 
-template <int DIM>
-__global__ __launch_bounds__(256) void k_prefix_f32(Dims D, int dense, const float *__restrict__ kc,
+template <int DIM, bool DENSE>
+__global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restrict__ kc,
                                                     const float *__restrict__ vc,
                                                     const int32_t *__restrict__ kv_off,
                                                     const int32_t *__restrict__ prefix_len, Work W,
                                                     int32_t *dbg_uidx, int32_t *dbg_ucnt, int dbg_cap) {
+    constexpr bool dense = DENSE;
     constexpr int DPT = DIM / 16;
     __shared__ uint32_t s_bm[kMaxBitmapWords];
     __shared__ int s_wsum[4], s_pg[kSparseChunk];
@@ -432,35 +434,44 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const v
                          int32_t *dbg_uidx, int32_t *dbg_ucnt, int dbg_cap, hipStream_t st) {
     const int nch = dense ? D.n_chunks_dense : D.n_chunks_sparse;
     dim3 grid(nch * D.S * D.Hk);
-    const int dn = dense ? 1 : 0;
     if (D.bf16) {
         auto *k = static_cast<const uint16_t *>(k_cache);
         auto *v = static_cast<const uint16_t *>(v_cache);
         const int rows = dense ? D.Rd : D.R;
         const int n_rt = (rows + 15) / 16;
         const int rtw = n_rt <= 4 ? 1 : (n_rt <= 8 ? 2 : 4);
-#define LAUNCH_P(DIMV, RTWV)                                                                    \
-    hipLaunchKernelGGL((k_prefix_bf16<DIMV, RTWV>), grid, dim3(256), 0, st, D, dn, k, v, kv_off, \
+#define LAUNCH_P(DIMV, RTWV, DN)                                                                 \
+    hipLaunchKernelGGL((k_prefix_bf16<DIMV, RTWV, DN>), grid, dim3(256), 0, st, D, k, v, kv_off, \
                        prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap)
+#define PICK_P(DIMV, DN)                         \
+    do {                                         \
+        if (rtw == 1) LAUNCH_P(DIMV, 1, DN);     \
+        else if (rtw == 2) LAUNCH_P(DIMV, 2, DN); \
+        else LAUNCH_P(DIMV, 4, DN);              \
+    } while (0)
         if (D.d == 128) {
-            if (rtw == 1) LAUNCH_P(128, 1);
-            else if (rtw == 2) LAUNCH_P(128, 2);
-            else LAUNCH_P(128, 4);
+            if (dense) PICK_P(128, true);
+            else PICK_P(128, false);
         } else {
-            if (rtw == 1) LAUNCH_P(64, 1);
-            else if (rtw == 2) LAUNCH_P(64, 2);
-            else LAUNCH_P(64, 4);
+            if (dense) PICK_P(64, true);
+            else PICK_P(64, false);
         }
+#undef PICK_P
 #undef LAUNCH_P
     } else {
         auto *k = static_cast<const float *>(k_cache);
         auto *v = static_cast<const float *>(v_cache);
-        if (D.d == 128)
-            hipLaunchKernelGGL((k_prefix_f32<128>), grid, dim3(256), 0, st, D, dn, k, v, kv_off,
-                               prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap);
-        else
-            hipLaunchKernelGGL((k_prefix_f32<64>), grid, dim3(256), 0, st, D, dn, k, v, kv_off,
-                               prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap);
+#define LAUNCH_F(DIMV, DN)                                                                      \
+    hipLaunchKernelGGL((k_prefix_f32<DIMV, DN>), grid, dim3(256), 0, st, D, k, v, kv_off,       \
+                       prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap)
+        if (D.d == 128) {
+            if (dense) LAUNCH_F(128, true);
+            else LAUNCH_F(128, false);
+        } else {
+            if (dense) LAUNCH_F(64, true);
+            else LAUNCH_F(64, false);
+        }
+#undef LAUNCH_F
     }
     return hipGetLastError();
 }

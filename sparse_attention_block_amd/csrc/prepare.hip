@@ -77,12 +77,13 @@ __device__ __forceinline__ float locality_chain(const T *a, const T *b) {
     return acc;
 }
 
-template <typename T, int DIM>
-__global__ __launch_bounds__(256) void k_prepare(Dims D, int dense, const T *__restrict__ q_t,
+template <typename T, int DIM, bool DENSE>
+__global__ __launch_bounds__(256) void k_prepare(Dims D, const T *__restrict__ q_t,
                                                  const T *__restrict__ q_prev, Work W,
                                                  float *__restrict__ dbg_loc,
                                                  int32_t *__restrict__ dbg_act,
                                                  int32_t *__restrict__ dbg_ucnt) {
+    constexpr bool dense = DENSE;
     constexpr bool BF = sizeof(T) == 2;
     constexpr int CH = 8;            // dimensions per work item when stacking rows
     constexpr int NCHK = DIM / CH;   // 8 or 16 items per row
@@ -225,26 +226,24 @@ hipError_t launch_prepare(const Dims &D, bool dense, const void *q_t, const void
                           const Work &W, float *dbg_loc, int32_t *dbg_act, int32_t *dbg_ucnt,
                           hipStream_t st) {
     dim3 grid(D.Hk, D.S);
-    const int dn = dense ? 1 : 0;
+#define LAUNCH_Q(T, DIMV, DN)                                                                   \
+    hipLaunchKernelGGL((k_prepare<T, DIMV, DN>), grid, dim3(256), 0, st, D,                    \
+                       static_cast<const T *>(q_t), static_cast<const T *>(q_prev), W, dbg_loc, \
+                       dbg_act, dbg_ucnt)
+#define PICK_Q(T, DIMV)                      \
+    do {                                     \
+        if (dense) LAUNCH_Q(T, DIMV, true);  \
+        else LAUNCH_Q(T, DIMV, false);       \
+    } while (0)
     if (D.bf16) {
-        auto *a = static_cast<const uint16_t *>(q_t);
-        auto *b = static_cast<const uint16_t *>(q_prev);
-        if (D.d == 128)
-            hipLaunchKernelGGL((k_prepare<uint16_t, 128>), grid, dim3(256), 0, st, D, dn, a, b, W,
-                               dbg_loc, dbg_act, dbg_ucnt);
-        else
-            hipLaunchKernelGGL((k_prepare<uint16_t, 64>), grid, dim3(256), 0, st, D, dn, a, b, W,
-                               dbg_loc, dbg_act, dbg_ucnt);
+        if (D.d == 128) PICK_Q(uint16_t, 128);
+        else PICK_Q(uint16_t, 64);
     } else {
-        auto *a = static_cast<const float *>(q_t);
-        auto *b = static_cast<const float *>(q_prev);
-        if (D.d == 128)
-            hipLaunchKernelGGL((k_prepare<float, 128>), grid, dim3(256), 0, st, D, dn, a, b, W,
-                               dbg_loc, dbg_act, dbg_ucnt);
-        else
-            hipLaunchKernelGGL((k_prepare<float, 64>), grid, dim3(256), 0, st, D, dn, a, b, W,
-                               dbg_loc, dbg_act, dbg_ucnt);
+        if (D.d == 128) PICK_Q(float, 128);
+        else PICK_Q(float, 64);
     }
+#undef PICK_Q
+#undef LAUNCH_Q
     return hipGetLastError();
 }
 

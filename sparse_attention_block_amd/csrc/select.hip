@@ -430,21 +430,34 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
 
 size_t select_lds_bytes(const Dims &D) { return (384 + 2 * (size_t)D.d) * 4; }
 
+hipError_t launch_score(const Dims &D, const void *meta, const int32_t *kv_off,
+                        const int32_t *prefix_len, const Work &W, hipStream_t st) {
+    const int ng = D.S * D.Hk;
+    const dim3 grid(((D.n_tiles_grid + 3) / 4) * ng);
+    auto *m = static_cast<const uint4 *>(meta);
+#define LAUNCH_S(DIMV, BFV)                                                                     \
+    hipLaunchKernelGGL((k_score<DIMV, BFV>), grid, dim3(256), 0, st, D, m, kv_off, prefix_len, W)
+    if (D.bf16) {
+        if (D.d == 128) LAUNCH_S(128, true);
+        else LAUNCH_S(64, true);
+    } else {
+        if (D.d == 128) LAUNCH_S(128, false);
+        else LAUNCH_S(64, false);
+    }
+#undef LAUNCH_S
+    return hipGetLastError();
+}
+
 hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
                          const int32_t *prefix_len, const Work &W, int32_t *dbg_page_sel,
                          hipStream_t st) {
     const int ng = D.S * D.Hk;
-    const dim3 grid1(((D.n_tiles_grid + 3) / 4) * ng);
     const size_t lds = select_lds_bytes(D);
     SelectDbg dbg{dbg_page_sel};
     auto *m = static_cast<const uint4 *>(meta);
-#define LAUNCH_S(DIMV, BFV)                                                                       \
-    do {                                                                                          \
-        hipLaunchKernelGGL((k_score<DIMV, BFV>), grid1, dim3(256), 0, st, D, m, kv_off,           \
-                           prefix_len, W);                                                        \
-        hipLaunchKernelGGL((k_select<DIMV, BFV>), dim3(ng * D.R), dim3(64), lds, st, D, m, kv_off, \
-                           prefix_len, W, W.qrows, W.qsel32, W.hbound, W.tmax, dbg);                       \
-    } while (0)
+#define LAUNCH_S(DIMV, BFV)                                                                      \
+    hipLaunchKernelGGL((k_select<DIMV, BFV>), dim3(ng * D.R), dim3(64), lds, st, D, m, kv_off,   \
+                       prefix_len, W, W.qrows, W.qsel32, W.hbound, W.tmax, dbg)
     if (D.bf16) {
         if (D.d == 128) LAUNCH_S(128, true);
         else LAUNCH_S(64, true);

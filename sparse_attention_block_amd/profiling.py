@@ -1,0 +1,134 @@
+"""Summaries of rocprofv3 CSV output for this library's kernels.
+
+  python -m sparse_attention_block_amd.profiling stats TRACE_kernel_stats.csv --command CMD
+      per-kernel call counts and durations (rocprofv3 --kernel-trace --stats)
+  python -m sparse_attention_block_amd.profiling counters FETCH.csv WRITE.csv --copy-mib N
+      --command CMD [--json-dir DIR]
+      HBM bytes per dispatch from a FETCH_SIZE pass and a WRITE_SIZE pass (each a
+      rocprofv3 --pmc run), scaled by what the same counters read for the plain
+      copy kernel k_copy of N MiB (read N MiB, write N MiB) in the same run; with
+      --json-dir, one counters_<tag>.json per library kernel tagged below, holding
+      the bytes per launch and a digest of the sources the kernel was built from.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+# tag -> (kernel-name pattern, sources whose digest identifies the build)
+KERNEL_TAGS = {
+    "dense_prefix": (r"k_prefix_bf16<\d+, \d+, true>", ["prefix.hip", "losa_internal.h"]),
+    "sparse_prefix": (r"k_prefix_bf16<\d+, \d+, false>", ["prefix.hip", "losa_internal.h"]),
+    "page_score": (r"k_score<\d+, true>", ["select.hip", "losa_internal.h"]),
+    "page_select": (r"k_select<\d+, true>", ["select.hip", "losa_internal.h"]),
+    "sparse_finish": (r"k_finish<unsigned short, \d+, false>", ["finish.hip", "losa_internal.h"]),
+    "sparse_prepare": (r"k_prepare<unsigned short, \d+, false>", ["prepare.hip", "losa_internal.h"]),
+}
+COPY_KERNEL = r"(^|\W)k_copy($|\W)"
+
+
+def source_digest(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(HERE, "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel_name: str) -> str:
+    n = kernel_name.replace("void ", "")
+    return n.split("(")[0]
+
+
+def stats_table(path: str) -> list:
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return rows
+
+
+def counter_means(path: str, counter: str) -> dict:
+    vals = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                vals[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def find(means: dict, pattern: str):
+    hits = [k for k in means if re.search(pattern, k)]
+    if len(hits) != 1:
+        raise SystemExit(f"kernel pattern {pattern!r} matches {hits}")
+    return hits[0]
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s1 = sub.add_parser("stats")
+    s1.add_argument("csv")
+    s1.add_argument("--command", required=True)
+    s2 = sub.add_parser("counters")
+    s2.add_argument("fetch_csv")
+    s2.add_argument("write_csv")
+    s2.add_argument("--copy-mib", type=int, required=True)
+    s2.add_argument("--command", required=True)
+    s2.add_argument("--json-dir")
+    a = ap.parse_args(argv)
+
+    if a.cmd == "stats":
+        print(f"# rocprofv3 kernel statistics\n# command: {a.command}\n")
+        print(f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'time%':>6s}")
+        for name, calls, avg, mn, mx, pct in stats_table(a.csv):
+            print(f"{name[:64]:64s} {calls:6d} {avg:9.2f} {mn:9.2f} {mx:9.2f} {pct:6.2f}")
+        return 0
+
+    fetch = counter_means(a.fetch_csv, "FETCH_SIZE")
+    write = counter_means(a.write_csv, "WRITE_SIZE")
+    copy_bytes = a.copy_mib << 20
+    kf = find(fetch, COPY_KERNEL)
+    kw = find(write, COPY_KERNEL)
+    f_scale = copy_bytes / (fetch[kf][0] * 1024)
+    w_scale = copy_bytes / (write[kw][0] * 1024)
+    print(f"# HBM traffic per dispatch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch)\n"
+          f"# command: {a.command}\n"
+          f"# calibration: k_copy of {a.copy_mib} MiB read {fetch[kf][0]:.1f} KiB fetched and "
+          f"{write[kw][0]:.1f} KiB written -> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}\n")
+    print(f"{'kernel':64s} {'n':>4s} {'fetch_KiB':>11s} {'write_KiB':>11s} {'hbm_MiB':>9s}")
+    for name in sorted(fetch, key=lambda k: -fetch[k][0]):
+        if "losa::" not in name and not re.search(COPY_KERNEL, name):
+            continue
+        fk = fetch[name][0]
+        wk = write.get(name, (0.0, 0))[0]
+        mib = (fk * f_scale + wk * w_scale) * 1024 / 2**20
+        print(f"{name[:64]:64s} {fetch[name][1]:4d} {fk:11.1f} {wk:11.1f} {mib:9.2f}")
+    if a.json_dir:
+        for tag, (pat, srcs) in KERNEL_TAGS.items():
+            try:
+                name = find(fetch, pat)
+            except SystemExit:
+                continue
+            fk = fetch[name][0]
+            wk = write.get(name, (0.0, 0))[0]
+            rec = {"kernel": name, "fetch_kib": fk, "write_kib": wk, "fetch_scale": f_scale,
+                   "write_scale": w_scale,
+                   "hbm_bytes_per_launch": (fk * f_scale + wk * w_scale) * 1024,
+                   "source_digest": source_digest(srcs), "command": a.command}
+            with open(os.path.join(a.json_dir, f"counters_{tag}.json"), "w") as f:
+                json.dump(rec, f, indent=1)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
