@@ -11,10 +11,11 @@ sparse-step traffic exceed the 256 MB MALL).  The page metadata of the fixed
 prefix is built before timing (it changes once per committed block).
 
 Prints one JSON line: value = attention microseconds per (layer, denoising
-step), amortised over the block (dense first step included); plus per-kernel
-durations from HIP events the library records between its launches inside the
-timed region, the roofline of the dominant kernel, and the CPU oracle timed on
-one layer-block of the same workload.
+step), amortised over the block (dense first step included), from K timed
+blocks with only the library's launches on the stream; plus per-kernel
+durations from HIP events the library records between its launches during a
+second timed pass of K blocks, the roofline of the dominant kernel, and the CPU
+oracle timed on one layer-block of the same workload.
 """
 from __future__ import annotations
 
@@ -210,19 +211,30 @@ def main():
         run_block(None)
     torch.cuda.synchronize()
 
-    use_events = not args.no_events
-    ev_blocks = [new_events() for _ in range(args.steps)] if use_events else None
+    # value: exactly K blocks with nothing but the library's launches in the
+    # timed region (an event between kernels costs GPU time of its own)
     e_start, e_stop = hip.create(), hip.create()
     log(f"[bench] timing {args.steps} blocks")
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     hip.record(e_start, stream)
     for k in range(args.steps):
-        run_block(ev_blocks[k] if use_events else None)
+        run_block(None)
     hip.record(e_stop, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = hip.ms(e_start, e_stop)
+
+    # per-kernel durations: a second timed pass of K blocks with the library's
+    # stage events recorded between its launches
+    use_events = not args.no_events
+    ev_blocks = [new_events() for _ in range(args.steps)] if use_events else None
+    if use_events:
+        log(f"[bench] timing {args.steps} blocks with per-kernel events")
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            run_block(ev_blocks[k])
+        torch.cuda.synchronize()
 
     n_calls = args.steps * STEPS_PER_BLOCK * len(layers)
     value_us = total_ms * 1e3 / n_calls

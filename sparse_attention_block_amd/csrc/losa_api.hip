@@ -229,10 +229,19 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
     hipStream_t s = static_cast<hipStream_t>(stream);
     void **ev = dbg.stage_events;
     hipError_t e = mark(ev, 0, s);
-    if (e == hipSuccess)
-        e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active, dbg.union_cnt, s);
-    if (e == hipSuccess) e = mark(ev, 1, s);
-    if (D.R > 0 && e == hipSuccess) e = launch_score(D, page_meta, kv_off, prefix_len, W, s);
+    if (score_prep_fits(D)) {
+        // preparation and page scoring in one kernel (its time shows as scoring)
+        if (e == hipSuccess) e = mark(ev, 1, s);
+        if (e == hipSuccess)
+            e = launch_score_prep(D, q_t, q_prev, page_meta, kv_off, prefix_len, W, dbg.locality,
+                                  dbg.active, dbg.union_cnt, s);
+    } else {
+        if (e == hipSuccess)
+            e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active, dbg.union_cnt,
+                               s);
+        if (e == hipSuccess) e = mark(ev, 1, s);
+        if (D.R > 0 && e == hipSuccess) e = launch_score(D, page_meta, kv_off, prefix_len, W, s);
+    }
     if (e == hipSuccess) e = mark(ev, 2, s);
     if (D.R > 0 && e == hipSuccess)
         e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, s);

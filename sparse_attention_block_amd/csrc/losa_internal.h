@@ -65,6 +65,13 @@ hipError_t launch_prepare(const Dims &D, bool dense, const void *q_t, const void
                           int32_t *dbg_union_cnt, hipStream_t st);
 hipError_t launch_score(const Dims &D, const void *meta, const int32_t *kv_off,
                         const int32_t *prefix_len, const Work &W, hipStream_t st);
+// The sparse step's preparation folded into page scoring (bf16, the group's
+// block queries fit in LDS); replaces launch_prepare + launch_score.
+constexpr int kPrepVecs = 8;  // 16-byte query vectors per thread in the folded preparation
+bool score_prep_fits(const Dims &D);
+hipError_t launch_score_prep(const Dims &D, const void *q_t, const void *q_prev, const void *meta,
+                             const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
+                             float *dbg_loc, int32_t *dbg_act, int32_t *dbg_ucnt, hipStream_t st);
 hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
                          const int32_t *prefix_len, const Work &W, int32_t *dbg_page_sel,
                          hipStream_t st);

@@ -68,6 +68,97 @@ struct PageRegs {
     }
 };
 
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// NP pages of 16 tokens for the wave's row tiles i (those with rt_ok[i]):
+// S^T = K.Q^T with v_mfma_f32_16x16x32_bf16, online softmax in log2 units over
+// the NP pages together, then O^T += V^T.P with v_mfma_f32_16x16x16bf16_1k.
+// kop[n]: the lane's K operand of page n (token l%16, dims 32*kk + 8*(l/16) ..
+// +7); vw[n]: V words of tokens 4*(l/16) + j for the lane's DPL dims; valid[n]:
+// tokens of page n inside the prefix (0 for no page).  P is rounded to bf16 for
+// the MFMA and the row sum is taken from the rounded weights.  The running
+// output is rescaled only when some row's maximum changed (the factor is
+// exactly 1 otherwise).  Several pages at once keep independent MFMA chains
+// in flight and share one max reduction.
+template <int DIM, int RTW, int NP>
+__device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
+                                             const uint32_t (&vw)[NP][4][DIM / 32],
+                                             const int (&valid)[NP],
+                                             const uint4 (&qop)[RTW][DIM / 32],
+                                             const bool (&rt_ok)[RTW], float scale_log2,
+                                             float4_t (&oacc)[RTW][DIM / 16], float (&m_run)[RTW],
+                                             float (&l_run)[RTW], int lg) {
+    constexpr int KSTEPS = DIM / 32, DPL = DIM / 16;
+    bool full[NP];
+#pragma unroll
+    for (int n = 0; n < NP; ++n) full[n] = valid[n] >= kPage;  // uniform
+    // V^T operands: output dim DPL*(l%16) + e, tokens 4*lg .. 4*lg+3
+    short4_t vop[NP][DPL];
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+            const int q = e >> 1, sh = (e & 1) * 16;
+            vop[n][e] = short4_t{static_cast<short>(vw[n][0][q] >> sh), static_cast<short>(vw[n][1][q] >> sh),
+                                 static_cast<short>(vw[n][2][q] >> sh), static_cast<short>(vw[n][3][q] >> sh)};
+        }
+        if (!full[n]) {  // tokens past the prefix get zero values (uniform branch)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (4 * lg + j >= valid[n]) vop[n][e][j] = 0;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        if (!rt_ok[i]) break;
+        float sv[NP][4];
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, kop[n][kk]), __builtin_bit_cast(bf16x8_t, qop[i][kk]),
+                    sacc, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[n][j] = sacc[j] * scale_log2;
+            if (!full[n]) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (4 * lg + j >= valid[n]) sv[n][j] = -__builtin_huge_valf();
+            }
+        }
+        float mp = -__builtin_huge_valf();
+#pragma unroll
+        for (int n = 0; n < NP; ++n) mp = fmaxf(mp, fmaxf(fmaxf(sv[n][0], sv[n][1]), fmaxf(sv[n][2], sv[n][3])));
+        mp = shfl_max32(mp);
+        const float mn = fmaxf(m_run[i], mp);
+        if (__ballot(mn != m_run[i]) != 0ull) {  // uniform branch
+            const float alpha = __builtin_amdgcn_exp2f(m_run[i] - mn);
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) oacc[i][e] *= alpha;
+            l_run[i] *= alpha;
+            m_run[i] = mn;
+        }
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][0] - mn)),
+                                  static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][1] - mn))};
+            const bf16x2_t p23 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][2] - mn)),
+                                  static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][3] - mn))};
+            const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
+            l_run[i] += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
+            const short4_t pop = __builtin_bit_cast(short4_t, make_uint2(w01, w23));
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[n][e], pop, oacc[i][e], 0, 0, 0);
+        }
+    }
+}
+
 // Union of the selected pages of one (sequence, KV head) -- the rows' lists
 // psel[0 .. n_sel), -1 for none -- as a bitmap in LDS (bm: ceil(pages/32)
 // words), compacted in ascending page order.  The pages at union positions
@@ -152,6 +243,8 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     const int rows = dense ? D.Rd : D.R;
     const int nch = dense ? D.n_chunks_dense : D.n_chunks_sparse;
     const int n_rt = (rows + 15) / 16;
+    // waves per page group: a wave takes row tiles wr, wr + WPG, ... (RTW at
+    // most) of its group's pages
     const int WPG = n_rt < 4 ? n_rt : 4;
     const int n_pg = 4 / WPG;
     const int pg = w / WPG, wr = w % WPG;
@@ -215,56 +308,13 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
                 const int pn = page_of(itn);
                 nxt.load(kc, vc, base_of(pn), min(kPage, sg.len - pn * kPage), l16, lg);
             }
-            const int valid = cur.valid;
-            // V^T operands: output dim DPL*m + e, tokens 4*lg .. 4*lg+3 (masked past the prefix)
-            short4_t vop[DPL];
+            bool rt_ok[RTW];
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) {
-                const int q = e >> 1, sh = (e & 1) * 16;
-                short vv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    vv[j] = (4 * lg + j < valid) ? static_cast<short>(cur.v[j][q] >> sh) : short(0);
-                vop[e] = short4_t{vv[0], vv[1], vv[2], vv[3]};
-            }
-#pragma unroll
-            for (int i = 0; i < RTW; ++i) {
-                const int rt = wr + i * WPG;
-                if (rt >= n_rt) break;
-                float4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KSTEPS; ++kk)
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, cur.k[kk]),
-                        __builtin_bit_cast(bf16x8_t, qop[i][kk]), sacc, 0, 0, 0);
-                float sv[4];
-                float mp = -__builtin_huge_valf();
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sv[j] = (4 * lg + j < valid) ? sacc[j] * D.scale_log2 : -__builtin_huge_valf();
-                    mp = fmaxf(mp, sv[j]);
-                }
-                mp = shfl_max32(mp);
-                const float mn = fmaxf(m_run[i], mp);
-                const float alpha = __builtin_amdgcn_exp2f(m_run[i] - mn);
-                // P in bf16 feeds the MFMA; the row sum uses the same rounded weights.
-                uint16_t pb[4];
-                float ls = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pb[j] = f32_to_bf16(__builtin_amdgcn_exp2f(sv[j] - mn));
-                    ls += bf16_to_f32(pb[j]);
-                }
-                l_run[i] = l_run[i] * alpha + ls;
-                m_run[i] = mn;
-                const short4_t pop = short4_t{static_cast<short>(pb[0]), static_cast<short>(pb[1]),
-                                              static_cast<short>(pb[2]), static_cast<short>(pb[3])};
-#pragma unroll
-                for (int e = 0; e < DPL; ++e) {
-                    oacc[i][e] *= alpha;
-                    oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[e], pop, oacc[i][e], 0, 0, 0);
-                }
-            }
+            for (int i = 0; i < RTW; ++i) rt_ok[i] = wr + i * WPG < n_rt;
+            const int vld[1] = {cur.valid};
+            attend_pages<DIM, RTW, 1>(reinterpret_cast<const uint4(&)[1][KSTEPS]>(cur.k),
+                                      reinterpret_cast<const uint32_t(&)[1][4][DPL / 2]>(cur.v), vld,
+                                      qop, rt_ok, D.scale_log2, oacc, m_run, l_run, lg);
             cur = nxt;
         }
     }
@@ -299,36 +349,195 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
         }
         return;
     }
-    // Several page groups (then RTW == 1 and n_rt <= 2): combine through LDS.
-    if (lg == 0) {
-        s_ml[w][l16][0] = m_run[0];
-        s_ml[w][l16][1] = l_run[0];
+    // Several page groups: combine them through LDS, RTW rounds of one row
+    // tile per wave (round i: the waves hold row tiles i*WPG .. i*WPG + WPG-1).
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        if (i * WPG >= n_rt) break;  // uniform
+        if (i > 0) __syncthreads();  // the previous round has read s_acc
+        if (lg == 0) {
+            s_ml[w][l16][0] = m_run[i];
+            s_ml[w][l16][1] = l_run[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) s_acc[w][l16][DPL * (4 * lg + j) + e] = oacc[i][e][j];
+        __syncthreads();
+        for (int idx = tid; idx < WPG * 16 * DIM; idx += 256) {
+            const int rtile = idx / (16 * DIM);
+            const int rr = (idx / DIM) % 16;
+            const int dim = idx % DIM;
+            const int r = (i * WPG + rtile) * 16 + rr;
+            if (r >= rows) continue;
+            float mx = -__builtin_huge_valf();
+            for (int q = 0; q < n_pg; ++q) mx = fmaxf(mx, s_ml[q * WPG + rtile][rr][0]);
+            float lsum = 0.0f, a = 0.0f;
+            for (int q = 0; q < n_pg; ++q) {
+                const int wq = q * WPG + rtile;
+                const float wgt = __builtin_amdgcn_exp2f(s_ml[wq][rr][0] - mx);
+                lsum += wgt * s_ml[wq][rr][1];
+                a += wgt * s_acc[wq][rr][dim];
+            }
+            const size_t pb = ((size_t)sgi * nch + chunk) * rows + r;
+            W.part_acc[pb * DIM + dim] = a;
+            if (dim == 0) {
+                W.part_ml[pb * 2 + 0] = mx;
+                W.part_ml[pb * 2 + 1] = lsum;
+            }
+        }
+    }
+}
+
+// Dense first-step pass, bf16.  Each page of the workgroup's chunk is read
+// from HBM once: every thread holds 16-byte pieces of the next kDensePrefetch
+// pages in registers and stores the oldest pair into a double-buffered pair of
+// LDS pages; the four waves (row tiles w, w + 4, ...) then read their K and V^T
+// operands from LDS and attend the two pages together.  Chunks of 8 elements are XOR-swizzled per token row, which makes both
+// operand reads free of bank conflicts.  Same arithmetic as k_prefix_bf16.
+constexpr int kDensePrefetch = 4;
+
+template <int DIM>
+__device__ __forceinline__ int swz(int t, int c) {
+    constexpr int CPT = DIM / 8;  // 16-byte chunks per token row
+    return t * CPT + (c ^ (t & (CPT - 1)));
+}
+
+template <int DIM, int RTW>
+__global__ __launch_bounds__(256) void k_prefix_dense_bf16(Dims D, const uint16_t *__restrict__ kc,
+                                                           const uint16_t *__restrict__ vc,
+                                                           const int32_t *__restrict__ kv_off,
+                                                           const int32_t *__restrict__ prefix_len,
+                                                           Work W) {
+    constexpr int KSTEPS = DIM / 32, DPL = DIM / 16, CPT = DIM / 8;
+    constexpr int NCK = 16 * CPT;            // chunks per page and tensor
+    constexpr int CPTH = 2 * NCK / 256;      // chunks per thread per page (K and V together)
+    __shared__ uint4 s_page[4][2][NCK];      // [buffer: 2 pairs of pages][K, V][swizzled chunk]
+    const int ng = D.S * D.Hk;
+    const int sgi = blockIdx.x % ng;
+    const int chunk = blockIdx.x / ng;
+    const int s = sgi / D.Hk, g = sgi % D.Hk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
+    const int first = chunk * kDenseChunk;
+    const int n_here = min(kDenseChunk, sg.pages - first);
+    if (n_here <= 0) return;
+    const int rows = D.Rd, nch = D.n_chunks_dense;
+    const int n_rt = (rows + 15) / 16;
+
+    // Q operands (B of QK^T) of row tiles w + 4i: lane l holds row l%16, dims
+    // 32*kk + 8*(l/16) .. +7 (row tiles past the last read tile n_rt-1, unused)
+    uint4 qop[RTW][KSTEPS];
+    const uint16_t *qr = static_cast<const uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        const int rt = min(w + 4 * i, n_rt - 1);
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            qop[i][kk] = *reinterpret_cast<const uint4 *>(qr + (size_t)(rt * 16 + l16) * DIM + 32 * kk + 8 * lg);
+    }
+    // this thread's pieces of a page: piece q = tid + 256*h is chunk q % NCK of
+    // K (q < NCK) or V, i.e. token (q % NCK) / CPT, elements 8*((q % NCK) % CPT) ..
+    auto load_piece = [&](int p, int h) {
+        const int q = tid + 256 * h, cq = q % NCK;
+        const size_t base = ((size_t)g * D.T + sg.off + (size_t)(first + p) * kPage) * DIM;
+        const uint16_t *src = (q < NCK ? kc : vc) + base + (cq / CPT) * DIM + (cq % CPT) * 8;
+        return *reinterpret_cast<const uint4 *>(src);
+    };
+    uint4 pf[kDensePrefetch][CPTH];
+#pragma unroll
+    for (int d = 0; d < kDensePrefetch; ++d)
+#pragma unroll
+        for (int h = 0; h < CPTH; ++h) pf[d][h] = load_piece(min(d, n_here - 1), h);
+
+    float4_t oacc[RTW][DPL];
+    float m_run[RTW], l_run[RTW];
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        m_run[i] = -__builtin_huge_valf();
+        l_run[i] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) oacc[i][e] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    bool rt_ok[RTW];
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) rt_ok[i] = w + 4 * i < n_rt;
+    // pages are attended in pairs (independent MFMA chains, one shared max)
+    static_assert(kDensePrefetch % 2 == 0, "pages are staged in pairs");
+    for (int it = 0; it < n_here; it += kDensePrefetch) {
+#pragma unroll
+        for (int d = 0; d < kDensePrefetch; d += 2) {
+            const int pi = it + d;
+            if (pi >= n_here) break;  // uniform
+            const int pb = 2 * ((pi >> 1) & 1);
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int h = 0; h < CPTH; ++h) {
+                    const int q = tid + 256 * h, cq = q % NCK;
+                    s_page[pb + n][q < NCK ? 0 : 1][swz<DIM>(cq / CPT, cq % CPT)] = pf[d + n][h];
+                }
+            // refill with the pages kDensePrefetch ahead (clamped: rereads the last page)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int h = 0; h < CPTH; ++h)
+                    pf[d + n][h] = load_piece(min(pi + n + kDensePrefetch, n_here - 1), h);
+            __syncthreads();  // pages pi, pi+1 complete in LDS; the pair before is no longer read
+
+            uint4 kop[2][KSTEPS];
+            uint32_t vw[2][4][DPL / 2];
+            int valid[2];
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                // a page past the chunk (odd count) attends nothing
+                valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + pi + n) * kPage) : 0;
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk) kop[n][kk] = s_page[pb + n][0][swz<DIM>(l16, 4 * kk + lg)];
+                // V words of tokens 4*lg + j for the lane's dims DPL*l16 .. +DPL-1
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 c4 = s_page[pb + n][1][swz<DIM>(4 * lg + j, (DPL * l16) / 8)];
+                    if constexpr (DPL == 8) {
+                        vw[n][j][0] = c4.x; vw[n][j][1] = c4.y; vw[n][j][2] = c4.z; vw[n][j][3] = c4.w;
+                    } else {
+                        const bool hi = (l16 & 1) != 0;
+                        vw[n][j][0] = hi ? c4.z : c4.x;
+                        vw[n][j][1] = hi ? c4.w : c4.y;
+                    }
+                }
+            }
+            attend_pages<DIM, RTW, 2>(kop, vw, valid, qop, rt_ok, D.scale_log2, oacc, m_run, l_run, lg);
+        }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < RTW; ++i) l_run[i] = shfl_sum32(l_run[i]);
+
+    // Lane l holds, for row l%16, dims DPL*(4*lg + j) + e.
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) s_acc[w][l16][DPL * (4 * lg + j) + e] = oacc[0][e][j];
-    __syncthreads();
-    for (int idx = tid; idx < n_rt * 16 * DIM; idx += 256) {
-        const int rtile = idx / (16 * DIM);
-        const int rr = (idx / DIM) % 16;
-        const int dim = idx % DIM;
-        const int r = rtile * 16 + rr;
+    for (int i = 0; i < RTW; ++i) {
+        const int rt = w + 4 * i;
+        if (rt >= n_rt) break;
+        const int r = rt * 16 + l16;
         if (r >= rows) continue;
-        float mx = -__builtin_huge_valf();
-        for (int q = 0; q < n_pg; ++q) mx = fmaxf(mx, s_ml[q * WPG + rtile][rr][0]);
-        float lsum = 0.0f, a = 0.0f;
-        for (int q = 0; q < n_pg; ++q) {
-            const int wq = q * WPG + rtile;
-            const float wgt = __builtin_amdgcn_exp2f(s_ml[wq][rr][0] - mx);
-            lsum += wgt * s_ml[wq][rr][1];
-            a += wgt * s_acc[wq][rr][dim];
-        }
         const size_t pb = ((size_t)sgi * nch + chunk) * rows + r;
-        W.part_acc[pb * DIM + dim] = a;
-        if (dim == 0) {
-            W.part_ml[pb * 2 + 0] = mx;
-            W.part_ml[pb * 2 + 1] = lsum;
+        if (lg == 0) {
+            W.part_ml[pb * 2 + 0] = m_run[i];
+            W.part_ml[pb * 2 + 1] = l_run[i];
+        }
+        float *dst = W.part_acc + pb * DIM;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float tmp[DPL];
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) tmp[e] = oacc[i][e][j];
+            float *d0 = dst + DPL * (4 * lg + j);
+#pragma unroll
+            for (int e = 0; e < DPL; e += 4)
+                *reinterpret_cast<float4 *>(d0 + e) = make_float4(tmp[e], tmp[e + 1], tmp[e + 2], tmp[e + 3]);
         }
     }
 }
@@ -449,13 +658,29 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const v
         else if (rtw == 2) LAUNCH_P(DIMV, 2, DN); \
         else LAUNCH_P(DIMV, 4, DN);              \
     } while (0)
+#define LAUNCH_D(DIMV, RTWV)                                                                      \
+    hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV>), grid, dim3(256), 0, st, D, k, v, kv_off, \
+                       prefix_len, W)
+        // dense pass: every wave takes row tiles w, w + 4, ...
+        const int rtwd = n_rt <= 4 ? 1 : (n_rt <= 8 ? 2 : 4);
         if (D.d == 128) {
-            if (dense) PICK_P(128, true);
-            else PICK_P(128, false);
+            if (dense) {
+                if (rtwd == 1) LAUNCH_D(128, 1);
+                else if (rtwd == 2) LAUNCH_D(128, 2);
+                else LAUNCH_D(128, 4);
+            } else {
+                PICK_P(128, false);
+            }
         } else {
-            if (dense) PICK_P(64, true);
-            else PICK_P(64, false);
+            if (dense) {
+                if (rtwd == 1) LAUNCH_D(64, 1);
+                else if (rtwd == 2) LAUNCH_D(64, 2);
+                else LAUNCH_D(64, 4);
+            } else {
+                PICK_P(64, false);
+            }
         }
+#undef LAUNCH_D
 #undef PICK_P
 #undef LAUNCH_P
     } else {

@@ -82,6 +82,50 @@ __device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {
 // ---------------------------------------------------------------------------
 // Phase 1: bounds of every (row, page) of one tile, as an interval.
 
+// Bounds of row tile rt (rows rt*16 .. +15) against the wave's 64-page tile
+// with v_mfma_f32_16x16x32_bf16: aop = the lane's row operand (row rt*16 + l16,
+// dims 16*kk + 4*lg .. +3 as (q+, q-) pairs), bop = the page operands (page
+// cb*16 + l16, chunk 4*kk + lg), qa = sum |q| bounds of rows rt*16 + 4*lg + j.
+// Writes each (row, page) upper end and each row's largest lower end of the tile.
+template <int DIM>
+__device__ __forceinline__ void bound_rowtile(const Dims &D, int rt, const uint4 (&aop)[DIM / 16],
+                                              const float (&qa)[4], const uint4 (&bop)[DIM / 16][4],
+                                              const float (&amax)[4], const int (&pl)[4], int pages,
+                                              int bx, int l16, int lg, float *hb, float *tm) {
+    constexpr int KS = DIM / 16;
+    const int R = D.R;
+    float4_t acc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, aop[kk]), __builtin_bit_cast(bf16x8_t, bop[kk][cb]),
+                acc[cb], 0, 0, 0);
+    // lane holds rows rt*16 + 4*lg + j of pages cb*16 + l16
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = rt * 16 + 4 * lg + j;
+        const float qa_j = r < R ? qa[j] : 0.0f;
+        uint32_t lmax = 0u;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const bool valid = r < R && pl[cb] >= 0 && pl[cb] < pages;
+            const float e = kBoundRel * qa_j * amax[cb] + kBoundAbs;
+            const float u = acc[cb][j];
+            if (valid) {
+                hb[(size_t)r * D.hb_stride + pl[cb]] = u + e;
+                lmax = max(lmax, ord_key(u - e));
+            }
+        }
+        lmax = row16_max_u32(lmax);
+        if (l16 == 15 && r < R) tm[(size_t)r * D.n_tiles_grid + bx] = ord_to_f32(lmax);
+    }
+}
+
+
 template <int DIM, bool BF>
 __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__ meta,
                                                const int32_t *__restrict__ kv_off,
@@ -144,39 +188,14 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
         __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
         const int n_rt = D.Rs16 / 16;
         for (int rt = 0; rt < n_rt; ++rt) {
-            float4_t acc[4];
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) acc[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
-                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, aop[kk]), __builtin_bit_cast(bf16x8_t, bop[kk][cb]),
-                        acc[cb], 0, 0, 0);
             float qcur[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) qcur[j] = qa[j];
+            uint4 acur[KS];
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) acur[kk] = aop[kk];
             if (rt + 1 < n_rt) load_rows(rt + 1);  // in flight during this tile's epilogue
-            // lane holds rows rt*16 + 4*lg + j of pages cb*16 + l16
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = rt * 16 + 4 * lg + j;
-                const float qa_j = r < R ? qcur[j] : 0.0f;
-                uint32_t lmax = 0u;
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    const bool valid = r < R && pl[cb] >= 0 && pl[cb] < sg.pages;
-                    const float e = kBoundRel * qa_j * amax[cb] + kBoundAbs;
-                    const float u = acc[cb][j];
-                    if (valid) {
-                        hb[(size_t)r * D.hb_stride + pl[cb]] = u + e;
-                        lmax = max(lmax, ord_key(u - e));
-                    }
-                }
-                lmax = row16_max_u32(lmax);
-                if (l16 == 15 && r < R) tm[(size_t)r * D.n_tiles_grid + bx] = ord_to_f32(lmax);
-            }
+            bound_rowtile<DIM>(D, rt, acur, qcur, bop, amax, pl, sg.pages, bx, l16, lg, hb, tm);
         }
     } else {
         // fp32 storage: lane = page, any summation order (the interval absorbs it)
@@ -200,6 +219,193 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
             const uint32_t lmax = wave_max_u32(valid ? ord_key(u - e) : 0u);
             if (lane == 0) tm[(size_t)r * D.n_tiles_grid + bx] = ord_to_f32(lmax);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 1 with the step's preparation folded in (bf16, the group's block
+// queries fit in LDS).  Every workgroup of a (sequence, KV head) repeats the
+// preparation from the same inputs -- locality chain, active set, stacked rows
+// -- so all of them agree, and builds its MFMA row operands from LDS; the
+// workgroup of the first tiles also writes the active list and the stacked rows
+// for the later kernels and resets the union size.  The locality chain is the
+// one of prepare.hip: each rounded square added in ascending dimension order.
+
+constexpr int kPrepPad = 4;  // words of padding per LDS row (bank spread)
+
+template <int DIM>
+__global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__restrict__ q_t,
+                                                    const uint16_t *__restrict__ q_prev,
+                                                    const uint4 *__restrict__ meta,
+                                                    const int32_t *__restrict__ kv_off,
+                                                    const int32_t *__restrict__ prefix_len,
+                                                    Work W, float *__restrict__ dbg_loc,
+                                                    int32_t *__restrict__ dbg_act,
+                                                    int32_t *__restrict__ dbg_ucnt) {
+    constexpr int KS = DIM / 16, NCH = DIM / 4;
+    constexpr int RWP = DIM / 2 + kPrepPad;  // words per LDS row: bf16 pairs of dims 2w, 2w+1
+    constexpr int VPR = DIM / 8;             // 16-byte vectors per row
+    extern __shared__ uint32_t qsm[];        // [2][G*B][RWP]: q_t rows, then q_prev rows
+    __shared__ float e_s[kMaxRows];
+    __shared__ int sel_s[kMaxRows];
+    __shared__ int act_s[kMaxRows];
+    __shared__ float qabs_s[kMaxRows];
+    const int ng = D.S * D.Hk;
+    const int sgi = blockIdx.x % ng, blk = blockIdx.x / ng;
+    const int s = sgi / D.Hk, g = sgi % D.Hk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int bx = blk * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = D.G, B = D.B, A = D.A, GB = G * B, R = D.R, Hq = D.Hq;
+    const bool writer = blk == 0;
+
+    // 1. requested together: the group's query rows (clamped 16-byte vectors)
+    //    and, for a tile in range, the tile's page operands
+    const int nvec = GB * VPR;
+    static_assert(kPrepVecs == 8, "one named register per query vector below");
+    auto qload = [&](int i) {
+        const int idx = min(tid + 256 * i, 2 * nvec - 1);
+        const int which = idx / nvec, v = idx % nvec;
+        const int row = v / VPR, c = v % VPR;
+        const uint16_t *src = (which ? q_prev : q_t) +
+                              ((size_t)(s * B + row % B) * Hq + g * G + row / B) * DIM + c * 8;
+        return *reinterpret_cast<const uint4 *>(src);
+    };
+    const uint4 qv0 = qload(0), qv1 = qload(1), qv2 = qload(2), qv3 = qload(3);
+    const uint4 qv4 = qload(4), qv5 = qload(5), qv6 = qload(6), qv7 = qload(7);
+    __builtin_amdgcn_sched_barrier(0);  // the query vectors are requested first
+    const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
+    const int64_t tile0 = sg.gp0 / kTile;
+    const int n_t = static_cast<int>((sg.gp0 + sg.pages - 1) / kTile - tile0 + 1);
+    const bool tile_ok = D.k < sg.pages && bx < n_t;  // uniform over the wave
+    // a wave without a tile in range loads a clamped, in-bounds tile and never
+    // uses it, so that no load sits in a branch
+    const int64_t tile =
+        min(tile0 + max(0, min(bx, n_t - 1)), static_cast<int64_t>(D.n_tiles_total - 1));
+    const int R1 = R > 0 ? R : 1;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const uint4 *mt = meta + (size_t)(g * D.n_tiles_total + tile) * NCH * kTile;
+    uint4 bop[KS][4];
+    float amax[4];
+    int pl[4];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) bop[kk][cb] = mt[(size_t)(4 * kk + lg) * kTile + cb * 16 + l16];
+    const float *aux = reinterpret_cast<const float *>(reinterpret_cast<const char *>(meta) +
+                                                       D.meta_main_bytes) +
+                       (size_t)g * D.n_tiles_total * kTile + tile * kTile;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        pl[cb] = static_cast<int>(tile * kTile + cb * 16 + l16 - sg.gp0);
+        amax[cb] = aux[cb * 16 + l16];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
+    auto qstore = [&](int i, const uint4 &q) {
+        const int idx = min(tid + 256 * i, 2 * nvec - 1);
+        const int which = idx / nvec, v = idx % nvec;
+        *reinterpret_cast<uint4 *>(&qsm[(which * GB + v / VPR) * RWP + (v % VPR) * 4]) = q;
+    };
+    qstore(0, qv0);
+    qstore(1, qv1);
+    qstore(2, qv2);
+    qstore(3, qv3);
+    qstore(4, qv4);
+    qstore(5, qv5);
+    qstore(6, qv6);
+    qstore(7, qv7);
+    if (writer && tid == 0) {
+        W.union_cnt[sgi] = 0;
+        if (dbg_ucnt) dbg_ucnt[sgi] = 0;  // the sparse prefix kernel overwrites them
+    }
+    __syncthreads();
+
+    // 2. locality chain per (query head, token), then the active set
+    if (tid < GB) {
+        const uint32_t *a = &qsm[tid * RWP], *b = &qsm[(GB + tid) * RWP];
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int w = 0; w < DIM / 2; ++w) {
+            const float d0 = bf16_lo(a[w]) - bf16_lo(b[w]);
+            const float s0 = d0 * d0;
+            acc = acc + s0;
+            const float d1 = bf16_hi(a[w]) - bf16_hi(b[w]);
+            const float s1 = d1 * d1;
+            acc = acc + s1;
+        }
+        e_s[tid] = acc;
+        if (writer && dbg_loc)
+            dbg_loc[((size_t)s * Hq + g * G + tid / B) * B + tid % B] = acc / static_cast<float>(DIM);
+    }
+    __syncthreads();
+    if (tid < GB) {
+        const int j = tid / B, t = tid % B;
+        const float et = e_s[tid];
+        int rank = 0;
+        for (int u = 0; u < B; ++u) {
+            const float eu = e_s[j * B + u];
+            rank += (eu > et) || (eu == et && u < t);
+        }
+        sel_s[tid] = rank < A;
+    }
+    __syncthreads();
+    if (tid < GB && sel_s[tid]) {
+        const int j = tid / B, t = tid % B;
+        int pos = 0;
+        for (int u = 0; u < t; ++u) pos += sel_s[j * B + u];
+        act_s[j * A + pos] = t;
+        if (writer) {
+            W.active[((size_t)s * Hq + g * G + j) * A + pos] = t;
+            if (dbg_act) dbg_act[((size_t)s * Hq + g * G + j) * A + pos] = t;
+        }
+    }
+    __syncthreads();
+
+    // 3. stacked rows r = j*|A| + a: sum |q| bounds; the writer stores the rows
+    //    (bf16, rows up to the next multiple of 16 zeroed) for the later kernels
+    if (tid < R) {
+        const uint32_t *a = &qsm[((tid / A) * B + act_s[tid]) * RWP];
+        float ab = 0.0f;
+        for (int w = 0; w < DIM / 2; ++w) ab += fabsf(bf16_lo(a[w])) + fabsf(bf16_hi(a[w]));
+        qabs_s[tid] = ab * (1.0f + 1.0f / 256.0f);
+    }
+    if (writer) {
+        uint16_t *qr = static_cast<uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
+        for (int i = tid; i < D.Rs16 * VPR; i += 256) {
+            const int r = i / VPR, c = i % VPR;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (r < R) v = *reinterpret_cast<const uint4 *>(&qsm[((r / A) * B + act_s[r]) * RWP + c * 4]);
+            *reinterpret_cast<uint4 *>(qr + (size_t)r * DIM + c * 8) = v;
+        }
+    }
+    __syncthreads();
+    if (!tile_ok) return;
+
+    // 4. the tile's bounds, row tile by row tile, row operands built from LDS
+    float *hb = W.hbound + (size_t)sgi * R1 * D.hb_stride;
+    float *tm = W.tmax + (size_t)sgi * R1 * D.n_tiles_grid;
+    for (int rt = 0; rt < D.Rs16 / 16; ++rt) {
+        const int row = rt * 16 + l16;
+        uint4 aop[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            uint32_t w4[4] = {0u, 0u, 0u, 0u};
+            if (row < R) {
+                const uint2 h2 =
+                    *reinterpret_cast<const uint2 *>(&qsm[((row / A) * B + act_s[row]) * RWP + 8 * kk + 2 * lg]);
+                const uint32_t hw[4] = {h2.x & 0xffffu, h2.x >> 16, h2.y & 0xffffu, h2.y >> 16};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // (q+, q-): q >= 0 (-0 included) -> low half, else high half
+                    const bool pos = __uint_as_float(hw[e] << 16) >= 0.0f;
+                    w4[e] = pos ? hw[e] : (hw[e] << 16);
+                }
+            }
+            aop[kk] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+        float qa[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qa[j] = qabs_s[min(rt * 16 + 4 * lg + j, R1 - 1)];
+        bound_rowtile<DIM>(D, rt, aop, qa, bop, amax, pl, sg.pages, bx, l16, lg, hb, tm);
     }
 }
 
@@ -445,6 +651,33 @@ hipError_t launch_score(const Dims &D, const void *meta, const int32_t *kv_off,
         else LAUNCH_S(64, false);
     }
 #undef LAUNCH_S
+    return hipGetLastError();
+}
+
+size_t score_prep_lds_bytes(const Dims &D) {
+    return (size_t)2 * D.G * D.B * (D.d / 2 + kPrepPad) * 4;
+}
+
+bool score_prep_fits(const Dims &D) {
+    return D.bf16 && D.R > 0 && 2 * D.G * D.B * D.d / 8 <= kPrepVecs * 256 &&
+           score_prep_lds_bytes(D) <= 40 * 1024;
+}
+
+hipError_t launch_score_prep(const Dims &D, const void *q_t, const void *q_prev, const void *meta,
+                             const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
+                             float *dbg_loc, int32_t *dbg_act, int32_t *dbg_ucnt, hipStream_t st) {
+    const int ng = D.S * D.Hk;
+    const dim3 grid(((D.n_tiles_grid + 3) / 4) * ng);
+    const size_t lds = score_prep_lds_bytes(D);
+    auto *a = static_cast<const uint16_t *>(q_t);
+    auto *b = static_cast<const uint16_t *>(q_prev);
+    auto *m = static_cast<const uint4 *>(meta);
+    if (D.d == 128)
+        hipLaunchKernelGGL((k_score_prep<128>), grid, dim3(256), lds, st, D, a, b, m, kv_off,
+                           prefix_len, W, dbg_loc, dbg_act, dbg_ucnt);
+    else
+        hipLaunchKernelGGL((k_score_prep<64>), grid, dim3(256), lds, st, D, a, b, m, kv_off,
+                           prefix_len, W, dbg_loc, dbg_act, dbg_ucnt);
     return hipGetLastError();
 }
 
