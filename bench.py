@@ -12,7 +12,9 @@ prefix is built before timing (it changes once per committed block).
 
 Prints one JSON line: value = attention microseconds per (layer, denoising
 step), amortised over the block (dense first step included), from K timed
-blocks with only the library's launches on the stream; plus per-kernel
+replays of the block captured once as a HIP graph -- the same launches with no
+host launch overhead, checked bit for bit against an eager block (--no-graph
+times eager launches; the eager rate is reported beside); plus per-kernel
 durations from HIP events the library records between its launches during a
 second timed pass of K blocks, the roofline of the dominant kernel, and the CPU
 oracle timed on one layer-block of the same workload.
@@ -36,48 +38,6 @@ STEPS_PER_BLOCK = 8
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-class HipEvents:
-    """Raw hipEvent_t handles from the HIP runtime torch has loaded."""
-
-    def __init__(self):
-        path = None
-        with open("/proc/self/maps") as f:
-            for line in f:
-                if "libamdhip64" in line:
-                    path = line.split()[-1]
-                    break
-        self.hip = ctypes.CDLL(path or "libamdhip64.so.7")
-        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                 ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-        self.made = []
-
-    # timing-only events: no system-scope fence (cache writeback/invalidate) on record
-    DISABLE_SYSTEM_FENCE = 0x20000000
-
-    def create(self) -> int:
-        ev = ctypes.c_void_p()
-        assert self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE) == 0
-        self.made.append(ev.value)
-        return ev.value
-
-    def record(self, ev: int, stream: int):
-        assert self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
-
-    def ms(self, e0: int, e1: int) -> float:
-        out = ctypes.c_float()
-        assert self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(e0),
-                                            ctypes.c_void_p(e1)) == 0
-        return float(out.value)
-
-    def destroy_all(self):
-        for ev in self.made:
-            self.hip.hipEventDestroy(ctypes.c_void_p(ev))
-        self.made = []
 
 
 def traffic_from_profile(kernel_tag: str):
@@ -124,6 +84,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="time without the per-kernel stage events")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of replays of the captured block")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="launch one plain copy kernel of MIB MiB before timing (reference "
                          "dispatch for profiler byte counters)")
@@ -138,6 +100,7 @@ def main():
 
     from sparse_attention_block_amd import binding as L
     from sparse_attention_block_amd import workloads as W
+    from sparse_attention_block_amd.hiprt import HipRuntime
     from sparse_attention_block_amd.layer import LayerState, to_device
 
     L.load()
@@ -161,7 +124,7 @@ def main():
     vb = [dev(x) for x in lay.v_blk]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
-    hip = HipEvents()
+    hip = HipRuntime()
 
     # union sizes of every LoSA step (identical across the replicated layers)
     union_cnt = []
@@ -173,24 +136,31 @@ def main():
         union_cnt.append(dbg.union_cnt.cpu().numpy().copy())
     union_pages = np.array([u.sum() for u in union_cnt], dtype=np.float64)  # per step, all KV heads
 
-    # one prepared call per (step, layer): checks and marshalling happen here, once
-    calls = {}
+    # one prepared call per (step, layer): checks and marshalling happen here,
+    # once; the same calls bound to a side stream are captured into a graph
+    gstream = torch.cuda.Stream()
+    calls, gcalls = {}, {}
     for t in range(STEPS_PER_BLOCK):
         for li, ls in enumerate(layers):
-            calls[(t, li)] = (ls.prepare_dense_first_step(q[0], kb[0], vb[0]) if t == 0 else
-                              ls.prepare_step(q[t], q[t - 1], kb[t], vb[t]))
+            for table, st in ((calls, None), (gcalls, gstream.cuda_stream)):
+                table[(t, li)] = (ls.prepare_dense_first_step(q[0], kb[0], vb[0], stream=st) if t == 0
+                                  else ls.prepare_step(q[t], q[t - 1], kb[t], vb[t], stream=st))
 
-    def run_block(events):
+    def run_block(events, table=calls):
         """One block for every layer; events[(t, l)] = stage events or None."""
         for t in range(STEPS_PER_BLOCK):
             for li in range(len(layers)):
-                c = calls[(t, li)]
+                c = table[(t, li)]
                 c.set_events(events[(t, li)] if events is not None else None)
                 c()
 
     def new_events():
-        return {(t, li): [hip.create() for _ in range(L.LOSA_STAGE_EVENTS)]
+        return {(t, li): [hip.event() for _ in range(L.LOSA_STAGE_EVENTS)]
                 for t in range(STEPS_PER_BLOCK) for li in range(len(layers))}
+
+    def block_outputs():
+        return [torch.cat([ls.out.flatten().view(torch.int16), ls.op_cache.flatten().view(torch.int16),
+                           ls.lp_cache.flatten().view(torch.int16)]).clone() for ls in layers]
 
     if args.copy_calibration:
         from sparse_attention_block_amd.build import SELFTEST_LIB
@@ -210,20 +180,46 @@ def main():
     for _ in range(args.warmup):
         run_block(None)
     torch.cuda.synchronize()
+    eager_ref = block_outputs()
+
+    # the block captured once into a HIP graph (the same launches, replayed
+    # without host launch overhead); every check replay must reproduce the
+    # eager block bit for bit, with eager work and synchronisations between
+    graph = None
+    if not args.no_graph:
+        torch.cuda.synchronize()
+        graph = hip.capture(gstream.cuda_stream, lambda: run_block(None, gcalls))
+        for rep_i in range(3):
+            hip.launch(graph, gstream.cuda_stream)
+            torch.cuda.synchronize()
+            got = block_outputs()
+            for a, b in zip(got, eager_ref):
+                if not torch.equal(a, b):
+                    raise SystemExit("graph replay differs from the eager block")
+            run_block(None)  # eager work between replays
+            torch.cuda.synchronize()
+        log("[bench] graph replays match the eager block")
 
     # value: exactly K blocks with nothing but the library's launches in the
     # timed region (an event between kernels costs GPU time of its own)
-    e_start, e_stop = hip.create(), hip.create()
-    log(f"[bench] timing {args.steps} blocks")
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    hip.record(e_start, stream)
-    for k in range(args.steps):
-        run_block(None)
-    hip.record(e_stop, stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    total_ms = hip.ms(e_start, e_stop)
+    def timed(use_graph):
+        st = gstream.cuda_stream if use_graph else stream
+        e0, e1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        hip.record(e0, st)
+        for k in range(args.steps):
+            if use_graph:
+                hip.launch(graph, st)
+            else:
+                run_block(None)
+        hip.record(e1, st)
+        torch.cuda.synchronize()
+        return hip.ms(e0, e1), time.perf_counter() - w0
+
+    log(f"[bench] timing {args.steps} blocks ({'graph replay' if graph else 'eager launches'})")
+    total_ms, wall = timed(graph is not None)
+    eager_ms = timed(False)[0] if graph is not None else total_ms
 
     # per-kernel durations: a second timed pass of K blocks with the library's
     # stage events recorded between its launches
@@ -239,6 +235,7 @@ def main():
     n_calls = args.steps * STEPS_PER_BLOCK * len(layers)
     value_us = total_ms * 1e3 / n_calls
     ms_per_step = total_ms / args.steps
+    eager_us = eager_ms * 1e3 / n_calls
 
     # per-kernel durations from the library's stage events (one kernel per stage)
     names = ["prepare", "score", "select", "prefix", "finish"]
@@ -332,9 +329,11 @@ def main():
         "roofline": roofline(dominant),
         "roofline_sparse_prefix": roofline("sparse_prefix") if use_events else None,
         "kernels": kernels,
+        "launch": "hip graph replay of the captured block" if graph else "eager launches",
+        "value_eager_launch": eager_us,
         "wall_s": wall,
     }
-    hip.destroy_all()
+    hip.close()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on one layer-block")
         rec["cpu_baseline"] = cpu_baseline(cfg, lay)

@@ -141,8 +141,11 @@ def _check(t: Optional[torch.Tensor], name: str, dtype, numel: int, optional=Fal
 
 
 def _stream(stream) -> c_void_p:
+    """A torch stream, a raw hipStream_t handle (int), or None for torch's current stream."""
     if stream is None:
         stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return c_void_p(stream)
     return c_void_p(stream.cuda_stream)
 
 

@@ -28,8 +28,8 @@ __device__ __forceinline__ float ldv(const T *p, size_t i) {
 
 constexpr int kFinishMaxThreads = 256;
 constexpr int kVReg = 16;    // block values per thread held in registers (the rest re-read)
-constexpr int kPartBatch = 24;  // prefix partials per thread requested together (each
-                                // wave keeps at most 63 vector loads in flight)
+constexpr int kPartBatch = 30;  // prefix partials per thread requested together (60
+                                // loads: each wave keeps at most 63 in flight)
 
 // running combination of prefix partials (log2 units): max, sum, weighted output
 struct PartAcc {
@@ -185,7 +185,9 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     const size_t pr0 = (size_t)sgi * nch * rows + row0 + (rho < 0 ? 0 : rho);
     const float *mlp = part_ml + pr0 * 2;
     const float *acp = part_acc + pr0 * DIM + x;
-    const size_t cs = (size_t)rows * 2, as = (size_t)rows * DIM;
+    // chunk strides in elements: a row's partials span < 2^31 bytes (at most
+    // 4096 chunks x 256 rows x DIM floats), so 32-bit offsets suffice
+    const int cs = rows * 2, as = rows * DIM;
     const int n0 = rho >= 0 ? min(nchu, kPartBatch) : 0;
     float mv[kPartBatch], lv[kPartBatch], av[kPartBatch];
     // rho is uniform over a wave (a wave holds one token); the chunk index is
@@ -226,18 +228,22 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
         }
     }
     __syncthreads();
-    if (tid < nt) {
-        float m = -__builtin_huge_valf();
-        for (int u = 0; u < B; ++u) m = fmaxf(m, ps[tid * B + u]);
-        float l = 0.0f;
-        for (int u = 0; u < B; ++u) {
-            const float p = __builtin_amdgcn_exp2f(ps[tid * B + u] - m);
-            ps[tid * B + u] = p;
-            l += p;
-        }
-        const float inv = 1.0f / l;
-        for (int u = 0; u < B; ++u) ps[tid * B + u] *= inv;
-        ls2[tid] = m + __log2f(l);
+    {
+        // softmax over each token's B scores: lanes (token, key) in segments of
+        // Bp = B rounded up to a power of two (nt * Bp <= 256 threads)
+        int Bp = 1;
+        while (Bp < B) Bp <<= 1;
+        const int tt = tid / Bp, u = tid % Bp;
+        const bool on = tt < nt && u < B;
+        const float v = on ? ps[tt * B + u] : -__builtin_huge_valf();
+        float m = v;
+        for (int o = 1; o < Bp; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        const float p = on ? __builtin_amdgcn_exp2f(v - m) : 0.0f;
+        float l = p;
+        for (int o = 1; o < Bp; o <<= 1) l += __shfl_xor(l, o);
+        __syncthreads();  // every score has been read
+        if (on) ps[tt * B + u] = p / l;
+        if (on && u == 0) ls2[tt] = m + __log2f(l);
     }
     __syncthreads();
     if (!live) return;

@@ -391,11 +391,12 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
 
 // Dense first-step pass, bf16.  Each page of the workgroup's chunk is read
 // from HBM once: every thread holds 16-byte pieces of the next kDensePrefetch
-// pages in registers and stores the oldest pair into a double-buffered pair of
-// LDS pages; the four waves (row tiles w, w + 4, ...) then read their K and V^T
-// operands from LDS and attend the two pages together.  Chunks of 8 elements are XOR-swizzled per token row, which makes both
+// pages in registers and stores the oldest group of kDenseGroup pages into a
+// double-buffered group of LDS pages; the four waves (row tiles w, w + 4, ...)
+// then read their K and V^T operands from LDS and attend the group together.  Chunks of 8 elements are XOR-swizzled per token row, which makes both
 // operand reads free of bank conflicts.  Same arithmetic as k_prefix_bf16.
-constexpr int kDensePrefetch = 4;
+constexpr int kDensePrefetch = 4;  // pages of register prefetch per thread
+constexpr int kDenseGroup = 2;     // pages attended together (independent MFMA chains)
 
 template <int DIM>
 __device__ __forceinline__ int swz(int t, int c) {
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(256) void k_prefix_dense_bf16(Dims D, const uint16_
     constexpr int KSTEPS = DIM / 32, DPL = DIM / 16, CPT = DIM / 8;
     constexpr int NCK = 16 * CPT;            // chunks per page and tensor
     constexpr int CPTH = 2 * NCK / 256;      // chunks per thread per page (K and V together)
-    __shared__ uint4 s_page[4][2][NCK];      // [buffer: 2 pairs of pages][K, V][swizzled chunk]
+    __shared__ uint4 s_page[2 * kDenseGroup][2][NCK];  // [two groups of pages][K, V][swizzled chunk]
     const int ng = D.S * D.Hk;
     const int sgi = blockIdx.x % ng;
     const int chunk = blockIdx.x / ng;
@@ -465,16 +466,16 @@ __global__ __launch_bounds__(256) void k_prefix_dense_bf16(Dims D, const uint16_
     bool rt_ok[RTW];
 #pragma unroll
     for (int i = 0; i < RTW; ++i) rt_ok[i] = w + 4 * i < n_rt;
-    // pages are attended in pairs (independent MFMA chains, one shared max)
-    static_assert(kDensePrefetch % 2 == 0, "pages are staged in pairs");
+    // pages are attended in groups (independent MFMA chains, one shared max)
+    static_assert(kDensePrefetch % kDenseGroup == 0, "pages are staged in whole groups");
     for (int it = 0; it < n_here; it += kDensePrefetch) {
 #pragma unroll
-        for (int d = 0; d < kDensePrefetch; d += 2) {
+        for (int d = 0; d < kDensePrefetch; d += kDenseGroup) {
             const int pi = it + d;
             if (pi >= n_here) break;  // uniform
-            const int pb = 2 * ((pi >> 1) & 1);
+            const int pb = kDenseGroup * ((pi / kDenseGroup) & 1);
 #pragma unroll
-            for (int n = 0; n < 2; ++n)
+            for (int n = 0; n < kDenseGroup; ++n)
 #pragma unroll
                 for (int h = 0; h < CPTH; ++h) {
                     const int q = tid + 256 * h, cq = q % NCK;
@@ -482,17 +483,17 @@ __global__ __launch_bounds__(256) void k_prefix_dense_bf16(Dims D, const uint16_
                 }
             // refill with the pages kDensePrefetch ahead (clamped: rereads the last page)
 #pragma unroll
-            for (int n = 0; n < 2; ++n)
+            for (int n = 0; n < kDenseGroup; ++n)
 #pragma unroll
                 for (int h = 0; h < CPTH; ++h)
                     pf[d + n][h] = load_piece(min(pi + n + kDensePrefetch, n_here - 1), h);
-            __syncthreads();  // pages pi, pi+1 complete in LDS; the pair before is no longer read
+            __syncthreads();  // this group complete in LDS; the group before is no longer read
 
-            uint4 kop[2][KSTEPS];
-            uint32_t vw[2][4][DPL / 2];
-            int valid[2];
+            uint4 kop[kDenseGroup][KSTEPS];
+            uint32_t vw[kDenseGroup][4][DPL / 2];
+            int valid[kDenseGroup];
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
+            for (int n = 0; n < kDenseGroup; ++n) {
                 // a page past the chunk (odd count) attends nothing
                 valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + pi + n) * kPage) : 0;
 #pragma unroll
@@ -510,7 +511,8 @@ __global__ __launch_bounds__(256) void k_prefix_dense_bf16(Dims D, const uint16_
                     }
                 }
             }
-            attend_pages<DIM, RTW, 2>(kop, vw, valid, qop, rt_ok, D.scale_log2, oacc, m_run, l_run, lg);
+            attend_pages<DIM, RTW, kDenseGroup>(kop, vw, valid, qop, rt_ok, D.scale_log2, oacc, m_run,
+                                                l_run, lg);
         }
     }
 #pragma unroll

@@ -321,16 +321,22 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
 
     // 2. locality chain per (query head, token), then the active set
     if (tid < GB) {
-        const uint32_t *a = &qsm[tid * RWP], *b = &qsm[(GB + tid) * RWP];
+        const uint4 *a = reinterpret_cast<const uint4 *>(&qsm[tid * RWP]);
+        const uint4 *b = reinterpret_cast<const uint4 *>(&qsm[(GB + tid) * RWP]);
         float acc = 0.0f;
-#pragma unroll 8
-        for (int w = 0; w < DIM / 2; ++w) {
-            const float d0 = bf16_lo(a[w]) - bf16_lo(b[w]);
-            const float s0 = d0 * d0;
-            acc = acc + s0;
-            const float d1 = bf16_hi(a[w]) - bf16_hi(b[w]);
-            const float s1 = d1 * d1;
-            acc = acc + s1;
+#pragma unroll 4
+        for (int v = 0; v < VPR; ++v) {
+            const uint4 av = a[v], bv = b[v];
+            const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float d0 = bf16_lo(aw[e]) - bf16_lo(bw[e]);
+                const float s0 = d0 * d0;
+                acc = acc + s0;
+                const float d1 = bf16_hi(aw[e]) - bf16_hi(bw[e]);
+                const float s1 = d1 * d1;
+                acc = acc + s1;
+            }
         }
         e_s[tid] = acc;
         if (writer && dbg_loc)
@@ -341,6 +347,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         const int j = tid / B, t = tid % B;
         const float et = e_s[tid];
         int rank = 0;
+#pragma unroll 8
         for (int u = 0; u < B; ++u) {
             const float eu = e_s[j * B + u];
             rank += (eu > et) || (eu == et && u < t);
@@ -362,11 +369,19 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
 
     // 3. stacked rows r = j*|A| + a: sum |q| bounds; the writer stores the rows
     //    (bf16, rows up to the next multiple of 16 zeroed) for the later kernels
-    if (tid < R) {
-        const uint32_t *a = &qsm[((tid / A) * B + act_s[tid]) * RWP];
+    // 16 lanes per row, each summing DIM/16 values; any order (an upper bound
+    // with 1/256 of margin)
+    for (int r0 = 0; r0 < R; r0 += 16) {
+        const int r = r0 + tid / 16, part = tid % 16;
         float ab = 0.0f;
-        for (int w = 0; w < DIM / 2; ++w) ab += fabsf(bf16_lo(a[w])) + fabsf(bf16_hi(a[w]));
-        qabs_s[tid] = ab * (1.0f + 1.0f / 256.0f);
+        if (r < R) {
+            const uint32_t *a = &qsm[((r / A) * B + act_s[r]) * RWP + part * (DIM / 32)];
+#pragma unroll
+            for (int w = 0; w < DIM / 32; ++w) ab += fabsf(bf16_lo(a[w])) + fabsf(bf16_hi(a[w]));
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) ab += __shfl_xor(ab, o);
+        if (r < R && part == 0) qabs_s[r] = ab * (1.0f + 1.0f / 256.0f);
     }
     if (writer) {
         uint16_t *qr = static_cast<uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
