@@ -25,12 +25,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 # tag -> (kernel-name pattern, sources whose digest identifies the build)
 KERNEL_TAGS = {
-    "dense_prefix": (r"k_prefix_bf16<\d+, \d+, true>", ["prefix.hip", "losa_internal.h"]),
+    "dense_prefix": (r"k_prefix_dense_bf16<\d+, \d+>", ["prefix.hip", "losa_internal.h"]),
     "sparse_prefix": (r"k_prefix_bf16<\d+, \d+, false>", ["prefix.hip", "losa_internal.h"]),
-    "page_score": (r"k_score<\d+, true>", ["select.hip", "losa_internal.h"]),
+    "page_score": (r"k_score_prep<\d+>", ["select.hip", "losa_internal.h"]),
     "page_select": (r"k_select<\d+, true>", ["select.hip", "losa_internal.h"]),
     "sparse_finish": (r"k_finish<unsigned short, \d+, false>", ["finish.hip", "losa_internal.h"]),
-    "sparse_prepare": (r"k_prepare<unsigned short, \d+, false>", ["prepare.hip", "losa_internal.h"]),
+    "dense_finish": (r"k_finish<unsigned short, \d+, true>", ["finish.hip", "losa_internal.h"]),
 }
 COPY_KERNEL = r"(^|\W)k_copy($|\W)"
 
