@@ -73,6 +73,300 @@ def cpu_baseline(cfg, lay):
                       f"{sec:.1f} s"}
 
 
+# ---------------------------------------------------------------------------
+# --sweep: the |A| x budget sweep, the KV-union density study against a
+# QUEST-style step (every block token active, same inputs) and a dense step
+# every step, other workload shapes, the 36-layer trace, and latency floors.
+
+SWEEP_LAYERS = 8          # layer replicas per 64K case (8 x 272 MiB defeats the 256 MB MALL)
+
+
+def _selftest():
+    from sparse_attention_block_amd.build import SELFTEST_LIB
+
+    st = ctypes.CDLL(SELFTEST_LIB)
+    st.losa_selftest_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_int, ctypes.c_void_p]
+    st.losa_selftest_empty.argtypes = [ctypes.c_void_p]
+    return st
+
+
+def latency_floors(hip, stream, reps=200):
+    """Back-to-back empty kernels, one event-bracketed empty kernel, and plain copies
+    of 1/8/64 MiB rotated over >= 512 MiB of buffers (so none is served from the MALL)."""
+    import torch
+
+    st = _selftest()
+    out = {}
+    e0, e1 = hip.event(), hip.event()
+    for _ in range(20):
+        st.losa_selftest_empty(stream)
+    torch.cuda.synchronize()
+    hip.record(e0, stream)
+    for _ in range(reps):
+        assert st.losa_selftest_empty(stream) == 0
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    out["empty_kernel_back_to_back_us"] = hip.ms(e0, e1) * 1e3 / reps
+    evs = [hip.event() for _ in range(2 * 50)]
+    for i in range(50):
+        hip.record(evs[2 * i], stream)
+        st.losa_selftest_empty(stream)
+        hip.record(evs[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    out["empty_kernel_between_events_us"] = float(sorted(
+        hip.ms(evs[2 * i], evs[2 * i + 1]) * 1e3 for i in range(50))[25])
+    evs = [hip.event() for _ in range(2 * 50)]
+    for i in range(50):
+        hip.record(evs[2 * i], stream)
+        hip.record(evs[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    out["empty_event_pair_us"] = float(sorted(
+        hip.ms(evs[2 * i], evs[2 * i + 1]) * 1e3 for i in range(50))[25])
+    copies = {}
+    for mib in (1, 8, 64):
+        nb = mib << 20
+        n_buf = max(2, (512 << 20) // nb)
+        bufs = [torch.empty(nb // 4, dtype=torch.float32, device="cuda") for _ in range(n_buf + 1)]
+        blocks = max(1, min(4096, nb // (16 * 256)))
+        evs = [hip.event() for _ in range(2 * n_buf)]
+        torch.cuda.synchronize()
+        for i in range(n_buf):
+            hip.record(evs[2 * i], stream)
+            assert st.losa_selftest_copy(bufs[i].data_ptr(), bufs[i + 1].data_ptr(), nb, blocks,
+                                         stream) == 0
+            hip.record(evs[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        us = sorted(hip.ms(evs[2 * i], evs[2 * i + 1]) * 1e3 for i in range(1, n_buf))
+        med = float(us[len(us) // 2])
+        copies[f"{mib}MiB"] = {"us": med, "gbps": 2 * nb / (med * 1e-6) / 1e9}
+        del bufs
+    out["copy"] = copies
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_case(hip, lay_kv, inputs_of, *, cfg, budget, active_of, dense_every_step, reps,
+                 union_layers=(0,)):
+    """Time one case over the device KV replicas ``lay_kv`` = (layer, [(k, v), ...]).
+
+    inputs_of(li) -> (q, k_blk, v_blk) device tensor lists per step for layer li.
+    Returns per-(layer, step) microseconds of the dense and of the other steps,
+    the mean union size (pages, all KV heads) of each layer in ``union_layers``
+    and the median per-stage event durations of the other steps."""
+    import numpy as np
+    import torch
+
+    from sparse_attention_block_amd import binding as L
+    from sparse_attention_block_amd.layer import LayerState
+
+    lay, kv = lay_kv
+    S_steps = cfg.n_steps
+    layers = []
+    for li, (k, v) in enumerate(kv):
+        ls = LayerState(n_seq=cfg.n_seq, block=cfg.block, n_qhead=cfg.n_qhead,
+                        n_kvhead=cfg.n_kvhead, head_dim=cfg.head_dim, budget_tokens=budget,
+                        n_active=active_of(li), dtype=cfg.dtype, k_cache=k, v_cache=v,
+                        kv_off=lay.kv_off, prefix_len=lay.prefix_len)
+        ls.build_page_meta()
+        layers.append(ls)
+    # union sizes over the block (from the library's debug outputs)
+    union = {}
+    for li in ([] if dense_every_step else union_layers):
+        ls0, (q, kb, vb) = layers[li], inputs_of(li)
+        dbg = L.Debug.alloc(ls0.shape)
+        ls0.dense_first_step(q[0], kb[0], vb[0])
+        counts = []
+        for t in range(1, S_steps):
+            ls0.step(q[t], q[t - 1], kb[t], vb[t], debug=dbg)
+            torch.cuda.synchronize()
+            counts.append(float(dbg.union_cnt.sum().item()))
+        union[li] = float(np.mean(counts))
+        del dbg
+    gst = torch.cuda.Stream()
+    sid = gst.cuda_stream
+    dense_calls, step_calls = [], []
+    for li, ls in enumerate(layers):
+        q, kb, vb = inputs_of(li)
+        dense_calls.append(ls.prepare_dense_first_step(q[0], kb[0], vb[0], stream=sid))
+    for t in range(1, S_steps):
+        for li, ls in enumerate(layers):
+            q, kb, vb = inputs_of(li)
+            step_calls.append(ls.prepare_dense_first_step(q[t], kb[t], vb[t], stream=sid)
+                              if dense_every_step else
+                              ls.prepare_step(q[t], q[t - 1], kb[t], vb[t], stream=sid))
+    run = lambda cs: [c() for c in cs]
+    for _ in range(2):
+        run(dense_calls)
+        run(step_calls)
+    torch.cuda.synchronize()
+    g_dense = hip.capture(sid, lambda: run(dense_calls))
+    g_steps = hip.capture(sid, lambda: run(step_calls))
+
+    def timed(g):
+        e0, e1 = hip.event(), hip.event()
+        hip.launch(g, sid)
+        torch.cuda.synchronize()
+        hip.record(e0, sid)
+        for _ in range(reps):
+            hip.launch(g, sid)
+        hip.record(e1, sid)
+        torch.cuda.synchronize()
+        return hip.ms(e0, e1) * 1e3 / reps
+
+    dense_us = timed(g_dense) / len(layers)
+    step_us = timed(g_steps) / (len(layers) * (S_steps - 1))
+    # per-stage durations of the non-first steps, from the library's stage events
+    names = ["prepare", "score", "select", "prefix", "finish"]
+    evs = [[hip.event() for _ in range(L.LOSA_STAGE_EVENTS)] for _ in step_calls]
+    for c, e in zip(step_calls, evs):
+        c.set_events(e)
+    run(dense_calls)
+    run(step_calls)
+    torch.cuda.synchronize()
+    for c in step_calls:
+        c.set_events(None)
+    stage = {n: float(np.median([hip.ms(e[i], e[i + 1]) * 1e3 for e in evs]))
+             for i, n in enumerate(names)}
+    del layers, dense_calls, step_calls
+    torch.cuda.empty_cache()
+    return {"dense_us": dense_us, "step_us": step_us, "stage_us": stage,
+            "union_pages": union.get(union_layers[0]), "union_by_layer": union}
+
+
+def sweep(args):
+    import numpy as np
+    import torch
+
+    from sparse_attention_block_amd import binding as L
+    from sparse_attention_block_amd import workloads as W
+    from sparse_attention_block_amd.hiprt import HipRuntime
+    from sparse_attention_block_amd.layer import to_device
+
+    L.load()
+    torch.cuda.set_device(0)
+    hip = HipRuntime()
+    stream = torch.cuda.current_stream().cuda_stream
+    t_start = time.perf_counter()
+    floors = latency_floors(hip, stream)
+    log(f"[sweep] floors {json.dumps(floors)}")
+    rows = []
+
+    def dev_inputs(lay, dtype):
+        return ([to_device(x, dtype) for x in lay.q], [to_device(x, dtype) for x in lay.k_blk],
+                [to_device(x, dtype) for x in lay.v_blk])
+
+    def replicas(lay, n):
+        k0, v0 = to_device(lay.k_cache, lay.cfg.dtype), to_device(lay.v_cache, lay.cfg.dtype)
+        return [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(n - 1)]
+
+    def bytes_model(cfg, union_pages, n_active):
+        sT = 2 if cfg.dtype == "bf16" else 4
+        Hk, d, P, S, B, Hq = cfg.n_kvhead, cfg.head_dim, cfg.page_size, cfg.n_seq, cfg.block, cfg.n_qhead
+        n_pages = sum((L_ + P - 1) // P for L_ in cfg.prefix_lens)
+        meta = Hk * n_pages * 2 * d * sT
+        union = (union_pages if union_pages is not None else Hk * n_pages) * P * 2 * d * sT
+        small = (2 * S * B * Hq * d * sT + 2 * S * B * Hk * d * sT + S * Hq * B * (d + 1) * 4
+                 + S * Hq * n_active * (d + 1) * 4 + S * B * Hq * d * sT)
+        return meta, union, small, Hk * n_pages
+
+    def add_row(group, label, cfg, budget, n_active, n_layers, res, dense_mode):
+        meta, union, small, pages_all = bytes_model(cfg, res["union_pages"], n_active)
+        st = res["stage_us"]
+        row = {"group": group, "case": label, "workload": cfg.name, "budget": budget,
+               "n_active": n_active, "layers": n_layers, "mode": "dense" if dense_mode else "losa",
+               "dense_step_us": res["dense_us"], "step_us": res["step_us"],
+               "block_us": (res["dense_us"] + (cfg.n_steps - 1) * res["step_us"]) / cfg.n_steps,
+               "stage_us": st}
+        if not dense_mode:
+            up = res["union_pages"]
+            row.update({
+                "union_pages_per_kv_head": up / (cfg.n_seq * cfg.n_kvhead),
+                "density": up / pages_all,
+                "union_bytes": union, "step_bytes": meta + union + small,
+                "step_gbps": (meta + union + small) / (res["step_us"] * 1e-6) / 1e9,
+                "prefix_gbps_on_union": union / (st["prefix"] * 1e-6) / 1e9,
+                "prefix_frac": union / (st["prefix"] * 1e-6) / 1e9 / PEAK_HBM_GBPS})
+        rows.append(row)
+        log(f"[sweep] {group} {label}: step {row['step_us']:.2f} us, dense {row['dense_step_us']:.2f} us"
+            + (f", union/head {row['union_pages_per_kv_head']:.1f}, prefix {st['prefix']:.2f} us"
+               if not dense_mode else ""))
+
+    # 64K: |A| x budget, QUEST-style (all 16 tokens active on the |A|=4 inputs), dense
+    base = W.long_64k(128, 4)
+    lay = W.make_layer(base, n_steps=base.n_steps)
+    kv = (lay, replicas(lay, SWEEP_LAYERS))
+    for budget in (128, 256):
+        for a in (2, 4, 8):
+            c = W.long_64k(budget, a)
+            li = W.make_layer(c, n_steps=c.n_steps, cache=False)
+            inp = dev_inputs(li, c.dtype)
+            res = measure_case(hip, kv, lambda i: inp, cfg=c, budget=budget, active_of=lambda i: a,
+                               dense_every_step=False, reps=args.steps)
+            add_row("64K", f"LoSA |A|={a}", c, budget, a, SWEEP_LAYERS, res, False)
+        inp4 = dev_inputs(lay, base.dtype)
+        res = measure_case(hip, kv, lambda i: inp4, cfg=base, budget=budget,
+                           active_of=lambda i: base.block, dense_every_step=False, reps=args.steps)
+        add_row("64K", "QUEST-style (all 16 tokens active, |A|=4 inputs)", base, budget,
+                base.block, SWEEP_LAYERS, res, False)
+    inp4 = dev_inputs(lay, base.dtype)
+    res = measure_case(hip, kv, lambda i: inp4, cfg=base, budget=128, active_of=lambda i: 4,
+                       dense_every_step=True, reps=args.steps)
+    add_row("64K", "dense every step", base, 128, 4, SWEEP_LAYERS, res, True)
+    del kv, lay
+    torch.cuda.empty_cache()
+
+    # 16K GQA layer and the ragged batch: LoSA, QUEST-style, dense
+    for c, n_layers in ((W.gqa_16k(), 16), (W.ragged_batch(), 4)):
+        lay = W.make_layer(c, n_steps=c.n_steps)
+        kv = (lay, replicas(lay, n_layers))
+        inp = dev_inputs(lay, c.dtype)
+        for label, a, dense_mode in ((f"LoSA |A|={c.n_active}", c.n_active, False),
+                                     (f"QUEST-style (all {c.block} tokens active)", c.block, False),
+                                     ("dense every step", c.n_active, True)):
+            res = measure_case(hip, kv, lambda i: inp, cfg=c, budget=c.budget,
+                               active_of=lambda i: a, dense_every_step=dense_mode, reps=args.steps)
+            add_row(c.name, label, c, c.budget, a, n_layers, res, dense_mode)
+        del kv, lay, inp
+        torch.cuda.empty_cache()
+
+    # the 36-layer 128K trace: |A| = 2 in the first and last four layers, 6 between;
+    # one block of every layer per replay (the whole model's attention per block)
+    c0, c4 = W.trace_128k(0), W.trace_128k(4)
+    lay = W.make_layer(c0, n_steps=c0.n_steps)
+    lay6 = W.make_layer(c4, n_steps=c4.n_steps, cache=False)
+    inp2, inp6 = dev_inputs(lay, c0.dtype), dev_inputs(lay6, c4.dtype)
+    n_tr = 36
+    kv = (lay, replicas(lay, n_tr))
+    act = W.trace_layer_active
+    res = measure_case(hip, kv, lambda i: inp2 if act(i) == 2 else inp6, cfg=c0, budget=c0.budget,
+                       active_of=act, dense_every_step=False, reps=max(2, args.steps // 4),
+                       union_layers=(0, 4))
+    u = res["union_by_layer"]
+    n2 = sum(1 for i in range(n_tr) if act(i) == 2)
+    res["union_pages"] = (n2 * u[0] + (n_tr - n2) * u[4]) / n_tr
+    add_row("trace 128K x 36", "LoSA, per-layer |A| (2/6)", c0, c0.budget,
+            (n2 * 2 + (n_tr - n2) * 6) / n_tr, n_tr, res, False)
+    rows[-1]["note"] = ("union statistics: layer-weighted mean of layer 0 (|A| = 2) and layer 4 "
+                        "(|A| = 6); n_active = the layer mean")
+    rows[-1]["union_pages_per_kv_head_by_active"] = {
+        "2": u[0] / (c0.n_seq * c0.n_kvhead), "6": u[4] / (c0.n_seq * c0.n_kvhead)}
+    rows[-1]["model_step_us"] = res["step_us"] * n_tr
+    rows[-1]["model_dense_step_us"] = res["dense_us"] * n_tr
+    del kv, lay, lay6
+    torch.cuda.empty_cache()
+    hip.close()
+
+    rec = {"sweep": "LoSA step sweep on one MI355X", "floors": floors, "rows": rows,
+           "wall_s": time.perf_counter() - t_start}
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            json.dump(rec, f, indent=1)
+    print(json.dumps({"sweep_rows": len(rows), "out": args.sweep_out,
+                      "wall_s": rec["wall_s"]}), flush=True)
+
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,11 +383,17 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="launch one plain copy kernel of MIB MiB before timing (reference "
                          "dispatch for profiler byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line: the |A| x budget sweep, the density study, "
+                         "other workload shapes, the 36-layer trace and latency floors")
+    ap.add_argument("--sweep-out", default=None, help="JSON file for --sweep results")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the LoSA step is measured on a single MI355X", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        return sweep(args)
 
     import numpy as np
     import torch

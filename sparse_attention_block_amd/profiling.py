@@ -9,6 +9,9 @@
       copy kernel k_copy of N MiB (read N MiB, write N MiB) in the same run; with
       --json-dir, one counters_<tag>.json per library kernel tagged below, holding
       the bytes per launch and a digest of the sources the kernel was built from.
+  python -m sparse_attention_block_amd.profiling sweep SWEEP.json --command CMD
+      a markdown table of a ``bench.py --sweep`` run (step times, union sizes and
+      densities, the sparse prefix kernel's rate on union bytes, latency floors)
 """
 from __future__ import annotations
 
@@ -73,6 +76,44 @@ def find(means: dict, pattern: str):
     return hits[0]
 
 
+def print_sweep(path: str, command: str):
+    with open(path) as f:
+        rec = json.load(f)
+    fl = rec["floors"]
+    print(f"# LoSA step sweep on one MI355X\n\ncommand: `{command}`\n")
+    print("Times are per (layer, step) from HIP-graph replays over the layer replicas; stage "
+          "times are medians of the library's stage events, each including one event pair "
+          f"({fl['empty_event_pair_us']:.2f} us for an empty pair).\n")
+    print("Latency floors: empty kernel back to back "
+          f"{fl['empty_kernel_back_to_back_us']:.2f} us, between two events "
+          f"{fl['empty_kernel_between_events_us']:.2f} us; plain copy (read + write): " +
+          ", ".join(f"{k} {v['us']:.1f} us ({v['gbps']:.0f} GB/s)" for k, v in fl["copy"].items())
+          + ".\n")
+    print("| workload | case | budget | \\|A\\| | layers | step us | dense step us | block us "
+          "| union pages / KV head | density | score | select | prefix | finish "
+          "| prefix GB/s on union | frac of 8 TB/s | step GB/s |")
+    print("|" + "---|" * 17)
+    for r in rec["rows"]:
+        st = r["stage_us"]
+        sparse = r["mode"] != "dense"
+        a = r["n_active"]
+        a = f"{a:.2f}" if isinstance(a, float) and not float(a).is_integer() else f"{int(a)}"
+        cells = [r["group"], r["case"], str(r["budget"]), a, str(r["layers"]),
+                 f"{r['step_us']:.1f}", f"{r['dense_step_us']:.1f}", f"{r['block_us']:.1f}",
+                 f"{r['union_pages_per_kv_head']:.1f}" if sparse else "all",
+                 f"{r['density']:.4f}" if sparse else "1",
+                 f"{st['score']:.1f}" if sparse else "-", f"{st['select']:.1f}" if sparse else "-",
+                 f"{st['prefix']:.1f}", f"{st['finish']:.1f}",
+                 f"{r['prefix_gbps_on_union']:.0f}" if sparse else "-",
+                 f"{r['prefix_frac']:.3f}" if sparse else "-",
+                 f"{r['step_gbps']:.0f}" if sparse else "-"]
+        print("| " + " | ".join(c.replace("|", "\\|") for c in cells) + " |")
+    for r in rec["rows"]:
+        if "note" in r:
+            print(f"\n{r['group']}: {r['note']}; whole-model attention per denoising step "
+                  f"{r['model_step_us']:.0f} us (dense first step {r['model_dense_step_us']:.0f} us).")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -85,7 +126,14 @@ def main(argv=None):
     s2.add_argument("--copy-mib", type=int, required=True)
     s2.add_argument("--command", required=True)
     s2.add_argument("--json-dir")
+    s3 = sub.add_parser("sweep")
+    s3.add_argument("json")
+    s3.add_argument("--command", required=True)
     a = ap.parse_args(argv)
+
+    if a.cmd == "sweep":
+        print_sweep(a.json, a.command)
+        return 0
 
     if a.cmd == "stats":
         print(f"# rocprofv3 kernel statistics\n# command: {a.command}\n")
