@@ -2,7 +2,10 @@
 
 Flags: -O3; -ffp-contract=off so that every a*b+c in the index-deciding fp32
 chains stays two roundings (the kernels call fmaf explicitly where a fused
-multiply-add is intended); packed fp32 instructions are disabled.
+multiply-add is intended); packed fp32 instructions are disabled; matrix-core
+instructions take their accumulators in ordinary VGPRs (gfx950 allows it), so
+that accumulators the vector ALU also touches (the online-softmax rescale) are
+not copied to and from AGPRs around every MFMA.
 """
 import os
 import subprocess
@@ -19,6 +22,7 @@ ARCH = os.environ.get("LOSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     // -- 1. every read that depends on no other read ---------------------------
     int nchu;  // prefix chunks that wrote partials
     {
-        const int cp = dense ? kDenseChunk : kSparseChunk;
+        const int cp = dense ? D.dense_chunk : D.sparse_chunk;
         const int n_items = dense ? seq_geom(D, kv_off, prefix_len, s).pages : union_cnt[sgi];
         nchu = (n_items + cp - 1) / cp;
     }

@@ -70,8 +70,22 @@ Dims make_dims(const losa_shape *sh) {
     const int64_t rk = (int64_t)D.R * D.k;
     int64_t cap = rk < D.max_pages ? rk : D.max_pages;
     D.union_cap = cap > 0 ? static_cast<int>(cap) : 1;
-    D.n_chunks_sparse = (D.union_cap + kSparseChunk - 1) / kSparseChunk;
-    D.n_chunks_dense = D.max_pages > 0 ? (D.max_pages + kDenseChunk - 1) / kDenseChunk : 1;
+    // Split-K sizes.  Dense pass: the largest chunk (up to 64 pages) that still
+    // gives kDenseTargetGroups workgroups.  Sparse pass: one page per wave unless
+    // the union capacity would give more than kSparseTargetGroups workgroups;
+    // then larger chunks, which also write fewer partial results.
+    const int64_t sgc = (int64_t)D.S * D.Hk;
+    auto chunks = [](int n, int c) { return (n + c - 1) / c; };
+    D.dense_chunk = kMaxDenseChunk;
+    while (D.dense_chunk > kMinDenseChunk &&
+           sgc * chunks(D.max_pages, D.dense_chunk) < kDenseTargetGroups)
+        D.dense_chunk /= 2;
+    D.sparse_chunk = kMinSparseChunk;
+    while (D.sparse_chunk < kMaxSparseChunk &&
+           sgc * chunks(D.union_cap, 2 * D.sparse_chunk) >= kSparseTargetGroups)
+        D.sparse_chunk *= 2;
+    D.n_chunks_sparse = chunks(D.union_cap, D.sparse_chunk);
+    D.n_chunks_dense = D.max_pages > 0 ? chunks(D.max_pages, D.dense_chunk) : 1;
     const float scale = sh->softmax_scale > 0.0f ? sh->softmax_scale
                                                  : 1.0f / sqrtf(static_cast<float>(D.d));
     D.scale_log2 = scale * 1.44269504088896340736f;

@@ -11,9 +11,13 @@ namespace losa {
 
 constexpr int kPage = 16;         // tokens per page
 constexpr int kTile = 64;         // pages per metadata tile: one page per lane of a wave
-constexpr int kSparseChunk = 4;   // union pages per prefix workgroup (sparse step): 1 per wave
+constexpr int kMinSparseChunk = 4;   // union pages per prefix workgroup (sparse step): 1 per wave
+constexpr int kMaxSparseChunk = 64;  // ... at most (one page per lane of a wave)
 constexpr int kMaxBitmapWords = 8192;  // union bitmap in LDS: 262144 pages
-constexpr int kDenseChunk = 64;   // prefix pages per prefix workgroup (dense first step)
+constexpr int kMinDenseChunk = 16;  // prefix pages per prefix workgroup (dense first step) ...
+constexpr int kMaxDenseChunk = 64;  // ... chosen between these so the grid covers the chip
+constexpr int kDenseTargetGroups = 512;   // workgroups a dense pass should have at least
+constexpr int kSparseTargetGroups = 1024; // workgroups a sparse pass may keep at most (by capacity)
 constexpr int kMaxRows = 256;     // G * B stacked rows per KV head at most
 constexpr int kMaxK = 64;         // pages per row the exact selection keeps in one register
 
@@ -38,6 +42,7 @@ struct Dims {
     int Rs16;                         // R rounded up to 16 (selection MFMA row tiles)
     int Rd;                           // stacked dense rows per KV head = G*B
     int R16;                          // Rd rounded up to 16
+    int sparse_chunk, dense_chunk;    // pages per prefix workgroup
     int n_chunks_sparse, n_chunks_dense;
     float scale_log2;                 // softmax scale * log2(e)
 };

@@ -71,6 +71,11 @@ struct PageRegs {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// A row's softmax reference may trail its running maximum by this much (log2
+// units): weights up to 2^8 are exact to bf16's relative precision and far
+// from any overflow in the fp32 sums.
+constexpr float kLazyRescale = 8.0f;
+
 // NP pages of 16 tokens for the wave's row tiles i (those with rt_ok[i]):
 // S^T = K.Q^T with v_mfma_f32_16x16x32_bf16, online softmax in log2 units over
 // the NP pages together, then O^T += V^T.P with v_mfma_f32_16x16x16bf16_1k.
@@ -78,8 +83,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // +7); vw[n]: V words of tokens 4*(l/16) + j for the lane's DPL dims; valid[n]:
 // tokens of page n inside the prefix (0 for no page).  P is rounded to bf16 for
 // the MFMA and the row sum is taken from the rounded weights.  The running
-// output is rescaled only when some row's maximum changed (the factor is
-// exactly 1 otherwise).  Several pages at once keep independent MFMA chains
+// output is rescaled only when some row's maximum passed its reference by more
+// than kLazyRescale (the factor is exactly 1 for the other rows).  Several pages at once keep independent MFMA chains
 // in flight and share one max reduction.
 template <int DIM, int RTW, int NP>
 __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
@@ -135,14 +140,20 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
 #pragma unroll
         for (int n = 0; n < NP; ++n) mp = fmaxf(mp, fmaxf(fmaxf(sv[n][0], sv[n][1]), fmaxf(sv[n][2], sv[n][3])));
         mp = shfl_max32(mp);
-        const float mn = fmaxf(m_run[i], mp);
-        if (__ballot(mn != m_run[i]) != 0ull) {  // uniform branch
+        // Lazy reference: a row's reference m_run moves to its running maximum
+        // only once a score exceeds it by more than kLazyRescale (log2 units), so
+        // weights stay below 2^kLazyRescale and the output is rescaled rarely
+        // (softmax does not depend on the reference; the partial keeps it).
+        const float mx = fmaxf(m_run[i], mp);
+        if (__ballot(mx > m_run[i] + kLazyRescale) != 0ull) {  // uniform branch
+            const float mn = mx > m_run[i] + kLazyRescale ? mx : m_run[i];
             const float alpha = __builtin_amdgcn_exp2f(m_run[i] - mn);
 #pragma unroll
             for (int e = 0; e < DPL; ++e) oacc[i][e] *= alpha;
             l_run[i] *= alpha;
             m_run[i] = mn;
         }
+        const float mn = m_run[i];
 #pragma unroll
         for (int n = 0; n < NP; ++n) {
             const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][0] - mn)),
@@ -226,7 +237,7 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     constexpr int DPL = DIM / 16;     // V dims per lane = PV MFMAs per page
     constexpr int RAW = 4 * 16 * DIM > kMaxBitmapWords ? 4 * 16 * DIM : kMaxBitmapWords;
     __shared__ float s_raw[RAW];  // the union bitmap first, then the page groups' outputs
-    __shared__ int s_wsum[4], s_pg[kSparseChunk];
+    __shared__ int s_wsum[4], s_pg[kMaxSparseChunk];
     auto s_acc = reinterpret_cast<float (*)[16][DIM]>(s_raw);
     __shared__ float s_ml[4][16][2];
 
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
     const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
-    const int cp = dense ? kDenseChunk : kSparseChunk;
+    const int cp = dense ? D.dense_chunk : D.sparse_chunk;
     const int first = chunk * cp;
     const int rows = dense ? D.Rd : D.R;
     const int nch = dense ? D.n_chunks_dense : D.n_chunks_sparse;
@@ -390,13 +401,16 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
 }
 
 // Dense first-step pass, bf16.  Each page of the workgroup's chunk is read
-// from HBM once: every thread holds 16-byte pieces of the next kDensePrefetch
-// pages in registers and stores the oldest group of kDenseGroup pages into a
-// double-buffered group of LDS pages; the four waves (row tiles w, w + 4, ...)
-// then read their K and V^T operands from LDS and attend the group together.  Chunks of 8 elements are XOR-swizzled per token row, which makes both
-// operand reads free of bank conflicts.  Same arithmetic as k_prefix_bf16.
-constexpr int kDensePrefetch = 4;  // pages of register prefetch per thread
-constexpr int kDenseGroup = 2;     // pages attended together (independent MFMA chains)
+// from HBM once, straight into a ring of kDenseSlots LDS page slots with
+// global_load_lds_dwordx4 (no register staging), so kDenseSlots - 2*kDenseGroup
+// pages stay in flight while a group is attended.  The NW waves (row tiles w,
+// w + NW, ...) read their K and V^T operands from LDS and attend kDenseGroup
+// pages together.  Chunks of 8 elements are XOR-swizzled per token row, which
+// makes both operand reads free of bank conflicts; a direct load writes lane
+// i's 16 bytes to LDS position i, so each lane fetches the global chunk that
+// belongs at its swizzled position.  Same arithmetic as k_prefix_bf16.
+constexpr int kDenseSlots = 10;  // LDS page slots per workgroup (ring)
+constexpr int kDenseGroup = 2;   // pages attended together (independent MFMA chains)
 
 template <int DIM>
 __device__ __forceinline__ int swz(int t, int c) {
@@ -404,16 +418,85 @@ __device__ __forceinline__ int swz(int t, int c) {
     return t * CPT + (c ^ (t & (CPT - 1)));
 }
 
-template <int DIM, int RTW>
-__global__ __launch_bounds__(256) void k_prefix_dense_bf16(Dims D, const uint16_t *__restrict__ kc,
-                                                           const uint16_t *__restrict__ vc,
-                                                           const int32_t *__restrict__ kv_off,
-                                                           const int32_t *__restrict__ prefix_len,
-                                                           Work W) {
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// The K and V operands of two LDS page slots (slot stride PS bytes) in one
+// block of ds_read_b128: ak[kk] / av[j] are the lane's byte addresses of K
+// chunk kk and V chunk j in the first slot.  Written as one asm block that
+// waits for its own reads, so that the compiler, which cannot tell the ring's
+// slots apart, does not make the reads wait for every direct load in flight.
+// (The low 32 bits of a generic pointer into LDS are its LDS address.)
+template <int DIM>
+struct GroupReads;
+
+template <>
+struct GroupReads<128> {
+    static __device__ __forceinline__ void read(const uint32_t (&ak)[4], const uint32_t (&av)[4],
+                                                u32x4_t (&k)[2][4], u32x4_t (&v)[2][4]) {
+        asm volatile(
+            "ds_read_b128 %0, %16\n\tds_read_b128 %1, %17\n\t"
+            "ds_read_b128 %2, %18\n\tds_read_b128 %3, %19\n\t"
+            "ds_read_b128 %4, %16 offset:8192\n\tds_read_b128 %5, %17 offset:8192\n\t"
+            "ds_read_b128 %6, %18 offset:8192\n\tds_read_b128 %7, %19 offset:8192\n\t"
+            "ds_read_b128 %8, %20\n\tds_read_b128 %9, %21\n\t"
+            "ds_read_b128 %10, %22\n\tds_read_b128 %11, %23\n\t"
+            "ds_read_b128 %12, %20 offset:8192\n\tds_read_b128 %13, %21 offset:8192\n\t"
+            "ds_read_b128 %14, %22 offset:8192\n\tds_read_b128 %15, %23 offset:8192\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[0][2]), "=&v"(k[0][3]),
+              "=&v"(k[1][0]), "=&v"(k[1][1]), "=&v"(k[1][2]), "=&v"(k[1][3]),
+              "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
+              "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
+            : "v"(ak[0]), "v"(ak[1]), "v"(ak[2]), "v"(ak[3]),
+              "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3])
+            : "memory");
+    }
+};
+
+template <>
+struct GroupReads<64> {
+    static __device__ __forceinline__ void read(const uint32_t (&ak)[2], const uint32_t (&av)[4],
+                                                u32x4_t (&k)[2][2], u32x4_t (&v)[2][4]) {
+        asm volatile(
+            "ds_read_b128 %0, %12\n\tds_read_b128 %1, %13\n\t"
+            "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %3, %13 offset:4096\n\t"
+            "ds_read_b128 %4, %14\n\tds_read_b128 %5, %15\n\t"
+            "ds_read_b128 %6, %16\n\tds_read_b128 %7, %17\n\t"
+            "ds_read_b128 %8, %14 offset:4096\n\tds_read_b128 %9, %15 offset:4096\n\t"
+            "ds_read_b128 %10, %16 offset:4096\n\tds_read_b128 %11, %17 offset:4096\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[1][0]), "=&v"(k[1][1]),
+              "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
+              "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
+            : "v"(ak[0]), "v"(ak[1]), "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3])
+            : "memory");
+    }
+};
+
+// s_waitcnt with only the vector-memory counter: at most N loads in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int DIM, int RTW, int NW>
+__global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uint16_t *__restrict__ kc,
+                                                               const uint16_t *__restrict__ vc,
+                                                               const int32_t *__restrict__ kv_off,
+                                                               const int32_t *__restrict__ prefix_len,
+                                                               Work W) {
     constexpr int KSTEPS = DIM / 32, DPL = DIM / 16, CPT = DIM / 8;
-    constexpr int NCK = 16 * CPT;            // chunks per page and tensor
-    constexpr int CPTH = 2 * NCK / 256;      // chunks per thread per page (K and V together)
-    __shared__ uint4 s_page[2 * kDenseGroup][2][NCK];  // [two groups of pages][K, V][swizzled chunk]
+    constexpr int NCK = 16 * CPT;            // 16-byte chunks per page and tensor
+    constexpr int NT = 64 * NW;              // threads
+    constexpr int LPT = 2 * NCK / NT;        // direct loads per thread per page (K and V)
+    static_assert(LPT >= 1 && LPT * NT == 2 * NCK, "whole wave loads per page");
+    constexpr int NS = kDenseSlots, NG = kDenseGroup;
+    static_assert(NS % NG == 0 && NS >= 2 * NG, "the ring holds whole groups");
+    // loads each thread may leave in flight when a group must have landed: the
+    // pages of the groups after it that have been issued
+    constexpr int kAhead = LPT * (NS - 2 * NG);
+    __shared__ uint4 s_page[NS][2 * NCK];  // [slot][K chunks, then V chunks], swizzled
     const int ng = D.S * D.Hk;
     const int sgi = blockIdx.x % ng;
     const int chunk = blockIdx.x / ng;
@@ -422,36 +505,51 @@ __global__ __launch_bounds__(256) void k_prefix_dense_bf16(Dims D, const uint16_
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
     const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
-    const int first = chunk * kDenseChunk;
-    const int n_here = min(kDenseChunk, sg.pages - first);
+    const int first = chunk * D.dense_chunk;
+    const int n_here = min(D.dense_chunk, sg.pages - first);
     if (n_here <= 0) return;
     const int rows = D.Rd, nch = D.n_chunks_dense;
     const int n_rt = (rows + 15) / 16;
 
-    // Q operands (B of QK^T) of row tiles w + 4i: lane l holds row l%16, dims
-    // 32*kk + 8*(l/16) .. +7 (row tiles past the last read tile n_rt-1, unused)
+    // Q operands (B of QK^T) of row tiles w + NW*i: lane l holds row l%16, dims
+    // 32*kk + 8*(l/16) .. +7 (row tiles past the last read tile n_rt-1, unused).
+    // Issued before any page so that waiting for them never waits for a page.
     uint4 qop[RTW][KSTEPS];
     const uint16_t *qr = static_cast<const uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
-        const int rt = min(w + 4 * i, n_rt - 1);
+        const int rt = min(w + NW * i, n_rt - 1);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
             qop[i][kk] = *reinterpret_cast<const uint4 *>(qr + (size_t)(rt * 16 + l16) * DIM + 32 * kk + 8 * lg);
     }
-    // this thread's pieces of a page: piece q = tid + 256*h is chunk q % NCK of
-    // K (q < NCK) or V, i.e. token (q % NCK) / CPT, elements 8*((q % NCK) % CPT) ..
-    auto load_piece = [&](int p, int h) {
-        const int q = tid + 256 * h, cq = q % NCK;
-        const size_t base = ((size_t)g * D.T + sg.off + (size_t)(first + p) * kPage) * DIM;
-        const uint16_t *src = (q < NCK ? kc : vc) + base + (cq / CPT) * DIM + (cq % CPT) * 8;
-        return *reinterpret_cast<const uint4 *>(src);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Direct load h of a page: wave w writes LDS chunks (h*NW + w)*64 .. +63 of
+    // the slot; lane i's chunk L holds token t = (L % NCK) / CPT, swizzled column
+    // c' = (L % NCK) % CPT, i.e. global column c' ^ (t & (CPT-1)) of K (L < NCK) or V.
+    const uint16_t *src_h[LPT];
+#pragma unroll
+    for (int h = 0; h < LPT; ++h) {
+        const int L = (h * NW + w) * 64 + lane, cq = L % NCK;
+        const int t = cq / CPT, c = (cq % CPT) ^ (t & (CPT - 1));
+        src_h[h] = (L < NCK ? kc : vc) + ((size_t)g * D.T + sg.off + (size_t)first * kPage) * DIM +
+                   t * DIM + c * 8;
+    }
+    // (the builtin's arguments are passed as plain void pointers: with typed or
+    // const ones the host pass silently drops the kernel's launch stub)
+    auto issue = [&](int p, int slot) {  // page p of the chunk (clamped) into a slot
+        const size_t off = (size_t)min(p, n_here - 1) * kPage * DIM;
+#pragma unroll
+        for (int h = 0; h < LPT; ++h)
+            __builtin_amdgcn_global_load_lds(static_cast<void *>(const_cast<uint16_t *>(src_h[h] + off)),
+                                             static_cast<void *>(&s_page[slot][(h * NW + w) * 64]),
+                                             16, 0, 0);
     };
-    uint4 pf[kDensePrefetch][CPTH];
 #pragma unroll
-    for (int d = 0; d < kDensePrefetch; ++d)
-#pragma unroll
-        for (int h = 0; h < CPTH; ++h) pf[d][h] = load_piece(min(d, n_here - 1), h);
+    for (int p = 0; p < NS; ++p) issue(p, p);
+    // the Q operands have landed; the ring's loads may still be in flight
+    wait_vmcnt<LPT * NS>();
 
     float4_t oacc[RTW][DPL];
     float m_run[RTW], l_run[RTW];
@@ -462,66 +560,79 @@ __global__ __launch_bounds__(256) void k_prefix_dense_bf16(Dims D, const uint16_
 #pragma unroll
         for (int e = 0; e < DPL; ++e) oacc[i][e] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
-
     bool rt_ok[RTW];
 #pragma unroll
-    for (int i = 0; i < RTW; ++i) rt_ok[i] = w + 4 * i < n_rt;
-    // pages are attended in groups (independent MFMA chains, one shared max)
-    static_assert(kDensePrefetch % kDenseGroup == 0, "pages are staged in whole groups");
-    for (int it = 0; it < n_here; it += kDensePrefetch) {
+    for (int i = 0; i < RTW; ++i) rt_ok[i] = w + NW * i < n_rt;
+    // the lane's operand chunks inside a slot (bytes): K chunk (token l%16,
+    // dims 32*kk + 8*(l/16) ..) and V chunk (token 4*(l/16) + j, dims DPL*(l%16) ..)
+    static_assert(NG == 2, "operand reads are written for page pairs");
+    constexpr int SLOT_BYTES = 2 * NCK * 16;
+    const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_page[0][0]));
+    uint32_t ak[KSTEPS], av[4];
 #pragma unroll
-        for (int d = 0; d < kDensePrefetch; d += kDenseGroup) {
-            const int pi = it + d;
-            if (pi >= n_here) break;  // uniform
-            const int pb = kDenseGroup * ((pi / kDenseGroup) & 1);
+    for (int kk = 0; kk < KSTEPS; ++kk) ak[kk] = ring + 16u * swz<DIM>(l16, 4 * kk + lg);
 #pragma unroll
-            for (int n = 0; n < kDenseGroup; ++n)
-#pragma unroll
-                for (int h = 0; h < CPTH; ++h) {
-                    const int q = tid + 256 * h, cq = q % NCK;
-                    s_page[pb + n][q < NCK ? 0 : 1][swz<DIM>(cq / CPT, cq % CPT)] = pf[d + n][h];
-                }
-            // refill with the pages kDensePrefetch ahead (clamped: rereads the last page)
-#pragma unroll
-            for (int n = 0; n < kDenseGroup; ++n)
-#pragma unroll
-                for (int h = 0; h < CPTH; ++h)
-                    pf[d + n][h] = load_piece(min(pi + n + kDensePrefetch, n_here - 1), h);
-            __syncthreads();  // this group complete in LDS; the group before is no longer read
+    for (int j = 0; j < 4; ++j) av[j] = ring + 16u * (NCK + swz<DIM>(4 * lg + j, (DPL * l16) / 8));
 
-            uint4 kop[kDenseGroup][KSTEPS];
-            uint32_t vw[kDenseGroup][4][DPL / 2];
-            int valid[kDenseGroup];
+    // Group at pages pi .. pi+NG-1 (slots pi % NS ..): loads are issued in page
+    // order and complete in order, and when the group is due the pages issued
+    // after it are at most NS - 2*NG (the prologue's NS pages, then NG per group
+    // from the second on), so once at most kAhead of this thread's loads are in
+    // flight the group's pieces of this thread have landed.  The barrier then
+    // covers every thread's pieces, and tells that the previous group's slots
+    // are no longer read, so they are refilled with the pages NS ahead (clamped
+    // to the chunk's last page: slots past the chunk are never attended).
+    for (int pi = 0; pi < n_here; pi += NG) {
+        wait_vmcnt<kAhead>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (pi > 0) {  // (the first group waits for a little more than it needs)
 #pragma unroll
-            for (int n = 0; n < kDenseGroup; ++n) {
-                // a page past the chunk (odd count) attends nothing
-                valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + pi + n) * kPage) : 0;
+            for (int n = 0; n < NG; ++n) issue(pi - NG + n + NS, (pi - NG + n) % NS);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t sbase = static_cast<uint32_t>((pi % NS) * SLOT_BYTES);
+        uint32_t akk[KSTEPS], avv[4];
 #pragma unroll
-                for (int kk = 0; kk < KSTEPS; ++kk) kop[n][kk] = s_page[pb + n][0][swz<DIM>(l16, 4 * kk + lg)];
-                // V words of tokens 4*lg + j for the lane's dims DPL*l16 .. +DPL-1
+        for (int kk = 0; kk < KSTEPS; ++kk) akk[kk] = ak[kk] + sbase;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 c4 = s_page[pb + n][1][swz<DIM>(4 * lg + j, (DPL * l16) / 8)];
-                    if constexpr (DPL == 8) {
-                        vw[n][j][0] = c4.x; vw[n][j][1] = c4.y; vw[n][j][2] = c4.z; vw[n][j][3] = c4.w;
-                    } else {
-                        const bool hi = (l16 & 1) != 0;
-                        vw[n][j][0] = hi ? c4.z : c4.x;
-                        vw[n][j][1] = hi ? c4.w : c4.y;
-                    }
+        for (int j = 0; j < 4; ++j) avv[j] = av[j] + sbase;
+        u32x4_t kraw[NG][KSTEPS], vraw[NG][4];
+        GroupReads<DIM>::read(akk, avv, kraw, vraw);
+
+        uint4 kop[NG][KSTEPS];
+        uint32_t vw[NG][4][DPL / 2];
+        int valid[NG];
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+            // a page past the chunk (odd count) attends nothing
+            valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + pi + n) * kPage) : 0;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) kop[n][kk] = __builtin_bit_cast(uint4, kraw[n][kk]);
+            // V words of tokens 4*lg + j for the lane's dims DPL*l16 .. +DPL-1
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4_t c4 = vraw[n][j];
+                if constexpr (DPL == 8) {
+                    vw[n][j][0] = c4[0]; vw[n][j][1] = c4[1]; vw[n][j][2] = c4[2]; vw[n][j][3] = c4[3];
+                } else {
+                    const bool hi = (l16 & 1) != 0;
+                    vw[n][j][0] = hi ? c4[2] : c4[0];
+                    vw[n][j][1] = hi ? c4[3] : c4[1];
                 }
             }
-            attend_pages<DIM, RTW, kDenseGroup>(kop, vw, valid, qop, rt_ok, D.scale_log2, oacc, m_run,
-                                                l_run, lg);
         }
+        attend_pages<DIM, RTW, NG>(kop, vw, valid, qop, rt_ok, D.scale_log2, oacc, m_run, l_run, lg);
     }
+    // no direct load may still be writing LDS when the workgroup ends
+    wait_vmcnt<0>();
 #pragma unroll
     for (int i = 0; i < RTW; ++i) l_run[i] = shfl_sum32(l_run[i]);
 
     // Lane l holds, for row l%16, dims DPL*(4*lg + j) + e.
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
-        const int rt = w + 4 * i;
+        const int rt = w + NW * i;
         if (rt >= n_rt) break;
         const int r = rt * 16 + l16;
         if (r >= rows) continue;
@@ -553,7 +664,7 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restr
     constexpr bool dense = DENSE;
     constexpr int DPT = DIM / 16;
     __shared__ uint32_t s_bm[kMaxBitmapWords];
-    __shared__ int s_wsum[4], s_pg[kSparseChunk];
+    __shared__ int s_wsum[4], s_pg[kMaxSparseChunk];
     __shared__ float q_s[16][DIM];
     __shared__ float k_s[16][DIM + 1];
     __shared__ float v_s[16][DIM];
@@ -563,7 +674,7 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restr
     const int chunk = blockIdx.x / ng;
     const int s = sgi / D.Hk, g = sgi % D.Hk;
     const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
-    const int cp = dense ? kDenseChunk : kSparseChunk;
+    const int cp = dense ? D.dense_chunk : D.sparse_chunk;
     const int first = chunk * cp;
     int n_items;
     if (dense) {
@@ -660,24 +771,25 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const v
         else if (rtw == 2) LAUNCH_P(DIMV, 2, DN); \
         else LAUNCH_P(DIMV, 4, DN);              \
     } while (0)
-#define LAUNCH_D(DIMV, RTWV)                                                                      \
-    hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV>), grid, dim3(256), 0, st, D, k, v, kv_off, \
-                       prefix_len, W)
-        // dense pass: every wave takes row tiles w, w + 4, ...
-        const int rtwd = n_rt <= 4 ? 1 : (n_rt <= 8 ? 2 : 4);
+#define LAUNCH_D(DIMV, RTWV, NWV)                                                                 \
+    hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV, NWV>), grid, dim3(64 * NWV), 0, st, D, k, v, \
+                       kv_off, prefix_len, W)
+        // dense pass: wave w of NW takes row tiles w, w + NW, ...; head_dim 128
+        // uses eight waves (one page of K and V is one 16-byte piece per thread)
+        // once there are more than four row tiles
         if (D.d == 128) {
             if (dense) {
-                if (rtwd == 1) LAUNCH_D(128, 1);
-                else if (rtwd == 2) LAUNCH_D(128, 2);
-                else LAUNCH_D(128, 4);
+                if (n_rt <= 4) LAUNCH_D(128, 1, 4);
+                else if (n_rt <= 8) LAUNCH_D(128, 1, 8);
+                else LAUNCH_D(128, 2, 8);
             } else {
                 PICK_P(128, false);
             }
         } else {
             if (dense) {
-                if (rtwd == 1) LAUNCH_D(64, 1);
-                else if (rtwd == 2) LAUNCH_D(64, 2);
-                else LAUNCH_D(64, 4);
+                if (n_rt <= 4) LAUNCH_D(64, 1, 4);
+                else if (n_rt <= 8) LAUNCH_D(64, 2, 4);
+                else LAUNCH_D(64, 4, 4);
             } else {
                 PICK_P(64, false);
             }

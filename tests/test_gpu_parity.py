@@ -126,6 +126,13 @@ SMALL = [
     ("bf16_d128_seq_offsets", dict(dtype="bf16", head_dim=128, block=16, n_active=3, budget=48,
                                    prefix_lens=(1040, 17, 2064, 999, 1), n_kvhead=2, n_qhead=4,
                                    needles=True)),
+    # 256 stacked dense rows per KV head (the most the library takes): eight-wave
+    # dense pass with two row tiles per wave (d=128), four per wave (d=64)
+    ("bf16_d128_G8_B32_rows256", dict(dtype="bf16", head_dim=128, block=32, n_active=8,
+                                      budget=64, prefix_lens=(1500, 300), n_kvhead=1,
+                                      n_qhead=8)),
+    ("bf16_d64_G8_B32_AB_rows256", dict(dtype="bf16", head_dim=64, block=32, n_active=32,
+                                        budget=64, prefix_lens=(1200,), n_kvhead=1, n_qhead=8)),
 ]
 
 
@@ -156,6 +163,19 @@ def test_gqa_16k_workload():
     p = Pair(W.make_layer(cfg), cfg.name)
     p.dense(0)
     for step in range(1, cfg.n_steps):
+        p.sparse(step)
+
+
+def test_wide_union_chunks():
+    """Two 16K-class sequences with every token active and a 1024-token budget:
+    union capacity 1024 pages for each of 16 (sequence, KV head) pairs, so the
+    sparse pass takes 16 union pages per workgroup and the dense pass 32."""
+    cfg = W.small_case(260, n_seq=2, block=16, n_qhead=32, n_kvhead=8, head_dim=128,
+                       budget=1024, n_active=16, dtype="bf16", prefix_lens=(16384, 12000),
+                       n_steps=3, needles=True, n_drift=4)
+    p = Pair(W.make_layer(cfg), "wide_union_chunks")
+    p.dense(0)
+    for step in (1, 2):
         p.sparse(step)
 
 
