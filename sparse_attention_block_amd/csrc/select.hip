@@ -258,8 +258,8 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     const int G = D.G, B = D.B, A = D.A, GB = G * B, R = D.R, Hq = D.Hq;
     const bool writer = blk == 0;
 
-    // 1. requested together: the group's query rows (clamped 16-byte vectors)
-    //    and, for a tile in range, the tile's page operands
+    // 1. the group's query rows (clamped 16-byte vectors) into LDS, then the
+    //    tile's page operands are requested
     const int nvec = GB * VPR;
     static_assert(kPrepVecs == 8, "one named register per query vector below");
     auto qload = [&](int i) {
@@ -284,6 +284,23 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     const int R1 = R > 0 ? R : 1;
     const int l16 = lane & 15, lg = lane >> 4;
     const uint4 *mt = meta + (size_t)(g * D.n_tiles_total + tile) * NCH * kTile;
+    auto qstore = [&](int i, const uint4 &q) {
+        const int idx = min(tid + 256 * i, 2 * nvec - 1);
+        const int which = idx / nvec, v = idx % nvec;
+        *reinterpret_cast<uint4 *>(&qsm[(which * GB + v / VPR) * RWP + (v % VPR) * 4]) = q;
+    };
+    qstore(0, qv0);
+    qstore(1, qv1);
+    qstore(2, qv2);
+    qstore(3, qv3);
+    qstore(4, qv4);
+    qstore(5, qv5);
+    qstore(6, qv6);
+    qstore(7, qv7);
+    // The tile is requested only now, after the query vectors have landed: the
+    // tiles of all workgroups together would otherwise queue ahead of them, and
+    // the preparation below waits for the queries, not for the tile.
+    __builtin_amdgcn_sched_barrier(0);
     uint4 bop[KS][4];
     float amax[4];
     int pl[4];
@@ -300,19 +317,6 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         amax[cb] = aux[cb * 16 + l16];
     }
     __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
-    auto qstore = [&](int i, const uint4 &q) {
-        const int idx = min(tid + 256 * i, 2 * nvec - 1);
-        const int which = idx / nvec, v = idx % nvec;
-        *reinterpret_cast<uint4 *>(&qsm[(which * GB + v / VPR) * RWP + (v % VPR) * 4]) = q;
-    };
-    qstore(0, qv0);
-    qstore(1, qv1);
-    qstore(2, qv2);
-    qstore(3, qv3);
-    qstore(4, qv4);
-    qstore(5, qv5);
-    qstore(6, qv6);
-    qstore(7, qv7);
     if (writer && tid == 0) {
         W.union_cnt[sgi] = 0;
         if (dbg_ucnt) dbg_ucnt[sgi] = 0;  // the sparse prefix kernel overwrites them
@@ -529,15 +533,15 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         float tmv[TMR];
 #pragma unroll
         for (int i = 0; i < TMR; ++i) tmv[i] = tm[min(lane + 64 * i, n_t - 1)];
-        float4 hv[16];
         // upper ends of pages base + 256*jj + 4*lane + e, jj < 16, e < 4
-        auto load_h = [&](int base) {
+        auto load_h = [&](int base, float4 (&hv)[16]) {
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj)
                 hv[jj] = *reinterpret_cast<const float4 *>(
                     hb + min(base + 256 * jj + 4 * lane, D.hb_stride - 4));
         };
-        load_h(0);
+        float4 hv0[16];
+        load_h(0, hv0);
         __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
         if constexpr (BF) {
             if (lane < DIM / 2) qw[lane] = qv[0];
@@ -566,8 +570,11 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         // 2. candidates: upper end >= threshold; exact chain in batches of 64
         uint64_t lst = 0ull;  // lane e < k: e-th best (score key << 32 | ~page)
         int npend = 0;
-        for (int base = 0; base < sg.pages; base += 4096) {
-            if (base > 0) load_h(base);
+        // One batch of 4096 pages: the candidates' bits, then every lane's
+        // candidates appended to the pending list, whose exact chains are taken
+        // 64 at a time.  The first batch uses the upper ends requested above;
+        // later ones load theirs (so the first set is dead after its batch).
+        auto batch = [&](int base, const float4 (&hv)[16]) {
             // bit 4*jj + e4 of cmask: page base + 256*jj + 4*lane + e4 is a candidate
             uint64_t cmask = 0ull;
             const int lim = sg.pages - base - 4 * lane;
@@ -576,7 +583,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                 const float hx[4] = {hv[jj].x, hv[jj].y, hv[jj].z, hv[jj].w};
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
-                    const bool c = 256 * jj + e4 < lim && ord_key(hx[e4]) >= lam;
+                    const bool c = (256 * jj + e4 < lim) & (ord_key(hx[e4]) >= lam);
                     cmask |= static_cast<uint64_t>(c) << (4 * jj + e4);
                 }
             }
@@ -635,6 +642,12 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                 }
                 if (bal == 0ull) break;
             }
+        };
+        batch(0, hv0);
+        for (int base = 4096; base < sg.pages; base += 4096) {
+            float4 hv[16];
+            load_h(base, hv);
+            batch(base, hv);
         }
         // 3. the row's pages (k of them: every page of the exact top-k is a candidate)
         const bool has = lane < k && lst != 0ull;
