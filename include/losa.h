@@ -153,6 +153,27 @@ int losa_build_page_meta(const losa_shape *shape, const void *k_cache, const int
                          const int32_t *prefix_len, void *page_meta, void *stream);
 
 /*
+ * Block commit: when the tokens first_token[s] .. prefix_len[s] - 1 of each
+ * sequence have joined its prefix (a committed block; the cache already holds
+ * their keys), rewrites the metadata of the pages holding them -- the same
+ * bytes losa_build_page_meta would write for those pages -- and nothing else.
+ * The pages before them keep their metadata (their keys do not change).
+ *   first_token: device int32 [n_seq], the first new token of each sequence
+ *                (a sequence with first_token[s] >= prefix_len[s] is left as is)
+ *   max_new_tokens: host bound on prefix_len[s] - first_token[s] over the
+ *                sequences (sizes the launch; pages past it are not rewritten)
+ *   prefix_len: the new prefix lengths; shape->max_prefix_len bounds them.
+ * Errors: LOSA_ERR_INVALID_ARG for null or misaligned pointers or
+ * max_new_tokens outside 0 .. max_prefix_len; nothing is enqueued then.
+ * The pages' tokens themselves are read from k_cache as in
+ * losa_build_page_meta (reading used for QUEST: per-page element-wise min and
+ * max, gist.science pt summary, "3. Metodologia", step 3).
+ */
+int losa_update_page_meta(const losa_shape *shape, const void *k_cache, const int32_t *kv_off,
+                          const int32_t *prefix_len, const int32_t *first_token,
+                          int32_t max_new_tokens, void *page_meta, void *stream);
+
+/*
  * Forced dense first step of a block (agifrontier tutorial, limitations
  * section): every block token of every query head attends over its whole
  * prefix; (o_p, L_p) of every token are written to op_cache/lp_cache

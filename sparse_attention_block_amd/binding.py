@@ -75,6 +75,9 @@ def load(path: str = LIB_PATH):
     lib.losa_union_capacity.restype = c_int32
     lib.losa_build_page_meta.argtypes = [S, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.losa_build_page_meta.restype = c_int
+    lib.losa_update_page_meta.argtypes = [S, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                          c_void_p, c_void_p]
+    lib.losa_update_page_meta.restype = c_int
     lib.losa_dense_first_step.argtypes = [S] + [c_void_p] * 10 + [POINTER(LosaDebug), c_void_p,
                                                                    c_size_t, c_void_p]
     lib.losa_dense_first_step.restype = c_int
@@ -173,6 +176,20 @@ def losa_build_page_meta(shape, k_cache, kv_off, prefix_len, page_meta, stream=N
     ]
     _raise(load().losa_build_page_meta(ctypes.byref(shape), *args, _stream(stream)),
            "losa_build_page_meta")
+
+
+def losa_update_page_meta(shape, k_cache, kv_off, prefix_len, first_token, max_new_tokens,
+                          page_meta, stream=None):
+    n = _sizes(shape)
+    args = [
+        _check(k_cache, "k_cache", _torch_dtype(shape), n["cache"]),
+        _check(kv_off, "kv_off", torch.int32, shape.n_seq),
+        _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+        _check(first_token, "first_token", torch.int32, shape.n_seq),
+    ]
+    meta = _check(page_meta, "page_meta", torch.uint8, page_meta_bytes(shape))
+    _raise(load().losa_update_page_meta(ctypes.byref(shape), *args, int(max_new_tokens), meta,
+                                        _stream(stream)), "losa_update_page_meta")
 
 
 def losa_dense_first_step(shape, q_t, k_blk, v_blk, k_cache, v_cache, kv_off, prefix_len,

@@ -173,8 +173,23 @@ int losa_build_page_meta(const losa_shape *shape, const void *k_cache, const int
         !aligned(prefix_len, 4))
         return LOSA_ERR_INVALID_ARG;
     const Dims D = make_dims(shape);
-    return hip_status(launch_page_meta(D, k_cache, kv_off, prefix_len, page_meta,
+    return hip_status(launch_page_meta(D, k_cache, kv_off, prefix_len, nullptr, 0, page_meta,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int losa_update_page_meta(const losa_shape *shape, const void *k_cache, const int32_t *kv_off,
+                          const int32_t *prefix_len, const int32_t *first_token,
+                          int32_t max_new_tokens, void *page_meta, void *stream) {
+    int st = check_shape(shape);
+    if (st != LOSA_OK) return st;
+    if (!k_cache || !kv_off || !prefix_len || !first_token || !page_meta) return LOSA_ERR_INVALID_ARG;
+    if (!aligned(k_cache, 16) || !aligned(page_meta, 16) || !aligned(kv_off, 4) ||
+        !aligned(prefix_len, 4) || !aligned(first_token, 4))
+        return LOSA_ERR_INVALID_ARG;
+    if (max_new_tokens < 0 || max_new_tokens > shape->max_prefix_len) return LOSA_ERR_INVALID_ARG;
+    const Dims D = make_dims(shape);
+    return hip_status(launch_page_meta(D, k_cache, kv_off, prefix_len, first_token, max_new_tokens,
+                                       page_meta, static_cast<hipStream_t>(stream)));
 }
 
 int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *k_blk,

@@ -64,7 +64,8 @@ struct Work {
 
 // Launchers (one per translation unit); each returns the hipGetLastError code.
 hipError_t launch_page_meta(const Dims &D, const void *k_cache, const int32_t *kv_off,
-                            const int32_t *prefix_len, void *meta, hipStream_t st);
+                            const int32_t *prefix_len, const int32_t *first_token,
+                            int max_new_tokens, void *meta, hipStream_t st);
 hipError_t launch_prepare(const Dims &D, bool dense, const void *q_t, const void *q_prev,
                           const Work &W, float *dbg_locality, int32_t *dbg_active,
                           int32_t *dbg_union_cnt, hipStream_t st);

@@ -18,96 +18,125 @@
 
 namespace losa {
 
+// One thread per (page, 16-byte column chunk of a token row): it loads that
+// chunk of each of the page's 16 tokens (the lanes of a page cover a token row
+// contiguously, so every load instruction reads whole rows), keeps the
+// element-wise minimum and maximum in registers, and writes its metadata chunks;
+// the page's largest |key| is reduced over the page's lanes.  With first_token,
+// only the pages holding tokens first_token[s] .. prefix_len[s] - 1 of each
+// sequence are rewritten (a committed block); page p of the launch is then page
+// first_token[s] / 16 + p.
 template <typename T, int DIM>
 __global__ __launch_bounds__(256) void k_page_meta(Dims D, const T *__restrict__ kc,
                                                    const int32_t *__restrict__ kv_off,
                                                    const int32_t *__restrict__ prefix_len,
+                                                   const int32_t *__restrict__ first_token,
                                                    uint32_t *__restrict__ meta) {
     constexpr bool BF = sizeof(T) == 2;
-    constexpr int DPC = BF ? 4 : 2;       // dimensions per 16-byte chunk
-    constexpr int NCH = DIM / DPC;
-    __shared__ uint32_t s_amax[kTile];
+    constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte column chunk
+    constexpr int CPR = DIM / EPC;        // column chunks per token row (= lanes per page)
+    constexpr int PPW = 256 / CPR;        // pages per workgroup
+    constexpr int DPC = BF ? 4 : 2;       // dimensions per metadata chunk
+    constexpr int NCH = DIM / DPC;        // metadata chunks per page
+    constexpr int MPT = EPC / DPC;        // metadata chunks per thread
+    static_assert(CPR <= 64 && 64 % CPR == 0, "a page's lanes lie in one wave");
     const int g = blockIdx.y, s = blockIdx.z;
+    const int tid = threadIdx.x, cc = tid % CPR;
     const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
-    if (threadIdx.x < kTile) s_amax[threadIdx.x] = 0u;
-    __syncthreads();
-    for (int item = threadIdx.x; item < kTile * NCH; item += blockDim.x) {
-        const int pl = blockIdx.x * kTile + (item % kTile);
-        const int c = item / kTile;
-        if (pl >= sg.pages) continue;
-        const int t0 = pl * kPage;
-        const int t1 = min(t0 + kPage, sg.len);
-        float mn[DPC], mx[DPC];
+    const int p0 = first_token ? max(0, first_token[s]) / kPage : 0;
+    const int pl = p0 + blockIdx.x * PPW + tid / CPR;  // local page
+    const bool live = pl < sg.pages;
+    const int valid = live ? min(kPage, sg.len - pl * kPage) : 0;
+    // the page's 16 rows of this column chunk (clamped rows: tokens past the
+    // prefix, and pages past the sequence, reread its last valid token)
+    const int last = max(sg.len - 1, 0);
+    uint4 v[kPage];
 #pragma unroll
-        for (int e = 0; e < DPC; ++e) {
-            mn[e] = __builtin_huge_valf();
-            mx[e] = -__builtin_huge_valf();
-        }
-        for (int t = t0; t < t1; ++t) {
-            const T *row = kc + ((size_t)g * D.T + sg.off + t) * DIM + c * DPC;
+    for (int t = 0; t < kPage; ++t) {
+        const int64_t row = min(sg.off + min(pl * kPage + t, last), D.T - 1);  // inside the cache
+        v[t] = *reinterpret_cast<const uint4 *>(kc + ((size_t)g * D.T + row) * DIM + cc * EPC);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float mn[EPC], mx[EPC];
 #pragma unroll
-            for (int e = 0; e < DPC; ++e) {
-                float v;
-                if constexpr (BF) v = bf16_to_f32(reinterpret_cast<const uint16_t *>(row)[e]);
-                else v = reinterpret_cast<const float *>(row)[e];
-                mn[e] = fminf(mn[e], v);
-                mx[e] = fmaxf(mx[e], v);
+    for (int e = 0; e < EPC; ++e) {
+        mn[e] = __builtin_huge_valf();
+        mx[e] = -__builtin_huge_valf();
+    }
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) {
+        const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+        float x[EPC];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (BF) {
+                x[2 * q] = bf16_lo(w[q]);
+                x[2 * q + 1] = bf16_hi(w[q]);
+            } else {
+                x[q] = __uint_as_float(w[q]);
             }
         }
-        float am = 0.0f;
+        if (t < valid) {
 #pragma unroll
-        for (int e = 0; e < DPC; ++e) am = fmaxf(am, fmaxf(fabsf(mn[e]), fabsf(mx[e])));
-        atomicMax(&s_amax[item % kTile], __float_as_uint(am));  // non-negative: bits order as values
-        const int64_t gp = sg.gp0 + pl;
-        const int64_t tile = gp / kTile;
-        const int lane = static_cast<int>(gp % kTile);
+            for (int e = 0; e < EPC; ++e) {
+                mn[e] = fminf(mn[e], x[e]);
+                mx[e] = fmaxf(mx[e], x[e]);
+            }
+        }
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) am = fmaxf(am, fmaxf(fabsf(mn[e]), fabsf(mx[e])));
+#pragma unroll
+    for (int o = 1; o < CPR; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+    if (!live) return;
+    const int64_t gp = sg.gp0 + pl;
+    const int64_t tile = gp / kTile;
+    const int lane = static_cast<int>(gp % kTile);
+#pragma unroll
+    for (int m = 0; m < MPT; ++m) {
+        const int c = cc * MPT + m;  // metadata chunk: dimensions c*DPC ..
         uint4 u;
         if constexpr (BF) {
-            // min/max of bf16 values are bf16 values: the top 16 bits are exact.
-            u.x = (__float_as_uint(mx[0]) >> 16) | (__float_as_uint(mn[0]) & 0xffff0000u);
-            u.y = (__float_as_uint(mx[1]) >> 16) | (__float_as_uint(mn[1]) & 0xffff0000u);
-            u.z = (__float_as_uint(mx[2]) >> 16) | (__float_as_uint(mn[2]) & 0xffff0000u);
-            u.w = (__float_as_uint(mx[3]) >> 16) | (__float_as_uint(mn[3]) & 0xffff0000u);
+            // min/max of bf16 values are bf16 values: the top 16 bits are exact
+            uint32_t wd[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                wd[e] = (__float_as_uint(mx[4 * m + e]) >> 16) | (__float_as_uint(mn[4 * m + e]) & 0xffff0000u);
+            u = make_uint4(wd[0], wd[1], wd[2], wd[3]);
         } else {
-            u.x = __float_as_uint(mx[0]);
-            u.y = __float_as_uint(mn[0]);
-            u.z = __float_as_uint(mx[1]);
-            u.w = __float_as_uint(mn[1]);
+            u = make_uint4(__float_as_uint(mx[2 * m]), __float_as_uint(mn[2 * m]),
+                           __float_as_uint(mx[2 * m + 1]), __float_as_uint(mn[2 * m + 1]));
         }
-        uint4 *dst = reinterpret_cast<uint4 *>(meta) +
-                     ((size_t)(g * D.n_tiles_total + tile) * NCH + c) * kTile + lane;
-        *dst = u;
+        reinterpret_cast<uint4 *>(meta)[((size_t)(g * D.n_tiles_total + tile) * NCH + c) * kTile + lane] = u;
     }
-    __syncthreads();
-    if (threadIdx.x < kTile) {
-        const int pl = blockIdx.x * kTile + threadIdx.x;
-        if (pl < sg.pages) {
-            float *aux = reinterpret_cast<float *>(reinterpret_cast<char *>(meta) + D.meta_main_bytes);
-            aux[(size_t)g * D.n_tiles_total * kTile + sg.gp0 + pl] = __uint_as_float(s_amax[threadIdx.x]);
-        }
+    if (cc == 0) {
+        float *aux = reinterpret_cast<float *>(reinterpret_cast<char *>(meta) + D.meta_main_bytes);
+        aux[(size_t)g * D.n_tiles_total * kTile + gp] = am;
     }
 }
 
 hipError_t launch_page_meta(const Dims &D, const void *k_cache, const int32_t *kv_off,
-                            const int32_t *prefix_len, void *meta, hipStream_t st) {
-    dim3 grid((D.max_pages + kTile - 1) / kTile, D.Hk, D.S);
-    if (grid.x == 0) return hipSuccess;
+                            const int32_t *prefix_len, const int32_t *first_token,
+                            int max_new_tokens, void *meta, hipStream_t st) {
+    // pages per sequence the launch covers: all of the longest prefix, or those
+    // a committed block of at most max_new_tokens tokens can touch
+    const int pages = first_token ? (max_new_tokens + kPage - 1) / kPage + 1 : D.max_pages;
+    const int cpr = D.d * (D.bf16 ? 2 : 4) / 16, ppw = 256 / cpr;
+    dim3 grid((pages + ppw - 1) / ppw, D.Hk, D.S);
+    if (pages <= 0 || grid.x == 0) return hipSuccess;
     auto *m = static_cast<uint32_t *>(meta);
+#define LAUNCH_M(TV, DIMV)                                                                       \
+    hipLaunchKernelGGL((k_page_meta<TV, DIMV>), grid, dim3(256), 0, st, D,                       \
+                       static_cast<const TV *>(k_cache), kv_off, prefix_len, first_token, m)
     if (D.bf16) {
-        if (D.d == 128)
-            hipLaunchKernelGGL((k_page_meta<uint16_t, 128>), grid, dim3(256), 0, st, D,
-                               static_cast<const uint16_t *>(k_cache), kv_off, prefix_len, m);
-        else
-            hipLaunchKernelGGL((k_page_meta<uint16_t, 64>), grid, dim3(256), 0, st, D,
-                               static_cast<const uint16_t *>(k_cache), kv_off, prefix_len, m);
+        if (D.d == 128) LAUNCH_M(uint16_t, 128);
+        else LAUNCH_M(uint16_t, 64);
     } else {
-        if (D.d == 128)
-            hipLaunchKernelGGL((k_page_meta<float, 128>), grid, dim3(256), 0, st, D,
-                               static_cast<const float *>(k_cache), kv_off, prefix_len, m);
-        else
-            hipLaunchKernelGGL((k_page_meta<float, 64>), grid, dim3(256), 0, st, D,
-                               static_cast<const float *>(k_cache), kv_off, prefix_len, m);
+        if (D.d == 128) LAUNCH_M(float, 128);
+        else LAUNCH_M(float, 64);
     }
+#undef LAUNCH_M
     return hipGetLastError();
 }
 

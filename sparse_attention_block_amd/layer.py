@@ -61,6 +61,13 @@ class LayerState:
         L.losa_build_page_meta(self.shape, self.k_cache, self.kv_off, self.prefix_len,
                                self.page_meta, stream)
 
+    def update_page_meta(self, first_token, max_new_tokens: int, stream=None):
+        """After a committed block: the new prefix lengths are already in
+        self.prefix_len; first_token[s] is each sequence's first new token."""
+        ft = torch.as_tensor(np.asarray(first_token, np.int32)).to(self.device)
+        L.losa_update_page_meta(self.shape, self.k_cache, self.kv_off, self.prefix_len, ft,
+                                max_new_tokens, self.page_meta, stream)
+
     def dense_first_step(self, q_t, k_blk, v_blk, out=None, debug: Optional[L.Debug] = None,
                          stream=None):
         out = self.out if out is None else out

@@ -87,6 +87,27 @@ def test_bad_shape_rejected(lib, kw, status):
     assert r == status
     r = lib.losa_build_page_meta(ctypes.byref(sh), fake, fake, fake, fake, None)
     assert r == status
+    r = lib.losa_update_page_meta(ctypes.byref(sh), fake, fake, fake, fake, 16, fake, None)
+    assert r == status
+
+
+def test_update_page_meta_checks(lib):
+    """Block-commit update: null or misaligned pointers and a token bound outside
+    0 .. max_prefix_len are rejected before anything is enqueued."""
+    sh = shape_of(W.gqa_16k())
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    ok = [fake] * 4
+    for i in range(4):
+        bad = list(ok)
+        bad[i] = None
+        assert lib.losa_update_page_meta(ctypes.byref(sh), *bad, 16, fake, None) == L.LOSA_ERR_INVALID_ARG
+    assert lib.losa_update_page_meta(ctypes.byref(sh), *ok, 16, None, None) == L.LOSA_ERR_INVALID_ARG
+    assert lib.losa_update_page_meta(ctypes.byref(sh), fake, fake, fake, odd, 16, fake,
+                                     None) == L.LOSA_ERR_INVALID_ARG
+    assert lib.losa_update_page_meta(ctypes.byref(sh), *ok, -1, fake, None) == L.LOSA_ERR_INVALID_ARG
+    assert lib.losa_update_page_meta(ctypes.byref(sh), *ok, sh.max_prefix_len + 1, fake,
+                                     None) == L.LOSA_ERR_INVALID_ARG
 
 
 def test_pointer_and_workspace_checks(lib):
