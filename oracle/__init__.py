@@ -28,7 +28,8 @@ class OracleShape(ctypes.Structure):
         ("n_seq", c_int32), ("block", c_int32), ("n_qhead", c_int32), ("n_kvhead", c_int32),
         ("head_dim", c_int32), ("page_size", c_int32), ("budget_tokens", c_int32),
         ("n_active", c_int32), ("out_bf16", c_int32), ("union_cap", c_int32),
-        ("kv_tokens", c_int64), ("softmax_scale", c_double),
+        ("kv_tokens", c_int64), ("softmax_scale", c_double), ("flags", c_int32),
+        ("pad_", c_int32),
     ]
 
 
@@ -52,6 +53,7 @@ def load(path: str = LIB_PATH):
     lib.oracle_page_meta.argtypes = [_S, _F, _I, _I, _F, _F]
     lib.oracle_locality.argtypes = [_S, _F, _F, _F]
     lib.oracle_active_set.argtypes = [_S, _F, _I]
+    lib.oracle_shared_active_set.argtypes = [_S, _F, _F, _I]
     lib.oracle_page_bound.argtypes = [_F, _F, _F, c_int]
     lib.oracle_page_bound.restype = c_float
     lib.oracle_select_pages.argtypes = [_S, _F, _F, _F, _I, _I, _I, _I, _I, _I, _F, c_int64]
@@ -95,7 +97,8 @@ def make_shape(cfg, kv_tokens: int, union_cap: int = 0, n_active=None, budget=No
         cfg.n_seq, cfg.block, cfg.n_qhead, cfg.n_kvhead, cfg.head_dim, cfg.page_size,
         cfg.budget if budget is None else budget,
         cfg.n_active if n_active is None else n_active,
-        1 if cfg.dtype == "bf16" else 0, union_cap, kv_tokens, softmax_scale)
+        1 if cfg.dtype == "bf16" else 0, union_cap, kv_tokens, softmax_scale,
+        getattr(cfg, "flags", 0), 0)
 
 
 class Oracle:

@@ -46,7 +46,27 @@ typedef struct {
     int32_t union_cap;     /* capacity of each union list in the debug output */
     int64_t kv_tokens;     /* T */
     double softmax_scale;  /* 0 => 1/sqrt(d) */
+    int32_t flags;         /* readings of three points the pages leave open (below); 0: the
+                              plain reading */
+    int32_t pad_;
 } oracle_shape;
+
+/* Variants of readings the pages leave open (0 = the plain reading):
+ *  ROW_MASK: each active query attends only over the pages it selected itself,
+ *    not over the whole union of its KV head (QUEST's own per-query selection;
+ *    the union still decides what is loaded) [FR "Réduction de l'Union KV"].
+ *  SHARED_ACTIVE: one active set per sequence, shared by all query heads: the
+ *    locality score of a token is the sum over query heads (ascending) of its
+ *    per-head scores, an fp32 chain; the |A| largest are active, equal sums to
+ *    the lower token [the tutorial's overhead estimate is per head; a
+ *    per-layer score is the other reading].
+ *  NO_WRITEBACK: a sparse step does not store the active tokens' new (o_p,
+ *    L_p): they serve that step's output only, and the cache keeps the
+ *    statistics of the block's dense first step [T "LoSA workflow": the cached
+ *    statistics are reused from the last full computation]. */
+#define ORACLE_ROW_MASK 1
+#define ORACLE_SHARED_ACTIVE 2
+#define ORACLE_NO_WRITEBACK 4
 
 static double scale_of(const oracle_shape *sh) {
     return sh->softmax_scale > 0 ? sh->softmax_scale : 1.0 / sqrt((double)sh->head_dim);
@@ -146,6 +166,37 @@ void oracle_active_set(const oracle_shape *sh, const float *score, int32_t *acti
             for (int t = 0; t < B; ++t)
                 if (taken[t]) out[n++] = t;
         }
+}
+
+/* Shared active set (SHARED_ACTIVE): per sequence, the sum over query heads in
+ * ascending order of each token's per-head score (fp32 chain), then the |A|
+ * largest as in oracle_active_set, the same list written for every head. */
+void oracle_shared_active_set(const oracle_shape *sh, const float *score, float *total,
+                              int32_t *active) {
+    const int B = sh->block, H = sh->n_qhead, A = sh->n_active;
+    char taken[4096];
+    if (B > 4096) return;
+    for (int s = 0; s < sh->n_seq; ++s) {
+        float *tot = total + (int64_t)s * B;
+        for (int t = 0; t < B; ++t) {
+            float acc = 0.0f;
+            for (int h = 0; h < H; ++h) acc = acc + score[((int64_t)s * H + h) * B + t];
+            tot[t] = acc;
+        }
+        memset(taken, 0, sizeof taken);
+        for (int a = 0; a < A; ++a) {
+            int best = -1;
+            for (int t = 0; t < B; ++t)
+                if (!taken[t] && (best < 0 || tot[t] > tot[best])) best = t;
+            taken[best] = 1;
+        }
+        for (int h = 0; h < H; ++h) {
+            int32_t *out = active + ((int64_t)s * H + h) * A;
+            int n = 0;
+            for (int t = 0; t < B; ++t)
+                if (taken[t]) out[n++] = t;
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */
@@ -352,7 +403,13 @@ void oracle_step(const oracle_shape *sh, const float *q_t, const float *q_prev, 
     float *score = (float *)malloc(sizeof(float) * (size_t)(nsh * B));
     int32_t *active = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nsh * A + 1));
     oracle_locality(sh, q_t, q_prev, score);
-    oracle_active_set(sh, score, active);
+    if (sh->flags & ORACLE_SHARED_ACTIVE) {
+        float *total = (float *)malloc(sizeof(float) * (size_t)(sh->n_seq * B));
+        oracle_shared_active_set(sh, score, total, active);
+        free(total);
+    } else {
+        oracle_active_set(sh, score, active);
+    }
 
     oracle_shape full = *sh;
     int32_t max_pages = 0;
@@ -361,9 +418,21 @@ void oracle_step(const oracle_shape *sh, const float *q_t, const float *q_prev, 
     full.union_cap = max_pages;
     int32_t *uidx = (int32_t *)malloc(sizeof(int32_t) * (size_t)((int64_t)sh->n_seq * Hk * max_pages + 1));
     int32_t *ucnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)(sh->n_seq * Hk));
-    oracle_select_pages(&full, q_t, kmin, kmax, kv_off, prefix_len, active, page_sel, uidx, ucnt,
+    const int64_t k = sh->budget_tokens / sh->page_size;
+    int32_t *psel = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nsh * A * k + 1));
+    oracle_select_pages(&full, q_t, kmin, kmax, kv_off, prefix_len, active, psel, uidx, ucnt,
                         NULL, 0);
+    if (page_sel) memcpy(page_sel, psel, sizeof(int32_t) * (size_t)(nsh * A * k));
 
+    /* the statistics this step merges: the cache itself, or (NO_WRITEBACK) a copy */
+    double *op_use = op_cache, *lp_use = lp_cache;
+    if (sh->flags & ORACLE_NO_WRITEBACK) {
+        op_use = (double *)malloc(sizeof(double) * (size_t)(nsh * B * d));
+        lp_use = (double *)malloc(sizeof(double) * (size_t)(nsh * B));
+        memcpy(op_use, op_cache, sizeof(double) * (size_t)(nsh * B * d));
+        memcpy(lp_use, lp_cache, sizeof(double) * (size_t)(nsh * B));
+    }
+    int32_t *own = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k + 1));
     double *o = (double *)malloc(sizeof(double) * (size_t)d);
     for (int s = 0; s < sh->n_seq; ++s)
         for (int h = 0; h < H; ++h) {
@@ -372,14 +441,32 @@ void oracle_step(const oracle_shape *sh, const float *q_t, const float *q_prev, 
                 const int t = active[((int64_t)s * H + h) * A + a];
                 const float *q = q_t + (((int64_t)s * B + t) * H + h) * d;
                 double lse;
-                prefix_attend(sh, s, g, q, k_cache, v_cache, kv_off, prefix_len,
-                              uidx + ((int64_t)s * Hk + g) * max_pages, ucnt[s * Hk + g], o, &lse);
+                if (sh->flags & ORACLE_ROW_MASK) {
+                    /* the row's own pages (page_sel lists them ascending, -1 past the end) */
+                    int64_t n_own = 0;
+                    for (int64_t e = 0; e < k; ++e) {
+                        const int32_t pg = psel[(((int64_t)s * H + h) * A + a) * k + e];
+                        if (pg >= 0) own[n_own++] = pg;
+                    }
+                    prefix_attend(sh, s, g, q, k_cache, v_cache, kv_off, prefix_len, own, n_own,
+                                  o, &lse);
+                } else {
+                    prefix_attend(sh, s, g, q, k_cache, v_cache, kv_off, prefix_len,
+                                  uidx + ((int64_t)s * Hk + g) * max_pages, ucnt[s * Hk + g], o,
+                                  &lse);
+                }
                 const int64_t row = ((int64_t)s * H + h) * B + t;
-                memcpy(op_cache + row * d, o, sizeof(double) * (size_t)d);
-                lp_cache[row] = lse;
+                memcpy(op_use + row * d, o, sizeof(double) * (size_t)d);
+                lp_use[row] = lse;
             }
         }
-    suffix_and_merge(sh, q_t, k_blk, v_blk, op_cache, lp_cache, out);
+    suffix_and_merge(sh, q_t, k_blk, v_blk, op_use, lp_use, out);
+    if (op_use != op_cache) {
+        free(op_use);
+        free(lp_use);
+    }
+    free(own);
+    free(psel);
 
     if (locality) memcpy(locality, score, sizeof(float) * (size_t)(nsh * B));
     if (active_out) memcpy(active_out, active, sizeof(int32_t) * (size_t)(nsh * A));

@@ -59,6 +59,7 @@ class Config:
     active_sigma: float = 0.5
     stable_sigma: float = 1e-3
     n_drift: Optional[int] = None   # drifting tokens per step (default: n_active)
+    flags: int = 0                  # reading variants (row mask, shared active set, no write-back)
 
     @property
     def group(self) -> int:
@@ -264,8 +265,8 @@ def trace_128k(layer: int = 0) -> Config:
 
 def small_case(cfg_id: int, *, n_seq=1, block=16, n_qhead=4, n_kvhead=1, head_dim=64,
                page_size=16, budget=64, n_active=4, dtype="f32", prefix_lens=(1024,),
-               n_steps=2, needles=False, n_drift=None) -> Config:
+               n_steps=2, needles=False, n_drift=None, flags=0) -> Config:
     """A free-form small workload for sweeps over shapes and edge cases."""
     return Config(f"small_{cfg_id}", 100 + cfg_id, n_seq, block, n_qhead, n_kvhead, head_dim,
                   page_size, budget, n_active, dtype, tuple(prefix_lens), n_steps,
-                  needles=needles, n_drift=n_drift)
+                  needles=needles, n_drift=n_drift, flags=flags)

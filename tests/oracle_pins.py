@@ -409,11 +409,93 @@ def pin_naive_sparse_per_query(lib):
             assert abs(orc.lp[0, h, t] - lse) < 1e-9
 
 
+# ---------------------------------------------------------------------------
+# reading variants (flags)
+
+ROW_MASK, SHARED_ACTIVE, NO_WRITEBACK = 1, 2, 4
+
+
+def pin_row_mask_attends_own_pages(lib):
+    """ROW_MASK: each active row's (o_p, L_p) is attention over the tokens of the
+    pages it selected itself (torch float64), and some row's pages differ from
+    its KV head's union (so the variant is exercised)."""
+    cfg = W.small_case(80, n_seq=2, n_qhead=4, n_kvhead=2, head_dim=32, budget=32, n_active=2,
+                       dtype="bf16", prefix_lens=(300, 77), n_steps=2, flags=ROW_MASK)
+    lay = W.make_layer(cfg)
+    orc = new_oracle(lib, lay)
+    orc.dense_first_step(lay.q[0], lay.k_blk[0], lay.v_blk[0])
+    res = orc.step(lay.q[1], lay.q[0], lay.k_blk[1], lay.v_blk[1])
+    scale = 1 / math.sqrt(cfg.head_dim)
+    narrower = 0
+    for s in range(cfg.n_seq):
+        for h in range(cfg.n_qhead):
+            g = h // cfg.group
+            for a, t in enumerate(res["active"][s, h].tolist()):
+                own = [p for p in res["page_sel"][s, h, a].tolist() if p >= 0]
+                narrower += len(own) < int(res["union_cnt"][s, g])
+                keys, vals = union_tokens(lay, s, g, own)
+                o, lse = sdpa64(lay.q[1][s, t, h], keys, vals, scale)
+                close(orc.op[s, h, t], o, 1e-9, 1e-12, "row-mask o_p")
+                assert abs(orc.lp[s, h, t] - lse) < 1e-9, (s, h, t)
+    assert narrower > 0
+
+
+def pin_shared_active_set_constructed(lib):
+    """SHARED_ACTIVE: one set per sequence from the head-summed locality.  Queries
+    are built so that only dimension 0 changes, by hand-chosen amounts: token 3
+    by 1 in all four heads, token 7 by 1.5 in head 0, token 9 by 1.9 in head 1,
+    token 12 by 1.2 in heads 0 and 1.  Summed over heads: 4, 2.25, 3.61, 2.88
+    (over d), so |A| = 2 keeps tokens 3 and 9 in every head, while head 0 alone
+    would keep 7 and 12; |A| = 1 keeps token 3 (a maximum over heads, or a sum
+    missing any one head, would keep token 9)."""
+    cfg = W.small_case(81, n_qhead=4, n_kvhead=2, head_dim=32, budget=32, n_active=2,
+                       dtype="f32", prefix_lens=(96,), n_steps=2)
+    lay = W.make_layer(cfg)
+    q_prev = lay.q[0].copy()
+    q_prev[..., 0] = 0.0
+    q_t = q_prev.copy()
+    for t, h, m in [(3, 0, 1.0), (3, 1, 1.0), (3, 2, 1.0), (3, 3, 1.0), (7, 0, 1.5),
+                    (9, 1, 1.9), (12, 0, 1.2), (12, 1, 1.2)]:
+        q_t[0, t, h, 0] = np.float32(m)
+    for flags, n_act, want in [(SHARED_ACTIVE, 2, [[3, 9]] * 4), (SHARED_ACTIVE, 1, [[3]] * 4),
+                               (0, 2, [[7, 12], [9, 12], [0, 3], [0, 3]])]:
+        c2 = cfg.replace(flags=flags, n_active=n_act)
+        orc = Oracle(c2, lay.kv_off, lay.prefix_len, lay.kv_tokens, lay.k_cache, lay.v_cache,
+                     lib=lib)
+        orc.dense_first_step(q_prev, lay.k_blk[0], lay.v_blk[0])
+        res = orc.step(q_t, q_prev, lay.k_blk[1], lay.v_blk[1])
+        assert res["active"][0].tolist() == want, (flags, res["active"][0].tolist())
+
+
+def pin_no_writeback_keeps_cache(lib):
+    """NO_WRITEBACK: the step leaves the (o_p, L_p) cache bit for bit as the dense
+    step left it, and its output equals the plain reading's (the fresh
+    statistics of the active rows serve that step either way)."""
+    cfg = W.small_case(82, n_seq=2, n_qhead=4, n_kvhead=2, head_dim=32, budget=32, n_active=3,
+                       dtype="bf16", prefix_lens=(200, 48), n_steps=2)
+    lay = W.make_layer(cfg)
+    outs = []
+    for flags in (NO_WRITEBACK, 0):
+        orc = new_oracle(lib, lay) if flags == 0 else Oracle(
+            cfg.replace(flags=flags), lay.kv_off, lay.prefix_len, lay.kv_tokens, lay.k_cache,
+            lay.v_cache, lib=lib)
+        orc.dense_first_step(lay.q[0], lay.k_blk[0], lay.v_blk[0])
+        op0, lp0 = orc.op.copy(), orc.lp.copy()
+        res = orc.step(lay.q[1], lay.q[0], lay.k_blk[1], lay.v_blk[1])
+        if flags:
+            assert np.array_equal(orc.op, op0) and np.array_equal(orc.lp, lp0)
+        else:
+            assert not np.array_equal(orc.lp, lp0)
+        outs.append(res["out"])
+    assert np.array_equal(outs[0], outs[1])
+
+
 ALL_PINS = [
     pin_page_meta, pin_locality_value, pin_locality_planted_drift, pin_active_set_order_and_ties,
     pin_page_bound_is_box_maximum, pin_topk_and_union, pin_needles_rank_high,
     pin_sparse_prefix_equals_sdpa, pin_dense_first_step_equals_attention,
     pin_dense_row_equals_attention,
     pin_all_active_full_budget_is_dense, pin_stable_reuse_and_merge, pin_mixed_step_rows,
-    pin_naive_sparse_per_query,
+    pin_naive_sparse_per_query, pin_row_mask_attends_own_pages, pin_shared_active_set_constructed,
+    pin_no_writeback_keeps_cache,
 ]

@@ -42,13 +42,19 @@ MUTANTS = [
     ("suffix_kv_head", "const int g = h / G;\n            for (int u = 0;",
      "const int g = h % Hk;\n            for (int u = 0;", None),
     ("dense_kv_head", "prefix_attend(sh, s, h / G,", "prefix_attend(sh, s, h % Hk,", None),
-    ("stable_rows_zeroed", "    suffix_and_merge(sh, q_t, k_blk, v_blk, op_cache, lp_cache, out);\n\n"
-     "    if (locality)",
+    ("stable_rows_zeroed", "    suffix_and_merge(sh, q_t, k_blk, v_blk, op_use, lp_use, out);\n",
      "    for (int s2 = 0; s2 < sh->n_seq * H * B; ++s2) { int keep = 0;\n"
      "        for (int a2 = 0; a2 < A; ++a2) if (active[(s2 / B) * A + a2] == s2 % B) keep = 1;\n"
-     "        if (!keep) { lp_cache[s2] = -INFINITY; } }\n"
-     "    suffix_and_merge(sh, q_t, k_blk, v_blk, op_cache, lp_cache, out);\n\n    if (locality)",
+     "        if (!keep) { lp_use[s2] = -INFINITY; } }\n"
+     "    suffix_and_merge(sh, q_t, k_blk, v_blk, op_use, lp_use, out);\n",
      None),
+    ("shared_dropped_head", "for (int h = 0; h < H; ++h) acc = acc + score[",
+     "for (int h = 1; h < H; ++h) acc = acc + score[", None),
+    ("shared_max_not_sum", "acc = acc + score[((int64_t)s * H + h) * B + t];",
+     "acc = fmaxf(acc, score[((int64_t)s * H + h) * B + t]);", None),
+    ("shared_set_ignored", "if (sh->flags & ORACLE_SHARED_ACTIVE) {", "if (0) {", None),
+    ("row_mask_ignored", "if (sh->flags & ORACLE_ROW_MASK) {", "if (0) {", None),
+    ("no_writeback_ignored", "if (sh->flags & ORACLE_NO_WRITEBACK) {", "if (0) {", None),
 ]
 
 
