@@ -106,8 +106,32 @@ typedef struct losa_shape {
     int32_t dtype;          /* losa_dtype of q, k, v and out */
     int64_t kv_tokens;      /* T: tokens per KV head in k_cache/v_cache, a multiple of page_size */
     float softmax_scale;    /* > 0, or 0 for 1/sqrt(head_dim) */
-    uint32_t flags;         /* must be 0 */
+    uint32_t flags;         /* 0 (the plain reading) or an OR of the losa_flags below */
 } losa_shape;
+
+/*
+ * Readings of three points the pages leave open; 0 selects the plain reading
+ * (every active row attends the whole union of its KV head; one active set per
+ * query head; the sparse statistics are written back to the cache).
+ *   LOSA_FLAG_ROW_MASK: each active row attends only the pages it selected
+ *     itself; the union still decides what is loaded (fr summary, "Réduction de
+ *     l'Union KV").  Needs at most 64 stacked rows per KV head (G * n_active),
+ *     else LOSA_ERR_UNSUPPORTED.
+ *   LOSA_FLAG_SHARED_ACTIVE: one active set per sequence, shared by all query
+ *     heads: a token's locality is the sum over query heads, in ascending head
+ *     order, of its per-head mean squared change (an fp32 chain); the n_active
+ *     largest sums are active, equal sums to the lower token.
+ *   LOSA_FLAG_NO_WRITEBACK: a sparse step does not store the active tokens' new
+ *     (o_p, L_p); they serve that step's output, and the caches keep what the
+ *     block's dense first step wrote (agifrontier tutorial, workflow section:
+ *     statistics are reused from the last full computation).
+ * losa_dense_first_step ignores the flags.
+ */
+typedef enum losa_flags {
+    LOSA_FLAG_ROW_MASK = 1,
+    LOSA_FLAG_SHARED_ACTIVE = 2,
+    LOSA_FLAG_NO_WRITEBACK = 4
+} losa_flags;
 
 /* Number of events in losa_debug.stage_events. */
 #define LOSA_STAGE_EVENTS 6

@@ -273,8 +273,10 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
             op = 0.0f;
             lp2 = -__builtin_huge_valf();
         }
-        op_cache[crow * DIM + x] = op;
-        if (x == 0) lp_cache[crow] = lp2 * kLn2;
+        if (!(D.flags & LOSA_FLAG_NO_WRITEBACK)) {  // the caches keep the dense statistics
+            op_cache[crow * DIM + x] = op;
+            if (x == 0) lp_cache[crow] = lp2 * kLn2;
+        }
     } else {
         op = opc;
         lp2 = lpc * kLog2e;

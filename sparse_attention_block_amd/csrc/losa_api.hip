@@ -31,11 +31,18 @@ int check_shape(const losa_shape *sh) {
     if (sh->kv_tokens < sh->page_size || sh->kv_tokens % sh->page_size) return LOSA_ERR_INVALID_ARG;
     if (sh->max_prefix_len < 0 || sh->max_prefix_len > sh->kv_tokens) return LOSA_ERR_INVALID_ARG;
     if (!(sh->softmax_scale >= 0.0f) || isinf(sh->softmax_scale)) return LOSA_ERR_INVALID_ARG;
-    if (sh->flags != 0) return LOSA_ERR_INVALID_ARG;
+    if (sh->flags & ~(uint32_t)(LOSA_FLAG_ROW_MASK | LOSA_FLAG_SHARED_ACTIVE | LOSA_FLAG_NO_WRITEBACK))
+        return LOSA_ERR_INVALID_ARG;
     if (sh->page_size != kPage) return LOSA_ERR_UNSUPPORTED;
     if (sh->head_dim != 64 && sh->head_dim != 128) return LOSA_ERR_UNSUPPORTED;
     if (sh->block > 64) return LOSA_ERR_UNSUPPORTED;
     if ((int64_t)(sh->n_qhead / sh->n_kvhead) * sh->block > kMaxRows) return LOSA_ERR_UNSUPPORTED;
+    if ((sh->flags & LOSA_FLAG_SHARED_ACTIVE) &&
+        ((int64_t)sh->n_qhead * sh->block > kMaxSharedScores))
+        return LOSA_ERR_UNSUPPORTED;
+    if ((sh->flags & LOSA_FLAG_ROW_MASK) &&
+        (int64_t)(sh->n_qhead / sh->n_kvhead) * sh->n_active > kMaxMaskRows)
+        return LOSA_ERR_UNSUPPORTED;
     if ((sh->max_prefix_len + kPage - 1) / kPage > kMaxPagesSupported) return LOSA_ERR_UNSUPPORTED;
     if (sh->kv_tokens / kPage > (int64_t)1 << 30) return LOSA_ERR_UNSUPPORTED;
     return LOSA_OK;
@@ -57,6 +64,7 @@ Dims make_dims(const losa_shape *sh) {
     D.A = sh->n_active;
     D.k = sh->budget_tokens / kPage;
     D.bf16 = sh->dtype == LOSA_BF16;
+    D.flags = static_cast<int>(sh->flags);
     D.max_pages = (sh->max_prefix_len + kPage - 1) / kPage;
     D.hb_stride = (std::max(D.max_pages, 1) + 3) / 4 * 4;
     D.T = sh->kv_tokens;
@@ -205,7 +213,8 @@ int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *
     if (!kv_off || !prefix_len || !lp_cache || !aligned(kv_off, 4) || !aligned(prefix_len, 4) ||
         !aligned(lp_cache, 4))
         return LOSA_ERR_INVALID_ARG;
-    const Dims D = make_dims(shape);
+    Dims D = make_dims(shape);
+    D.flags = 0;  // the dense first step has no reading variants
     Work W;
     const size_t need = carve(D, static_cast<char *>(workspace), &W);
     if (workspace_bytes < need) return LOSA_ERR_WORKSPACE;
@@ -265,6 +274,8 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
             e = launch_score_prep(D, q_t, q_prev, page_meta, kv_off, prefix_len, W, dbg.locality,
                                   dbg.active, dbg.union_cnt, s);
     } else {
+        if ((D.flags & LOSA_FLAG_SHARED_ACTIVE) && e == hipSuccess)
+            e = launch_shared_active(D, q_t, q_prev, W, dbg.locality, dbg.active, s);
         if (e == hipSuccess)
             e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active, dbg.union_cnt,
                                s);

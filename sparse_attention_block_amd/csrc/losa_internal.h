@@ -20,6 +20,8 @@ constexpr int kDenseTargetGroups = 512;   // workgroups a dense pass should have
 constexpr int kSparseTargetGroups = 1024; // workgroups a sparse pass may keep at most (by capacity)
 constexpr int kMaxRows = 256;     // G * B stacked rows per KV head at most
 constexpr int kMaxK = 64;         // pages per row the exact selection keeps in one register
+constexpr int kMaxMaskRows = 64;  // stacked rows per KV head with per-row page masks (bits)
+constexpr int kMaxSharedScores = 8192;  // query heads x block tokens for a shared active set
 
 // Relative error bound between the MFMA-accumulated page bound and the exact
 // fp32 chain (both sides together), and an absolute floor for flushed
@@ -31,6 +33,7 @@ constexpr float kBoundAbs = 1.0e-30f;
 struct Dims {
     int S, B, Hq, Hk, G, d, A, k;     // k = budget pages per row
     int bf16;                         // 1: bf16 storage, 0: fp32
+    int flags;                        // losa_flags of the shape
     int max_pages;                    // pages of the longest prefix
     int hb_stride;                    // row stride of the upper-bound buffer (max_pages, 4-aligned)
     int64_t T;                        // kv_tokens
@@ -66,6 +69,8 @@ struct Work {
 hipError_t launch_page_meta(const Dims &D, const void *k_cache, const int32_t *kv_off,
                             const int32_t *prefix_len, const int32_t *first_token,
                             int max_new_tokens, void *meta, hipStream_t st);
+hipError_t launch_shared_active(const Dims &D, const void *q_t, const void *q_prev, const Work &W,
+                                float *dbg_loc, int32_t *dbg_act, hipStream_t st);
 hipError_t launch_prepare(const Dims &D, bool dense, const void *q_t, const void *q_prev,
                           const Work &W, float *dbg_locality, int32_t *dbg_active,
                           int32_t *dbg_union_cnt, hipStream_t st);

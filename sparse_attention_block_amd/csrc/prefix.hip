@@ -86,14 +86,16 @@ constexpr float kLazyRescale = 8.0f;
 // output is rescaled only when some row's maximum passed its reference by more
 // than kLazyRescale (the factor is exactly 1 for the other rows).  Several pages at once keep independent MFMA chains
 // in flight and share one max reduction.
-template <int DIM, int RTW, int NP>
+template <int DIM, int RTW, int NP, bool MASK = false>
 __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
                                              const uint32_t (&vw)[NP][4][DIM / 32],
                                              const int (&valid)[NP],
                                              const uint4 (&qop)[RTW][DIM / 32],
                                              const bool (&rt_ok)[RTW], float scale_log2,
                                              float4_t (&oacc)[RTW][DIM / 16], float (&m_run)[RTW],
-                                             float (&l_run)[RTW], int lg) {
+                                             float (&l_run)[RTW], int lg,
+                                             const uint64_t (&rmask)[NP] = {},
+                                             const int (&row0)[RTW] = {}) {
     constexpr int KSTEPS = DIM / 32, DPL = DIM / 16;
     bool full[NP];
 #pragma unroll
@@ -135,6 +137,13 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
                 for (int j = 0; j < 4; ++j)
                     if (4 * lg + j >= valid[n]) sv[n][j] = -__builtin_huge_valf();
             }
+            if constexpr (MASK) {  // rows that did not select the page attend none of it
+                const int l16 = __lane_id() & 15;
+                if (!((rmask[n] >> (row0[i] + l16)) & 1ull)) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[n][j] = -__builtin_huge_valf();
+                }
+            }
         }
         float mp = -__builtin_huge_valf();
 #pragma unroll
@@ -147,13 +156,15 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
         const float mx = fmaxf(m_run[i], mp);
         if (__ballot(mx > m_run[i] + kLazyRescale) != 0ull) {  // uniform branch
             const float mn = mx > m_run[i] + kLazyRescale ? mx : m_run[i];
-            const float alpha = __builtin_amdgcn_exp2f(m_run[i] - mn);
+            // (with masks a row's reference may still be -inf: it keeps factor 1)
+            const float alpha = MASK && mn == m_run[i] ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - mn);
 #pragma unroll
             for (int e = 0; e < DPL; ++e) oacc[i][e] *= alpha;
             l_run[i] *= alpha;
             m_run[i] = mn;
         }
-        const float mn = m_run[i];
+        // (with masks a row may have seen no score yet: its weights are zero)
+        const float mn = MASK && m_run[i] == -__builtin_huge_valf() ? 0.0f : m_run[i];
 #pragma unroll
         for (int n = 0; n < NP; ++n) {
             const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][0] - mn)),
@@ -177,10 +188,11 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
 // there too.  Returns the union size.  Called by all 256 threads.
 __device__ int union_slice(const int32_t *__restrict__ psel, int n_sel, int pages, bool all_pages,
                            int first, int cp, uint32_t *bm, int *wsum, int *pg_out,
-                           int32_t *dbg_idx, int dbg_cap) {
+                           int32_t *dbg_idx, int dbg_cap, int k = 0, uint64_t *rmask = nullptr) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (all_pages) {
         if (tid < cp) pg_out[tid] = first + tid;
+        if (rmask && tid < cp) rmask[tid] = ~0ull;  // every row selected every page
         if (dbg_idx)
             for (int i = tid; i < min(pages, dbg_cap); i += 256) dbg_idx[i] = i;
         __syncthreads();
@@ -221,10 +233,29 @@ __device__ int union_slice(const int32_t *__restrict__ psel, int n_sel, int page
         }
     }
     __syncthreads();
+    if (rmask) {
+        // bit r of rmask[x]: row r (entries r*k .. of psel) selected this chunk's page x
+        const int n_here = max(0, min(cp, total - first));
+        for (int x = tid; x < cp; x += 256) rmask[x] = 0ull;
+        __syncthreads();
+        for (int e = tid; e < n_sel; e += 256) {
+            const int pg = psel[e];
+            if (pg < 0) continue;
+            int lo = 0, hi = n_here;  // the chunk's pages ascend
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (pg_out[mid] < pg) lo = mid + 1;
+                else hi = mid;
+            }
+            if (lo < n_here && pg_out[lo] == pg)
+                atomicOr(reinterpret_cast<unsigned long long *>(&rmask[lo]), 1ull << (e / k));
+        }
+        __syncthreads();
+    }
     return total;
 }
 
-template <int DIM, int RTW, bool DENSE>
+template <int DIM, int RTW, bool DENSE, bool MASK>
 __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
                                                      const uint16_t *__restrict__ kc,
                                                      const uint16_t *__restrict__ vc,
@@ -238,6 +269,7 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     constexpr int RAW = 4 * 16 * DIM > kMaxBitmapWords ? 4 * 16 * DIM : kMaxBitmapWords;
     __shared__ float s_raw[RAW];  // the union bitmap first, then the page groups' outputs
     __shared__ int s_wsum[4], s_pg[kMaxSparseChunk];
+    __shared__ uint64_t s_rmask[MASK ? kMaxSparseChunk : 1];  // rows that selected each page
     auto s_acc = reinterpret_cast<float (*)[16][DIM]>(s_raw);
     __shared__ float s_ml[4][16][2];
 
@@ -285,7 +317,7 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
         n_items = union_slice(W.psel + (size_t)sgi * R1 * D.k, D.R * D.k, sg.pages, D.k >= sg.pages,
                               first, cp, reinterpret_cast<uint32_t *>(s_raw), s_wsum, s_pg,
                               chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
-                              dbg_cap);
+                              dbg_cap, D.k, MASK ? s_rmask : nullptr);
         if (chunk == 0 && tid == 0) {
             W.union_cnt[sgi] = min(n_items, D.union_cap);
             if (dbg_ucnt) dbg_ucnt[sgi] = n_items;
@@ -294,6 +326,9 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     }
     if (first >= n_items) return;
     const int n_here = min(cp, n_items - first);
+    int row0[RTW];  // first row of each of the wave's row tiles
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) row0[i] = (wr + i * WPG) * 16;
 
     float4_t oacc[RTW][DPL];
     float m_run[RTW], l_run[RTW];
@@ -323,9 +358,11 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
 #pragma unroll
             for (int i = 0; i < RTW; ++i) rt_ok[i] = wr + i * WPG < n_rt;
             const int vld[1] = {cur.valid};
-            attend_pages<DIM, RTW, 1>(reinterpret_cast<const uint4(&)[1][KSTEPS]>(cur.k),
-                                      reinterpret_cast<const uint32_t(&)[1][4][DPL / 2]>(cur.v), vld,
-                                      qop, rt_ok, D.scale_log2, oacc, m_run, l_run, lg);
+            const uint64_t rm[1] = {MASK ? s_rmask[it] : 0ull};
+            attend_pages<DIM, RTW, 1, MASK>(reinterpret_cast<const uint4(&)[1][KSTEPS]>(cur.k),
+                                            reinterpret_cast<const uint32_t(&)[1][4][DPL / 2]>(cur.v),
+                                            vld, qop, rt_ok, D.scale_log2, oacc, m_run, l_run, lg,
+                                            rm, row0);
             cur = nxt;
         }
     }
@@ -383,10 +420,12 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
             if (r >= rows) continue;
             float mx = -__builtin_huge_valf();
             for (int q = 0; q < n_pg; ++q) mx = fmaxf(mx, s_ml[q * WPG + rtile][rr][0]);
+            // (with masks a row may have no page in any group: zero weights)
+            const float mref = MASK && mx == -__builtin_huge_valf() ? 0.0f : mx;
             float lsum = 0.0f, a = 0.0f;
             for (int q = 0; q < n_pg; ++q) {
                 const int wq = q * WPG + rtile;
-                const float wgt = __builtin_amdgcn_exp2f(s_ml[wq][rr][0] - mx);
+                const float wgt = __builtin_amdgcn_exp2f(s_ml[wq][rr][0] - mref);
                 lsum += wgt * s_ml[wq][rr][1];
                 a += wgt * s_acc[wq][rr][dim];
             }
@@ -655,7 +694,7 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     }
 }
 
-template <int DIM, bool DENSE>
+template <int DIM, bool DENSE, bool MASK>
 __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restrict__ kc,
                                                     const float *__restrict__ vc,
                                                     const int32_t *__restrict__ kv_off,
@@ -665,6 +704,7 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restr
     constexpr int DPT = DIM / 16;
     __shared__ uint32_t s_bm[kMaxBitmapWords];
     __shared__ int s_wsum[4], s_pg[kMaxSparseChunk];
+    __shared__ uint64_t s_rmask[MASK ? kMaxSparseChunk : 1];  // rows that selected each page
     __shared__ float q_s[16][DIM];
     __shared__ float k_s[16][DIM + 1];
     __shared__ float v_s[16][DIM];
@@ -684,7 +724,7 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restr
         n_items = union_slice(W.psel + (size_t)sgi * R1 * D.k, D.R * D.k, sg.pages, D.k >= sg.pages,
                               first, cp, s_bm, s_wsum, s_pg,
                               chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
-                              dbg_cap);
+                              dbg_cap, D.k, MASK ? s_rmask : nullptr);
         if (chunk == 0 && threadIdx.x == 0) {
             W.union_cnt[sgi] = min(n_items, D.union_cap);
             if (dbg_ucnt) dbg_ucnt[sgi] = n_items;
@@ -718,15 +758,19 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restr
             __syncthreads();
             float dot = 0.0f;
             for (int x = 0; x < DIM; ++x) dot = fmaf(q_s[r16][x], k_s[j16][x], dot);
-            s_s[r16][j16] = j16 < valid ? dot * D.scale_log2 : -__builtin_huge_valf();
+            bool keep = j16 < valid;
+            if constexpr (MASK) keep = keep && ((s_rmask[it] >> (rt * 16 + r16)) & 1ull);
+            s_s[r16][j16] = keep ? dot * D.scale_log2 : -__builtin_huge_valf();
             __syncthreads();
             float mp = -__builtin_huge_valf();
             for (int u = 0; u < 16; ++u) mp = fmaxf(mp, s_s[r16][u]);
             const float mn = fmaxf(m_run, mp);
-            const float alpha = exp2f(m_run - mn);
+            // (with masks a row may have seen no score yet: its weights are zero)
+            const float mref = MASK && mn == -__builtin_huge_valf() ? 0.0f : mn;
+            const float alpha = exp2f(m_run - mref);
             float pu[16], ls = 0.0f;
             for (int u = 0; u < 16; ++u) {
-                pu[u] = exp2f(s_s[r16][u] - mn);
+                pu[u] = exp2f(s_s[r16][u] - mref);
                 ls += pu[u];
             }
 #pragma unroll
@@ -762,14 +806,16 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const v
         const int rows = dense ? D.Rd : D.R;
         const int n_rt = (rows + 15) / 16;
         const int rtw = n_rt <= 4 ? 1 : (n_rt <= 8 ? 2 : 4);
-#define LAUNCH_P(DIMV, RTWV, DN)                                                                 \
-    hipLaunchKernelGGL((k_prefix_bf16<DIMV, RTWV, DN>), grid, dim3(256), 0, st, D, k, v, kv_off, \
+#define LAUNCH_P(DIMV, RTWV, DN, MK)                                                              \
+    hipLaunchKernelGGL((k_prefix_bf16<DIMV, RTWV, DN, MK>), grid, dim3(256), 0, st, D, k, v, kv_off, \
                        prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap)
-#define PICK_P(DIMV, DN)                         \
-    do {                                         \
-        if (rtw == 1) LAUNCH_P(DIMV, 1, DN);     \
-        else if (rtw == 2) LAUNCH_P(DIMV, 2, DN); \
-        else LAUNCH_P(DIMV, 4, DN);              \
+        // row masks: at most 64 rows, so one row tile per wave
+#define PICK_P(DIMV, DN)                                     \
+    do {                                                     \
+        if (D.flags & LOSA_FLAG_ROW_MASK) LAUNCH_P(DIMV, 1, DN, true); \
+        else if (rtw == 1) LAUNCH_P(DIMV, 1, DN, false);     \
+        else if (rtw == 2) LAUNCH_P(DIMV, 2, DN, false);     \
+        else LAUNCH_P(DIMV, 4, DN, false);                   \
     } while (0)
 #define LAUNCH_D(DIMV, RTWV, NWV)                                                                 \
     hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV, NWV>), grid, dim3(64 * NWV), 0, st, D, k, v, \
@@ -800,15 +846,18 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const v
     } else {
         auto *k = static_cast<const float *>(k_cache);
         auto *v = static_cast<const float *>(v_cache);
-#define LAUNCH_F(DIMV, DN)                                                                      \
-    hipLaunchKernelGGL((k_prefix_f32<DIMV, DN>), grid, dim3(256), 0, st, D, k, v, kv_off,       \
+#define LAUNCH_F(DIMV, DN, MK)                                                                  \
+    hipLaunchKernelGGL((k_prefix_f32<DIMV, DN, MK>), grid, dim3(256), 0, st, D, k, v, kv_off,   \
                        prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap)
+        const bool mask = !dense && (D.flags & LOSA_FLAG_ROW_MASK);
         if (D.d == 128) {
-            if (dense) LAUNCH_F(128, true);
-            else LAUNCH_F(128, false);
+            if (dense) LAUNCH_F(128, true, false);
+            else if (mask) LAUNCH_F(128, false, true);
+            else LAUNCH_F(128, false, false);
         } else {
-            if (dense) LAUNCH_F(64, true);
-            else LAUNCH_F(64, false);
+            if (dense) LAUNCH_F(64, true, false);
+            else if (mask) LAUNCH_F(64, false, true);
+            else LAUNCH_F(64, false, false);
         }
 #undef LAUNCH_F
     }

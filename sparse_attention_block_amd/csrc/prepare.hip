@@ -77,6 +77,52 @@ __device__ __forceinline__ float locality_chain(const T *a, const T *b) {
     return acc;
 }
 
+// Shared active set (LOSA_FLAG_SHARED_ACTIVE), one workgroup per sequence:
+// every (query head, token) locality chain as above, divided by d; per token
+// the sum over query heads in ascending order (an fp32 chain); the |A| largest
+// sums are active, equal sums going to the lower token; the same ascending list
+// is written for every head (the per-layer reading of the locality score).
+template <typename T, int DIM>
+__global__ __launch_bounds__(256) void k_shared_active(Dims D, const T *__restrict__ q_t,
+                                                       const T *__restrict__ q_prev, Work W,
+                                                       float *__restrict__ dbg_loc,
+                                                       int32_t *__restrict__ dbg_act) {
+    __shared__ float sc[kMaxSharedScores];
+    __shared__ float tot[64];
+    __shared__ int sel[64];
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const int B = D.B, A = D.A, Hq = D.Hq;
+    for (int i = tid; i < Hq * B; i += blockDim.x) {
+        const int h = i / B, t = i % B;
+        const size_t off = ((size_t)(s * B + t) * Hq + h) * DIM;
+        const float e = locality_chain<T, DIM>(q_t + off, q_prev + off) / static_cast<float>(DIM);
+        sc[i] = e;
+        if (dbg_loc) dbg_loc[((size_t)s * Hq + h) * B + t] = e;
+    }
+    __syncthreads();
+    if (tid < B) {
+        float acc = 0.0f;
+        for (int h = 0; h < Hq; ++h) acc = acc + sc[h * B + tid];
+        tot[tid] = acc;
+    }
+    __syncthreads();
+    if (tid < B) {
+        const float et = tot[tid];
+        int rank = 0;
+        for (int u = 0; u < B; ++u) rank += (tot[u] > et) || (tot[u] == et && u < tid);
+        sel[tid] = rank < A;
+    }
+    __syncthreads();
+    if (tid < B && sel[tid]) {
+        int pos = 0;
+        for (int u = 0; u < tid; ++u) pos += sel[u];
+        for (int h = 0; h < Hq; ++h) {
+            W.active[((size_t)s * Hq + h) * A + pos] = tid;
+            if (dbg_act) dbg_act[((size_t)s * Hq + h) * A + pos] = tid;
+        }
+    }
+}
+
 template <typename T, int DIM, bool DENSE>
 __global__ __launch_bounds__(256) void k_prepare(Dims D, const T *__restrict__ q_t,
                                                  const T *__restrict__ q_prev, Work W,
@@ -98,7 +144,13 @@ __global__ __launch_bounds__(256) void k_prepare(Dims D, const T *__restrict__ q
         if (dbg_ucnt) dbg_ucnt[sg] = 0;  // the sparse prefix kernel overwrites them when |A| > 0
     }
     int rows;
-    if (!dense) {
+    if (!dense && (D.flags & LOSA_FLAG_SHARED_ACTIVE)) {
+        // the active set shared by all heads, from k_shared_active
+        for (int i = threadIdx.x; i < G * A; i += blockDim.x)
+            act_s[i] = W.active[((size_t)s * Hq + g * G + i / A) * A + i % A];
+        __syncthreads();
+        rows = G * A;
+    } else if (!dense) {
         for (int i = threadIdx.x; i < G * B; i += blockDim.x) {
             const int j = i / B, t = i % B, h = g * G + j;
             const size_t off = ((size_t)(s * B + t) * Hq + h) * DIM;
@@ -220,6 +272,23 @@ __global__ __launch_bounds__(256) void k_prepare(Dims D, const T *__restrict__ q
             }
         }
     }
+}
+
+hipError_t launch_shared_active(const Dims &D, const void *q_t, const void *q_prev, const Work &W,
+                                float *dbg_loc, int32_t *dbg_act, hipStream_t st) {
+#define LAUNCH_A(TV, DIMV)                                                                    \
+    hipLaunchKernelGGL((k_shared_active<TV, DIMV>), dim3(D.S), dim3(256), 0, st, D,           \
+                       static_cast<const TV *>(q_t), static_cast<const TV *>(q_prev), W, dbg_loc, \
+                       dbg_act)
+    if (D.bf16) {
+        if (D.d == 128) LAUNCH_A(uint16_t, 128);
+        else LAUNCH_A(uint16_t, 64);
+    } else {
+        if (D.d == 128) LAUNCH_A(float, 128);
+        else LAUNCH_A(float, 64);
+    }
+#undef LAUNCH_A
+    return hipGetLastError();
 }
 
 hipError_t launch_prepare(const Dims &D, bool dense, const void *q_t, const void *q_prev,

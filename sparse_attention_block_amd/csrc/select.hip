@@ -687,7 +687,7 @@ size_t score_prep_lds_bytes(const Dims &D) {
 }
 
 bool score_prep_fits(const Dims &D) {
-    return D.bf16 && D.R > 0 && 2 * D.G * D.B * D.d / 8 <= kPrepVecs * 256 &&
+    return D.bf16 && D.R > 0 && !(D.flags & LOSA_FLAG_SHARED_ACTIVE) && 2 * D.G * D.B * D.d / 8 <= kPrepVecs * 256 &&
            score_prep_lds_bytes(D) <= 40 * 1024;
 }
 

@@ -23,7 +23,8 @@ def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 class LayerState:
     def __init__(self, *, n_seq, block, n_qhead, n_kvhead, head_dim, budget_tokens, n_active,
                  dtype, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_off, prefix_len,
-                 max_prefix_len: Optional[int] = None, softmax_scale=0.0, device="cuda"):
+                 max_prefix_len: Optional[int] = None, softmax_scale=0.0, flags=0,
+                 device="cuda"):
         self.device = device
         kv_off = torch.as_tensor(np.asarray(kv_off, np.int32)).to(device)
         prefix_len_t = torch.as_tensor(np.asarray(prefix_len, np.int32)).to(device)
@@ -32,7 +33,8 @@ class LayerState:
         self.shape = L.make_shape(n_seq=n_seq, block=block, n_qhead=n_qhead, n_kvhead=n_kvhead,
                                   head_dim=head_dim, budget_tokens=budget_tokens,
                                   n_active=n_active, max_prefix_len=max_prefix_len, dtype=dtype,
-                                  kv_tokens=k_cache.shape[1], softmax_scale=softmax_scale)
+                                  kv_tokens=k_cache.shape[1], softmax_scale=softmax_scale,
+                                  flags=flags)
         self.dtype = dtype
         self.k_cache, self.v_cache = k_cache, v_cache
         self.kv_off, self.prefix_len = kv_off, prefix_len_t
@@ -55,7 +57,8 @@ class LayerState:
                    n_active=c.n_active if n_active is None else n_active, dtype=c.dtype,
                    k_cache=to_device(lay.k_cache, c.dtype, device),
                    v_cache=to_device(lay.v_cache, c.dtype, device),
-                   kv_off=lay.kv_off, prefix_len=lay.prefix_len, device=device)
+                   kv_off=lay.kv_off, prefix_len=lay.prefix_len,
+                   flags=getattr(c, "flags", 0), device=device)
 
     def build_page_meta(self, stream=None):
         L.losa_build_page_meta(self.shape, self.k_cache, self.kv_off, self.prefix_len,

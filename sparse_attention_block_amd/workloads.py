@@ -263,10 +263,14 @@ def trace_128k(layer: int = 0) -> Config:
                   trace_layer_active(layer), "bf16", (131072,), 8, needles=True)
 
 
-def small_case(cfg_id: int, *, n_seq=1, block=16, n_qhead=4, n_kvhead=1, head_dim=64,
+def small_case(cfg_id: int, *, n_seq=None, block=16, n_qhead=4, n_kvhead=1, head_dim=64,
                page_size=16, budget=64, n_active=4, dtype="f32", prefix_lens=(1024,),
                n_steps=2, needles=False, n_drift=None, flags=0) -> Config:
-    """A free-form small workload for sweeps over shapes and edge cases."""
+    """A free-form small workload for sweeps over shapes and edge cases; one
+    sequence per prefix length."""
+    if n_seq is None:
+        n_seq = len(prefix_lens)
+    assert n_seq == len(prefix_lens), (n_seq, prefix_lens)
     return Config(f"small_{cfg_id}", 100 + cfg_id, n_seq, block, n_qhead, n_kvhead, head_dim,
                   page_size, budget, n_active, dtype, tuple(prefix_lens), n_steps,
                   needles=needles, n_drift=n_drift, flags=flags)

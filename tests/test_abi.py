@@ -66,7 +66,8 @@ BAD_SHAPES = [
     (dict(head_dim=96), L.LOSA_ERR_UNSUPPORTED),
     (dict(page_size=32, budget_tokens=64), L.LOSA_ERR_UNSUPPORTED),
     (dict(dtype=7), L.LOSA_ERR_INVALID_ARG),
-    (dict(flags=1), L.LOSA_ERR_INVALID_ARG),
+    (dict(flags=8), L.LOSA_ERR_INVALID_ARG),
+    (dict(flags=1, n_qhead=32, n_kvhead=1, n_active=4), L.LOSA_ERR_UNSUPPORTED),
     (dict(max_prefix_len=2048), L.LOSA_ERR_INVALID_ARG),
     (dict(softmax_scale=-1.0), L.LOSA_ERR_INVALID_ARG),
     (dict(kv_tokens=1000), L.LOSA_ERR_INVALID_ARG),
