@@ -146,8 +146,63 @@ def latency_floors(hip, stream, reps=200):
     return out
 
 
+def page_meta_times(hip, lay, kv, reps):
+    """Full metadata build of a layer vs the update after one committed block of
+    16 tokens (losa_update_page_meta), over the layer replicas, each captured as
+    one HIP graph so that host launch cost does not enter."""
+    import numpy as np
+    import torch
+
+    from sparse_attention_block_amd import binding as L
+    from sparse_attention_block_amd.layer import LayerState
+
+    c = lay.cfg
+    new_len = np.asarray(lay.prefix_len, np.int32)
+    old_len = np.maximum(new_len - c.block, 0).astype(np.int32)
+    states = [LayerState(n_seq=c.n_seq, block=c.block, n_qhead=c.n_qhead, n_kvhead=c.n_kvhead,
+                         head_dim=c.head_dim, budget_tokens=c.budget, n_active=c.n_active,
+                         dtype=c.dtype, k_cache=k, v_cache=v, kv_off=lay.kv_off,
+                         prefix_len=new_len) for k, v in kv]
+    first = torch.as_tensor(old_len).cuda()
+    gst = torch.cuda.Stream()
+    sid = gst.cuda_stream
+
+    def full():
+        for st in states:
+            L.losa_build_page_meta(st.shape, st.k_cache, st.kv_off, st.prefix_len, st.page_meta,
+                                   sid)
+
+    def update():
+        for st in states:
+            L.losa_update_page_meta(st.shape, st.k_cache, st.kv_off, st.prefix_len, first,
+                                    c.block, st.page_meta, sid)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        fn()
+        torch.cuda.synchronize()
+        g = hip.capture(sid, fn)
+        hip.launch(g, sid)
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, sid)
+        for _ in range(reps):
+            hip.launch(g, sid)
+        hip.record(e1, sid)
+        torch.cuda.synchronize()
+        return hip.ms(e0, e1) * 1e3 / (reps * len(states))
+
+    full_us = timed(full)
+    upd_us = timed(update)
+    k_bytes = c.n_kvhead * int(new_len.sum()) * c.head_dim * (2 if c.dtype == "bf16" else 4)
+    del states
+    torch.cuda.empty_cache()
+    return {"full_build_us": full_us, "full_build_gbps_on_keys": k_bytes / (full_us * 1e-6) / 1e9,
+            "commit_16_tokens_us": upd_us}
+
+
 def measure_case(hip, lay_kv, inputs_of, *, cfg, budget, active_of, dense_every_step, reps,
-                 union_layers=(0,)):
+                 union_layers=(0,), flags=0):
     """Time one case over the device KV replicas ``lay_kv`` = (layer, [(k, v), ...]).
 
     inputs_of(li) -> (q, k_blk, v_blk) device tensor lists per step for layer li.
@@ -167,7 +222,7 @@ def measure_case(hip, lay_kv, inputs_of, *, cfg, budget, active_of, dense_every_
         ls = LayerState(n_seq=cfg.n_seq, block=cfg.block, n_qhead=cfg.n_qhead,
                         n_kvhead=cfg.n_kvhead, head_dim=cfg.head_dim, budget_tokens=budget,
                         n_active=active_of(li), dtype=cfg.dtype, k_cache=k, v_cache=v,
-                        kv_off=lay.kv_off, prefix_len=lay.prefix_len)
+                        kv_off=lay.kv_off, prefix_len=lay.prefix_len, flags=flags)
         ls.build_page_meta()
         layers.append(ls)
     # union sizes over the block (from the library's debug outputs)
@@ -313,6 +368,13 @@ def sweep(args):
     res = measure_case(hip, kv, lambda i: inp4, cfg=base, budget=128, active_of=lambda i: 4,
                        dense_every_step=True, reps=args.steps)
     add_row("64K", "dense every step", base, 128, 4, SWEEP_LAYERS, res, True)
+    # the reading variants (losa_shape.flags) on the same inputs
+    for flags, label in ((1, "row mask"), (2, "shared active set"), (4, "no write-back")):
+        res = measure_case(hip, kv, lambda i: inp4, cfg=base, budget=128, active_of=lambda i: 4,
+                           dense_every_step=False, reps=args.steps, flags=flags)
+        add_row("64K", f"LoSA |A|=4, {label}", base, 128, 4, SWEEP_LAYERS, res, False)
+    floors["page_meta"] = page_meta_times(hip, lay, kv[1], reps=args.steps)
+    log(f"[sweep] page metadata {json.dumps(floors['page_meta'])}")
     del kv, lay
     torch.cuda.empty_cache()
 

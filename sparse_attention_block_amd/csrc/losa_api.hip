@@ -37,9 +37,6 @@ int check_shape(const losa_shape *sh) {
     if (sh->head_dim != 64 && sh->head_dim != 128) return LOSA_ERR_UNSUPPORTED;
     if (sh->block > 64) return LOSA_ERR_UNSUPPORTED;
     if ((int64_t)(sh->n_qhead / sh->n_kvhead) * sh->block > kMaxRows) return LOSA_ERR_UNSUPPORTED;
-    if ((sh->flags & LOSA_FLAG_SHARED_ACTIVE) &&
-        ((int64_t)sh->n_qhead * sh->block > kMaxSharedScores))
-        return LOSA_ERR_UNSUPPORTED;
     if ((sh->flags & LOSA_FLAG_ROW_MASK) &&
         (int64_t)(sh->n_qhead / sh->n_kvhead) * sh->n_active > kMaxMaskRows)
         return LOSA_ERR_UNSUPPORTED;
@@ -126,6 +123,8 @@ size_t carve(const Dims &D, char *base, Work *W) {
     w.union_cnt = reinterpret_cast<int32_t *>(take(SG * 4));
     w.part_acc = reinterpret_cast<float *>(take(SG * part_rows * D.d * 4));
     w.part_ml = reinterpret_cast<float *>(take(SG * part_rows * 2 * 4));
+    w.shloc = reinterpret_cast<float *>(
+        take(D.flags & LOSA_FLAG_SHARED_ACTIVE ? (size_t)D.S * D.Hq * D.B * 4 : 0));
     if (W) *W = w;
     return off;
 }
@@ -267,6 +266,8 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
     hipStream_t s = static_cast<hipStream_t>(stream);
     void **ev = dbg.stage_events;
     hipError_t e = mark(ev, 0, s);
+    if ((D.flags & LOSA_FLAG_SHARED_ACTIVE) && e == hipSuccess)
+        e = launch_shared_locality(D, q_t, q_prev, W, dbg.locality, s);
     if (score_prep_fits(D)) {
         // preparation and page scoring in one kernel (its time shows as scoring)
         if (e == hipSuccess) e = mark(ev, 1, s);
@@ -274,8 +275,6 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
             e = launch_score_prep(D, q_t, q_prev, page_meta, kv_off, prefix_len, W, dbg.locality,
                                   dbg.active, dbg.union_cnt, s);
     } else {
-        if ((D.flags & LOSA_FLAG_SHARED_ACTIVE) && e == hipSuccess)
-            e = launch_shared_active(D, q_t, q_prev, W, dbg.locality, dbg.active, s);
         if (e == hipSuccess)
             e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active, dbg.union_cnt,
                                s);

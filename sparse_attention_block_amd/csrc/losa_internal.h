@@ -21,7 +21,8 @@ constexpr int kSparseTargetGroups = 1024; // workgroups a sparse pass may keep a
 constexpr int kMaxRows = 256;     // G * B stacked rows per KV head at most
 constexpr int kMaxK = 64;         // pages per row the exact selection keeps in one register
 constexpr int kMaxMaskRows = 64;  // stacked rows per KV head with per-row page masks (bits)
-constexpr int kMaxSharedScores = 8192;  // query heads x block tokens for a shared active set
+constexpr int kMaxSharedPrep = 1024;  // query heads x block tokens staged in LDS by the
+                                      // folded preparation for a shared active set
 
 // Relative error bound between the MFMA-accumulated page bound and the exact
 // fp32 chain (both sides together), and an absolute floor for flushed
@@ -63,14 +64,16 @@ struct Work {
     int32_t *union_cnt;  // [S][Hk] union size, written by the sparse prefix kernel
     float *part_acc;     // [S][Hk][n_chunks][rows][d]
     float *part_ml;      // [S][Hk][n_chunks][rows][2] (running max in log2 units, sum)
+    float *shloc;        // [S][Hq][B] per-head locality / d (shared active set only)
 };
 
 // Launchers (one per translation unit); each returns the hipGetLastError code.
 hipError_t launch_page_meta(const Dims &D, const void *k_cache, const int32_t *kv_off,
                             const int32_t *prefix_len, const int32_t *first_token,
                             int max_new_tokens, void *meta, hipStream_t st);
-hipError_t launch_shared_active(const Dims &D, const void *q_t, const void *q_prev, const Work &W,
-                                float *dbg_loc, int32_t *dbg_act, hipStream_t st);
+// Per-head locality of every (query head, token) for the shared active set.
+hipError_t launch_shared_locality(const Dims &D, const void *q_t, const void *q_prev, const Work &W,
+                                  float *dbg_loc, hipStream_t st);
 hipError_t launch_prepare(const Dims &D, bool dense, const void *q_t, const void *q_prev,
                           const Work &W, float *dbg_locality, int32_t *dbg_active,
                           int32_t *dbg_union_cnt, hipStream_t st);

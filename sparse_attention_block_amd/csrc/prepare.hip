@@ -77,50 +77,27 @@ __device__ __forceinline__ float locality_chain(const T *a, const T *b) {
     return acc;
 }
 
-// Shared active set (LOSA_FLAG_SHARED_ACTIVE), one workgroup per sequence:
-// every (query head, token) locality chain as above, divided by d; per token
-// the sum over query heads in ascending order (an fp32 chain); the |A| largest
-// sums are active, equal sums going to the lower token; the same ascending list
-// is written for every head (the per-layer reading of the locality score).
+// Shared active set (LOSA_FLAG_SHARED_ACTIVE), first half: one thread per
+// (sequence, token, query head) row -- consecutive threads read consecutive
+// rows of the query arrays -- computes that row's locality chain as above,
+// divided by d, into W.shloc[s][h][t].  The second half (the sum over query
+// heads in ascending order, an fp32 chain, and the |A| largest sums, equal sums
+// going to the lower token; the per-layer reading of the locality score) runs
+// at the start of the kernel that stacks the rows, for all of its heads.
 template <typename T, int DIM>
-__global__ __launch_bounds__(256) void k_shared_active(Dims D, const T *__restrict__ q_t,
-                                                       const T *__restrict__ q_prev, Work W,
-                                                       float *__restrict__ dbg_loc,
-                                                       int32_t *__restrict__ dbg_act) {
-    __shared__ float sc[kMaxSharedScores];
-    __shared__ float tot[64];
-    __shared__ int sel[64];
-    const int s = blockIdx.x, tid = threadIdx.x;
-    const int B = D.B, A = D.A, Hq = D.Hq;
-    for (int i = tid; i < Hq * B; i += blockDim.x) {
-        const int h = i / B, t = i % B;
-        const size_t off = ((size_t)(s * B + t) * Hq + h) * DIM;
-        const float e = locality_chain<T, DIM>(q_t + off, q_prev + off) / static_cast<float>(DIM);
-        sc[i] = e;
-        if (dbg_loc) dbg_loc[((size_t)s * Hq + h) * B + t] = e;
-    }
-    __syncthreads();
-    if (tid < B) {
-        float acc = 0.0f;
-        for (int h = 0; h < Hq; ++h) acc = acc + sc[h * B + tid];
-        tot[tid] = acc;
-    }
-    __syncthreads();
-    if (tid < B) {
-        const float et = tot[tid];
-        int rank = 0;
-        for (int u = 0; u < B; ++u) rank += (tot[u] > et) || (tot[u] == et && u < tid);
-        sel[tid] = rank < A;
-    }
-    __syncthreads();
-    if (tid < B && sel[tid]) {
-        int pos = 0;
-        for (int u = 0; u < tid; ++u) pos += sel[u];
-        for (int h = 0; h < Hq; ++h) {
-            W.active[((size_t)s * Hq + h) * A + pos] = tid;
-            if (dbg_act) dbg_act[((size_t)s * Hq + h) * A + pos] = tid;
-        }
-    }
+__global__ __launch_bounds__(64) void k_shared_locality(Dims D, const T *__restrict__ q_t,
+                                                        const T *__restrict__ q_prev, Work W,
+                                                        float *__restrict__ dbg_loc) {
+    const int64_t n = (int64_t)D.S * D.B * D.Hq;
+    const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (i >= n) return;
+    const int h = static_cast<int>(i % D.Hq);
+    const int64_t st = i / D.Hq;
+    const int t = static_cast<int>(st % D.B), s = static_cast<int>(st / D.B);
+    const float e = locality_chain<T, DIM>(q_t + i * DIM, q_prev + i * DIM) / static_cast<float>(DIM);
+    const size_t o = ((size_t)s * D.Hq + h) * D.B + t;
+    W.shloc[o] = e;
+    if (dbg_loc) dbg_loc[o] = e;
 }
 
 template <typename T, int DIM, bool DENSE>
@@ -145,9 +122,32 @@ __global__ __launch_bounds__(256) void k_prepare(Dims D, const T *__restrict__ q
     }
     int rows;
     if (!dense && (D.flags & LOSA_FLAG_SHARED_ACTIVE)) {
-        // the active set shared by all heads, from k_shared_active
-        for (int i = threadIdx.x; i < G * A; i += blockDim.x)
-            act_s[i] = W.active[((size_t)s * Hq + g * G + i / A) * A + i % A];
+        // the active set shared by all heads, from the per-head localities
+        if (threadIdx.x < B) {
+            const float *e = W.shloc + (size_t)s * Hq * B + threadIdx.x;
+            float acc = 0.0f;
+            for (int h = 0; h < Hq; ++h) acc = acc + e[(size_t)h * B];
+            e_s[threadIdx.x] = acc;
+        }
+        __syncthreads();
+        if (threadIdx.x < B) {
+            const int t = threadIdx.x;
+            const float et = e_s[t];
+            int rank = 0;
+            for (int u = 0; u < B; ++u) rank += (e_s[u] > et) || (e_s[u] == et && u < t);
+            sel_s[t] = rank < A;
+        }
+        __syncthreads();
+        if (threadIdx.x < B && sel_s[threadIdx.x]) {
+            const int t = threadIdx.x;
+            int pos = 0;
+            for (int u = 0; u < t; ++u) pos += sel_s[u];
+            for (int j = 0; j < G; ++j) {
+                act_s[j * A + pos] = t;
+                W.active[((size_t)s * Hq + g * G + j) * A + pos] = t;
+                if (dbg_act) dbg_act[((size_t)s * Hq + g * G + j) * A + pos] = t;
+            }
+        }
         __syncthreads();
         rows = G * A;
     } else if (!dense) {
@@ -274,12 +274,14 @@ __global__ __launch_bounds__(256) void k_prepare(Dims D, const T *__restrict__ q
     }
 }
 
-hipError_t launch_shared_active(const Dims &D, const void *q_t, const void *q_prev, const Work &W,
-                                float *dbg_loc, int32_t *dbg_act, hipStream_t st) {
-#define LAUNCH_A(TV, DIMV)                                                                    \
-    hipLaunchKernelGGL((k_shared_active<TV, DIMV>), dim3(D.S), dim3(256), 0, st, D,           \
-                       static_cast<const TV *>(q_t), static_cast<const TV *>(q_prev), W, dbg_loc, \
-                       dbg_act)
+hipError_t launch_shared_locality(const Dims &D, const void *q_t, const void *q_prev, const Work &W,
+                                  float *dbg_loc, hipStream_t st) {
+    const int64_t n = (int64_t)D.S * D.B * D.Hq;
+    const dim3 grid(static_cast<unsigned>((n + 63) / 64));
+    if (n == 0) return hipSuccess;
+#define LAUNCH_A(TV, DIMV)                                                                      \
+    hipLaunchKernelGGL((k_shared_locality<TV, DIMV>), grid, dim3(64), 0, st, D,                 \
+                       static_cast<const TV *>(q_t), static_cast<const TV *>(q_prev), W, dbg_loc)
     if (D.bf16) {
         if (D.d == 128) LAUNCH_A(uint16_t, 128);
         else LAUNCH_A(uint16_t, 64);

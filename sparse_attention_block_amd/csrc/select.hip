@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
 
 constexpr int kPrepPad = 4;  // words of padding per LDS row (bank spread)
 
-template <int DIM>
+template <int DIM, bool SHARED>
 __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__restrict__ q_t,
                                                     const uint16_t *__restrict__ q_prev,
                                                     const uint4 *__restrict__ meta,
@@ -250,6 +250,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     __shared__ int sel_s[kMaxRows];
     __shared__ int act_s[kMaxRows];
     __shared__ float qabs_s[kMaxRows];
+    __shared__ float shl_s[SHARED ? kMaxSharedPrep : 1];  // per-head localities [Hq][B]
     const int ng = D.S * D.Hk;
     const int sgi = blockIdx.x % ng, blk = blockIdx.x / ng;
     const int s = sgi / D.Hk, g = sgi % D.Hk;
@@ -272,6 +273,14 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     };
     const uint4 qv0 = qload(0), qv1 = qload(1), qv2 = qload(2), qv3 = qload(3);
     const uint4 qv4 = qload(4), qv5 = qload(5), qv6 = qload(6), qv7 = qload(7);
+    // shared active set: the sequence's per-head localities (clamped reads)
+    constexpr int kShl = SHARED ? kMaxSharedPrep / 256 : 1;
+    float shl[kShl];
+    if constexpr (SHARED) {
+        const float *e = W.shloc + (size_t)s * Hq * B;
+#pragma unroll
+        for (int i = 0; i < kShl; ++i) shl[i] = e[min(tid + 256 * i, Hq * B - 1)];
+    }
     __builtin_amdgcn_sched_barrier(0);  // the query vectors are requested first
     const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
     const int64_t tile0 = sg.gp0 / kTile;
@@ -297,6 +306,10 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     qstore(5, qv5);
     qstore(6, qv6);
     qstore(7, qv7);
+    if constexpr (SHARED) {
+#pragma unroll
+        for (int i = 0; i < kShl; ++i) shl_s[tid + 256 * i] = shl[i];
+    }
     // The tile is requested only now, after the query vectors have landed: the
     // tiles of all workgroups together would otherwise queue ahead of them, and
     // the preparation below waits for the queries, not for the tile.
@@ -323,53 +336,83 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     }
     __syncthreads();
 
-    // 2. locality chain per (query head, token), then the active set
-    if (tid < GB) {
-        const uint4 *a = reinterpret_cast<const uint4 *>(&qsm[tid * RWP]);
-        const uint4 *b = reinterpret_cast<const uint4 *>(&qsm[(GB + tid) * RWP]);
-        float acc = 0.0f;
-#pragma unroll 4
-        for (int v = 0; v < VPR; ++v) {
-            const uint4 av = a[v], bv = b[v];
-            const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float d0 = bf16_lo(aw[e]) - bf16_lo(bw[e]);
-                const float s0 = d0 * d0;
-                acc = acc + s0;
-                const float d1 = bf16_hi(aw[e]) - bf16_hi(bw[e]);
-                const float s1 = d1 * d1;
-                acc = acc + s1;
+    // 2. locality chain per (query head, token), then the active set; with a
+    //    shared active set, the sum of the per-head localities over the query
+    //    heads in ascending order, then one set for all of the group's heads
+    if constexpr (SHARED) {
+        if (tid < B) {
+            float acc = 0.0f;
+            for (int h = 0; h < Hq; ++h) acc = acc + shl_s[h * B + tid];
+            e_s[tid] = acc;
+        }
+        __syncthreads();
+        if (tid < B) {
+            const float et = e_s[tid];
+            int rank = 0;
+            for (int u = 0; u < B; ++u) rank += (e_s[u] > et) || (e_s[u] == et && u < tid);
+            sel_s[tid] = rank < A;
+        }
+        __syncthreads();
+        if (tid < B && sel_s[tid]) {
+            int pos = 0;
+            for (int u = 0; u < tid; ++u) pos += sel_s[u];
+            for (int j = 0; j < G; ++j) {
+                act_s[j * A + pos] = tid;
+                if (writer) {
+                    W.active[((size_t)s * Hq + g * G + j) * A + pos] = tid;
+                    if (dbg_act) dbg_act[((size_t)s * Hq + g * G + j) * A + pos] = tid;
+                }
             }
         }
-        e_s[tid] = acc;
-        if (writer && dbg_loc)
-            dbg_loc[((size_t)s * Hq + g * G + tid / B) * B + tid % B] = acc / static_cast<float>(DIM);
-    }
-    __syncthreads();
-    if (tid < GB) {
-        const int j = tid / B, t = tid % B;
-        const float et = e_s[tid];
-        int rank = 0;
+        __syncthreads();
+    } else {
+        if (tid < GB) {
+            const uint4 *a = reinterpret_cast<const uint4 *>(&qsm[tid * RWP]);
+            const uint4 *b = reinterpret_cast<const uint4 *>(&qsm[(GB + tid) * RWP]);
+            float acc = 0.0f;
+#pragma unroll 4
+            for (int v = 0; v < VPR; ++v) {
+                const uint4 av = a[v], bv = b[v];
+                const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float d0 = bf16_lo(aw[e]) - bf16_lo(bw[e]);
+                    const float s0 = d0 * d0;
+                    acc = acc + s0;
+                    const float d1 = bf16_hi(aw[e]) - bf16_hi(bw[e]);
+                    const float s1 = d1 * d1;
+                    acc = acc + s1;
+                }
+            }
+            e_s[tid] = acc;
+            if (writer && dbg_loc)
+                dbg_loc[((size_t)s * Hq + g * G + tid / B) * B + tid % B] = acc / static_cast<float>(DIM);
+        }
+        __syncthreads();
+        if (tid < GB) {
+            const int j = tid / B, t = tid % B;
+            const float et = e_s[tid];
+            int rank = 0;
 #pragma unroll 8
-        for (int u = 0; u < B; ++u) {
-            const float eu = e_s[j * B + u];
-            rank += (eu > et) || (eu == et && u < t);
+            for (int u = 0; u < B; ++u) {
+                const float eu = e_s[j * B + u];
+                rank += (eu > et) || (eu == et && u < t);
+            }
+            sel_s[tid] = rank < A;
         }
-        sel_s[tid] = rank < A;
-    }
-    __syncthreads();
-    if (tid < GB && sel_s[tid]) {
-        const int j = tid / B, t = tid % B;
-        int pos = 0;
-        for (int u = 0; u < t; ++u) pos += sel_s[j * B + u];
-        act_s[j * A + pos] = t;
-        if (writer) {
-            W.active[((size_t)s * Hq + g * G + j) * A + pos] = t;
-            if (dbg_act) dbg_act[((size_t)s * Hq + g * G + j) * A + pos] = t;
+        __syncthreads();
+        if (tid < GB && sel_s[tid]) {
+            const int j = tid / B, t = tid % B;
+            int pos = 0;
+            for (int u = 0; u < t; ++u) pos += sel_s[j * B + u];
+            act_s[j * A + pos] = t;
+            if (writer) {
+                W.active[((size_t)s * Hq + g * G + j) * A + pos] = t;
+                if (dbg_act) dbg_act[((size_t)s * Hq + g * G + j) * A + pos] = t;
+            }
         }
+        __syncthreads();
     }
-    __syncthreads();
 
     // 3. stacked rows r = j*|A| + a: sum |q| bounds; the writer stores the rows
     //    (bf16, rows up to the next multiple of 16 zeroed) for the later kernels
@@ -687,8 +730,9 @@ size_t score_prep_lds_bytes(const Dims &D) {
 }
 
 bool score_prep_fits(const Dims &D) {
-    return D.bf16 && D.R > 0 && !(D.flags & LOSA_FLAG_SHARED_ACTIVE) && 2 * D.G * D.B * D.d / 8 <= kPrepVecs * 256 &&
-           score_prep_lds_bytes(D) <= 40 * 1024;
+    return D.bf16 && D.R > 0 && 2 * D.G * D.B * D.d / 8 <= kPrepVecs * 256 &&
+           score_prep_lds_bytes(D) <= 40 * 1024 &&
+           (!(D.flags & LOSA_FLAG_SHARED_ACTIVE) || D.Hq * D.B <= kMaxSharedPrep);
 }
 
 hipError_t launch_score_prep(const Dims &D, const void *q_t, const void *q_prev, const void *meta,
@@ -700,12 +744,18 @@ hipError_t launch_score_prep(const Dims &D, const void *q_t, const void *q_prev,
     auto *a = static_cast<const uint16_t *>(q_t);
     auto *b = static_cast<const uint16_t *>(q_prev);
     auto *m = static_cast<const uint4 *>(meta);
-    if (D.d == 128)
-        hipLaunchKernelGGL((k_score_prep<128>), grid, dim3(256), lds, st, D, a, b, m, kv_off,
-                           prefix_len, W, dbg_loc, dbg_act, dbg_ucnt);
-    else
-        hipLaunchKernelGGL((k_score_prep<64>), grid, dim3(256), lds, st, D, a, b, m, kv_off,
-                           prefix_len, W, dbg_loc, dbg_act, dbg_ucnt);
+#define LAUNCH_P(DIMV, SH)                                                                    \
+    hipLaunchKernelGGL((k_score_prep<DIMV, SH>), grid, dim3(256), lds, st, D, a, b, m, kv_off,  \
+                       prefix_len, W, dbg_loc, dbg_act, dbg_ucnt)
+    const bool shared = D.flags & LOSA_FLAG_SHARED_ACTIVE;
+    if (D.d == 128) {
+        if (shared) LAUNCH_P(128, true);
+        else LAUNCH_P(128, false);
+    } else {
+        if (shared) LAUNCH_P(64, true);
+        else LAUNCH_P(64, false);
+    }
+#undef LAUNCH_P
     return hipGetLastError();
 }
 

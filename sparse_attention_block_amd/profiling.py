@@ -30,10 +30,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_TAGS = {
     "dense_prefix": (r"k_prefix_dense_bf16<\d+, \d+>", ["prefix.hip", "losa_internal.h"]),
     "sparse_prefix": (r"k_prefix_bf16<\d+, \d+, false>", ["prefix.hip", "losa_internal.h"]),
-    "page_score": (r"k_score_prep<\d+>", ["select.hip", "losa_internal.h"]),
+    "page_score": (r"k_score_prep<\d+, false>", ["select.hip", "losa_internal.h"]),
     "page_select": (r"k_select<\d+, true>", ["select.hip", "losa_internal.h"]),
     "sparse_finish": (r"k_finish<unsigned short, \d+, false>", ["finish.hip", "losa_internal.h"]),
     "dense_finish": (r"k_finish<unsigned short, \d+, true>", ["finish.hip", "losa_internal.h"]),
+    "page_meta": (r"k_page_meta<unsigned short, \d+>", ["page_meta.hip", "losa_internal.h"]),
 }
 COPY_KERNEL = r"(^|\W)k_copy($|\W)"
 
@@ -89,6 +90,11 @@ def print_sweep(path: str, command: str):
           f"{fl['empty_kernel_between_events_us']:.2f} us; plain copy (read + write): " +
           ", ".join(f"{k} {v['us']:.1f} us ({v['gbps']:.0f} GB/s)" for k, v in fl["copy"].items())
           + ".\n")
+    if "page_meta" in fl:
+        pm = fl["page_meta"]
+        print(f"Page metadata of a 64K layer (8 KV heads): full build {pm['full_build_us']:.1f} us "
+              f"({pm['full_build_gbps_on_keys']:.0f} GB/s on the keys); update after a committed "
+              f"block of 16 tokens {pm['commit_16_tokens_us']:.2f} us.\n")
     print("| workload | case | budget | \\|A\\| | layers | step us | dense step us | block us "
           "| union pages / KV head | density | score | select | prefix | finish "
           "| prefix GB/s on union | frac of 8 TB/s | step GB/s |")

@@ -38,6 +38,14 @@ CASES = [
                                         n_qhead=8)),
     ("shared_f32_B32", SHARED_ACTIVE, dict(dtype="f32", head_dim=64, block=32, n_active=8,
                                            budget=64, prefix_lens=(1500,), n_kvhead=2, n_qhead=8)),
+    # bf16 shapes whose preparation does not fold into scoring: G * B rows too
+    # many for its LDS, and query heads x block tokens past what it stages
+    ("shared_bf16_G8_B32", SHARED_ACTIVE, dict(dtype="bf16", head_dim=128, block=32, n_active=8,
+                                               budget=64, prefix_lens=(900, 1600), n_kvhead=1,
+                                               n_qhead=8)),
+    ("shared_bf16_96_heads", SHARED_ACTIVE, dict(dtype="bf16", head_dim=64, block=16, n_active=2,
+                                                 budget=32, prefix_lens=(260,), n_kvhead=48,
+                                                 n_qhead=96)),
     ("no_writeback_bf16", NO_WRITEBACK, dict(dtype="bf16", head_dim=128, block=16, n_active=4,
                                              budget=64, prefix_lens=(1000, 300), n_kvhead=2,
                                              n_qhead=8)),
@@ -73,3 +81,15 @@ def test_row_mask_long_64k():
     p.set_cache(op, lp)
     for step in (1, 2):
         p.sparse(step)
+
+
+def test_shared_long_64k():
+    """The shared active set at the full long-context shape (64K prefix, 32/8 heads)."""
+    cfg = W.long_64k(128, 4).replace(flags=SHARED_ACTIVE, cfg_id=78, name="shared_64k")
+    lay = W.make_layer(cfg, n_steps=3)
+    p = Pair(lay, cfg.name)
+    op, lp = W.make_cache_state(cfg)
+    p.set_cache(op, lp)
+    for step in (1, 2):
+        act = p.sparse(step)["res"]["active"]
+        assert (act == act[:, :1]).all(), "heads disagree"
