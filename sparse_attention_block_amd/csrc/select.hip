@@ -230,6 +230,8 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
 // workgroup of the first tiles also writes the active list and the stacked rows
 // for the later kernels and resets the union size.  The locality chain is the
 // one of prepare.hip: each rounded square added in ascending dimension order.
+// Each thread holds matching 16-byte vectors of both steps, so all threads
+// compute the rounded squares (into LDS), and one thread per row adds them.
 
 constexpr int kPrepPad = 4;  // words of padding per LDS row (bank spread)
 
@@ -243,12 +245,15 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
                                                     int32_t *__restrict__ dbg_act,
                                                     int32_t *__restrict__ dbg_ucnt) {
     constexpr int KS = DIM / 16, NCH = DIM / 4;
-    constexpr int RWP = DIM / 2 + kPrepPad;  // words per LDS row: bf16 pairs of dims 2w, 2w+1
+    constexpr int RWP = DIM / 2 + kPrepPad;  // words per LDS query row: bf16 pairs of dims 2w, 2w+1
+    constexpr int RWS = DIM + kPrepPad;      // words per LDS row of squares
     constexpr int VPR = DIM / 8;             // 16-byte vectors per row
-    extern __shared__ uint32_t qsm[];        // [2][G*B][RWP]: q_t rows, then q_prev rows
+    constexpr int NV = kPrepVecs / 2;        // vectors per thread and step
+    extern __shared__ uint32_t qsm[];        // [G*B][RWP] q_t rows, then [G*B][RWS] fp32 squares
     __shared__ float e_s[kMaxRows];
     __shared__ int sel_s[kMaxRows];
     __shared__ int act_s[kMaxRows];
+    __shared__ int rbase_s[kMaxRows];        // stacked row r: word offset of its query row in qsm
     __shared__ float qabs_s[kMaxRows];
     __shared__ float shl_s[SHARED ? kMaxSharedPrep : 1];  // per-head localities [Hq][B]
     const int ng = D.S * D.Hk;
@@ -259,20 +264,24 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     const int G = D.G, B = D.B, A = D.A, GB = G * B, R = D.R, Hq = D.Hq;
     const bool writer = blk == 0;
 
-    // 1. the group's query rows (clamped 16-byte vectors) into LDS, then the
+    // 1. the group's query rows of both steps (clamped 16-byte vectors; a thread
+    //    holds the same vectors of q_t and q_prev), q_t into LDS, then the
     //    tile's page operands are requested
     const int nvec = GB * VPR;
-    static_assert(kPrepVecs == 8, "one named register per query vector below");
-    auto qload = [&](int i) {
-        const int idx = min(tid + 256 * i, 2 * nvec - 1);
-        const int which = idx / nvec, v = idx % nvec;
+    static_assert(NV * 2 == kPrepVecs, "vectors per thread");
+    auto qaddr = [&](const uint16_t *base, int i) {
+        const int v = min(tid + 256 * i, nvec - 1);
         const int row = v / VPR, c = v % VPR;
-        const uint16_t *src = (which ? q_prev : q_t) +
-                              ((size_t)(s * B + row % B) * Hq + g * G + row / B) * DIM + c * 8;
-        return *reinterpret_cast<const uint4 *>(src);
+        return reinterpret_cast<const uint4 *>(
+            base + ((size_t)(s * B + row % B) * Hq + g * G + row / B) * DIM + c * 8);
     };
-    const uint4 qv0 = qload(0), qv1 = qload(1), qv2 = qload(2), qv3 = qload(3);
-    const uint4 qv4 = qload(4), qv5 = qload(5), qv6 = qload(6), qv7 = qload(7);
+    uint4 qa_v[NV], qb_v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) qa_v[i] = *qaddr(q_t, i);
+    if constexpr (!SHARED) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) qb_v[i] = *qaddr(q_prev, i);
+    }
     // shared active set: the sequence's per-head localities (clamped reads)
     constexpr int kShl = SHARED ? kMaxSharedPrep / 256 : 1;
     float shl[kShl];
@@ -293,19 +302,11 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     const int R1 = R > 0 ? R : 1;
     const int l16 = lane & 15, lg = lane >> 4;
     const uint4 *mt = meta + (size_t)(g * D.n_tiles_total + tile) * NCH * kTile;
-    auto qstore = [&](int i, const uint4 &q) {
-        const int idx = min(tid + 256 * i, 2 * nvec - 1);
-        const int which = idx / nvec, v = idx % nvec;
-        *reinterpret_cast<uint4 *>(&qsm[(which * GB + v / VPR) * RWP + (v % VPR) * 4]) = q;
-    };
-    qstore(0, qv0);
-    qstore(1, qv1);
-    qstore(2, qv2);
-    qstore(3, qv3);
-    qstore(4, qv4);
-    qstore(5, qv5);
-    qstore(6, qv6);
-    qstore(7, qv7);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int v = min(tid + 256 * i, nvec - 1);
+        *reinterpret_cast<uint4 *>(&qsm[(v / VPR) * RWP + (v % VPR) * 4]) = qa_v[i];
+    }
     if constexpr (SHARED) {
 #pragma unroll
         for (int i = 0; i < kShl; ++i) shl_s[tid + 256 * i] = shl[i];
@@ -330,6 +331,27 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         amax[cb] = aux[cb * 16 + l16];
     }
     __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
+    float *sq = reinterpret_cast<float *>(qsm + GB * RWP);
+    if constexpr (!SHARED) {
+        // rounded squares of the change, dimensions c*8 .. c*8+7 of a row
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = min(tid + 256 * i, nvec - 1);
+            const uint32_t aw[4] = {qa_v[i].x, qa_v[i].y, qa_v[i].z, qa_v[i].w};
+            const uint32_t bw[4] = {qb_v[i].x, qb_v[i].y, qb_v[i].z, qb_v[i].w};
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float d0 = bf16_lo(aw[e]) - bf16_lo(bw[e]);
+                sv[2 * e] = d0 * d0;
+                const float d1 = bf16_hi(aw[e]) - bf16_hi(bw[e]);
+                sv[2 * e + 1] = d1 * d1;
+            }
+            float4 *dst = reinterpret_cast<float4 *>(sq + (v / VPR) * RWS + (v % VPR) * 8);
+            dst[0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+            dst[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
+        }
+    }
     if (writer && tid == 0) {
         W.union_cnt[sgi] = 0;
         if (dbg_ucnt) dbg_ucnt[sgi] = 0;  // the sparse prefix kernel overwrites them
@@ -358,6 +380,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             for (int u = 0; u < tid; ++u) pos += sel_s[u];
             for (int j = 0; j < G; ++j) {
                 act_s[j * A + pos] = tid;
+                rbase_s[j * A + pos] = (j * B + tid) * RWP;
                 if (writer) {
                     W.active[((size_t)s * Hq + g * G + j) * A + pos] = tid;
                     if (dbg_act) dbg_act[((size_t)s * Hq + g * G + j) * A + pos] = tid;
@@ -367,22 +390,15 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         __syncthreads();
     } else {
         if (tid < GB) {
-            const uint4 *a = reinterpret_cast<const uint4 *>(&qsm[tid * RWP]);
-            const uint4 *b = reinterpret_cast<const uint4 *>(&qsm[(GB + tid) * RWP]);
+            const float4 *sr = reinterpret_cast<const float4 *>(sq + tid * RWS);
             float acc = 0.0f;
-#pragma unroll 4
-            for (int v = 0; v < VPR; ++v) {
-                const uint4 av = a[v], bv = b[v];
-                const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float d0 = bf16_lo(aw[e]) - bf16_lo(bw[e]);
-                    const float s0 = d0 * d0;
-                    acc = acc + s0;
-                    const float d1 = bf16_hi(aw[e]) - bf16_hi(bw[e]);
-                    const float s1 = d1 * d1;
-                    acc = acc + s1;
-                }
+            for (int v = 0; v < DIM / 4; ++v) {
+                const float4 x = sr[v];
+                acc = acc + x.x;
+                acc = acc + x.y;
+                acc = acc + x.z;
+                acc = acc + x.w;
             }
             e_s[tid] = acc;
             if (writer && dbg_loc)
@@ -406,6 +422,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             int pos = 0;
             for (int u = 0; u < t; ++u) pos += sel_s[j * B + u];
             act_s[j * A + pos] = t;
+            rbase_s[j * A + pos] = tid * RWP;
             if (writer) {
                 W.active[((size_t)s * Hq + g * G + j) * A + pos] = t;
                 if (dbg_act) dbg_act[((size_t)s * Hq + g * G + j) * A + pos] = t;
@@ -422,7 +439,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         const int r = r0 + tid / 16, part = tid % 16;
         float ab = 0.0f;
         if (r < R) {
-            const uint32_t *a = &qsm[((r / A) * B + act_s[r]) * RWP + part * (DIM / 32)];
+            const uint32_t *a = &qsm[rbase_s[r] + part * (DIM / 32)];
 #pragma unroll
             for (int w = 0; w < DIM / 32; ++w) ab += fabsf(bf16_lo(a[w])) + fabsf(bf16_hi(a[w]));
         }
@@ -435,7 +452,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         for (int i = tid; i < D.Rs16 * VPR; i += 256) {
             const int r = i / VPR, c = i % VPR;
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (r < R) v = *reinterpret_cast<const uint4 *>(&qsm[((r / A) * B + act_s[r]) * RWP + c * 4]);
+            if (r < R) v = *reinterpret_cast<const uint4 *>(&qsm[rbase_s[r] + c * 4]);
             *reinterpret_cast<uint4 *>(qr + (size_t)r * DIM + c * 8) = v;
         }
     }
@@ -447,20 +464,23 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     float *tm = W.tmax + (size_t)sgi * R1 * D.n_tiles_grid;
     for (int rt = 0; rt < D.Rs16 / 16; ++rt) {
         const int row = rt * 16 + l16;
+        const bool live = row < R;
+        // the row's query words (a clamped row for the padding rows, zeroed below)
+        const uint32_t *qrow = &qsm[rbase_s[min(row, R - 1)] + 2 * lg];
+        uint2 h2[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) h2[kk] = *reinterpret_cast<const uint2 *>(qrow + 8 * kk);
         uint4 aop[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            uint32_t w4[4] = {0u, 0u, 0u, 0u};
-            if (row < R) {
-                const uint2 h2 =
-                    *reinterpret_cast<const uint2 *>(&qsm[((row / A) * B + act_s[row]) * RWP + 8 * kk + 2 * lg]);
-                const uint32_t hw[4] = {h2.x & 0xffffu, h2.x >> 16, h2.y & 0xffffu, h2.y >> 16};
+            const uint32_t hw[4] = {h2[kk].x & 0xffffu, h2[kk].x >> 16, h2[kk].y & 0xffffu,
+                                    h2[kk].y >> 16};
+            uint32_t w4[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // (q+, q-): q >= 0 (-0 included) -> low half, else high half
-                    const bool pos = __uint_as_float(hw[e] << 16) >= 0.0f;
-                    w4[e] = pos ? hw[e] : (hw[e] << 16);
-                }
+            for (int e = 0; e < 4; ++e) {
+                // (q+, q-): q >= 0 (-0 included) -> low half, else high half
+                const bool pos = __uint_as_float(hw[e] << 16) >= 0.0f;
+                w4[e] = live ? (pos ? hw[e] : (hw[e] << 16)) : 0u;
             }
             aop[kk] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
         }
@@ -480,11 +500,14 @@ struct SelectDbg {
 
 // The exact chain for global page gp (contract of include/losa.h); the page's
 // metadata chunks are loaded before the chain starts.  bf16: qw holds the
-// row's bf16 query values (word w = dimensions 2w, 2w+1); per dimension one
-// fused multiply-add with max_i (q >= 0, -0 included) or min_i (q < 0) -- the
-// same value as the pair q+ * max then q- * min, whose other product is an
-// exact zero.  fp32: qw holds (max(q,0), min(q,0)) per dimension, each product
-// rounded, then added.
+// row's query values as fp32 (DIM words), then per dimension the byte
+// selector that turns the metadata word (max | min << 16) into the fp32 bits
+// of max_i (q >= 0, -0 included) or of min_i (q < 0); per dimension one fused
+// multiply-add with that value -- the same value as the pair q+ * max then
+// q- * min, whose other product is an exact zero.  fp32: qw holds (max(q,0),
+// min(q,0)) per dimension, each product rounded, then added.
+constexpr uint32_t kSelMax = 0x01000c0cu;  // v_perm_b32: bytes 1,0 of the word to 3,2; zeros below
+constexpr uint32_t kSelMin = 0x03020c0cu;  // bytes 3,2 to 3,2; zeros below
 template <int DIM, bool BF>
 __device__ __forceinline__ float exact_bound(const uint4 *meta, const Dims &D, int g, int64_t gp,
                                              const uint32_t *qw) {
@@ -503,12 +526,14 @@ __device__ __forceinline__ float exact_bound(const uint4 *meta, const Dims &D, i
             const uint4 m4 = mv[c];
             const int cc = c0 + c;
             if constexpr (BF) {
-                const uint2 q2 = *reinterpret_cast<const uint2 *>(qw + 2 * cc);
-                const float qd[4] = {bf16_lo(q2.x), bf16_hi(q2.x), bf16_lo(q2.y), bf16_hi(q2.y)};
-                const uint32_t wd[4] = {m4.x, m4.y, m4.z, m4.w};
+                const float4 q4 = *reinterpret_cast<const float4 *>(qw + 4 * cc);
+                const uint4 sl = *reinterpret_cast<const uint4 *>(qw + DIM + 4 * cc);
+                const float qd[4] = {q4.x, q4.y, q4.z, q4.w};
+                const uint32_t wd[4] = {m4.x, m4.y, m4.z, m4.w}, sd[4] = {sl.x, sl.y, sl.z, sl.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    acc = __builtin_fmaf(qd[e], qd[e] >= 0.0f ? bf16_lo(wd[e]) : bf16_hi(wd[e]), acc);
+                    acc = __builtin_fmaf(qd[e], __uint_as_float(__builtin_amdgcn_perm(0u, wd[e], sd[e])),
+                                         acc);
             } else {
                 const float *q = reinterpret_cast<const float *>(qw);
                 const float p0 = q[4 * cc + 0] * __uint_as_float(m4.x);
@@ -587,7 +612,12 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         load_h(0, hv0);
         __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
         if constexpr (BF) {
-            if (lane < DIM / 2) qw[lane] = qv[0];
+            if (lane < DIM / 2) {
+                const float q0 = bf16_lo(qv[0]), q1 = bf16_hi(qv[0]);
+                *reinterpret_cast<float2 *>(qw + 2 * lane) = make_float2(q0, q1);
+                *reinterpret_cast<uint2 *>(qw + DIM + 2 * lane) =
+                    make_uint2(q0 >= 0.0f ? kSelMax : kSelMin, q1 >= 0.0f ? kSelMax : kSelMin);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < QPL; ++i) qw[lane + 64 * i] = qv[i];
@@ -726,12 +756,14 @@ hipError_t launch_score(const Dims &D, const void *meta, const int32_t *kv_off,
 }
 
 size_t score_prep_lds_bytes(const Dims &D) {
-    return (size_t)2 * D.G * D.B * (D.d / 2 + kPrepPad) * 4;
+    const size_t rows = (size_t)D.G * D.B;
+    const size_t squares = (D.flags & LOSA_FLAG_SHARED_ACTIVE) ? 0 : rows * (D.d + kPrepPad) * 4;
+    return rows * (D.d / 2 + kPrepPad) * 4 + squares;
 }
 
 bool score_prep_fits(const Dims &D) {
     return D.bf16 && D.R > 0 && 2 * D.G * D.B * D.d / 8 <= kPrepVecs * 256 &&
-           score_prep_lds_bytes(D) <= 40 * 1024 &&
+           score_prep_lds_bytes(D) <= 56 * 1024 &&
            (!(D.flags & LOSA_FLAG_SHARED_ACTIVE) || D.Hq * D.B <= kMaxSharedPrep);
 }
 
