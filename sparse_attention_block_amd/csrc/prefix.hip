@@ -185,9 +185,10 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
 // psel[0 .. n_sel), -1 for none -- as a bitmap in LDS (bm: ceil(pages/32)
 // words), compacted in ascending page order.  The pages at union positions
 // [first, first + cp) go to pg_out; with dbg_idx, every position is written
-// there too.  Returns the union size.  Called by all 256 threads.
-__device__ int union_slice(const int32_t *__restrict__ psel, int n_sel, int pages, bool all_pages,
-                           int first, int cp, uint32_t *bm, int *wsum, int *pg_out,
+// there too.  Returns the union size.  Called by all 256 threads; pre0 is
+// psel[tid] (read by the caller ahead of time; ignored for tid >= n_sel).
+__device__ int union_slice(const int32_t *__restrict__ psel, int pre0, int n_sel, int pages,
+                           bool all_pages, int first, int cp, uint32_t *bm, int *wsum, int *pg_out,
                            int32_t *dbg_idx, int dbg_cap, int k = 0, uint64_t *rmask = nullptr) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (all_pages) {
@@ -201,7 +202,8 @@ __device__ int union_slice(const int32_t *__restrict__ psel, int n_sel, int page
     const int words = (pages + 31) / 32;
     for (int i = tid; i < words; i += 256) bm[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < n_sel; i += 256) {
+    if (tid < n_sel && pre0 >= 0) atomicOr(&bm[pre0 >> 5], 1u << (pre0 & 31));
+    for (int i = tid + 256; i < n_sel; i += 256) {
         const int pg = psel[i];
         if (pg >= 0) atomicOr(&bm[pg >> 5], 1u << (pg & 31));
     }
@@ -267,11 +269,12 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     constexpr int KSTEPS = DIM / 32;  // QK^T k-steps of 32 dims
     constexpr int DPL = DIM / 16;     // V dims per lane = PV MFMAs per page
     constexpr int RAW = 4 * 16 * DIM > kMaxBitmapWords ? 4 * 16 * DIM : kMaxBitmapWords;
-    __shared__ float s_raw[RAW];  // the union bitmap first, then the page groups' outputs
+    __shared__ __align__(16) float s_raw[RAW];  // the union bitmap, then the page groups' outputs
     __shared__ int s_wsum[4], s_pg[kMaxSparseChunk];
     __shared__ uint64_t s_rmask[MASK ? kMaxSparseChunk : 1];  // rows that selected each page
     auto s_acc = reinterpret_cast<float (*)[16][DIM]>(s_raw);
     __shared__ float s_ml[4][16][2];
+    __shared__ __align__(16) float s_wt[4][16][4];  // each row's page-group weights (combine)
 
     const int ng = D.S * D.Hk;
     const int sgi = blockIdx.x % ng;
@@ -292,6 +295,10 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     const int n_pg = 4 / WPG;
     const int pg = w / WPG, wr = w % WPG;
 
+    // the rows' page lists (one entry per thread, clamped), requested first
+    const int32_t *psel_g = W.psel + (size_t)sgi * (D.R > 0 ? D.R : 1) * D.k;
+    const int n_sel = D.R * D.k;
+    const int pre0 = dense ? -1 : psel_g[min(tid, max(n_sel - 1, 0))];
     // Q operands (B of QK^T): lane l holds row l%16, dims 32*kk + 8*(l/16) .. +7;
     // requested before the union is built.
     uint4 qop[RTW][KSTEPS];
@@ -313,8 +320,7 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     if (dense) {
         n_items = sg.pages;
     } else {
-        const int R1 = D.R > 0 ? D.R : 1;
-        n_items = union_slice(W.psel + (size_t)sgi * R1 * D.k, D.R * D.k, sg.pages, D.k >= sg.pages,
+        n_items = union_slice(psel_g, pre0, n_sel, sg.pages, D.k >= sg.pages,
                               first, cp, reinterpret_cast<uint32_t *>(s_raw), s_wsum, s_pg,
                               chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
                               dbg_cap, D.k, MASK ? s_rmask : nullptr);
@@ -399,10 +405,12 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     }
     // Several page groups: combine them through LDS, RTW rounds of one row
     // tile per wave (round i: the waves hold row tiles i*WPG .. i*WPG + WPG-1).
+    // Per row, one thread forms the groups' weights (and the row's m, l); then
+    // every thread combines 4 dimensions of a row, groups in ascending order.
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
         if (i * WPG >= n_rt) break;  // uniform
-        if (i > 0) __syncthreads();  // the previous round has read s_acc
+        if (i > 0) __syncthreads();  // the previous round has read s_acc and s_wt
         if (lg == 0) {
             s_ml[w][l16][0] = m_run[i];
             s_ml[w][l16][1] = l_run[i];
@@ -412,29 +420,56 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
 #pragma unroll
             for (int e = 0; e < DPL; ++e) s_acc[w][l16][DPL * (4 * lg + j) + e] = oacc[i][e][j];
         __syncthreads();
-        for (int idx = tid; idx < WPG * 16 * DIM; idx += 256) {
-            const int rtile = idx / (16 * DIM);
-            const int rr = (idx / DIM) % 16;
-            const int dim = idx % DIM;
+        if (tid < WPG * 16) {
+            const int rtile = tid / 16, rr = tid % 16;
             const int r = (i * WPG + rtile) * 16 + rr;
-            if (r >= rows) continue;
+            float mq[4], wq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) mq[q] = s_ml[min(q * WPG + rtile, 3)][rr][0];
             float mx = -__builtin_huge_valf();
-            for (int q = 0; q < n_pg; ++q) mx = fmaxf(mx, s_ml[q * WPG + rtile][rr][0]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (q < n_pg) mx = fmaxf(mx, mq[q]);
             // (with masks a row may have no page in any group: zero weights)
             const float mref = MASK && mx == -__builtin_huge_valf() ? 0.0f : mx;
-            float lsum = 0.0f, a = 0.0f;
-            for (int q = 0; q < n_pg; ++q) {
-                const int wq = q * WPG + rtile;
-                const float wgt = __builtin_amdgcn_exp2f(s_ml[wq][rr][0] - mref);
-                lsum += wgt * s_ml[wq][rr][1];
-                a += wgt * s_acc[wq][rr][dim];
+            float lsum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wq[q] = q < n_pg ? __builtin_amdgcn_exp2f(mq[q] - mref) : 0.0f;
+                if (q < n_pg) lsum += wq[q] * s_ml[q * WPG + rtile][rr][1];
+            }
+            *reinterpret_cast<float4 *>(&s_wt[rtile][rr][0]) = make_float4(wq[0], wq[1], wq[2], wq[3]);
+            if (r < rows) {
+                const size_t pb = ((size_t)sgi * nch + chunk) * rows + r;
+                *reinterpret_cast<float2 *>(&W.part_ml[pb * 2]) = make_float2(mx, lsum);
+            }
+        }
+        __syncthreads();
+        constexpr int D4 = DIM / 4;
+        for (int idx = tid; idx < WPG * 16 * D4; idx += 256) {
+            const int rtile = idx / (16 * D4);
+            const int rr = (idx / D4) % 16;
+            const int d4 = idx % D4;
+            const int r = (i * WPG + rtile) * 16 + rr;
+            if (r >= rows) continue;
+            const float4 wv = *reinterpret_cast<const float4 *>(&s_wt[rtile][rr][0]);
+            const float wq[4] = {wv.x, wv.y, wv.z, wv.w};
+            float4 av[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                av[q] = *reinterpret_cast<const float4 *>(&s_acc[min(q * WPG + rtile, 3)][rr][4 * d4]);
+            float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q < n_pg) {  // uniform
+                    a0 += wq[q] * av[q].x;
+                    a1 += wq[q] * av[q].y;
+                    a2 += wq[q] * av[q].z;
+                    a3 += wq[q] * av[q].w;
+                }
             }
             const size_t pb = ((size_t)sgi * nch + chunk) * rows + r;
-            W.part_acc[pb * DIM + dim] = a;
-            if (dim == 0) {
-                W.part_ml[pb * 2 + 0] = mx;
-                W.part_ml[pb * 2 + 1] = lsum;
-            }
+            *reinterpret_cast<float4 *>(&W.part_acc[pb * DIM + 4 * d4]) = make_float4(a0, a1, a2, a3);
         }
     }
 }
@@ -720,8 +755,10 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restr
     if (dense) {
         n_items = sg.pages;
     } else {
-        const int R1 = D.R > 0 ? D.R : 1;
-        n_items = union_slice(W.psel + (size_t)sgi * R1 * D.k, D.R * D.k, sg.pages, D.k >= sg.pages,
+        const int32_t *psel_g = W.psel + (size_t)sgi * (D.R > 0 ? D.R : 1) * D.k;
+        const int n_sel = D.R * D.k;
+        const int pre0 = psel_g[min(static_cast<int>(threadIdx.x), max(n_sel - 1, 0))];
+        n_items = union_slice(psel_g, pre0, n_sel, sg.pages, D.k >= sg.pages,
                               first, cp, s_bm, s_wsum, s_pg,
                               chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
                               dbg_cap, D.k, MASK ? s_rmask : nullptr);
