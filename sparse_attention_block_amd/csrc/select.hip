@@ -647,19 +647,34 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         // candidates appended to the pending list, whose exact chains are taken
         // 64 at a time.  The first batch uses the upper ends requested above;
         // later ones load theirs (so the first set is dead after its batch).
+        // the threshold as a float: ord_key preserves the order of floats (-0
+        // and +0 alike), so ord_key(x) >= lam is x >= lamf; key 0 (every page
+        // qualifies) is below every finite value
+        const float lamf = lam == 0u ? -__builtin_huge_valf() : ord_to_f32(lam);
         auto batch = [&](int base, const float4 (&hv)[16]) {
             // bit 4*jj + e4 of cmask: page base + 256*jj + 4*lane + e4 is a candidate
-            uint64_t cmask = 0ull;
+            // (pages past the sequence only in a partial batch: uniform branch)
+            uint32_t cm[2] = {0u, 0u};
             const int lim = sg.pages - base - 4 * lane;
+            if (sg.pages - base >= 4096) {
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const float hx[4] = {hv[jj].x, hv[jj].y, hv[jj].z, hv[jj].w};
+                for (int jj = 0; jj < 16; ++jj) {
+                    const float hx[4] = {hv[jj].x, hv[jj].y, hv[jj].z, hv[jj].w};
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const bool c = (256 * jj + e4 < lim) & (ord_key(hx[e4]) >= lam);
-                    cmask |= static_cast<uint64_t>(c) << (4 * jj + e4);
+                    for (int e4 = 0; e4 < 4; ++e4)
+                        cm[jj >> 3] |= static_cast<uint32_t>(hx[e4] >= lamf) << ((4 * jj + e4) & 31);
+                }
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                    const float hx[4] = {hv[jj].x, hv[jj].y, hv[jj].z, hv[jj].w};
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4)
+                        cm[jj >> 3] |= static_cast<uint32_t>((256 * jj + e4 < lim) & (hx[e4] >= lamf))
+                                       << ((4 * jj + e4) & 31);
                 }
             }
+            uint64_t cmask = (static_cast<uint64_t>(cm[1]) << 32) | cm[0];
             const bool last_batch = base + 4096 >= sg.pages;
             // append each lane's candidates, lowest bit first, while any lane has some
             for (;;) {
