@@ -91,7 +91,8 @@ template <int DIM>
 __device__ __forceinline__ void bound_rowtile(const Dims &D, int rt, const uint4 (&aop)[DIM / 16],
                                               const float (&qa)[4], const uint4 (&bop)[DIM / 16][4],
                                               const float (&amax)[4], const int (&pl)[4], int pages,
-                                              int bx, int l16, int lg, float *hb, float *tm) {
+                                              int bx, int l16, int lg, float *hb, float *tm,
+                                              bool tile_full) {
     constexpr int KS = DIM / 16;
     const int R = D.R;
     float4_t acc[4];
@@ -105,6 +106,26 @@ __device__ __forceinline__ void bound_rowtile(const Dims &D, int rt, const uint4
                 __builtin_bit_cast(bf16x8_t, aop[kk]), __builtin_bit_cast(bf16x8_t, bop[kk][cb]),
                 acc[cb], 0, 0, 0);
     // lane holds rows rt*16 + 4*lg + j of pages cb*16 + l16
+    if (tile_full && (rt + 1) * 16 <= R) {
+        // every page of the tile and every row of the tile is live (uniform):
+        // no per-element guards; the row's maximum lower end as a float, then
+        // its order key (order keys are monotone, -0 and +0 alike)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rt * 16 + 4 * lg + j;
+            float lm = -__builtin_huge_valf();
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const float e = kBoundRel * qa[j] * amax[cb] + kBoundAbs;
+                const float u = acc[cb][j];
+                hb[(size_t)r * D.hb_stride + pl[cb]] = u + e;
+                lm = fmaxf(lm, u - e);
+            }
+            const uint32_t lmax = row16_max_u32(ord_key(lm));
+            if (l16 == 15) tm[(size_t)r * D.n_tiles_grid + bx] = ord_to_f32(lmax);
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = rt * 16 + 4 * lg + j;
@@ -143,6 +164,7 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
     const int n_t = static_cast<int>((sg.gp0 + sg.pages - 1) / kTile - tile0 + 1);
     if (bx >= n_t) return;
     const int64_t tile = tile0 + bx;
+    const bool tile_full = tile * kTile >= sg.gp0 && tile * kTile + kTile <= sg.gp0 + sg.pages;
     const int R = D.R, R1 = R > 0 ? R : 1;
     const float *aux = reinterpret_cast<const float *>(reinterpret_cast<const char *>(meta) +
                                                        D.meta_main_bytes) +
@@ -195,7 +217,8 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) acur[kk] = aop[kk];
             if (rt + 1 < n_rt) load_rows(rt + 1);  // in flight during this tile's epilogue
-            bound_rowtile<DIM>(D, rt, acur, qcur, bop, amax, pl, sg.pages, bx, l16, lg, hb, tm);
+            bound_rowtile<DIM>(D, rt, acur, qcur, bop, amax, pl, sg.pages, bx, l16, lg, hb, tm,
+                               tile_full);
         }
     } else {
         // fp32 storage: lane = page, any summation order (the interval absorbs it)
@@ -299,6 +322,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     // uses it, so that no load sits in a branch
     const int64_t tile =
         min(tile0 + max(0, min(bx, n_t - 1)), static_cast<int64_t>(D.n_tiles_total - 1));
+    const bool tile_full = tile * kTile >= sg.gp0 && tile * kTile + kTile <= sg.gp0 + sg.pages;
     const int R1 = R > 0 ? R : 1;
     const int l16 = lane & 15, lg = lane >> 4;
     const uint4 *mt = meta + (size_t)(g * D.n_tiles_total + tile) * NCH * kTile;
@@ -405,22 +429,34 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
                 dbg_loc[((size_t)s * Hq + g * G + tid / B) * B + tid % B] = acc / static_cast<float>(DIM);
         }
         __syncthreads();
+        // rank inside the row's head (score desc, token asc); the |A| best are
+        // active, listed in ascending token order
+        const int j = tid / B, t = tid % B;
+        bool sel = false;
         if (tid < GB) {
-            const int j = tid / B, t = tid % B;
             const float et = e_s[tid];
             int rank = 0;
-#pragma unroll 8
+#pragma unroll 16
             for (int u = 0; u < B; ++u) {
                 const float eu = e_s[j * B + u];
                 rank += (eu > et) || (eu == et && u < t);
             }
-            sel_s[tid] = rank < A;
+            sel = rank < A;
         }
-        __syncthreads();
-        if (tid < GB && sel_s[tid]) {
-            const int j = tid / B, t = tid % B;
-            int pos = 0;
-            for (int u = 0; u < t; ++u) pos += sel_s[j * B + u];
+        int pos = 0;
+        if (64 % B == 0) {
+            // a head's B rows are B consecutive lanes of one wave: the position
+            // is the count of selected lanes of the head below this one
+            const uint64_t bal = __ballot(sel);
+            const uint64_t below = (1ull << lane) - 1ull, before_head = (1ull << (lane - t)) - 1ull;
+            pos = __popcll(bal & below & ~before_head);
+        } else {
+            if (tid < GB) sel_s[tid] = sel;
+            __syncthreads();
+            if (sel)
+                for (int u = 0; u < t; ++u) pos += sel_s[j * B + u];
+        }
+        if (sel) {
             act_s[j * A + pos] = t;
             rbase_s[j * A + pos] = tid * RWP;
             if (writer) {
@@ -487,7 +523,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         float qa[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) qa[j] = qabs_s[min(rt * 16 + 4 * lg + j, R1 - 1)];
-        bound_rowtile<DIM>(D, rt, aop, qa, bop, amax, pl, sg.pages, bx, l16, lg, hb, tm);
+        bound_rowtile<DIM>(D, rt, aop, qa, bop, amax, pl, sg.pages, bx, l16, lg, hb, tm, tile_full);
     }
 }
 
