@@ -1,21 +1,28 @@
-// Finishing kernel, one workgroup per (sequence, query head, group of block
-// tokens):
-//  * active rows (every row on a dense first step): combine the prefix
-//    workgroups' partial statistics in chunk order into (o_p, L_p) and
-//    overwrite the cache entry -- "updated statistics are stored for the next
-//    step" (gist.science pt summary, "3. Metodologia", step 4);
-//  * stable rows: read the cached (o_p, L_p) unchanged (pt step 2);
+// Finishing kernels.
+//
+// k_finish (dense first step), one workgroup per (sequence, query head, group
+// of block tokens), one thread per output element:
+//  * every row: combine the prefix workgroups' partial statistics in chunk
+//    order into (o_p, L_p) and overwrite the cache entry -- updated statistics
+//    are kept for the next step (gist.science pt summary, "3. Metodologia",
+//    step 4);
 //  * dense attention of the tokens over the B in-block keys/values, giving
 //    (o_s, L_s) (agifrontier tutorial, workflow section: the block is short
 //    and attended densely);
 //  * the online-softmax merge L = log(e^L_p + e^L_s),
 //    out = e^(L_p-L) o_p + e^(L_s-L) o_s, rounded to the storage type.
-// One thread per output element.  The reads that depend on no other read
-// (block keys and values, queries, the active list, the union size, the
-// cached statistics) are requested together; a token's prefix partials are
-// requested next, in batches of 32 chunks, and the first batch is in flight
-// while the block scores are computed.  All arithmetic is fp32; scores and
-// log-normalisers are in log2 units inside.
+// The reads that depend on no other read (block keys and values, queries, the
+// cached statistics) are requested together with the first batch of a token's
+// prefix partials, which is in flight while the block scores are computed.
+//
+// k_finish_active (sparse step), one workgroup per active row (sequence, query
+// head, active slot), one thread per dimension: the row's partials in chunk
+// order, its cache entry, and the merge with the row's (o_s, L_s) from the
+// in-block attention that ran beside the selection.  Stable rows were finished
+// there.  The row's partials are requested at once, chunk indexes clamped
+// into the buffer and those past the union masked, so that no read waits for
+// another.  All arithmetic is fp32; scores and log-normalisers are in log2
+// units inside.
 #include "losa_internal.h"
 
 namespace losa {
@@ -57,17 +64,29 @@ struct PartAcc {
     }
 };
 
-template <typename T, int DIM, bool DENSE>
+// online-softmax merge of a prefix part (o_p, L_p) and a block part (o_s, L_s),
+// log-normalisers in log2 units; a prefix part with L_p = -inf is empty
+__device__ __forceinline__ float merge_parts(float op, float lp2, float os, float ls2) {
+    if (lp2 == -__builtin_huge_valf()) return os;
+    const float M = fmaxf(lp2, ls2);
+    const float ep = __builtin_amdgcn_exp2f(lp2 - M), es = __builtin_amdgcn_exp2f(ls2 - M);
+    return (ep * op + es * os) / (ep + es);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(T *o, float v) {
+    if constexpr (sizeof(T) == 2) *reinterpret_cast<uint16_t *>(o) = f32_to_bf16(v);
+    else *reinterpret_cast<float *>(o) = v;
+}
+
+template <typename T, int DIM>
 __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     Dims D, int TG, const T *__restrict__ q_t, const T *__restrict__ k_blk,
     const T *__restrict__ v_blk, const int32_t *__restrict__ kv_off,
-    const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ union_cnt, const float *__restrict__ part_ml,
+    const int32_t *__restrict__ prefix_len, const float *__restrict__ part_ml,
     const float *__restrict__ part_acc, float *__restrict__ op_cache,
     float *__restrict__ lp_cache, T *__restrict__ out) {
-    constexpr bool dense = DENSE;
     constexpr float kLn2 = 0.69314718055994530942f;
-    constexpr float kLog2e = 1.44269504088896340736f;
     extern __shared__ float sm[];
     const int B = D.B, G = D.G;
     const int t0 = blockIdx.x * TG, h = blockIdx.y, s = blockIdx.z;
@@ -78,29 +97,22 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     const int t = tid / DIM, x = tid % DIM;  // this thread's output element
     const bool live = t < nt;
     const int tok = t0 + t;
-    const int nch = dense ? D.n_chunks_dense : D.n_chunks_sparse;
-    const int rows = dense ? D.Rd : D.R;
-    // prefix rows: stacked row row0 + rho; on the dense step row rho is token
-    // t0 + rho, on a sparse step active slot rho of head h
-    const int row0 = dense ? j * B + t0 : j * D.A;
+    const int nch = D.n_chunks_dense;
+    const int rows = D.Rd;
+    const int row0 = j * B + t0;  // the prefix row of token t0 + t is row0 + t
 
-    // LDS: at most 64*129 + 4*128 + 4*64 + 4 + 64 words + 64*DIM bf16 (< 49 KiB)
+    // LDS: at most 64*129 + 4*128 + 4*64 + 4 words + 64*DIM bf16 (< 49 KiB)
     constexpr bool BF = sizeof(T) == 2;
     float *kb = sm;                        // [B][DIM + 1]
     float *qs = kb + B * (DIM + 1);        // [TG][DIM]
     float *ps = qs + TG * DIM;             // [TG][B] scores, then softmax weights
     float *ls2 = ps + TG * B;              // [TG] L_s (log2 units)
-    int *act = reinterpret_cast<int *>(ls2 + TG);  // [A] token of each active slot (sparse)
-    const int vb_words = (B * (DIM + 1) + TG * DIM + TG * B + TG + (D.A > 0 ? D.A : 1) + 3) & ~3;
+    const int vb_words = (B * (DIM + 1) + TG * DIM + TG * B + TG + 3) & ~3;
     uint16_t *vb = reinterpret_cast<uint16_t *>(sm + vb_words);  // [B][DIM] (bf16), 16-byte aligned
 
     // -- 1. every read that depends on no other read ---------------------------
-    int nchu;  // prefix chunks that wrote partials
-    {
-        const int cp = dense ? D.dense_chunk : D.sparse_chunk;
-        const int n_items = dense ? seq_geom(D, kv_off, prefix_len, s).pages : union_cnt[sgi];
-        nchu = (n_items + cp - 1) / cp;
-    }
+    // prefix chunks that wrote partials
+    const int nchu = (seq_geom(D, kv_off, prefix_len, s).pages + D.dense_chunk - 1) / D.dense_chunk;
     // Block keys (and values, bf16) and the queries as 16-byte vectors, every
     // address clamped into its tensor so that no load is conditional: all of
     // them are in flight before the first is used.
@@ -119,7 +131,6 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     const int qi = min(tid, nq - 1);
     const uint4 qv4 = *reinterpret_cast<const uint4 *>(
         q_t + ((size_t)(s * B + t0 + qi * EV / DIM) * D.Hq + h) * DIM + (qi * EV) % DIM);
-    const int av_ = dense || D.A == 0 ? 0 : active[((size_t)s * D.Hq + h) * D.A + min(tid, D.A - 1)];
     // fp32 storage: this thread's column of the block values, from global memory
     const T *vcol = v_blk + ((size_t)s * B * D.Hk + g) * DIM + x;
     const size_t vs = (size_t)D.Hk * DIM;
@@ -129,11 +140,6 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
         for (int u = 0; u < kVReg; ++u) vr[u] = ldv(vcol, min(u, B - 1) * vs);
     }
     const size_t crow = ((size_t)s * D.Hq + h) * B + tok;
-    // cached statistics of the token (used if its row is stable); clamped row
-    const size_t crow_c = ((size_t)s * D.Hq + h) * B + min(tok, B - 1);
-    const float opc = op_cache[crow_c * DIM + x];
-    const float lpc = lp_cache[crow_c];
-    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
     auto unpack = [](const uint4 &w, float *f) {
         if constexpr (BF) {
             const uint32_t a[4] = {w.x, w.y, w.z, w.w};
@@ -168,20 +174,11 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
 #pragma unroll
         for (int e = 0; e < EV; ++e) qs[qi * EV + e] = f[e];
     }
-    if (!dense && D.A > 0) act[min(tid, D.A - 1)] = av_;
     __syncthreads();
 
     // -- 2. this token's prefix row; its first batch of partials is requested
     //       before the block scores are computed -------------------------------
-    int rho = -1;
-    if (live) {
-        if (dense) {
-            rho = t;
-        } else {
-            for (int a = 0; a < D.A; ++a)
-                if (act[a] == tok) rho = a;
-        }
-    }
+    const int rho = live ? t : -1;
     const size_t pr0 = (size_t)sgi * nch * rows + row0 + (rho < 0 ? 0 : rho);
     const float *mlp = part_ml + pr0 * 2;
     const float *acp = part_acc + pr0 * DIM + x;
@@ -258,45 +255,82 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
             if (u < B) os = fmaf(ps[t * B + u], vr[u], os);
         for (int u = kVReg; u < B; ++u) os = fmaf(ps[t * B + u], ldv(vcol, u * vs), os);
     }
-    float op, lp2;
-    if (rho >= 0) {
-        PartAcc pa;
-        pa.add(mv, lv, av, n0);
-        for (int c0 = kPartBatch; c0 < nchu; c0 += kPartBatch) {
-            load_parts(c0);
-            pa.add(mv, lv, av, min(kPartBatch, nchu - c0));
-        }
-        if (nchu > 0) {
-            op = pa.oa / pa.ls;
-            lp2 = pa.mx + __log2f(pa.ls);
-        } else {
-            op = 0.0f;
-            lp2 = -__builtin_huge_valf();
-        }
-        if (!(D.flags & LOSA_FLAG_NO_WRITEBACK)) {  // the caches keep the dense statistics
-            op_cache[crow * DIM + x] = op;
-            if (x == 0) lp_cache[crow] = lp2 * kLn2;
-        }
-    } else {
-        op = opc;
-        lp2 = lpc * kLog2e;
+    // the row's prefix statistics, in chunk order; they overwrite the cache
+    PartAcc pa;
+    pa.add(mv, lv, av, n0);
+    for (int c0 = kPartBatch; c0 < nchu; c0 += kPartBatch) {
+        load_parts(c0);
+        pa.add(mv, lv, av, min(kPartBatch, nchu - c0));
     }
-    float v;
-    if (lp2 == -__builtin_huge_valf()) {
-        v = os;
-    } else {
-        const float M = fmaxf(lp2, ls2[t]);
-        const float ep = __builtin_amdgcn_exp2f(lp2 - M), es = __builtin_amdgcn_exp2f(ls2[t] - M);
-        v = (ep * op + es * os) / (ep + es);
+    float op = 0.0f, lp2 = -__builtin_huge_valf();
+    if (nchu > 0) {
+        op = pa.oa / pa.ls;
+        lp2 = pa.mx + __log2f(pa.ls);
+    }
+    op_cache[crow * DIM + x] = op;
+    if (x == 0) lp_cache[crow] = lp2 * kLn2;
+    T *o = out + ((size_t)(s * B + tok) * D.Hq + h) * DIM + x;
+    store_out(o, merge_parts(op, lp2, os, ls2[t]));
+}
+
+template <typename T, int DIM>
+__global__ __launch_bounds__(DIM) void k_finish_active(
+    Dims D, const int32_t *__restrict__ active, const int32_t *__restrict__ union_cnt,
+    const float *__restrict__ part_ml, const float *__restrict__ part_acc,
+    const float *__restrict__ blk_o, const float *__restrict__ blk_l, float *__restrict__ op_cache,
+    float *__restrict__ lp_cache, T *__restrict__ out) {
+    constexpr float kLn2 = 0.69314718055994530942f;
+    const int a = blockIdx.x, h = blockIdx.y, s = blockIdx.z, x = threadIdx.x;
+    const int A = D.A, B = D.B, g = h / D.G, j = h % D.G;
+    const int sgi = s * D.Hk + g;
+    const int nch = D.n_chunks_sparse, rows = D.R;
+    const size_t ar = ((size_t)s * D.Hq + h) * A + a;
+    // every read at once: the row's token, the union size, its block part and
+    // its partials (chunk indexes clamped into the buffer)
+    const int tok = active[ar];
+    const int ucnt = union_cnt[sgi];
+    const float os = blk_o[ar * DIM + x], ls2 = blk_l[ar];
+    const size_t pr0 = (size_t)sgi * nch * rows + j * A + a;
+    const float *mlp = part_ml + pr0 * 2;
+    const float *acp = part_acc + pr0 * DIM + x;
+    const int cs = rows * 2, as = rows * DIM;  // chunk strides (elements)
+    float mv[kPartBatch], lv[kPartBatch], av[kPartBatch];
+    auto load_parts = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < kPartBatch; ++i) {
+            const int c = min(c0 + i, nch - 1);
+            const float2 v = *reinterpret_cast<const float2 *>(mlp + c * cs);
+            mv[i] = v.x;
+            lv[i] = v.y;
+            av[i] = acp[c * as];
+        }
+    };
+    load_parts(0);
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
+    const int nchu = (ucnt + D.sparse_chunk - 1) / D.sparse_chunk;  // chunks that wrote partials
+    PartAcc pa;
+    pa.add(mv, lv, av, min(nchu, kPartBatch));
+    for (int c0 = kPartBatch; c0 < nchu; c0 += kPartBatch) {
+        load_parts(c0);
+        pa.add(mv, lv, av, min(kPartBatch, nchu - c0));
+    }
+    float op = 0.0f, lp2 = -__builtin_huge_valf();
+    if (nchu > 0) {
+        op = pa.oa / pa.ls;
+        lp2 = pa.mx + __log2f(pa.ls);
+    }
+    const size_t crow = ((size_t)s * D.Hq + h) * B + tok;
+    if (!(D.flags & LOSA_FLAG_NO_WRITEBACK)) {  // else the caches keep the dense statistics
+        op_cache[crow * DIM + x] = op;
+        if (x == 0) lp_cache[crow] = lp2 * kLn2;
     }
     T *o = out + ((size_t)(s * B + tok) * D.Hq + h) * DIM + x;
-    if constexpr (sizeof(T) == 2) *reinterpret_cast<uint16_t *>(o) = f32_to_bf16(v);
-    else *reinterpret_cast<float *>(o) = v;
+    store_out(o, merge_parts(op, lp2, os, ls2));
 }
 
 size_t finish_lds_bytes(const Dims &D, int TG) {
-    const size_t words = ((size_t)D.B * (D.d + 1) + (size_t)TG * D.d + (size_t)TG * D.B + TG +
-                          (size_t)(D.A > 0 ? D.A : 1) + 3) & ~(size_t)3;
+    const size_t words = ((size_t)D.B * (D.d + 1) + (size_t)TG * D.d + (size_t)TG * D.B + TG + 3) &
+                         ~(size_t)3;
     return words * 4 + (D.bf16 ? (size_t)D.B * D.d * 2 : 0);
 }
 
@@ -308,33 +342,45 @@ int finish_group(const Dims &D) {
     return D.B < tg ? D.B : tg;
 }
 
-hipError_t launch_finish(const Dims &D, bool dense, const void *q_t, const void *k_blk,
-                         const void *v_blk, const int32_t *kv_off, const int32_t *prefix_len,
-                         const Work &W, float *op_cache, float *lp_cache, void *out,
-                         hipStream_t st) {
+hipError_t launch_finish(const Dims &D, const void *q_t, const void *k_blk, const void *v_blk,
+                         const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
+                         float *op_cache, float *lp_cache, void *out, hipStream_t st) {
     const int TG = finish_group(D);
     dim3 grid((D.B + TG - 1) / TG, D.Hq, D.S);
     const size_t lds = finish_lds_bytes(D, TG);
     const int threads = TG * D.d;
-#define LAUNCH_F(T, DIMV, DN)                                                                     \
-    hipLaunchKernelGGL((k_finish<T, DIMV, DN>), grid, dim3(threads), lds, st, D, TG,             \
+#define LAUNCH_F(T, DIMV)                                                                         \
+    hipLaunchKernelGGL((k_finish<T, DIMV>), grid, dim3(threads), lds, st, D, TG,                 \
                        static_cast<const T *>(q_t), static_cast<const T *>(k_blk),               \
-                       static_cast<const T *>(v_blk), kv_off, prefix_len, W.active, W.union_cnt, \
-                       W.part_ml, W.part_acc, op_cache, lp_cache, static_cast<T *>(out))
-#define PICK_F(T, DIMV)                          \
-    do {                                         \
-        if (dense) LAUNCH_F(T, DIMV, true);      \
-        else LAUNCH_F(T, DIMV, false);           \
-    } while (0)
+                       static_cast<const T *>(v_blk), kv_off, prefix_len, W.part_ml, W.part_acc, \
+                       op_cache, lp_cache, static_cast<T *>(out))
     if (D.bf16) {
-        if (D.d == 128) PICK_F(uint16_t, 128);
-        else PICK_F(uint16_t, 64);
+        if (D.d == 128) LAUNCH_F(uint16_t, 128);
+        else LAUNCH_F(uint16_t, 64);
     } else {
-        if (D.d == 128) PICK_F(float, 128);
-        else PICK_F(float, 64);
+        if (D.d == 128) LAUNCH_F(float, 128);
+        else LAUNCH_F(float, 64);
     }
-#undef PICK_F
 #undef LAUNCH_F
+    return hipGetLastError();
+}
+
+hipError_t launch_finish_active(const Dims &D, const Work &W, float *op_cache, float *lp_cache,
+                                void *out, hipStream_t st) {
+    if (D.A == 0) return hipSuccess;
+    const dim3 grid(D.A, D.Hq, D.S);
+#define LAUNCH_A(T, DIMV)                                                                        \
+    hipLaunchKernelGGL((k_finish_active<T, DIMV>), grid, dim3(DIMV), 0, st, D, W.active,         \
+                       W.union_cnt, W.part_ml, W.part_acc, W.blk_o, W.blk_l, op_cache, lp_cache, \
+                       static_cast<T *>(out))
+    if (D.bf16) {
+        if (D.d == 128) LAUNCH_A(uint16_t, 128);
+        else LAUNCH_A(uint16_t, 64);
+    } else {
+        if (D.d == 128) LAUNCH_A(float, 128);
+        else LAUNCH_A(float, 64);
+    }
+#undef LAUNCH_A
     return hipGetLastError();
 }
 

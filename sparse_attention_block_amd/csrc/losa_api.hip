@@ -125,6 +125,8 @@ size_t carve(const Dims &D, char *base, Work *W) {
     w.part_ml = reinterpret_cast<float *>(take(SG * part_rows * 2 * 4));
     w.shloc = reinterpret_cast<float *>(
         take(D.flags & LOSA_FLAG_SHARED_ACTIVE ? (size_t)D.S * D.Hq * D.B * 4 : 0));
+    w.blk_o = reinterpret_cast<float *>(take((size_t)D.S * D.Hq * A1 * D.d * 4));
+    w.blk_l = reinterpret_cast<float *>(take((size_t)D.S * D.Hq * A1 * 4));
     if (W) *W = w;
     return off;
 }
@@ -228,8 +230,7 @@ int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *
         e = launch_prefix(D, true, k_cache, v_cache, kv_off, prefix_len, W, nullptr, nullptr, 0, s);
     if (e == hipSuccess) e = mark(ev, 4, s);
     if (e == hipSuccess)
-        e = launch_finish(D, true, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache,
-                          out, s);
+        e = launch_finish(D, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache, out, s);
     if (e == hipSuccess) e = mark(ev, 5, s);
     return hip_status(e);
 }
@@ -282,16 +283,16 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
         if (D.R > 0 && e == hipSuccess) e = launch_score(D, page_meta, kv_off, prefix_len, W, s);
     }
     if (e == hipSuccess) e = mark(ev, 2, s);
-    if (D.R > 0 && e == hipSuccess)
-        e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, s);
+    // selection (active rows) and the in-block attention of every token
+    const BlockArgs blk{q_t, k_blk, v_blk, op_cache, lp_cache, out};
+    if (e == hipSuccess)
+        e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, blk, s);
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (D.R > 0 && e == hipSuccess)
         e = launch_prefix(D, false, k_cache, v_cache, kv_off, prefix_len, W, dbg.union_idx,
                           dbg.union_cnt, dbg.union_cap, s);
     if (e == hipSuccess) e = mark(ev, 4, s);
-    if (e == hipSuccess)
-        e = launch_finish(D, false, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache,
-                          out, s);
+    if (D.R > 0 && e == hipSuccess) e = launch_finish_active(D, W, op_cache, lp_cache, out, s);
     if (e == hipSuccess) e = mark(ev, 5, s);
     return hip_status(e);
 }

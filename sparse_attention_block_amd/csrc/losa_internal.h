@@ -65,6 +65,8 @@ struct Work {
     float *part_acc;     // [S][Hk][n_chunks][rows][d]
     float *part_ml;      // [S][Hk][n_chunks][rows][2] (running max in log2 units, sum)
     float *shloc;        // [S][Hq][B] per-head locality / d (shared active set only)
+    float *blk_o;        // [S][Hq][max(A,1)][d] in-block attention output of each active row
+    float *blk_l;        // [S][Hq][max(A,1)] its log-normaliser (log2 units)
 };
 
 // Launchers (one per translation unit); each returns the hipGetLastError code.
@@ -86,9 +88,17 @@ bool score_prep_fits(const Dims &D);
 hipError_t launch_score_prep(const Dims &D, const void *q_t, const void *q_prev, const void *meta,
                              const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
                              float *dbg_loc, int32_t *dbg_act, int32_t *dbg_ucnt, hipStream_t st);
+// The step's in-block attention runs in extra one-wave workgroups of the
+// selection launch (they need no selection result): stable tokens' outputs are
+// final there, active tokens' (o_s, L_s) go to the workspace.
+struct BlockArgs {
+    const void *q_t, *k_blk, *v_blk;
+    const float *op_cache, *lp_cache;
+    void *out;
+};
 hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
                          const int32_t *prefix_len, const Work &W, int32_t *dbg_page_sel,
-                         hipStream_t st);
+                         const BlockArgs &blk, hipStream_t st);
 size_t select_lds_bytes(const Dims &D);  // dynamic LDS of the exact-selection kernel
 // Sparse step: the union of the rows' pages is built here (the dbg_union_*
 // outputs are optional).
@@ -96,10 +106,13 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const v
                          const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
                          int32_t *dbg_union_idx, int32_t *dbg_union_cnt, int dbg_union_cap,
                          hipStream_t st);
-hipError_t launch_finish(const Dims &D, bool dense, const void *q_t, const void *k_blk,
-                         const void *v_blk, const int32_t *kv_off, const int32_t *prefix_len,
-                         const Work &W, float *op_cache, float *lp_cache, void *out,
-                         hipStream_t st);
+// Dense first step: every row's prefix partials, the block attention and the merge.
+hipError_t launch_finish(const Dims &D, const void *q_t, const void *k_blk, const void *v_blk,
+                         const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
+                         float *op_cache, float *lp_cache, void *out, hipStream_t st);
+// Sparse step: the active rows' prefix partials merged with their block part.
+hipError_t launch_finish_active(const Dims &D, const Work &W, float *op_cache, float *lp_cache,
+                                void *out, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Device helpers.

@@ -28,6 +28,10 @@
 // q- * min, one of them an exact zero and the products exact for bf16 -- and
 // the exact top-k is taken on keys (score bits, page).  Each row's pages go to
 // the workspace; the prefix kernel builds their union.
+#include <algorithm>
+#include <type_traits>
+
+#include "block_attn.h"
 #include "losa_internal.h"
 
 namespace losa {
@@ -593,9 +597,24 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                                                const void *__restrict__ qrows,
                                                const float *__restrict__ qsel32,
                                                const float *__restrict__ hbound,
-                                               const float *__restrict__ tmax, SelectDbg dbg) {
+                                               const float *__restrict__ tmax, SelectDbg dbg,
+                                               BlockArgs blk) {
     extern __shared__ uint32_t smem[];
     const int ng = D.S * D.Hk;
+    if (blockIdx.x >= ng * D.R) {
+        // one token's in-block attention: workgroup ng*R + (s*Hq + h)*B + t
+        using T = typename std::conditional<BF, uint16_t, float>::type;
+        const int b = blockIdx.x - ng * D.R;
+        const int t = b % D.B, h = (b / D.B) % D.Hq, s = b / (D.B * D.Hq);
+        const T *q = static_cast<const T *>(blk.q_t), *kb = static_cast<const T *>(blk.k_blk),
+                *vb = static_cast<const T *>(blk.v_blk);
+        T *o = static_cast<T *>(blk.out);
+        if (D.B <= 16)
+            block_token<T, DIM, 16>(D, q, kb, vb, W, blk.op_cache, blk.lp_cache, o, smem, s, h, t);
+        else
+            block_token<T, DIM, 64>(D, q, kb, vb, W, blk.op_cache, blk.lp_cache, o, smem, s, h, t);
+        return;
+    }
     const int sgi = blockIdx.x % ng;
     const int r = blockIdx.x / ng;
     const int s = sgi / D.Hk, g = sgi % D.Hk;
@@ -844,14 +863,16 @@ hipError_t launch_score_prep(const Dims &D, const void *q_t, const void *q_prev,
 
 hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
                          const int32_t *prefix_len, const Work &W, int32_t *dbg_page_sel,
-                         hipStream_t st) {
+                         const BlockArgs &blk, hipStream_t st) {
     const int ng = D.S * D.Hk;
-    const size_t lds = select_lds_bytes(D);
+    const size_t blk_lds = D.B <= 16 ? block_lds_bytes<16>(D.d, D.bf16) : block_lds_bytes<64>(D.d, D.bf16);
+    const size_t lds = std::max(D.R > 0 ? select_lds_bytes(D) : 0, blk_lds);
+    const dim3 grid(ng * D.R + D.S * D.Hq * D.B);  // selection rows, then block tokens
     SelectDbg dbg{dbg_page_sel};
     auto *m = static_cast<const uint4 *>(meta);
 #define LAUNCH_S(DIMV, BFV)                                                                      \
-    hipLaunchKernelGGL((k_select<DIMV, BFV>), dim3(ng * D.R), dim3(64), lds, st, D, m, kv_off,   \
-                       prefix_len, W, W.qrows, W.qsel32, W.hbound, W.tmax, dbg)
+    hipLaunchKernelGGL((k_select<DIMV, BFV>), grid, dim3(64), lds, st, D, m, kv_off,             \
+                       prefix_len, W, W.qrows, W.qsel32, W.hbound, W.tmax, dbg, blk)
     if (D.bf16) {
         if (D.d == 128) LAUNCH_S(128, true);
         else LAUNCH_S(64, true);
