@@ -20,14 +20,17 @@
 // units of 2^-24 relative to sum|q_i * k_i| <= sum|q| * max|k|).  The upper
 // ends go to the workspace, with the largest lower end of every tile.
 //
-// Phase 2 (k_select), one workgroup per (sequence, KV head), one wave per row:
-// the k-th largest tile maximum of the lower ends is at most the k-th largest
-// exact bound, so every page of the exact top-k has an upper end at or above
-// it; those candidate pages (typically a little more than k) get the exact
-// fp32 chain -- two IEEE fused multiply-adds per dimension, q+ * max then
-// q- * min, one of them an exact zero and the products exact for bf16 -- and
-// the exact top-k is taken on keys (score bits, page).  Each row's pages go to
-// the workspace; the prefix kernel builds their union.
+// Phase 2 (k_select), one one-wave workgroup per (sequence, KV head, active
+// row): the k-th largest tile maximum of the lower ends is at most the k-th
+// largest exact bound, so every page of the exact top-k has an upper end at or
+// above it; those candidate pages (typically a little more than k) get the
+// exact fp32 chain -- one IEEE fused multiply-add per dimension with max_i or
+// min_i chosen by the sign of q_i, the same value as the pair q+ * max then
+// q- * min (one of them an exact zero, the products exact for bf16) -- and the
+// exact top-k is taken on keys (score bits, page).  Each row's pages go to the
+// workspace; the prefix kernel builds their union.  The same launch carries
+// one more one-wave workgroup per (sequence, query head, block token) for the
+// step's in-block attention (block_attn.h), which needs no selection result.
 #include <algorithm>
 #include <type_traits>
 
