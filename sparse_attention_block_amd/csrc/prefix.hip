@@ -78,7 +78,8 @@ constexpr float kLazyRescale = 8.0f;
 
 // NP pages of 16 tokens for the wave's row tiles i (those with rt_ok[i]):
 // S^T = K.Q^T with v_mfma_f32_16x16x32_bf16, online softmax in log2 units over
-// the NP pages together, then O^T += V^T.P with v_mfma_f32_16x16x16bf16_1k.
+// the NP pages together, then O^T += V^T.P: two pages per
+// v_mfma_f32_16x16x32_bf16 when NP is even, else v_mfma_f32_16x16x16bf16_1k.
 // kop[n]: the lane's K operand of page n (token l%16, dims 32*kk + 8*(l/16) ..
 // +7); vw[n]: V words of tokens 4*(l/16) + j for the lane's DPL dims; valid[n]:
 // tokens of page n inside the prefix (0 for no page).  P is rounded to bf16 for
@@ -165,6 +166,7 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
         }
         // (with masks a row may have seen no score yet: its weights are zero)
         const float mn = MASK && m_run[i] == -__builtin_huge_valf() ? 0.0f : m_run[i];
+        uint2 pw[NP];  // the lane's weights of page n (tokens 4*lg .. +3), bf16
 #pragma unroll
         for (int n = 0; n < NP; ++n) {
             const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][0] - mn)),
@@ -173,10 +175,30 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
                                   static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][3] - mn))};
             const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
             l_run[i] += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
-            const short4_t pop = __builtin_bit_cast(short4_t, make_uint2(w01, w23));
+            pw[n] = make_uint2(w01, w23);
+        }
+        if constexpr (NP % 2 == 0) {
+            // pages n and n+1 in one v_mfma_f32_16x16x32_bf16: its k index
+            // 8*lg + c stands for token 4*lg + c%4 of page n + c/4, in both
+            // operands (the sum over k does not depend on the order)
 #pragma unroll
-            for (int e = 0; e < DPL; ++e)
-                oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[n][e], pop, oacc[i][e], 0, 0, 0);
+            for (int n = 0; n < NP; n += 2) {
+                const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[n].x, pw[n].y, pw[n + 1].x, pw[n + 1].y));
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) {
+                    const uint2 v0 = __builtin_bit_cast(uint2, vop[n][e]), v1 = __builtin_bit_cast(uint2, vop[n + 1][e]);
+                    const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                    oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop, oacc[i][e], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NP; ++n) {
+                const short4_t pop = __builtin_bit_cast(short4_t, pw[n]);
+#pragma unroll
+                for (int e = 0; e < DPL; ++e)
+                    oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[n][e], pop, oacc[i][e], 0, 0, 0);
+            }
         }
     }
 }
