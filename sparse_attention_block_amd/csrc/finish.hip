@@ -280,9 +280,13 @@ __global__ __launch_bounds__(DIM) void k_finish_active(
     const float *__restrict__ blk_o, const float *__restrict__ blk_l, float *__restrict__ op_cache,
     float *__restrict__ lp_cache, T *__restrict__ out) {
     constexpr float kLn2 = 0.69314718055994530942f;
-    const int a = blockIdx.x, h = blockIdx.y, s = blockIdx.z, x = threadIdx.x;
-    const int A = D.A, B = D.B, g = h / D.G, j = h % D.G;
-    const int sgi = s * D.Hk + g;
+    // workgroup u * (S*Hk) + (s*Hk + g): consecutive workgroups go to the XCDs
+    // in turn, so a group's rows run on the XCD that ran its prefix workgroups
+    // (whose partials are still in that XCD's L2) whenever S*Hk is a multiple of 8
+    const int ng = D.S * D.Hk;
+    const int sgi = blockIdx.x % ng, u = blockIdx.x / ng;
+    const int A = D.A, B = D.B, j = u / A, a = u % A, x = threadIdx.x;
+    const int s = sgi / D.Hk, g = sgi % D.Hk, h = g * D.G + j;
     const int nch = D.n_chunks_sparse, rows = D.R;
     const size_t ar = ((size_t)s * D.Hq + h) * A + a;
     // every read at once: the row's token, the union size, its block part and
@@ -368,7 +372,7 @@ hipError_t launch_finish(const Dims &D, const void *q_t, const void *k_blk, cons
 hipError_t launch_finish_active(const Dims &D, const Work &W, float *op_cache, float *lp_cache,
                                 void *out, hipStream_t st) {
     if (D.A == 0) return hipSuccess;
-    const dim3 grid(D.A, D.Hq, D.S);
+    const dim3 grid(D.S * D.Hk * D.G * D.A);  // (row of the group, group)
 #define LAUNCH_A(T, DIMV)                                                                        \
     hipLaunchKernelGGL((k_finish_active<T, DIMV>), grid, dim3(DIMV), 0, st, D, W.active,         \
                        W.union_cnt, W.part_ml, W.part_acc, W.blk_o, W.blk_l, op_cache, lp_cache, \

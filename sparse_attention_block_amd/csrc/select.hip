@@ -605,10 +605,13 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
     extern __shared__ uint32_t smem[];
     const int ng = D.S * D.Hk;
     if (blockIdx.x >= ng * D.R) {
-        // one token's in-block attention: workgroup ng*R + (s*Hq + h)*B + t
+        // one token's in-block attention: workgroup ng*R + u*ng + (s*Hk + g) for
+        // token t = u % B of head g*G + u / B, so that a group's tokens run on
+        // the XCD of its selection and prefix workgroups (ng a multiple of 8)
         using T = typename std::conditional<BF, uint16_t, float>::type;
         const int b = blockIdx.x - ng * D.R;
-        const int t = b % D.B, h = (b / D.B) % D.Hq, s = b / (D.B * D.Hq);
+        const int sg2 = b % ng, u = b / ng;
+        const int t = u % D.B, s = sg2 / D.Hk, h = (sg2 % D.Hk) * D.G + u / D.B;
         const T *q = static_cast<const T *>(blk.q_t), *kb = static_cast<const T *>(blk.k_blk),
                 *vb = static_cast<const T *>(blk.v_blk);
         T *o = static_cast<T *>(blk.out);
