@@ -35,17 +35,19 @@ __device__ __forceinline__ float ldv(const T *p, size_t i) {
 
 constexpr int kFinishMaxThreads = 256;
 constexpr int kVReg = 16;    // block values per thread held in registers (the rest re-read)
+constexpr int kActBatch = 32;  // prefix chunks per batch in the active-row finish
 constexpr int kPartBatch = 30;  // prefix partials per thread requested together (60
                                 // loads: each wave keeps at most 63 in flight)
 
 // running combination of prefix partials (log2 units): max, sum, weighted output
+template <int N = kPartBatch>
 struct PartAcc {
     float mx = -__builtin_huge_valf(), ls = 0.0f, oa = 0.0f;
-    // entries i < n of m, l, a (arrays of kPartBatch)
+    // entries i < n of m, l, a (arrays of N)
     __device__ __forceinline__ void add(const float *m, const float *l, const float *a, int n) {
         float bm = -__builtin_huge_valf();
 #pragma unroll
-        for (int i = 0; i < kPartBatch; ++i)
+        for (int i = 0; i < N; ++i)
             if (i < n) bm = fmaxf(bm, m[i]);
         const float nm = fmaxf(mx, bm);
         if (nm == -__builtin_huge_valf()) return;
@@ -53,7 +55,7 @@ struct PartAcc {
         ls *= sc;
         oa *= sc;
 #pragma unroll
-        for (int i = 0; i < kPartBatch; ++i) {
+        for (int i = 0; i < N; ++i) {
             if (i < n) {
                 const float w = __builtin_amdgcn_exp2f(m[i] - nm);
                 ls = fmaf(w, l[i], ls);
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
         for (int u = kVReg; u < B; ++u) os = fmaf(ps[t * B + u], ldv(vcol, u * vs), os);
     }
     // the row's prefix statistics, in chunk order; they overwrite the cache
-    PartAcc pa;
+    PartAcc<> pa;
     pa.add(mv, lv, av, n0);
     for (int c0 = kPartBatch; c0 < nchu; c0 += kPartBatch) {
         load_parts(c0);
@@ -298,25 +300,39 @@ __global__ __launch_bounds__(DIM) void k_finish_active(
     const float *mlp = part_ml + pr0 * 2;
     const float *acp = part_acc + pr0 * DIM + x;
     const int cs = rows * 2, as = rows * DIM;  // chunk strides (elements)
-    float mv[kPartBatch], lv[kPartBatch], av[kPartBatch];
-    auto load_parts = [&](int c0) {
-#pragma unroll
-        for (int i = 0; i < kPartBatch; ++i) {
-            const int c = min(c0 + i, nch - 1);
-            const float2 v = *reinterpret_cast<const float2 *>(mlp + c * cs);
-            mv[i] = v.x;
-            lv[i] = v.y;
-            av[i] = acp[c * as];
-        }
+    // a batch of kActBatch chunks: (m, l) once per chunk (thread c of the
+    // batch, through LDS), this thread's dimension of each chunk's output
+    __shared__ float s_m[kActBatch], s_l[kActBatch];
+    float mv[kActBatch], lv[kActBatch], av[kActBatch];
+    auto load_ml = [&](int c0) {
+        return *reinterpret_cast<const float2 *>(mlp + min(c0 + min(x, kActBatch - 1), nch - 1) * cs);
     };
-    load_parts(0);
+    auto load_acc = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < kActBatch; ++i) av[i] = acp[min(c0 + i, nch - 1) * as];
+    };
+    float2 ml = load_ml(0);
+    load_acc(0);
     __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
     const int nchu = (ucnt + D.sparse_chunk - 1) / D.sparse_chunk;  // chunks that wrote partials
-    PartAcc pa;
-    pa.add(mv, lv, av, min(nchu, kPartBatch));
-    for (int c0 = kPartBatch; c0 < nchu; c0 += kPartBatch) {
-        load_parts(c0);
-        pa.add(mv, lv, av, min(kPartBatch, nchu - c0));
+    PartAcc<kActBatch> pa;
+    for (int c0 = 0; c0 < nchu; c0 += kActBatch) {
+        if (c0 > 0) {
+            ml = load_ml(c0);
+            load_acc(c0);
+            __syncthreads();  // the previous batch's (m, l) have been read
+        }
+        if (x < kActBatch) {
+            s_m[x] = ml.x;
+            s_l[x] = ml.y;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kActBatch; ++i) {
+            mv[i] = s_m[i];
+            lv[i] = s_l[i];
+        }
+        pa.add(mv, lv, av, min(kActBatch, nchu - c0));
     }
     float op = 0.0f, lp2 = -__builtin_huge_valf();
     if (nchu > 0) {
