@@ -36,15 +36,16 @@ __device__ __forceinline__ float ldv(const T *p, size_t i) {
 constexpr int kFinishMaxThreads = 256;
 constexpr int kVReg = 16;    // block values per thread held in registers (the rest re-read)
 constexpr int kActBatch = 32;  // prefix chunks per batch in the active-row finish
+constexpr int kDenseBatch = 64;  // first batch of prefix chunks in the dense finish
 constexpr int kPartBatch = 30;  // prefix partials per thread requested together (60
                                 // loads: each wave keeps at most 63 in flight)
 
 // running combination of prefix partials (log2 units): max, sum, weighted output
-template <int N = kPartBatch>
 struct PartAcc {
     float mx = -__builtin_huge_valf(), ls = 0.0f, oa = 0.0f;
-    // entries i < n of m, l, a (arrays of N)
-    __device__ __forceinline__ void add(const float *m, const float *l, const float *a, int n) {
+    // entries i < n of m, l, a
+    template <int N>
+    __device__ __forceinline__ void add(const float (&m)[N], const float (&l)[N], const float (&a)[N], int n) {
         float bm = -__builtin_huge_valf();
 #pragma unroll
         for (int i = 0; i < N; ++i)
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     float *__restrict__ lp_cache, T *__restrict__ out) {
     constexpr float kLn2 = 0.69314718055994530942f;
     extern __shared__ float sm[];
+    __shared__ float s_m0[kFinishMaxThreads / 64][kDenseBatch], s_l0[kFinishMaxThreads / 64][kDenseBatch];
     const int B = D.B, G = D.G;
     const int t0 = blockIdx.x * TG, h = blockIdx.y, s = blockIdx.z;
     const int nt = min(TG, B - t0);
@@ -187,21 +189,16 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     // chunk strides in elements: a row's partials span < 2^31 bytes (at most
     // 4096 chunks x 256 rows x DIM floats), so 32-bit offsets suffice
     const int cs = rows * 2, as = rows * DIM;
-    const int n0 = rho >= 0 ? min(nchu, kPartBatch) : 0;
-    float mv[kPartBatch], lv[kPartBatch], av[kPartBatch];
-    // rho is uniform over a wave (a wave holds one token); the chunk index is
-    // clamped so that no load is conditional, and entries past n0 are ignored
-    auto load_parts = [&](int c0) {
+    // The first kDenseBatch chunks: (m, l) of chunk x by thread x of the token
+    // (shared through LDS), this thread's dimension of each chunk's output; the
+    // chunk index is clamped so that no load is conditional, and entries past
+    // the chunk count are ignored.  Later chunks (long prefixes) are read in
+    // batches of kPartBatch.
+    const int clast = max(nchu - 1, 0);
+    const float2 ml0 = *reinterpret_cast<const float2 *>(mlp + min(min(x, kDenseBatch - 1), clast) * cs);
+    float av0[kDenseBatch];
 #pragma unroll
-        for (int i = 0; i < kPartBatch; ++i) {
-            const int c = min(c0 + i, nchu - 1);
-            const float2 v = *reinterpret_cast<const float2 *>(mlp + c * cs);
-            mv[i] = v.x;
-            lv[i] = v.y;
-            av[i] = acp[c * as];
-        }
-    };
-    if (n0 > 0) load_parts(0);
+    for (int i = 0; i < kDenseBatch; ++i) av0[i] = acp[min(i, clast) * as];
     __builtin_amdgcn_sched_barrier(0);  // the partials stay in flight during the block scores
 
     // block scores q.k (scaled, log2 units): 8 threads per (token, key) pair
@@ -225,6 +222,10 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
             dot += __shfl_xor(dot, 4);
             if (pr < n_pairs && part == 0) ps[pr] = dot * D.scale_log2;
         }
+    }
+    if (x < kDenseBatch) {
+        s_m0[t][x] = ml0.x;
+        s_l0[t][x] = ml0.y;
     }
     __syncthreads();
     {
@@ -258,10 +259,26 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
         for (int u = kVReg; u < B; ++u) os = fmaf(ps[t * B + u], ldv(vcol, u * vs), os);
     }
     // the row's prefix statistics, in chunk order; they overwrite the cache
-    PartAcc<> pa;
-    pa.add(mv, lv, av, n0);
-    for (int c0 = kPartBatch; c0 < nchu; c0 += kPartBatch) {
-        load_parts(c0);
+    PartAcc pa;
+    {
+        float mv[kDenseBatch], lv[kDenseBatch];
+#pragma unroll
+        for (int i = 0; i < kDenseBatch; ++i) {
+            mv[i] = s_m0[t][i];
+            lv[i] = s_l0[t][i];
+        }
+        pa.add(mv, lv, av0, min(nchu, kDenseBatch));
+    }
+    for (int c0 = kDenseBatch; c0 < nchu; c0 += kPartBatch) {
+        float mv[kPartBatch], lv[kPartBatch], av[kPartBatch];
+#pragma unroll
+        for (int i = 0; i < kPartBatch; ++i) {
+            const int c = min(c0 + i, nchu - 1);
+            const float2 v = *reinterpret_cast<const float2 *>(mlp + c * cs);
+            mv[i] = v.x;
+            lv[i] = v.y;
+            av[i] = acp[c * as];
+        }
         pa.add(mv, lv, av, min(kPartBatch, nchu - c0));
     }
     float op = 0.0f, lp2 = -__builtin_huge_valf();
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(DIM) void k_finish_active(
     load_acc(0);
     __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
     const int nchu = (ucnt + D.sparse_chunk - 1) / D.sparse_chunk;  // chunks that wrote partials
-    PartAcc<kActBatch> pa;
+    PartAcc pa;
     for (int c0 = 0; c0 < nchu; c0 += kActBatch) {
         if (c0 > 0) {
             ml = load_ml(c0);
