@@ -93,7 +93,12 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     extern __shared__ float sm[];
     __shared__ float s_m0[kFinishMaxThreads / 64][kDenseBatch], s_l0[kFinishMaxThreads / 64][kDenseBatch];
     const int B = D.B, G = D.G;
-    const int t0 = blockIdx.x * TG, h = blockIdx.y, s = blockIdx.z;
+    // workgroup u * (S*Hk) + (s*Hk + g) takes token group u % n_tg of head
+    // g*G + u / n_tg: a group's workgroups run on the XCD that ran its prefix
+    // workgroups (their partials are in that XCD's L2) when S*Hk is a multiple of 8
+    const int ng = D.S * D.Hk, n_tg = (D.B + TG - 1) / TG;
+    const int sg_ = blockIdx.x % ng, u_ = blockIdx.x / ng;
+    const int t0 = (u_ % n_tg) * TG, h = (sg_ % D.Hk) * D.G + u_ / n_tg, s = sg_ / D.Hk;
     const int nt = min(TG, B - t0);
     const int g = h / G, j = h % G;
     const int sgi = s * D.Hk + g;
@@ -383,7 +388,7 @@ hipError_t launch_finish(const Dims &D, const void *q_t, const void *k_blk, cons
                          const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
                          float *op_cache, float *lp_cache, void *out, hipStream_t st) {
     const int TG = finish_group(D);
-    dim3 grid((D.B + TG - 1) / TG, D.Hq, D.S);
+    dim3 grid(((D.B + TG - 1) / TG) * D.Hq * D.S);
     const size_t lds = finish_lds_bytes(D, TG);
     const int threads = TG * D.d;
 #define LAUNCH_F(T, DIMV)                                                                         \
