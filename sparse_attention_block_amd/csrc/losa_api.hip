@@ -222,12 +222,15 @@ int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *
     hipStream_t s = static_cast<hipStream_t>(stream);
     void **ev = debug ? debug->stage_events : nullptr;
     hipError_t e = mark(ev, 0, s);
-    if (e == hipSuccess) e = launch_prepare(D, true, q_t, nullptr, W, nullptr, nullptr, nullptr, s);
+    // (the bf16 dense pass reads its query rows from q_t; fp32 reads stacked rows)
+    if (!D.bf16 && e == hipSuccess)
+        e = launch_prepare(D, true, q_t, nullptr, W, nullptr, nullptr, nullptr, s);
     if (e == hipSuccess) e = mark(ev, 1, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (e == hipSuccess)
-        e = launch_prefix(D, true, k_cache, v_cache, kv_off, prefix_len, W, nullptr, nullptr, 0, s);
+        e = launch_prefix(D, true, q_t, k_cache, v_cache, kv_off, prefix_len, W, nullptr, nullptr, 0,
+                          s);
     if (e == hipSuccess) e = mark(ev, 4, s);
     if (e == hipSuccess)
         e = launch_finish(D, q_t, k_blk, v_blk, kv_off, prefix_len, W, op_cache, lp_cache, out, s);
@@ -289,7 +292,7 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
         e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, blk, s);
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (D.R > 0 && e == hipSuccess)
-        e = launch_prefix(D, false, k_cache, v_cache, kv_off, prefix_len, W, dbg.union_idx,
+        e = launch_prefix(D, false, q_t, k_cache, v_cache, kv_off, prefix_len, W, dbg.union_idx,
                           dbg.union_cnt, dbg.union_cap, s);
     if (e == hipSuccess) e = mark(ev, 4, s);
     if (D.R > 0 && e == hipSuccess) e = launch_finish_active(D, W, op_cache, lp_cache, out, s);

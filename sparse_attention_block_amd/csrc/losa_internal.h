@@ -102,10 +102,11 @@ hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
 size_t select_lds_bytes(const Dims &D);  // dynamic LDS of the exact-selection kernel
 // Sparse step: the union of the rows' pages is built here (the dbg_union_*
 // outputs are optional).
-hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const void *v_cache,
-                         const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
-                         int32_t *dbg_union_idx, int32_t *dbg_union_cnt, int dbg_union_cap,
-                         hipStream_t st);
+// Dense bf16: the Q operands come straight from q_t (no stacked rows needed).
+hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void *k_cache,
+                         const void *v_cache, const int32_t *kv_off, const int32_t *prefix_len,
+                         const Work &W, int32_t *dbg_union_idx, int32_t *dbg_union_cnt,
+                         int dbg_union_cap, hipStream_t st);
 // Dense first step: every row's prefix partials, the block attention and the merge.
 hipError_t launch_finish(const Dims &D, const void *q_t, const void *k_blk, const void *v_blk,
                          const int32_t *kv_off, const int32_t *prefix_len, const Work &W,

@@ -577,7 +577,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int DIM, int RTW, int NW>
-__global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uint16_t *__restrict__ kc,
+__global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uint16_t *__restrict__ q_t,
+                                                               const uint16_t *__restrict__ kc,
                                                                const uint16_t *__restrict__ vc,
                                                                const int32_t *__restrict__ kv_off,
                                                                const int32_t *__restrict__ prefix_len,
@@ -607,17 +608,20 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     const int rows = D.Rd, nch = D.n_chunks_dense;
     const int n_rt = (rows + 15) / 16;
 
-    // Q operands (B of QK^T) of row tiles w + NW*i: lane l holds row l%16, dims
-    // 32*kk + 8*(l/16) .. +7 (row tiles past the last read tile n_rt-1, unused).
-    // Issued before any page so that waiting for them never waits for a page.
+    // Q operands (B of QK^T) of row tiles w + NW*i, read straight from the
+    // block queries: row r = j*B + t of the group is head g*G + j, token t.  Lane
+    // l holds row l%16, dims 32*kk + 8*(l/16) .. +7; rows past the group read
+    // its last row (their outputs are not stored).  Issued before any page so
+    // that waiting for them never waits for a page.
     uint4 qop[RTW][KSTEPS];
-    const uint16_t *qr = static_cast<const uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
         const int rt = min(w + NW * i, n_rt - 1);
+        const int r = min(rt * 16 + l16, rows - 1);
+        const uint16_t *qrow = q_t + ((size_t)(s * D.B + r % D.B) * D.Hq + g * D.G + r / D.B) * DIM;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
-            qop[i][kk] = *reinterpret_cast<const uint4 *>(qr + (size_t)(rt * 16 + l16) * DIM + 32 * kk + 8 * lg);
+            qop[i][kk] = *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * lg);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -854,9 +858,10 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restr
     }
 }
 
-hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const void *v_cache,
-                         const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
-                         int32_t *dbg_uidx, int32_t *dbg_ucnt, int dbg_cap, hipStream_t st) {
+hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void *k_cache,
+                         const void *v_cache, const int32_t *kv_off, const int32_t *prefix_len,
+                         const Work &W, int32_t *dbg_uidx, int32_t *dbg_ucnt, int dbg_cap,
+                         hipStream_t st) {
     const int nch = dense ? D.n_chunks_dense : D.n_chunks_sparse;
     dim3 grid(nch * D.S * D.Hk);
     if (D.bf16) {
@@ -877,8 +882,8 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *k_cache, const v
         else LAUNCH_P(DIMV, 4, DN, false);                   \
     } while (0)
 #define LAUNCH_D(DIMV, RTWV, NWV)                                                                 \
-    hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV, NWV>), grid, dim3(64 * NWV), 0, st, D, k, v, \
-                       kv_off, prefix_len, W)
+    hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV, NWV>), grid, dim3(64 * NWV), 0, st, D,    \
+                       static_cast<const uint16_t *>(q_t), k, v, kv_off, prefix_len, W)
         // dense pass: wave w of NW takes row tiles w, w + NW, ...; head_dim 128
         // uses eight waves (one page of K and V is one 16-byte piece per thread)
         // once there are more than four row tiles
