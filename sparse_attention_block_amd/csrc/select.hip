@@ -423,13 +423,20 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         if (tid < GB) {
             const float4 *sr = reinterpret_cast<const float4 *>(sq + tid * RWS);
             float acc = 0.0f;
+            constexpr int RB = 8;  // 16-byte reads requested together
 #pragma unroll
-            for (int v = 0; v < DIM / 4; ++v) {
-                const float4 x = sr[v];
-                acc = acc + x.x;
-                acc = acc + x.y;
-                acc = acc + x.z;
-                acc = acc + x.w;
+            for (int v0 = 0; v0 < DIM / 4; v0 += RB) {
+                float4 x[RB];
+#pragma unroll
+                for (int i = 0; i < RB; ++i) x[i] = sr[v0 + i];
+                __builtin_amdgcn_sched_barrier(0);  // the batch is requested before the adds
+#pragma unroll
+                for (int i = 0; i < RB; ++i) {
+                    acc = acc + x[i].x;
+                    acc = acc + x[i].y;
+                    acc = acc + x[i].z;
+                    acc = acc + x[i].w;
+                }
             }
             e_s[tid] = acc;
             if (writer && dbg_loc)
