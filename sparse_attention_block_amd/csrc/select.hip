@@ -680,12 +680,13 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         load_h(0, hv0);
         __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
         if constexpr (BF) {
-            if (lane < DIM / 2) {
-                const float q0 = bf16_lo(qv[0]), q1 = bf16_hi(qv[0]);
-                *reinterpret_cast<float2 *>(qw + 2 * lane) = make_float2(q0, q1);
-                *reinterpret_cast<uint2 *>(qw + DIM + 2 * lane) =
-                    make_uint2(q0 >= 0.0f ? kSelMax : kSelMin, q1 >= 0.0f ? kSelMax : kSelMin);
-            }
+            // every lane stores (lanes past DIM/2 repeat a word with its own value),
+            // so that the query word's load is not sunk into a branch
+            const int wl = lane % (DIM / 2);
+            const float q0 = bf16_lo(qv[0]), q1 = bf16_hi(qv[0]);
+            *reinterpret_cast<float2 *>(qw + 2 * wl) = make_float2(q0, q1);
+            *reinterpret_cast<uint2 *>(qw + DIM + 2 * wl) =
+                make_uint2(q0 >= 0.0f ? kSelMax : kSelMin, q1 >= 0.0f ? kSelMax : kSelMin);
         } else {
 #pragma unroll
             for (int i = 0; i < QPL; ++i) qw[lane + 64 * i] = qv[i];
