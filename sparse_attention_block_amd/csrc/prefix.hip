@@ -325,16 +325,16 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     // requested before the union is built.
     uint4 qop[RTW][KSTEPS];
     const uint16_t *qr = static_cast<const uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
+    // (row tiles past the rows read the last tile -- the buffer holds whole
+    // tiles -- and are zeroed: no load is conditional)
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
-        const int rt = wr + i * WPG;
+        const int rt = wr + i * WPG, rtc = min(rt, max(n_rt - 1, 0));
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            if (rt < n_rt)
-                qop[i][kk] = *reinterpret_cast<const uint4 *>(qr + (size_t)(rt * 16 + l16) * DIM +
-                                                              32 * kk + 8 * lg);
-            else
-                qop[i][kk] = make_uint4(0, 0, 0, 0);
+            const uint4 v = *reinterpret_cast<const uint4 *>(qr + (size_t)(rtc * 16 + l16) * DIM +
+                                                             32 * kk + 8 * lg);
+            qop[i][kk] = rt < n_rt ? v : make_uint4(0, 0, 0, 0);
         }
     }
     // this chunk's pages (lane i: union position first + i)
@@ -346,13 +346,20 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
                               first, cp, reinterpret_cast<uint32_t *>(s_raw), s_wsum, s_pg,
                               chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
                               dbg_cap, D.k, MASK ? s_rmask : nullptr);
-        if (chunk == 0 && tid == 0) {
+        my_page = lane < cp ? s_pg[lane] : 0;
+    }
+    // The union size, for the finishing kernel: stored once the page loads are
+    // out (a wait for the pages would otherwise wait for this store too).
+    auto store_count = [&]() {
+        if (!dense && chunk == 0 && tid == 0) {
             W.union_cnt[sgi] = min(n_items, D.union_cap);
             if (dbg_ucnt) dbg_ucnt[sgi] = n_items;
         }
-        my_page = lane < cp ? s_pg[lane] : 0;
+    };
+    if (first >= n_items) {
+        store_count();
+        return;
     }
-    if (first >= n_items) return;
     const int n_here = min(cp, n_items - first);
     int row0[RTW];  // first row of each of the wave's row tiles
 #pragma unroll
@@ -394,6 +401,7 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
             cur = nxt;
         }
     }
+    store_count();
 #pragma unroll
     for (int i = 0; i < RTW; ++i) l_run[i] = shfl_sum32(l_run[i]);
 

@@ -383,10 +383,6 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             dst[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
         }
     }
-    if (writer && tid == 0) {
-        W.union_cnt[sgi] = 0;
-        if (dbg_ucnt) dbg_ucnt[sgi] = 0;  // the sparse prefix kernel overwrites them
-    }
     __syncthreads();
 
     // 2. locality chain per (query head, token), then the active set; with a
@@ -412,10 +408,6 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             for (int j = 0; j < G; ++j) {
                 act_s[j * A + pos] = tid;
                 rbase_s[j * A + pos] = (j * B + tid) * RWP;
-                if (writer) {
-                    W.active[((size_t)s * Hq + g * G + j) * A + pos] = tid;
-                    if (dbg_act) dbg_act[((size_t)s * Hq + g * G + j) * A + pos] = tid;
-                }
             }
         }
         __syncthreads();
@@ -473,10 +465,6 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         if (sel) {
             act_s[j * A + pos] = t;
             rbase_s[j * A + pos] = tid * RWP;
-            if (writer) {
-                W.active[((size_t)s * Hq + g * G + j) * A + pos] = t;
-                if (dbg_act) dbg_act[((size_t)s * Hq + g * G + j) * A + pos] = t;
-            }
         }
         __syncthreads();
     }
@@ -497,7 +485,22 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         for (int o = 1; o < 16; o <<= 1) ab += __shfl_xor(ab, o);
         if (r < R && part == 0) qabs_s[r] = ab * (1.0f + 1.0f / 256.0f);
     }
-    if (writer) {
+    __syncthreads();
+    // The writer's stores for the later kernels -- the active list, the stacked
+    // rows (from LDS) and a zero union count, which the sparse prefix kernel
+    // overwrites -- go out after the wave's bounds (or before an early return):
+    // the wait for the metadata tile waits for every store issued before it.
+    auto writer_stores = [&]() {
+        if (!writer) return;
+        if (tid == 0) {
+            W.union_cnt[sgi] = 0;
+            if (dbg_ucnt) dbg_ucnt[sgi] = 0;
+        }
+        int32_t *act = W.active + ((size_t)s * Hq + g * G) * A;  // [G][A], rows j*A + a
+        for (int i = tid; i < R; i += 256) {
+            act[i] = act_s[i];
+            if (dbg_act) dbg_act[((size_t)s * Hq + g * G) * A + i] = act_s[i];
+        }
         uint16_t *qr = static_cast<uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
         for (int i = tid; i < D.Rs16 * VPR; i += 256) {
             const int r = i / VPR, c = i % VPR;
@@ -505,9 +508,11 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             if (r < R) v = *reinterpret_cast<const uint4 *>(&qsm[rbase_s[r] + c * 4]);
             *reinterpret_cast<uint4 *>(qr + (size_t)r * DIM + c * 8) = v;
         }
+    };
+    if (!tile_ok) {
+        writer_stores();
+        return;
     }
-    __syncthreads();
-    if (!tile_ok) return;
 
     // 4. the tile's bounds, row tile by row tile, row operands built from LDS
     float *hb = W.hbound + (size_t)sgi * R1 * D.hb_stride;
@@ -539,6 +544,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         for (int j = 0; j < 4; ++j) qa[j] = qabs_s[min(rt * 16 + 4 * lg + j, R1 - 1)];
         bound_rowtile<DIM>(D, rt, aop, qa, bop, amax, pl, sg.pages, bx, l16, lg, hb, tm, tile_full);
     }
+    writer_stores();
 }
 
 // ---------------------------------------------------------------------------
