@@ -504,6 +504,203 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     }
 }
 
+// Sparse prefix, bf16, head_dim 128, chunks of 4 union pages and at most RTW
+// row tiles of stacked rows.  Wave w reads the keys of the chunk's page w and
+// forms its scores (S^T = K.Q^T, as in attend_pages); the scores of the 4
+// pages meet in LDS.  Each wave then takes the softmax of its rows over all 4
+// pages and multiplies the weights by its quarter of the output dimensions of
+// V, read for all 4 pages.  So K and V are each read once, and the waves need
+// no combine of outputs: each writes its dimensions of the chunk's partial,
+// wave 0 the (m, l).  The union slice, the arithmetic (log2-unit scores,
+// weights rounded to bf16, row sums of the rounded weights) and the partial
+// layout are those of k_prefix_bf16.
+template <int DIM, int RTW, bool MASK>
+__global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
+                                                             const uint16_t *__restrict__ kc,
+                                                             const uint16_t *__restrict__ vc,
+                                                             const int32_t *__restrict__ kv_off,
+                                                             const int32_t *__restrict__ prefix_len,
+                                                             Work W, int32_t *dbg_uidx,
+                                                             int32_t *dbg_ucnt, int dbg_cap) {
+    constexpr int KSTEPS = DIM / 32;
+    constexpr int DQ = DIM / 4;    // output dimensions per wave
+    constexpr int DPLQ = DQ / 16;  // PV products per page pair: 16 dimensions each
+    constexpr int NP = 4;          // the chunk's pages: one per wave
+    static_assert(DPLQ == 2, "one 32-bit V word per token and lane");
+    __shared__ uint32_t s_bm[kMaxBitmapWords];
+    __shared__ int s_wsum[4], s_pg[kMaxSparseChunk];
+    __shared__ uint64_t s_rmask[MASK ? kMaxSparseChunk : 1];  // rows that selected each page
+    __shared__ float4 s_sc[RTW][NP][64];                       // scores, in the MFMA's lane layout
+
+    const int ng = D.S * D.Hk;
+    const int sgi = blockIdx.x % ng;
+    const int chunk = blockIdx.x / ng;
+    const int s = sgi / D.Hk, g = sgi % D.Hk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
+    const int cp = D.sparse_chunk, first = chunk * cp;  // cp == NP
+    const int rows = D.R, nch = D.n_chunks_sparse;
+    const int n_rt = (rows + 15) / 16;
+
+    // the rows' page lists (one entry per thread, clamped) and the Q operands
+    // (row tiles past the rows read the last one and are zeroed), requested first
+    const int32_t *psel_g = W.psel + (size_t)sgi * rows * D.k;
+    const int n_sel = rows * D.k;
+    const int pre0 = psel_g[min(tid, max(n_sel - 1, 0))];
+    uint4 qop[RTW][KSTEPS];
+    const uint16_t *qr = static_cast<const uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        const int rtc = min(i, n_rt - 1);
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(qr + (size_t)(rtc * 16 + l16) * DIM +
+                                                             32 * kk + 8 * lg);
+            qop[i][kk] = i < n_rt ? v : make_uint4(0, 0, 0, 0);
+        }
+    }
+    const int n_items = union_slice(psel_g, pre0, n_sel, sg.pages, D.k >= sg.pages, first, cp,
+                                    s_bm, s_wsum, s_pg,
+                                    chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
+                                    dbg_cap, D.k, MASK ? s_rmask : nullptr);
+    auto store_count = [&]() {
+        if (chunk == 0 && tid == 0) {
+            W.union_cnt[sgi] = min(n_items, D.union_cap);
+            if (dbg_ucnt) dbg_ucnt[sgi] = n_items;
+        }
+    };
+    if (first >= n_items) {
+        store_count();
+        return;
+    }
+    const int n_here = min(cp, n_items - first);
+    const int my_page = lane < cp ? s_pg[min(lane, n_here - 1)] : 0;
+
+    // K of page w (token l%16, dims 32*kk + 8*(l/16) ..), then this wave's
+    // quarter of V for every page (tokens 4*(l/16) + j, dims DQ*w + 2*(l%16), +1);
+    // slots past the chunk repeat its last page and count no token
+    int valid[NP];
+    size_t base[NP];
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+        const int p = __builtin_amdgcn_readlane(my_page, min(n, n_here - 1));
+        base[n] = ((size_t)g * D.T + sg.off + (size_t)p * kPage) * DIM;
+        valid[n] = n < n_here ? min(kPage, sg.len - p * kPage) : 0;
+    }
+    const size_t kbase = base[min(w, n_here - 1)];
+    const int kvalid = w < n_here ? valid[min(w, NP - 1)] : 0;
+    uint4 kop[KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+        kop[kk] = *reinterpret_cast<const uint4 *>(kc + kbase + (size_t)l16 * DIM + 32 * kk + 8 * lg);
+    uint32_t vw[NP][4];
+#pragma unroll
+    for (int n = 0; n < NP; ++n)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            vw[n][j] = *reinterpret_cast<const uint32_t *>(vc + base[n] + (size_t)(4 * lg + j) * DIM +
+                                                           DQ * w + DPLQ * l16);
+    __builtin_amdgcn_sched_barrier(0);  // K and V are requested together, before any is used
+
+    // scores of page w, log2 units; tokens past the prefix (and, with row
+    // masks, rows that did not select the page) get -inf
+    const uint64_t rmw = MASK ? s_rmask[min(w, NP - 1)] : 0ull;
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[kk]),
+                                                           __builtin_bit_cast(bf16x8_t, qop[i][kk]),
+                                                           sacc, 0, 0, 0);
+        float sv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sv[j] = 4 * lg + j < kvalid ? sacc[j] * D.scale_log2 : -__builtin_huge_valf();
+            if (MASK && !((rmw >> (i * 16 + l16)) & 1ull)) sv[j] = -__builtin_huge_valf();
+        }
+        s_sc[i][w][lane] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+    }
+    // (the V words are held to be in use here: else the compiler issues their
+    // loads only behind the barrier, a second round trip)
+#pragma unroll
+    for (int n = 0; n < NP; ++n)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(vw[n][j]));
+    __syncthreads();
+
+    // V^T operands of the wave's quarter: dim 2*(l%16) + e, tokens 4*lg .. +3
+    // (tokens past the prefix zeroed)
+    short4_t vop[NP][DPLQ];
+#pragma unroll
+    for (int n = 0; n < NP; ++n)
+#pragma unroll
+        for (int e = 0; e < DPLQ; ++e) {
+            short4_t x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                x[j] = 4 * lg + j < valid[n] ? static_cast<short>(vw[n][j] >> (16 * e)) : short(0);
+            vop[n][e] = x;
+        }
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        if (i >= n_rt) break;
+        float sv[NP][4];
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            const float4 x = s_sc[i][n][lane];
+            sv[n][0] = x.x; sv[n][1] = x.y; sv[n][2] = x.z; sv[n][3] = x.w;
+        }
+        float mp = -__builtin_huge_valf();
+#pragma unroll
+        for (int n = 0; n < NP; ++n) mp = fmaxf(mp, fmaxf(fmaxf(sv[n][0], sv[n][1]), fmaxf(sv[n][2], sv[n][3])));
+        mp = shfl_max32(mp);
+        // (with row masks a row may have no score in the chunk: zero weights)
+        const float mref = MASK && mp == -__builtin_huge_valf() ? 0.0f : mp;
+        float lsum = 0.0f;
+        uint2 pw[NP];
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][0] - mref)),
+                                  static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][1] - mref))};
+            const bf16x2_t p23 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][2] - mref)),
+                                  static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][3] - mref))};
+            const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
+            lsum += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
+            pw[n] = make_uint2(w01, w23);
+        }
+        lsum = shfl_sum32(lsum);
+        // O^T += V^T.P, pages n and n+1 in one v_mfma_f32_16x16x32_bf16 (its k
+        // index 8*lg + c: token 4*lg + c%4 of page n + c/4, in both operands)
+        float4_t oacc[DPLQ];
+#pragma unroll
+        for (int e = 0; e < DPLQ; ++e) oacc[e] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n = 0; n < NP; n += 2) {
+            const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[n].x, pw[n].y, pw[n + 1].x, pw[n + 1].y));
+#pragma unroll
+            for (int e = 0; e < DPLQ; ++e) {
+                const uint2 v0 = __builtin_bit_cast(uint2, vop[n][e]), v1 = __builtin_bit_cast(uint2, vop[n + 1][e]);
+                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop, oacc[e], 0, 0, 0);
+            }
+        }
+        // lane l holds, for row 16*i + l%16, dims DQ*w + 2*(4*lg + j) + e: 8
+        // consecutive dimensions
+        const int r = i * 16 + l16;
+        if (r < rows) {
+            const size_t pb = ((size_t)sgi * nch + chunk) * rows + r;
+            if (w == 0 && lg == 0) *reinterpret_cast<float2 *>(&W.part_ml[pb * 2]) = make_float2(mp, lsum);
+            float *dst = W.part_acc + pb * DIM + DQ * w + DPLQ * 4 * lg;
+            *reinterpret_cast<float4 *>(dst) = make_float4(oacc[0][0], oacc[1][0], oacc[0][1], oacc[1][1]);
+            *reinterpret_cast<float4 *>(dst + 4) = make_float4(oacc[0][2], oacc[1][2], oacc[0][3], oacc[1][3]);
+        }
+    }
+    store_count();  // after the waits for the pages, which would wait for it too
+}
+
 // Dense first-step pass, bf16.  Each page of the workgroup's chunk is read
 // from HBM once, straight into a ring of kDenseSlots LDS page slots with
 // global_load_lds_dwordx4 (no register staging), so kDenseSlots - 2*kDenseGroup
@@ -900,6 +1097,20 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
                 if (n_rt <= 4) LAUNCH_D(128, 1, 4);
                 else if (n_rt <= 8) LAUNCH_D(128, 1, 8);
                 else LAUNCH_D(128, 2, 8);
+            } else if (D.sparse_chunk == 4 && n_rt <= 2) {
+                // chunks of 4 pages, at most 32 rows: waves split the dimensions
+                const bool mk = D.flags & LOSA_FLAG_ROW_MASK;
+#define LAUNCH_Q(RTWV, MK)                                                                          \
+    hipLaunchKernelGGL((k_prefix_quarter_bf16<128, RTWV, MK>), grid, dim3(256), 0, st, D, k, v,     \
+                       kv_off, prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap)
+                if (n_rt == 1) {
+                    if (mk) LAUNCH_Q(1, true);
+                    else LAUNCH_Q(1, false);
+                } else {
+                    if (mk) LAUNCH_Q(2, true);
+                    else LAUNCH_Q(2, false);
+                }
+#undef LAUNCH_Q
             } else {
                 PICK_P(128, false);
             }
