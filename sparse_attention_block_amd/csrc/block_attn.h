@@ -116,21 +116,26 @@ __device__ __forceinline__ void block_token(const Dims &D, const T *__restrict__
 #pragma unroll
             for (int e = 0; e < EV; ++e) dot = fmaf(qf[i * EV + e], kf[e], dot);
         }
-        dot += __shfl_xor(dot, 1);
-        dot += __shfl_xor(dot, 2);
+        dot += lane_xor1(dot);
+        dot += lane_xor2(dot);
         sc[p] = p * 16 + ku < B ? dot * D.scale_log2 : -__builtin_huge_valf();
         m = fmaxf(m, sc[p]);
     }
-#pragma unroll
-    for (int o = 4; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    // over the keys (lane bits 2-5; m is equal across bits 0-1): l^4, l^8, l^16, l^32
+    m = fmaxf(m, lane_xor7(m));
+    m = fmaxf(m, lane_xor15(m));
+    m = fmaxf(m, lane_xor16(m));
+    m = fmaxf(m, lane_xor32(m));
     float l = 0.0f, pw[KG];
 #pragma unroll
     for (int p = 0; p < KG; ++p) {
         pw[p] = p * 16 + ku < B ? __builtin_amdgcn_exp2f(sc[p] - m) : 0.0f;
         l += pw[p];
     }
-#pragma unroll
-    for (int o = 4; o < 64; o <<= 1) l += __shfl_xor(l, o);
+    l += lane_xor7(l);
+    l += lane_xor15(l);
+    l += lane_xor16(l);
+    l += lane_xor32(l);
     const float ls2 = m + __log2f(l);
     // normalised weights to LDS, one lane per key
     if (qq == 0) {

@@ -222,9 +222,9 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
 #pragma unroll
                 for (int i = 0; i < SEG; ++i) dot = fmaf(qp[i], kp[i], dot);
             }
-            dot += __shfl_xor(dot, 1);
-            dot += __shfl_xor(dot, 2);
-            dot += __shfl_xor(dot, 4);
+            dot += lane_xor1(dot);  // then l^2, l^4: the 8 parts of the pair
+            dot += lane_xor2(dot);
+            dot += lane_xor7(dot);
             if (pr < n_pairs && part == 0) ps[pr] = dot * D.scale_log2;
         }
     }
@@ -241,11 +241,29 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
         const int tt = tid / Bp, u = tid % Bp;
         const bool on = tt < nt && u < B;
         const float v = on ? ps[tt * B + u] : -__builtin_huge_valf();
-        float m = v;
-        for (int o = 1; o < Bp; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        // butterflies over the segment: l^1, l^2, then l^4, l^8, l^16, l^32
+        // (xor 7 and 15 once the value is equal across the lower lane bits)
+        auto seg_max = [&](float y) {
+            if (Bp > 1) y = fmaxf(y, lane_xor1(y));
+            if (Bp > 2) y = fmaxf(y, lane_xor2(y));
+            if (Bp > 4) y = fmaxf(y, lane_xor7(y));
+            if (Bp > 8) y = fmaxf(y, lane_xor15(y));
+            if (Bp > 16) y = fmaxf(y, lane_xor16(y));
+            if (Bp > 32) y = fmaxf(y, lane_xor32(y));
+            return y;
+        };
+        auto seg_sum = [&](float y) {
+            if (Bp > 1) y += lane_xor1(y);
+            if (Bp > 2) y += lane_xor2(y);
+            if (Bp > 4) y += lane_xor7(y);
+            if (Bp > 8) y += lane_xor15(y);
+            if (Bp > 16) y += lane_xor16(y);
+            if (Bp > 32) y += lane_xor32(y);
+            return y;
+        };
+        const float m = seg_max(v);
         const float p = on ? __builtin_amdgcn_exp2f(v - m) : 0.0f;
-        float l = p;
-        for (int o = 1; o < Bp; o <<= 1) l += __shfl_xor(l, o);
+        const float l = seg_sum(p);
         __syncthreads();  // every score has been read
         if (on) ps[tt * B + u] = p / l;
         if (on && u == 0) ls2[tt] = m + __log2f(l);

@@ -139,6 +139,30 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Values of partner lanes without an LDS round trip: l^1 and l^2 (DPP quad
+// permutes), l^7 and l^15 inside each row of 16 lanes (DPP row half-mirror
+// and mirror), l^16 and l^32 (v_permlane16_swap / v_permlane32_swap of a
+// register with itself: in every lane its two results are the values of the
+// lane's pair of rows, or of wave halves, and the partner's is the one that
+// is not the lane's own).  In a butterfly over a value already equal across
+// lane bits 0-1, l^7 stands for l^4; equal across bits 0-2, l^15 for l^8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_xor1(float v) { return dpp_f32<0xb1>(v); }    // quad_perm [1,0,3,2]
+__device__ __forceinline__ float lane_xor2(float v) { return dpp_f32<0x4e>(v); }    // quad_perm [2,3,0,1]
+__device__ __forceinline__ float lane_xor7(float v) { return dpp_f32<0x141>(v); }   // row_half_mirror
+__device__ __forceinline__ float lane_xor15(float v) { return dpp_f32<0x140>(v); }  // row_mirror
+__device__ __forceinline__ float lane_xor16(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((__lane_id() & 16) ? a[0] : a[1]);
+}
+__device__ __forceinline__ float lane_xor32(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((__lane_id() & 32) ? a[0] : a[1]);
+}
+
 // Sequence geometry with out-of-range values clamped into the cache.
 struct SeqGeom {
     int64_t off;   // first cache token

@@ -28,14 +28,35 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// Reductions over the lanes l, l^16, l^32, l^48 (the 4 lane rows of 16).
+// v_permlane16_swap of a register with itself gives, in every lane, the
+// values of its row pair (rows 0 and 1, or 2 and 3) in its two results, and
+// v_permlane32_swap those of its two halves; a symmetric operation on the
+// two results so combines lane l with l^16, then with l^32, in one VALU
+// instruction each (no LDS round trip), the same value in all four lanes.
 __device__ __forceinline__ float shfl_max32(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float shfl_sum32(float v) {
-    v = v + __shfl_xor(v, 16);
-    v = v + __shfl_xor(v, 32);
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// inclusive prefix sum over the 64 lanes with DPP: row shifts 1, 2, 4, 8 sum
+// inside each row of 16 lanes (a lane with no source adds 0), then row
+// broadcasts 15 and 31 carry the row totals into the later rows
+__device__ __forceinline__ int wave_incl_sum(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
     return v;
 }
 
@@ -234,11 +255,7 @@ __device__ int union_slice(const int32_t *__restrict__ psel, int pre0, int n_sel
     const int w0 = min(tid * wpt, words), w1 = min(w0 + wpt, words);
     int cnt = 0;
     for (int i = w0; i < w1; ++i) cnt += __popc(bm[i]);
-    int incl = cnt;
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
-    }
+    const int incl = wave_incl_sum(cnt);
     if (lane == 63) wsum[w] = incl;
     __syncthreads();
     int pos = incl - cnt, total = 0;

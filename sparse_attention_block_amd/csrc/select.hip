@@ -481,8 +481,10 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
 #pragma unroll
             for (int w = 0; w < DIM / 32; ++w) ab += fabsf(bf16_lo(a[w])) + fabsf(bf16_hi(a[w]));
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) ab += __shfl_xor(ab, o);
+        ab += lane_xor1(ab);  // then l^2, l^4, l^8: the row's sum in each of its lanes
+        ab += lane_xor2(ab);
+        ab += lane_xor7(ab);
+        ab += lane_xor15(ab);
         if (r < R && part == 0) qabs_s[r] = ab * (1.0f + 1.0f / 256.0f);
     }
     __syncthreads();
