@@ -645,8 +645,8 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
     const int h = g * D.G + r / D.A, a = r % D.A;
     const bool all_pages = k >= sg.pages;
     uint64_t *mk = reinterpret_cast<uint64_t *>(smem);  // [128] keys being merged
-    volatile int32_t *pend = reinterpret_cast<int32_t *>(smem + 256);  // [128] candidate pages
-    uint32_t *qw = smem + 384;                                          // the row's chain operands
+    uint32_t *qw = smem + 256;                           // [2*DIM] the row's chain operands
+    int32_t *pend = reinterpret_cast<int32_t *>(smem + 256 + 2 * DIM);  // [4096] candidate pages
     int32_t *psel = W.psel + ((size_t)sgi * R1 + r) * k;
 
     if (all_pages) {
@@ -707,111 +707,113 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         for (int i = 0; i < TMR; ++i)
             if (lane + 64 * i < n_t) gm = max(gm, ord_key(tmv[i]));
         for (int x = lane + 64 * TMR; x < n_t; x += 64) gm = max(gm, ord_key(tm[x]));
+        // Any lower value serves as well (more candidates, the same result):
+        // the threshold is the largest key with 16 low zero bits that at least
+        // k lanes reach, found bit by bit with ballots -- the k-th largest key
+        // with its low 16 bits cleared (within 2^-7 of it as a float).
         uint32_t lam = 0u;  // below every finite key: all pages qualify
         if (min(n_t, 64) >= k) {
-            for (int e = 0; e < k; ++e) {
-                const uint32_t m = wave_max_u32(gm);
-                const uint64_t own = __ballot(gm == m);
-                if (lane == __ffsll(static_cast<unsigned long long>(own)) - 1) gm = 0u;
-                lam = m;
+#pragma unroll
+            for (int b = 31; b >= 16; --b) {
+                const uint32_t c = lam | (1u << b);
+                if (__popcll(__ballot(gm >= c)) >= k) lam = c;
             }
         }
         __syncthreads();  // qw visible to the chains
         // 2. candidates: upper end >= threshold; exact chain in batches of 64
         uint64_t lst = 0ull;  // lane e < k: e-th best (score key << 32 | ~page)
-        int npend = 0;
-        // One batch of 4096 pages: the candidates' bits, then every lane's
-        // candidates appended to the pending list, whose exact chains are taken
-        // 64 at a time.  The first batch uses the upper ends requested above;
-        // later ones load theirs (so the first set is dead after its batch).
         // the threshold as a float: ord_key preserves the order of floats (-0
         // and +0 alike), so ord_key(x) >= lam is x >= lamf; key 0 (every page
         // qualifies) is below every finite value
         const float lamf = lam == 0u ? -__builtin_huge_valf() : ord_to_f32(lam);
+        // exact chains of the pending pages pend[c0 .. c0 + n), n <= 64, merged
+        // into the list: rank every key of (chains, current list) among all of
+        // them (keys are distinct: one per page); rank e < k -> lane e
+        auto chains = [&](int c0, int n) {
+            uint64_t cand = 0ull;
+            if (lane < n) {
+                const int pc = pend[c0 + lane];
+                const float u = exact_bound<DIM, BF>(meta, D, g, sg.gp0 + pc, qw);
+                cand = (static_cast<uint64_t>(ord_key(u)) << 32) |
+                       static_cast<uint32_t>(~static_cast<uint32_t>(pc));
+            }
+            const int nlst = __popcll(__ballot(lane < k && lst != 0ull));
+            if (lane < n) mk[lane] = cand;
+            if (lane < nlst) mk[n + lane] = lst;
+            __syncthreads();
+            const int tot = n + nlst;
+            const uint64_t x0 = lane < tot ? mk[lane] : 0ull;
+            const uint64_t x1 = lane + 64 < tot ? mk[lane + 64] : 0ull;
+            int r0 = 0, r1 = 0;
+#pragma unroll 4
+            for (int i = 0; i < tot; ++i) {
+                const uint64_t y = mk[i];
+                r0 += y > x0;
+                r1 += y > x1;
+            }
+            __syncthreads();
+            if (lane < tot && r0 < k) mk[r0] = x0;
+            if (lane + 64 < tot && r1 < k) mk[r1] = x1;
+            __syncthreads();
+            lst = lane < min(tot, k) ? mk[lane] : 0ull;
+            __syncthreads();
+        };
+        // The largest float below lamf: hx >= lamf is then lamb - hx < 0, the
+        // sign bit of one subtraction (exact in sign: denormals are kept).
+        // lam == 0: -inf, below every finite upper end.
+        const uint32_t lb = __float_as_uint(lamf);
+        const float lamb = lam == 0u ? -__builtin_huge_valf()
+                                     : __uint_as_float(lb == 0u ? 0x80000001u
+                                                                : ((lb & 0x80000000u) ? lb + 1u : lb - 1u));
+        // One batch of 4096 pages.  Candidate bits: element i = 4*jj + e4 (page
+        // base + 256*jj + 4*lane + e4) at bit 31 - i%32 of cm[i/32], shifted in
+        // with v_alignbit (two instructions per upper end, no branch).  Each
+        // lane then lists its candidates in pend, lowest bit first, while any
+        // lane has some; their chains go 64 at a time.  The first batch uses
+        // the upper ends requested above; later ones load theirs.
         auto batch = [&](int base, const float4 (&hv)[16]) {
-            // bit 4*jj + e4 of cmask: page base + 256*jj + 4*lane + e4 is a candidate
-            // (pages past the sequence only in a partial batch: uniform branch)
             uint32_t cm[2] = {0u, 0u};
-            const int lim = sg.pages - base - 4 * lane;
-            if (sg.pages - base >= 4096) {
+            if (sg.pages - base >= 4096) {  // uniform: every page of the batch is in the sequence
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) {
                     const float hx[4] = {hv[jj].x, hv[jj].y, hv[jj].z, hv[jj].w};
 #pragma unroll
                     for (int e4 = 0; e4 < 4; ++e4)
-                        cm[jj >> 3] |= static_cast<uint32_t>(hx[e4] >= lamf) << ((4 * jj + e4) & 31);
+                        cm[jj >> 3] = __builtin_amdgcn_alignbit(cm[jj >> 3], __float_as_uint(lamb - hx[e4]), 31);
                 }
             } else {
+                const int lim = sg.pages - base - 4 * lane;  // in the sequence: 256*jj + e4 < lim
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) {
                     const float hx[4] = {hv[jj].x, hv[jj].y, hv[jj].z, hv[jj].w};
 #pragma unroll
                     for (int e4 = 0; e4 < 4; ++e4)
-                        cm[jj >> 3] |= static_cast<uint32_t>((256 * jj + e4 < lim) & (hx[e4] >= lamf))
-                                       << ((4 * jj + e4) & 31);
+                        cm[jj >> 3] = (cm[jj >> 3] << 1) |
+                                      static_cast<uint32_t>((256 * jj + e4 < lim) & (hx[e4] >= lamf));
                 }
             }
             uint64_t cmask = (static_cast<uint64_t>(cm[1]) << 32) | cm[0];
-            const bool last_batch = base + 4096 >= sg.pages;
-            // append each lane's candidates, lowest bit first, while any lane has some
+            int npend = 0;
             for (;;) {
                 const bool c = cmask != 0ull;
                 const uint64_t bal = __ballot(c);
-                if (bal) {
-                    const int bit = c ? __ffsll(static_cast<unsigned long long>(cmask)) - 1 : 0;
-                    if (c) {
-                        pend[npend + lanes_below(bal, lane)] = base + 256 * (bit >> 2) + 4 * lane + (bit & 3);
-                        cmask &= cmask - 1ull;
-                    }
-                    npend += __popcll(bal);
-                }
-                const bool last = last_batch && bal == 0ull;
-                while (npend >= 64 || (last && npend > 0)) {
-                    __builtin_amdgcn_wave_barrier();
-                    const int n = npend < 64 ? npend : 64;
-                    uint64_t cand = 0ull;
-                    if (lane < n) {
-                        const int pc = pend[lane];
-                        const float u = exact_bound<DIM, BF>(meta, D, g, sg.gp0 + pc, qw);
-                        cand = (static_cast<uint64_t>(ord_key(u)) << 32) |
-                               static_cast<uint32_t>(~static_cast<uint32_t>(pc));
-                    }
-                    __builtin_amdgcn_wave_barrier();
-                    const int rest = npend - n;
-                    const int moved = lane < rest ? pend[lane + n] : 0;
-                    __builtin_amdgcn_wave_barrier();
-                    if (lane < rest) pend[lane] = moved;
-                    npend = rest;
-                    // merge: rank every key of (batch, current list) among all of
-                    // them (keys are distinct: one per page); rank e < k -> lane e
-                    const int nlst = __popcll(__ballot(lane < k && lst != 0ull));
-                    if (lane < n) mk[lane] = cand;
-                    if (lane < nlst) mk[n + lane] = lst;
-                    __syncthreads();
-                    const int tot = n + nlst;
-                    const uint64_t x0 = lane < tot ? mk[lane] : 0ull;
-                    const uint64_t x1 = lane + 64 < tot ? mk[lane + 64] : 0ull;
-                    int r0 = 0, r1 = 0;
-#pragma unroll 4
-                    for (int i = 0; i < tot; ++i) {
-                        const uint64_t y = mk[i];
-                        r0 += y > x0;
-                        r1 += y > x1;
-                    }
-                    __syncthreads();
-                    if (lane < tot && r0 < k) mk[r0] = x0;
-                    if (lane + 64 < tot && r1 < k) mk[r1] = x1;
-                    __syncthreads();
-                    lst = lane < min(tot, k) ? mk[lane] : 0ull;
-                    __syncthreads();
-                }
                 if (bal == 0ull) break;
+                if (c) {
+                    const int b = __ffsll(static_cast<unsigned long long>(cmask)) - 1;
+                    const int e = (b & 32) + 31 - (b & 31);  // the element
+                    pend[npend + lanes_below(bal, lane)] = base + 256 * (e >> 2) + 4 * lane + (e & 3);
+                    cmask &= cmask - 1ull;
+                }
+                npend += __popcll(bal);
             }
+            __syncthreads();  // pend visible to every lane
+            for (int c0 = 0; c0 < npend; c0 += 64) chains(c0, min(npend - c0, 64));
         };
         batch(0, hv0);
         for (int base = 4096; base < sg.pages; base += 4096) {
             float4 hv[16];
             load_h(base, hv);
+            __syncthreads();  // the previous batch has read pend
             batch(base, hv);
         }
         // 3. the row's pages (k of them: every page of the exact top-k is a candidate)
@@ -827,7 +829,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
     }
 }
 
-size_t select_lds_bytes(const Dims &D) { return (384 + 2 * (size_t)D.d) * 4; }
+size_t select_lds_bytes(const Dims &D) { return (256 + 2 * (size_t)D.d + 4096) * 4; }
 
 hipError_t launch_score(const Dims &D, const void *meta, const int32_t *kv_off,
                         const int32_t *prefix_len, const Work &W, hipStream_t st) {
