@@ -280,7 +280,10 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     constexpr int VPR = DIM / 8;             // 16-byte vectors per row
     constexpr int NV = kPrepVecs / 2;        // vectors per thread and step
     extern __shared__ uint32_t qsm[];        // [G*B][RWP] q_t rows, then [G*B][RWS] fp32 squares
-    __shared__ float e_s[kMaxRows];
+    // localities as rank keys: the fp32 bits (localities are >= +0, so their
+    // bits order as the values) above ~token, so that "greater key" is
+    // "larger locality, or equal and earlier token"
+    __shared__ uint64_t ek_s[kMaxRows];
     __shared__ int sel_s[kMaxRows];
     __shared__ int act_s[kMaxRows];
     __shared__ int rbase_s[kMaxRows];        // stacked row r: word offset of its query row in qsm
@@ -392,13 +395,13 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         if (tid < B) {
             float acc = 0.0f;
             for (int h = 0; h < Hq; ++h) acc = acc + shl_s[h * B + tid];
-            e_s[tid] = acc;
+            ek_s[tid] = (static_cast<uint64_t>(__float_as_uint(acc)) << 32) | static_cast<uint32_t>(~tid);
         }
         __syncthreads();
         if (tid < B) {
-            const float et = e_s[tid];
+            const uint64_t kt = ek_s[tid];
             int rank = 0;
-            for (int u = 0; u < B; ++u) rank += (e_s[u] > et) || (e_s[u] == et && u < tid);
+            for (int u = 0; u < B; ++u) rank += ek_s[u] > kt;
             sel_s[tid] = rank < A;
         }
         __syncthreads();
@@ -430,7 +433,8 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
                     acc = acc + x[i].w;
                 }
             }
-            e_s[tid] = acc;
+            ek_s[tid] = (static_cast<uint64_t>(__float_as_uint(acc)) << 32) |
+                        static_cast<uint32_t>(~(tid % B));
             if (writer && dbg_loc)
                 dbg_loc[((size_t)s * Hq + g * G + tid / B) * B + tid % B] = acc / static_cast<float>(DIM);
         }
@@ -440,13 +444,10 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         const int j = tid / B, t = tid % B;
         bool sel = false;
         if (tid < GB) {
-            const float et = e_s[tid];
+            const uint64_t kt = ek_s[tid];
             int rank = 0;
 #pragma unroll 16
-            for (int u = 0; u < B; ++u) {
-                const float eu = e_s[j * B + u];
-                rank += (eu > et) || (eu == et && u < t);
-            }
+            for (int u = 0; u < B; ++u) rank += ek_s[j * B + u] > kt;
             sel = rank < A;
         }
         int pos = 0;
