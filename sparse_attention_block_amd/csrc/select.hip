@@ -115,21 +115,38 @@ __device__ __forceinline__ void bound_rowtile(const Dims &D, int rt, const uint4
     // lane holds rows rt*16 + 4*lg + j of pages cb*16 + l16
     if (tile_full && (rt + 1) * 16 <= R) {
         // every page of the tile and every row of the tile is live (uniform):
-        // no per-element guards; the row's maximum lower end as a float, then
-        // its order key (order keys are monotone, -0 and +0 alike)
+        // no per-element guards; the pages of a row are pl[0] + 16*cb (one
+        // address per row, constant offsets); the row's maximum lower end as a
+        // float, then its order key (monotone, -0 and +0 alike), reduced over
+        // the 16 lanes of the row for the 4 rows together
+        float *h0 = hb + (size_t)(rt * 16 + 4 * lg) * D.hb_stride + pl[0];
+        uint32_t lk[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = rt * 16 + 4 * lg + j;
+            float *hr = h0 + (size_t)j * D.hb_stride;
+            const float qe = kBoundRel * qa[j];
             float lm = -__builtin_huge_valf();
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
-                const float e = kBoundRel * qa[j] * amax[cb] + kBoundAbs;
+                const float e = qe * amax[cb] + kBoundAbs;
                 const float u = acc[cb][j];
-                hb[(size_t)r * D.hb_stride + pl[cb]] = u + e;
+                hr[16 * cb] = u + e;
                 lm = fmaxf(lm, u - e);
             }
-            const uint32_t lmax = row16_max_u32(ord_key(lm));
-            if (l16 == 15) tm[(size_t)r * D.n_tiles_grid + bx] = ord_to_f32(lmax);
+            lk[j] = ord_key(lm);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lk[j] = dpp_step_max<0x111, 0xf>(lk[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lk[j] = dpp_step_max<0x112, 0xf>(lk[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lk[j] = dpp_step_max<0x114, 0xf>(lk[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lk[j] = dpp_step_max<0x118, 0xf>(lk[j]);
+        if (l16 == 15) {
+            float *t0 = tm + (size_t)(rt * 16 + 4 * lg) * D.n_tiles_grid + bx;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t0[(size_t)j * D.n_tiles_grid] = ord_to_f32(lk[j]);
         }
         return;
     }
@@ -528,19 +545,24 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         uint2 h2[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) h2[kk] = *reinterpret_cast<const uint2 *>(qrow + 8 * kk);
+        // (q+, q-) pairs by byte permutes: a bf16 value goes to the low half of
+        // its word when its sign bit is clear, else to the high half (so -0 sits
+        // in the q- slot: a zero product either way); padding rows take the
+        // selector of four zero bytes
+        constexpr uint32_t kZero = 0x0c0c0c0cu;
+        const uint32_t lo_p = live ? 0x0c0c0100u : kZero, lo_n = live ? 0x01000c0cu : kZero;
+        const uint32_t hi_p = live ? 0x0c0c0302u : kZero, hi_n = live ? 0x03020c0cu : kZero;
+        auto split = [&](uint32_t x) {
+            const uint32_t ml = static_cast<uint32_t>(static_cast<int32_t>(x << 16) >> 31);  // sign of low
+            const uint32_t mh = static_cast<uint32_t>(static_cast<int32_t>(x) >> 31);        // sign of high
+            return make_uint2(__builtin_amdgcn_perm(x, x, (ml & lo_n) | (~ml & lo_p)),
+                              __builtin_amdgcn_perm(x, x, (mh & hi_n) | (~mh & hi_p)));
+        };
         uint4 aop[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            const uint32_t hw[4] = {h2[kk].x & 0xffffu, h2[kk].x >> 16, h2[kk].y & 0xffffu,
-                                    h2[kk].y >> 16};
-            uint32_t w4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // (q+, q-): q >= 0 (-0 included) -> low half, else high half
-                const bool pos = __uint_as_float(hw[e] << 16) >= 0.0f;
-                w4[e] = live ? (pos ? hw[e] : (hw[e] << 16)) : 0u;
-            }
-            aop[kk] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+            const uint2 a = split(h2[kk].x), b = split(h2[kk].y);
+            aop[kk] = make_uint4(a.x, a.y, b.x, b.y);
         }
         float qa[4];
 #pragma unroll
