@@ -340,10 +340,12 @@ __global__ __launch_bounds__(DIM) void k_finish_active(
     const float *mlp = part_ml + pr0 * 2;
     const float *acp = part_acc + pr0 * DIM + x;
     const int cs = rows * 2, as = rows * DIM;  // chunk strides (elements)
-    // a batch of kActBatch chunks: (m, l) once per chunk (thread c of the
-    // batch, through LDS), this thread's dimension of each chunk's output
-    __shared__ float s_m[kActBatch], s_l[kActBatch];
-    float mv[kActBatch], lv[kActBatch], av[kActBatch];
+    // a batch of kActBatch chunks: thread c of the batch reads chunk c's (m, l);
+    // wave 0 forms the batch's running maximum and each chunk's weight
+    // exp2(m - max) once, shared through LDS; every thread then combines its
+    // dimension of the chunks' outputs in chunk order
+    __shared__ float s_w[kActBatch], s_l[kActBatch], s_scale[2];  // weights, sums; factor, max
+    float av[kActBatch];
     auto load_ml = [&](int c0) {
         return *reinterpret_cast<const float2 *>(mlp + min(c0 + min(x, kActBatch - 1), nch - 1) * cs);
     };
@@ -355,29 +357,52 @@ __global__ __launch_bounds__(DIM) void k_finish_active(
     load_acc(0);
     __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
     const int nchu = (ucnt + D.sparse_chunk - 1) / D.sparse_chunk;  // chunks that wrote partials
-    PartAcc pa;
+    float mx = -__builtin_huge_valf(), ls = 0.0f, oa = 0.0f;  // running max, sum, output
     for (int c0 = 0; c0 < nchu; c0 += kActBatch) {
         if (c0 > 0) {
             ml = load_ml(c0);
             load_acc(c0);
-            __syncthreads();  // the previous batch's (m, l) have been read
+            __syncthreads();  // the previous batch's weights have been read
         }
-        if (x < kActBatch) {
-            s_m[x] = ml.x;
-            s_l[x] = ml.y;
+        const int n = min(kActBatch, nchu - c0);
+        if (x < 64) {
+            const bool v = x < n;
+            const float m = v ? ml.x : -__builtin_huge_valf();
+            float bm = m;  // maximum over the batch: butterflies over the wave
+            bm = fmaxf(bm, lane_xor1(bm));
+            bm = fmaxf(bm, lane_xor2(bm));
+            bm = fmaxf(bm, lane_xor7(bm));
+            bm = fmaxf(bm, lane_xor15(bm));
+            bm = fmaxf(bm, lane_xor16(bm));
+            bm = fmaxf(bm, lane_xor32(bm));
+            const float nm = fmaxf(mx, bm);
+            // (every chunk so far empty: zero weights, factor 1)
+            const bool none = nm == -__builtin_huge_valf();
+            if (x < kActBatch) {
+                s_w[x] = v && !none ? __builtin_amdgcn_exp2f(m - nm) : 0.0f;
+                s_l[x] = v ? ml.y : 0.0f;
+            }
+            if (x == 0) {
+                s_scale[0] = none ? 1.0f : __builtin_amdgcn_exp2f(mx - nm);
+                s_scale[1] = nm;
+            }
         }
         __syncthreads();
+        const float sc = s_scale[0];
+        mx = s_scale[1];
+        ls *= sc;
+        oa *= sc;
 #pragma unroll
         for (int i = 0; i < kActBatch; ++i) {
-            mv[i] = s_m[i];
-            lv[i] = s_l[i];
+            const float w = s_w[i];
+            ls = fmaf(w, s_l[i], ls);
+            oa = fmaf(w, i < n ? av[i] : 0.0f, oa);  // (chunks past the batch: clamped reads)
         }
-        pa.add(mv, lv, av, min(kActBatch, nchu - c0));
     }
     float op = 0.0f, lp2 = -__builtin_huge_valf();
     if (nchu > 0) {
-        op = pa.oa / pa.ls;
-        lp2 = pa.mx + __log2f(pa.ls);
+        op = oa / ls;
+        lp2 = mx + __log2f(ls);
     }
     const size_t crow = ((size_t)s * D.Hq + h) * B + tok;
     if (!(D.flags & LOSA_FLAG_NO_WRITEBACK)) {  // else the caches keep the dense statistics

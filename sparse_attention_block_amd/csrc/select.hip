@@ -435,19 +435,25 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         if (tid < GB) {
             const float4 *sr = reinterpret_cast<const float4 *>(sq + tid * RWS);
             float acc = 0.0f;
-            constexpr int RB = 8;  // 16-byte reads requested together
+            // 16-byte reads in batches of RB, the next batch requested before
+            // the adds of this one
+            constexpr int RB = 8, NB = DIM / 4 / RB;
+            float4 x[2][RB];
 #pragma unroll
-            for (int v0 = 0; v0 < DIM / 4; v0 += RB) {
-                float4 x[RB];
+            for (int i = 0; i < RB; ++i) x[0][i] = sr[i];
 #pragma unroll
-                for (int i = 0; i < RB; ++i) x[i] = sr[v0 + i];
-                __builtin_amdgcn_sched_barrier(0);  // the batch is requested before the adds
+            for (int b = 0; b < NB; ++b) {
+                if (b + 1 < NB) {
+#pragma unroll
+                    for (int i = 0; i < RB; ++i) x[(b + 1) & 1][i] = sr[(b + 1) * RB + i];
+                }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < RB; ++i) {
-                    acc = acc + x[i].x;
-                    acc = acc + x[i].y;
-                    acc = acc + x[i].z;
-                    acc = acc + x[i].w;
+                    acc = acc + x[b & 1][i].x;
+                    acc = acc + x[b & 1][i].y;
+                    acc = acc + x[b & 1][i].z;
+                    acc = acc + x[b & 1][i].w;
                 }
             }
             ek_s[tid] = (static_cast<uint64_t>(__float_as_uint(acc)) << 32) |
