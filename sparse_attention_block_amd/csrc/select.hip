@@ -756,8 +756,10 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         // qualifies) is below every finite value
         const float lamf = lam == 0u ? -__builtin_huge_valf() : ord_to_f32(lam);
         // exact chains of the pending pages pend[c0 .. c0 + n), n <= 64, merged
-        // into the list: rank every key of (chains, current list) among all of
-        // them (keys are distinct: one per page); rank e < k -> lane e
+        // into the list: a key's rank is the number of greater keys among the
+        // chains' (lanes < n) and the list's (lanes < nlst), read lane by lane
+        // into scalar registers (keys are distinct: one per page); the key of
+        // rank e < k goes to lane e through LDS
         auto chains = [&](int c0, int n) {
             uint64_t cand = 0ull;
             if (lane < n) {
@@ -767,25 +769,27 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                        static_cast<uint32_t>(~static_cast<uint32_t>(pc));
             }
             const int nlst = __popcll(__ballot(lane < k && lst != 0ull));
-            if (lane < n) mk[lane] = cand;
-            if (lane < nlst) mk[n + lane] = lst;
-            __syncthreads();
-            const int tot = n + nlst;
-            const uint64_t x0 = lane < tot ? mk[lane] : 0ull;
-            const uint64_t x1 = lane + 64 < tot ? mk[lane + 64] : 0ull;
-            int r0 = 0, r1 = 0;
-#pragma unroll 4
-            for (int i = 0; i < tot; ++i) {
-                const uint64_t y = mk[i];
-                r0 += y > x0;
-                r1 += y > x1;
+            auto lane_key = [](uint64_t v, int i) {
+                const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), i);
+                const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), i);
+                return (static_cast<uint64_t>(hi) << 32) | lo;
+            };
+            int rc = 0, rl = 0;
+            for (int i = 0; i < n; ++i) {
+                const uint64_t y = lane_key(cand, i);
+                rc += y > cand;
+                rl += y > lst;
             }
+            for (int e = 0; e < nlst; ++e) {
+                const uint64_t y = lane_key(lst, e);
+                rc += y > cand;
+                rl += y > lst;
+            }
+            __syncthreads();  // the previous list has been read from mk
+            if (lane < n && rc < k) mk[rc] = cand;
+            if (lane < nlst && rl < k) mk[rl] = lst;
             __syncthreads();
-            if (lane < tot && r0 < k) mk[r0] = x0;
-            if (lane + 64 < tot && r1 < k) mk[r1] = x1;
-            __syncthreads();
-            lst = lane < min(tot, k) ? mk[lane] : 0ull;
-            __syncthreads();
+            lst = lane < min(n + nlst, k) ? mk[lane] : 0ull;
         };
         // The largest float below lamf: hx >= lamf is then lamb - hx < 0, the
         // sign bit of one subtraction (exact in sign: denormals are kept).
