@@ -233,6 +233,24 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
         s_l0[t][x] = ml0.y;
     }
     __syncthreads();
+    // the first batch's chunk weights, once per (token, chunk): lane c of the
+    // token's first wave takes chunk c, after the batch maximum by lane
+    // butterflies (published by the barriers of the block softmax below)
+    __shared__ float s_w0[kFinishMaxThreads / 64][kDenseBatch], s_mx0[kFinishMaxThreads / 64];
+    static_assert(kDenseBatch == 64, "one chunk per lane of a wave");
+    if (x < 64) {
+        const bool v = x < min(nchu, kDenseBatch);
+        const float m = v ? s_m0[t][x] : -__builtin_huge_valf();
+        float bm = m;
+        bm = fmaxf(bm, lane_xor1(bm));
+        bm = fmaxf(bm, lane_xor2(bm));
+        bm = fmaxf(bm, lane_xor7(bm));
+        bm = fmaxf(bm, lane_xor15(bm));
+        bm = fmaxf(bm, lane_xor16(bm));
+        bm = fmaxf(bm, lane_xor32(bm));
+        s_w0[t][x] = v && bm != -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(m - bm) : 0.0f;
+        if (x == 0) s_mx0[t] = bm;
+    }
     {
         // softmax over each token's B scores: lanes (token, key) in segments of
         // Bp = B rounded up to a power of two (nt * Bp <= 256 threads)
@@ -283,14 +301,18 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     }
     // the row's prefix statistics, in chunk order; they overwrite the cache
     PartAcc pa;
-    {
-        float mv[kDenseBatch], lv[kDenseBatch];
+    if (nchu > 0) {
+        const int nb = min(nchu, kDenseBatch);
+        float ls = 0.0f, oa = 0.0f;
 #pragma unroll
         for (int i = 0; i < kDenseBatch; ++i) {
-            mv[i] = s_m0[t][i];
-            lv[i] = s_l0[t][i];
+            const float w = s_w0[t][i];
+            ls = fmaf(w, s_l0[t][i], ls);
+            oa = fmaf(w, i < nb ? av0[i] : 0.0f, oa);
         }
-        pa.add(mv, lv, av0, min(nchu, kDenseBatch));
+        pa.mx = s_mx0[t];
+        pa.ls = ls;
+        pa.oa = oa;
     }
     for (int c0 = kDenseBatch; c0 < nchu; c0 += kPartBatch) {
         float mv[kPartBatch], lv[kPartBatch], av[kPartBatch];
