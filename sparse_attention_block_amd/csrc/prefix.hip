@@ -26,6 +26,8 @@ namespace losa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // Reductions over the lanes l, l^16, l^32, l^48 (the 4 lane rows of 16).
@@ -122,22 +124,50 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
     bool full[NP];
 #pragma unroll
     for (int n = 0; n < NP; ++n) full[n] = valid[n] >= kPage;  // uniform
-    // V^T operands: output dim DPL*(l%16) + e, tokens 4*lg .. 4*lg+3
-    short4_t vop[NP][DPL];
+    // V^T operands: output dim DPL*(l%16) + e, tokens 4*lg .. 4*lg+3 of a
+    // page, as two words (tokens 0,1 and 2,3) from byte permutes of the
+    // tokens' words; for page pairs both pages' words are formed straight
+    // into one 4-register operand (no register moves).  Tokens past the
+    // prefix get zero values.
+    constexpr int NPP = NP % 2 == 0 ? NP / 2 : 1;
+    u32x4_t vpair[NPP][DPL];
+    short4_t vop[NP % 2 == 0 ? 1 : NP][DPL];
+    auto tok2 = [&](int n, int j, int e) {  // tokens j, j+1 of page n, dim half e&1 of word e/2
+        return __builtin_amdgcn_perm(vw[n][j + 1][e >> 1], vw[n][j][e >> 1],
+                                     (e & 1) ? 0x07060302u : 0x05040100u);
+    };
+    auto page_masks = [&](int n, uint32_t &m0, uint32_t &m1) {
+        m0 = (4 * lg + 0 < valid[n] ? 0x0000ffffu : 0u) | (4 * lg + 1 < valid[n] ? 0xffff0000u : 0u);
+        m1 = (4 * lg + 2 < valid[n] ? 0x0000ffffu : 0u) | (4 * lg + 3 < valid[n] ? 0xffff0000u : 0u);
+    };
+    if constexpr (NP % 2 == 0) {
 #pragma unroll
-    for (int n = 0; n < NP; ++n) {
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-            const int q = e >> 1, sh = (e & 1) * 16;
-            vop[n][e] = short4_t{static_cast<short>(vw[n][0][q] >> sh), static_cast<short>(vw[n][1][q] >> sh),
-                                 static_cast<short>(vw[n][2][q] >> sh), static_cast<short>(vw[n][3][q] >> sh)};
-        }
-        if (!full[n]) {  // tokens past the prefix get zero values (uniform branch)
+        for (int np = 0; np < NPP; ++np) {
 #pragma unroll
             for (int e = 0; e < DPL; ++e)
+                vpair[np][e] = u32x4_t{tok2(2 * np, 0, e), tok2(2 * np, 2, e), tok2(2 * np + 1, 0, e),
+                                       tok2(2 * np + 1, 2, e)};
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (4 * lg + j >= valid[n]) vop[n][e][j] = 0;
+            for (int h = 0; h < 2; ++h) {
+                if (!full[2 * np + h]) {  // uniform branch
+                    uint32_t m0, m1;
+                    page_masks(2 * np + h, m0, m1);
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) {
+                        vpair[np][e][2 * h] &= m0;
+                        vpair[np][e][2 * h + 1] &= m1;
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            uint32_t m0 = ~0u, m1 = ~0u;
+            if (!full[n]) page_masks(n, m0, m1);
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                vop[n][e] = __builtin_bit_cast(short4_t, u32x2_t{tok2(n, 0, e) & m0, tok2(n, 2, e) & m1});
         }
     }
 #pragma unroll
@@ -187,7 +217,7 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
         }
         // (with masks a row may have seen no score yet: its weights are zero)
         const float mn = MASK && m_run[i] == -__builtin_huge_valf() ? 0.0f : m_run[i];
-        uint2 pw[NP];  // the lane's weights of page n (tokens 4*lg .. +3), bf16
+        u32x2_t pw[NP];  // the lane's weights of page n (tokens 4*lg .. +3), bf16
 #pragma unroll
         for (int n = 0; n < NP; ++n) {
             const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][0] - mn)),
@@ -196,7 +226,7 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
                                   static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][3] - mn))};
             const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
             l_run[i] += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
-            pw[n] = make_uint2(w01, w23);
+            pw[n] = u32x2_t{w01, w23};
         }
         if constexpr (NP % 2 == 0) {
             // pages n and n+1 in one v_mfma_f32_16x16x32_bf16: its k index
@@ -204,13 +234,11 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
             // operands (the sum over k does not depend on the order)
 #pragma unroll
             for (int n = 0; n < NP; n += 2) {
-                const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[n].x, pw[n].y, pw[n + 1].x, pw[n + 1].y));
+                const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[n].x, pw[n].y, pw[n + 1].x, pw[n + 1].y});
 #pragma unroll
-                for (int e = 0; e < DPL; ++e) {
-                    const uint2 v0 = __builtin_bit_cast(uint2, vop[n][e]), v1 = __builtin_bit_cast(uint2, vop[n + 1][e]);
-                    const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
-                    oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop, oacc[i][e], 0, 0, 0);
-                }
+                for (int e = 0; e < DPL; ++e)
+                    oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, vpair[n / 2][e]), pop, oacc[i][e], 0, 0, 0);
             }
         } else {
 #pragma unroll
@@ -735,8 +763,6 @@ __device__ __forceinline__ int swz(int t, int c) {
     constexpr int CPT = DIM / 8;  // 16-byte chunks per token row
     return t * CPT + (c ^ (t & (CPT - 1)));
 }
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // The K and V operands of two LDS page slots (slot stride PS bytes) in one
 // block of ds_read_b128: ak[kk] / av[j] are the lane's byte addresses of K
