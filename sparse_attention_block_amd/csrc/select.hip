@@ -637,7 +637,10 @@ __device__ __forceinline__ float exact_bound(const uint4 *meta, const Dims &D, i
     return acc;
 }
 
-template <int DIM, bool BF>
+// MAXB: the block-size bound of the in-block attention workgroups (16, 32 or
+// 64), a template parameter so that the larger blocks' registers do not lower
+// the occupancy of launches with small blocks.
+template <int DIM, bool BF, int MAXB>
 __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__ meta,
                                                const int32_t *__restrict__ kv_off,
                                                const int32_t *__restrict__ prefix_len, Work W,
@@ -659,10 +662,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         const T *q = static_cast<const T *>(blk.q_t), *kb = static_cast<const T *>(blk.k_blk),
                 *vb = static_cast<const T *>(blk.v_blk);
         T *o = static_cast<T *>(blk.out);
-        if (D.B <= 16)
-            block_token<T, DIM, 16>(D, q, kb, vb, W, blk.op_cache, blk.lp_cache, o, smem, s, h, t);
-        else
-            block_token<T, DIM, 64>(D, q, kb, vb, W, blk.op_cache, blk.lp_cache, o, smem, s, h, t);
+        block_token<T, DIM, MAXB>(D, q, kb, vb, W, blk.op_cache, blk.lp_cache, o, smem, s, h, t);
         return;
     }
     const int sgi = blockIdx.x % ng;
@@ -922,21 +922,31 @@ hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
                          const int32_t *prefix_len, const Work &W, int32_t *dbg_page_sel,
                          const BlockArgs &blk, hipStream_t st) {
     const int ng = D.S * D.Hk;
-    const size_t blk_lds = D.B <= 16 ? block_lds_bytes<16>(D.d, D.bf16) : block_lds_bytes<64>(D.d, D.bf16);
+    const int maxb = D.B <= 16 ? 16 : (D.B <= 32 ? 32 : 64);
+    const size_t blk_lds = maxb == 16   ? block_lds_bytes<16>(D.d, D.bf16)
+                           : maxb == 32 ? block_lds_bytes<32>(D.d, D.bf16)
+                                        : block_lds_bytes<64>(D.d, D.bf16);
     const size_t lds = std::max(D.R > 0 ? select_lds_bytes(D) : 0, blk_lds);
     const dim3 grid(ng * D.R + D.S * D.Hq * D.B);  // selection rows, then block tokens
     SelectDbg dbg{dbg_page_sel};
     auto *m = static_cast<const uint4 *>(meta);
-#define LAUNCH_S(DIMV, BFV)                                                                      \
-    hipLaunchKernelGGL((k_select<DIMV, BFV>), grid, dim3(64), lds, st, D, m, kv_off,             \
+#define LAUNCH_S(DIMV, BFV, MB)                                                                  \
+    hipLaunchKernelGGL((k_select<DIMV, BFV, MB>), grid, dim3(64), lds, st, D, m, kv_off,         \
                        prefix_len, W, W.qrows, W.qsel32, W.hbound, W.tmax, dbg, blk)
+#define PICK_S(DIMV, BFV)                           \
+    do {                                            \
+        if (maxb == 16) LAUNCH_S(DIMV, BFV, 16);    \
+        else if (maxb == 32) LAUNCH_S(DIMV, BFV, 32); \
+        else LAUNCH_S(DIMV, BFV, 64);               \
+    } while (0)
     if (D.bf16) {
-        if (D.d == 128) LAUNCH_S(128, true);
-        else LAUNCH_S(64, true);
+        if (D.d == 128) PICK_S(128, true);
+        else PICK_S(64, true);
     } else {
-        if (D.d == 128) LAUNCH_S(128, false);
-        else LAUNCH_S(64, false);
+        if (D.d == 128) PICK_S(128, false);
+        else PICK_S(64, false);
     }
+#undef PICK_S
 #undef LAUNCH_S
     return hipGetLastError();
 }

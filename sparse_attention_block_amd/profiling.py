@@ -31,7 +31,7 @@ KERNEL_TAGS = {
     "dense_prefix": (r"k_prefix_dense_bf16<\d+, \d+, \d+>", ["prefix.hip", "losa_internal.h"]),
     "sparse_prefix": (r"k_prefix_quarter_bf16<\d+, \d+, false>", ["prefix.hip", "losa_internal.h"]),
     "page_score": (r"k_score_prep<\d+, false>", ["select.hip", "block_attn.h", "losa_internal.h"]),
-    "page_select": (r"k_select<\d+, true>", ["select.hip", "block_attn.h", "losa_internal.h"]),
+    "page_select": (r"k_select<\d+, true, \d+>", ["select.hip", "block_attn.h", "losa_internal.h"]),
     "sparse_finish": (r"k_finish_active<unsigned short, \d+>", ["finish.hip", "losa_internal.h"]),
     "dense_finish": (r"k_finish<unsigned short, \d+>", ["finish.hip", "losa_internal.h"]),
     "page_meta": (r"k_page_meta<unsigned short, \d+>", ["page_meta.hip", "losa_internal.h"]),
