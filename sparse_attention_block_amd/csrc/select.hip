@@ -71,13 +71,6 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
     return v;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    const uint32_t hi = wave_max_u32(static_cast<uint32_t>(v >> 32));
-    const uint32_t lo =
-        wave_max_u32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0u);
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
 __device__ __forceinline__ float ord_to_f32(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
