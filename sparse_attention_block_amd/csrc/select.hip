@@ -518,6 +518,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         int32_t *act = W.active + ((size_t)s * Hq + g * G) * A;  // [G][A], rows j*A + a
         for (int i = tid; i < R; i += 256) {
             act[i] = act_s[i];
+            W.qabs[(size_t)sgi * R1 + i] = qabs_s[i];  // for the selection's short-sequence threshold
             if (dbg_act) dbg_act[((size_t)s * Hq + g * G) * A + i] = act_s[i];
         }
         uint16_t *qr = static_cast<uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
@@ -733,8 +734,38 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         // the threshold is the largest key with 16 low zero bits that at least
         // k lanes reach, found bit by bit with ballots -- the k-th largest key
         // with its low 16 bits cleared (within 2^-7 of it as a float).
+        // A sequence with fewer tiles than k (fewer than 4096 pages, so every
+        // page is in the first batch) takes each lane's maximum over its pages
+        // of a lower end formed from the upper end: u + e rounded is hx, so u - e
+        // >= hx - 2e - (|hx| + 2e) * 2^-21 whatever the roundings, with e the
+        // scoring kernel's bound recomputed from the same operands (the row's
+        // sum |q| and the page's max |k|).  Each lane's maximum is reached by a
+        // page of its own, so the k-th largest of them is again a valid
+        // threshold.  (Lanes without pages keep key 0.)
+        const bool short_seq = min(n_t, 64) < k && sg.pages >= 4 * k;  // uniform
+        if (short_seq) {
+            const float qa = W.qabs[(size_t)sgi * R1 + r];
+            const float *am = reinterpret_cast<const float *>(reinterpret_cast<const char *>(meta) +
+                                                              D.meta_main_bytes) +
+                              (size_t)g * D.n_tiles_total * kTile + sg.gp0;
+            float lmax = -__builtin_huge_valf();
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                if (256 * jj < sg.pages) {  // uniform
+                    const float hx[4] = {hv0[jj].x, hv0[jj].y, hv0[jj].z, hv0[jj].w};
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        const int p = 256 * jj + 4 * lane + e4;
+                        const float e = kBoundRel * qa * am[min(p, sg.pages - 1)] + kBoundAbs;
+                        const float lo = (hx[e4] - 2.0f * e) - (fabsf(hx[e4]) + 2.0f * e) * (1.0f / 2097152.0f);
+                        if (p < sg.pages) lmax = fmaxf(lmax, lo);
+                    }
+                }
+            }
+            gm = lmax == -__builtin_huge_valf() ? 0u : ord_key(lmax);
+        }
         uint32_t lam = 0u;  // below every finite key: all pages qualify
-        if (min(n_t, 64) >= k) {
+        if (min(n_t, 64) >= k || short_seq) {
 #pragma unroll
             for (int b = 31; b >= 16; --b) {
                 const uint32_t c = lam | (1u << b);
