@@ -646,13 +646,15 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
     extern __shared__ uint32_t smem[];
     const int ng = D.S * D.Hk;
     if (blockIdx.x >= ng * D.R) {
-        // one token's in-block attention: workgroup ng*R + u*ng + (s*Hk + g) for
-        // token t = u % B of head g*G + u / B, so that a group's tokens run on
-        // the XCD of its selection and prefix workgroups (ng a multiple of 8)
+        // in-block attention of kBlockTPW tokens: workgroup ng*R + u*ng +
+        // (s*Hk + g) for tokens kBlockTPW*(u % ntg) .. of head g*G + u / ntg, so
+        // that a group's tokens run on the XCD of its selection and prefix
+        // workgroups (ng a multiple of 8)
         using T = typename std::conditional<BF, uint16_t, float>::type;
+        const int ntg = (D.B + kBlockTPW - 1) / kBlockTPW;
         const int b = blockIdx.x - ng * D.R;
         const int sg2 = b % ng, u = b / ng;
-        const int t = u % D.B, s = sg2 / D.Hk, h = (sg2 % D.Hk) * D.G + u / D.B;
+        const int t = (u % ntg) * kBlockTPW, s = sg2 / D.Hk, h = (sg2 % D.Hk) * D.G + u / ntg;
         const T *q = static_cast<const T *>(blk.q_t), *kb = static_cast<const T *>(blk.k_blk),
                 *vb = static_cast<const T *>(blk.v_blk);
         T *o = static_cast<T *>(blk.out);
@@ -951,7 +953,8 @@ hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
                            : maxb == 32 ? block_lds_bytes<32>(D.d, D.bf16)
                                         : block_lds_bytes<64>(D.d, D.bf16);
     const size_t lds = std::max(D.R > 0 ? select_lds_bytes(D) : 0, blk_lds);
-    const dim3 grid(ng * D.R + D.S * D.Hq * D.B);  // selection rows, then block tokens
+    const int ntg = (D.B + kBlockTPW - 1) / kBlockTPW;
+    const dim3 grid(ng * D.R + D.S * D.Hq * ntg);  // selection rows, then block token groups
     SelectDbg dbg{dbg_page_sel};
     auto *m = static_cast<const uint4 *>(meta);
 #define LAUNCH_S(DIMV, BFV, MB)                                                                  \
