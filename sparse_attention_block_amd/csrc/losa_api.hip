@@ -67,6 +67,7 @@ Dims make_dims(const losa_shape *sh) {
     D.T = sh->kv_tokens;
     D.n_tiles_total = (D.T / kPage + kTile - 1) / kTile;
     D.meta_main_bytes = static_cast<int64_t>(meta_main_bytes(D));
+    D.meta_pm_off = D.meta_main_bytes + D.Hk * D.n_tiles_total * kTile * 4;
     D.n_tiles_grid = (D.max_pages + kTile - 1) / kTile + 1;
     D.R = D.G * D.A;
     D.Rs16 = (D.R + 15) / 16 * 16;
@@ -132,7 +133,8 @@ size_t carve(const Dims &D, char *base, Work *W) {
 }
 
 size_t meta_bytes(const Dims &D) {
-    return meta_main_bytes(D) + (size_t)D.Hk * D.n_tiles_total * kTile * 4;
+    // chunk-major min/max, largest |key| per page, page-major min/max
+    return 2 * meta_main_bytes(D) + (size_t)D.Hk * D.n_tiles_total * kTile * 4;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LOSA_OK : LOSA_ERR_HIP; }

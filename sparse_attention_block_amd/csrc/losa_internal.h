@@ -40,6 +40,7 @@ struct Dims {
     int64_t T;                        // kv_tokens
     int64_t n_tiles_total;            // metadata tiles per KV head over the whole cache
     int64_t meta_main_bytes;          // bytes of the min/max part of the page metadata
+    int64_t meta_pm_off;              // byte offset of its page-major copy
     int n_tiles_grid;                 // tiles a sequence can touch
     int union_cap;                    // min(max_pages, G*A*k)
     int R;                            // stacked active rows per KV head = G*A

@@ -14,6 +14,11 @@
 // v_mfma_f32_16x16x32_bf16 for 8 consecutive k-slots (max_i, min_i pairs).
 // After the min/max part follows, per KV head and global page, the largest
 // |key| element of the page (fp32), which bounds the error of MFMA scoring.
+// Last comes a page-major copy of the min/max part: per KV head and global
+// page, the page's chunks 0 .. DIM/DPC - 1 back to back (DIM*2 element sizes
+// contiguous), for the exact bound of selection, whose lanes each take one
+// page scattered over the prefix: one page then fills whole cache lines
+// instead of one 16-byte piece of a line per chunk.
 #include "losa_internal.h"
 
 namespace losa {
@@ -109,6 +114,8 @@ __global__ __launch_bounds__(256) void k_page_meta(Dims D, const T *__restrict__
                            __float_as_uint(mx[2 * m + 1]), __float_as_uint(mn[2 * m + 1]));
         }
         reinterpret_cast<uint4 *>(meta)[((size_t)(g * D.n_tiles_total + tile) * NCH + c) * kTile + lane] = u;
+        reinterpret_cast<uint4 *>(reinterpret_cast<char *>(meta) + D.meta_pm_off)
+            [((size_t)g * D.n_tiles_total * kTile + gp) * NCH + c] = u;
     }
     if (cc == 0) {
         float *aux = reinterpret_cast<float *>(reinterpret_cast<char *>(meta) + D.meta_main_bytes);

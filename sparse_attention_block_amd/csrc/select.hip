@@ -580,10 +580,11 @@ struct SelectDbg {
 };
 
 // The exact chain for global page gp (contract of include/losa.h); the page's
-// metadata chunks are loaded before the chain starts.  bf16: qw holds the
-// row's query values as fp32 (DIM words), then per dimension the byte
-// selector that turns the metadata word (max | min << 16) into the fp32 bits
-// of max_i (q >= 0, -0 included) or of min_i (q < 0); per dimension one fused
+// metadata chunks are loaded, from the page-major copy, before the chain
+// starts.  bf16: qw holds the row's query values as fp32 (DIM words), then per
+// dimension the byte selector that turns the metadata word (max | min << 16)
+// into the fp32 bits of max_i (q >= 0, -0 included) or of min_i (q < 0); per
+// dimension one fused
 // multiply-add with that value -- the same value as the pair q+ * max then
 // q- * min, whose other product is an exact zero.  fp32: qw holds (max(q,0),
 // min(q,0)) per dimension, each product rounded, then added.
@@ -594,14 +595,17 @@ __device__ __forceinline__ float exact_bound(const uint4 *meta, const Dims &D, i
                                              const uint32_t *qw) {
     constexpr int DPC = BF ? 4 : 2;
     constexpr int NCH = DIM / DPC;
-    const uint4 *m = meta + (size_t)(g * D.n_tiles_total + gp / kTile) * NCH * kTile + gp % kTile;
+    // the page-major copy: the page's chunks are contiguous
+    const uint4 *m =
+        reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(meta) + D.meta_pm_off) +
+        ((size_t)g * D.n_tiles_total * kTile + gp) * NCH;
     float acc = 0.0f;
     constexpr int BATCH = NCH < 32 ? NCH : 32;
 #pragma unroll
     for (int c0 = 0; c0 < NCH; c0 += BATCH) {
         uint4 mv[BATCH];
 #pragma unroll
-        for (int c = 0; c < BATCH; ++c) mv[c] = m[(size_t)(c0 + c) * kTile];
+        for (int c = 0; c < BATCH; ++c) mv[c] = m[c0 + c];
 #pragma unroll
         for (int c = 0; c < BATCH; ++c) {
             const uint4 m4 = mv[c];

@@ -52,7 +52,7 @@ def test_sizes(cfg):
     s_t = 2 if cfg.dtype == "bf16" else 4
     tiles = (T // 16 + 63) // 64
     # min/max pairs per (page, dimension), then one fp32 max |key| per page
-    assert L.page_meta_bytes(sh) == cfg.n_kvhead * tiles * 64 * (cfg.head_dim * 2 * s_t + 4)
+    assert L.page_meta_bytes(sh) == cfg.n_kvhead * tiles * 64 * (2 * cfg.head_dim * 2 * s_t + 4)
     ws = L.workspace_bytes(sh)
     assert 0 < ws < 1 << 31
 

@@ -2,8 +2,8 @@
 maxima, and the block-commit update (losa_update_page_meta) against a full
 rebuild at the new prefix lengths.  The library's documented metadata layout
 (page_meta.hip: per KV head, tiles of 64 pages; chunk c of every page of a tile
-back to back, 16 bytes per page; then the largest |key| of every page) is
-decoded on the host."""
+back to back, 16 bytes per page; then the largest |key| of every page; then
+the page-major copy, each page's chunks back to back) is decoded on the host."""
 import numpy as np
 import pytest
 import torch
@@ -34,6 +34,9 @@ def decode(meta: np.ndarray, cfg, kv_tokens: int):
     main = Hk * n_tiles * 64 * d * 2 * (2 if bf else 4)
     u = meta[:main].view(np.uint32).reshape(Hk, n_tiles, nch, 64, 4)
     u = u.transpose(0, 1, 3, 2, 4).reshape(Hk, n_tiles * 64, nch, 4)[:, :TP]
+    pm_off = main + Hk * n_tiles * 64 * 4
+    pm = meta[pm_off:pm_off + main].view(np.uint32).reshape(Hk, n_tiles * 64, nch, 4)[:, :TP]
+    assert np.array_equal(pm, u), "page-major copy differs from the chunk-major metadata"
     if bf:  # one word per dimension: max in the low half, min in the high half
         kmax = (u << 16).view(np.float32).reshape(Hk, TP, d)
         kmin = (u & 0xFFFF0000).view(np.float32).reshape(Hk, TP, d)
