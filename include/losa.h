@@ -156,7 +156,10 @@ typedef struct losa_debug {
 /* Human-readable name of a status code (static string). */
 const char *losa_status_string(int status);
 
-/* Bytes of the page metadata for this shape's cache (0 if the shape is invalid). */
+/* Bytes of the page metadata for this shape's cache (0 if the shape is invalid):
+ * per KV head and page of the whole cache, the page's per-dimension min and
+ * max twice (two layouts: one for scoring, one for the exact bounds of
+ * selection), 4 * head_dim element sizes, plus one fp32 (the largest |key|). */
 size_t losa_page_meta_bytes(const losa_shape *shape);
 
 /* Workspace bytes that losa_step and losa_dense_first_step need (0 if invalid). */
