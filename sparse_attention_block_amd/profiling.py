@@ -22,6 +22,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -120,6 +121,45 @@ def print_sweep(path: str, command: str):
                   f"{r['model_step_us']:.0f} us (dense first step {r['model_dense_step_us']:.0f} us).")
 
 
+def resource_rows() -> list:
+    """Per-kernel register, scratch, occupancy and static LDS figures of the
+    library's kernels, from the compiler's resource-usage remarks when each
+    source is compiled for the device with the library's own flags."""
+    import tempfile
+    from . import build as B
+    remarks = []
+    with tempfile.TemporaryDirectory() as td:
+        for src in B.SOURCES:
+            r = subprocess.run([B.HIPCC, *B.FLAGS, "--cuda-device-only", "-c", os.path.join(B.CSRC, src),
+                                "-o", os.path.join(td, src + ".o"), "-Rpass-analysis=kernel-resource-usage"],
+                               stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"device compile of {src} failed")
+            remarks += r.stdout.splitlines()
+    rows, cur = [], None
+    for line in remarks:
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = {"mangled": m.group(1)}
+            rows.append(cur)
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|TotalSGPRs|ScratchSize \[bytes/lane\]|"
+                      r"Occupancy \[waves/SIMD\]|LDS Size \[bytes/block\]): (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).split()[0]] = int(m.group(2))
+    names = subprocess.run(["c++filt"], input="\n".join(r["mangled"] for r in rows),
+                           stdout=subprocess.PIPE, text=True).stdout.splitlines()
+    out = []
+    for r, n in zip(rows, names):
+        n = re.sub(r"\(.*$", "", n)
+        n = n[5:] if n.startswith("void ") else n
+        if n.startswith("losa::k_"):
+            out.append((n.replace("unsigned short", "bf16"), r.get("VGPRs", 0), r.get("AGPRs", 0),
+                        r.get("TotalSGPRs", 0), r.get("ScratchSize", 0), r.get("Occupancy", 0),
+                        r.get("LDS", 0)))
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -135,7 +175,19 @@ def main(argv=None):
     s3 = sub.add_parser("sweep")
     s3.add_argument("json")
     s3.add_argument("--command", required=True)
+    sub.add_parser("resources")
     a = ap.parse_args(argv)
+
+    if a.cmd == "resources":
+        print("# gfx950 resource usage of the library's kernels (compiler remarks)\n"
+              "# command: python3 -m sparse_attention_block_amd.profiling resources\n"
+              "# waves/SIMD is the compiler's bound from registers and static LDS; the\n"
+              "# dynamic LDS a launch asks for (not counted here) can lower it further\n")
+        print(f"{'kernel':52s} {'VGPRs':>5s} {'AGPRs':>5s} {'SGPRs':>5s} {'scratch':>7s} "
+              f"{'waves/SIMD':>10s} {'static_LDS':>10s}")
+        for n, v, ag, sg, sc, oc, lds in resource_rows():
+            print(f"{n[:52]:52s} {v:5d} {ag:5d} {sg:5d} {sc:7d} {oc:10d} {lds:10d}")
+        return 0
 
     if a.cmd == "sweep":
         print_sweep(a.json, a.command)
