@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from concurrent.futures import ThreadPoolExecutor
 from ctypes import POINTER, c_double, c_float, c_int, c_int32, c_int64
 
 import numpy as np
@@ -229,6 +230,84 @@ class Oracle:
                                   _d(lp), _f(out))
         return op, float(lp[0]), out
 
+    def dense_rows(self, q_t, k_blk, v_blk, rows, threads=None):
+        """oracle_dense_row for each (s, h, t) of ``rows``, on a pool of threads
+        (ctypes releases the interpreter lock during each call, and every call
+        reads shared inputs and writes only its own outputs).  Returns (o_p
+        [n][d] float64, L_p [n] float64, out rows [n][d] float32); the cache is
+        not touched."""
+        q_t, k_blk, v_blk = _f32(q_t), _f32(k_blk), _f32(v_blk)
+        with ThreadPoolExecutor(max_workers=threads or host_threads()) as ex:
+            res = list(ex.map(lambda r: self.dense_row(q_t, k_blk, v_blk, *r), rows))
+        return (np.stack([r[0] for r in res]), np.array([r[1] for r in res]),
+                np.stack([r[2] for r in res]))
+
+    def dense_first_step_threaded(self, q_t, k_blk, v_blk, threads=None):
+        """dense_first_step computed row by row over a thread pool: the same
+        per-row arithmetic (oracle_dense_row), so the same bits."""
+        c = self.cfg
+        rows = [(s, h, t) for s in range(c.n_seq) for h in range(c.n_qhead) for t in range(c.block)]
+        op, lp, out_rows = self.dense_rows(q_t, k_blk, v_blk, rows, threads)
+        out = np.zeros((c.n_seq, c.block, c.n_qhead, c.head_dim), np.float32)
+        for i, (s, h, t) in enumerate(rows):
+            self.op[s, h, t] = op[i]
+            self.lp[s, h, t] = lp[i]
+            out[s, t, h] = out_rows[i]
+        return out
+
+    def step_threaded(self, q_t, q_prev, k_blk, v_blk, threads=None):
+        """step() as independent per-KV-head sub-problems on a pool of threads.
+
+        A KV head's group of query heads, its pages, union, prefix attention,
+        block attention and cache rows depend on no other KV head (the active
+        sets are per query head), so oracle_step on each group alone -- shape
+        with n_qhead = G, n_kvhead = 1 -- gives the same bits as one call over
+        all heads.  Not for the shared active set, whose score sums over every
+        query head."""
+        c = self.cfg
+        assert not (getattr(c, "flags", 0) & 2), "the shared active set spans all KV heads"
+        if self.kmin is None:
+            self.page_meta()
+        G, Hk, A = c.group, c.n_kvhead, c.n_active
+        k = c.budget // c.page_size
+        q_t, q_prev, k_blk, v_blk = _f32(q_t), _f32(q_prev), _f32(k_blk), _f32(v_blk)
+        sub_cfg = _SubShape(c, n_qhead=G, n_kvhead=1)
+
+        def one(g):
+            hs = slice(g * G, (g + 1) * G)
+            sub = Oracle.__new__(Oracle)
+            sub.lib, sub.cfg, sub.kv_off, sub.prefix_len = self.lib, sub_cfg, self.kv_off, self.prefix_len
+            sub.kv_tokens, sub.scale, sub.max_pages = self.kv_tokens, self.scale, self.max_pages
+            sub.k_cache, sub.v_cache = self.k_cache[g:g + 1], self.v_cache[g:g + 1]
+            sub.kmin, sub.kmax = self.kmin[g:g + 1], self.kmax[g:g + 1]
+            sub.op = np.ascontiguousarray(self.op[:, hs])
+            sub.lp = np.ascontiguousarray(self.lp[:, hs])
+            res = sub.step(np.ascontiguousarray(q_t[:, :, hs]), np.ascontiguousarray(q_prev[:, :, hs]),
+                           np.ascontiguousarray(k_blk[:, :, g:g + 1]),
+                           np.ascontiguousarray(v_blk[:, :, g:g + 1]))
+            return g, res, sub.op, sub.lp
+
+        with ThreadPoolExecutor(max_workers=min(Hk, threads or host_threads())) as ex:
+            parts = list(ex.map(one, range(Hk)))
+        out = np.zeros((c.n_seq, c.block, c.n_qhead, c.head_dim), np.float32)
+        loc = np.zeros((c.n_seq, c.n_qhead, c.block), np.float32)
+        act = np.zeros((c.n_seq, c.n_qhead, A), np.int32)
+        psel = np.zeros((c.n_seq, c.n_qhead, A, k), np.int32)
+        uidx = np.full((c.n_seq, Hk, self.max_pages), -1, np.int32)
+        ucnt = np.zeros((c.n_seq, Hk), np.int32)
+        for g, res, op, lp in parts:
+            hs = slice(g * G, (g + 1) * G)
+            out[:, :, hs] = res["out"]
+            loc[:, hs] = res["locality"]
+            act[:, hs] = res["active"]
+            psel[:, hs] = res["page_sel"]
+            uidx[:, g] = res["union_idx"][:, 0]
+            ucnt[:, g] = res["union_cnt"][:, 0]
+            self.op[:, hs] = op
+            self.lp[:, hs] = lp
+        return dict(out=out, locality=loc, active=act, page_sel=psel, union_idx=uidx,
+                    union_cnt=ucnt)
+
     def naive_sparse_step(self, q_t, k_blk, v_blk):
         c = self.cfg
         if self.kmin is None:
@@ -240,6 +319,30 @@ class Oracle:
                                           _f(self.kmin), _f(self.kmax), _i(self.kv_off),
                                           _i(self.prefix_len), _d(self.op), _d(self.lp), _f(out))
         return out
+
+
+class _SubShape:
+    """The attributes make_shape reads, from a workload shape with some replaced."""
+
+    def __init__(self, cfg, **kw):
+        for a in ("n_seq", "block", "n_qhead", "n_kvhead", "head_dim", "page_size", "budget",
+                  "n_active", "dtype"):
+            setattr(self, a, kw.get(a, getattr(cfg, a)))
+        self.flags = kw.get("flags", getattr(cfg, "flags", 0))
+
+    @property
+    def group(self):
+        return self.n_qhead // self.n_kvhead
+
+
+def host_threads() -> int:
+    """Threads for the row-parallel oracle calls: the CPUs this process may run
+    on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def page_bound(q, mn, mx, lib=None):

@@ -255,9 +255,10 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
 // Union of the selected pages of one (sequence, KV head) -- the rows' lists
 // psel[0 .. n_sel), -1 for none -- as a bitmap in LDS (bm: ceil(pages/32)
 // words), compacted in ascending page order.  The pages at union positions
-// [first, first + cp) go to pg_out; with dbg_idx, every position is written
-// there too.  Returns the union size.  Called by all 256 threads; pre0 is
-// psel[tid] (read by the caller ahead of time; ignored for tid >= n_sel).
+// [first, first + cp) go to pg_out, and with dbg_idx to the same positions
+// there (so every workgroup reports the pages it loads).  Returns the union
+// size.  Called by all 256 threads; pre0 is psel[tid] (read by the caller
+// ahead of time; ignored for tid >= n_sel).
 __device__ int union_slice(const int32_t *__restrict__ psel, int pre0, int n_sel, int pages,
                            bool all_pages, int first, int cp, uint32_t *bm, int *wsum, int *pg_out,
                            int32_t *dbg_idx, int dbg_cap, int k = 0, uint64_t *rmask = nullptr) {
@@ -266,7 +267,8 @@ __device__ int union_slice(const int32_t *__restrict__ psel, int pre0, int n_sel
         if (tid < cp) pg_out[tid] = first + tid;
         if (rmask && tid < cp) rmask[tid] = ~0ull;  // every row selected every page
         if (dbg_idx)
-            for (int i = tid; i < min(pages, dbg_cap); i += 256) dbg_idx[i] = i;
+            for (int i = first + tid; i < min(min(pages, dbg_cap), first + cp); i += 256)
+                dbg_idx[i] = i;
         __syncthreads();
         return pages;
     }
@@ -296,8 +298,10 @@ __device__ int union_slice(const int32_t *__restrict__ psel, int pre0, int n_sel
         while (b) {
             const int pg = i * 32 + __ffs(b) - 1;
             b &= b - 1u;
-            if (pos >= first && pos < first + cp) pg_out[pos - first] = pg;
-            if (dbg_idx && pos < dbg_cap) dbg_idx[pos] = pg;
+            if (pos >= first && pos < first + cp) {
+                pg_out[pos - first] = pg;
+                if (dbg_idx && pos < dbg_cap) dbg_idx[pos] = pg;
+            }
             ++pos;
         }
     }
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     } else {
         n_items = union_slice(psel_g, pre0, n_sel, sg.pages, D.k >= sg.pages,
                               first, cp, reinterpret_cast<uint32_t *>(s_raw), s_wsum, s_pg,
-                              chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
+                              dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
                               dbg_cap, D.k, MASK ? s_rmask : nullptr);
         my_page = lane < cp ? s_pg[lane] : 0;
     }
@@ -608,7 +612,7 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
     }
     const int n_items = union_slice(psel_g, pre0, n_sel, sg.pages, D.k >= sg.pages, first, cp,
                                     s_bm, s_wsum, s_pg,
-                                    chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
+                                    dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
                                     dbg_cap, D.k, MASK ? s_rmask : nullptr);
     auto store_count = [&]() {
         if (chunk == 0 && tid == 0) {
@@ -1037,7 +1041,7 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restr
         const int pre0 = psel_g[min(static_cast<int>(threadIdx.x), max(n_sel - 1, 0))];
         n_items = union_slice(psel_g, pre0, n_sel, sg.pages, D.k >= sg.pages,
                               first, cp, s_bm, s_wsum, s_pg,
-                              chunk == 0 && dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
+                              dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr,
                               dbg_cap, D.k, MASK ? s_rmask : nullptr);
         if (chunk == 0 && threadIdx.x == 0) {
             W.union_cnt[sgi] = min(n_items, D.union_cap);

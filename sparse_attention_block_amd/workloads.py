@@ -17,7 +17,10 @@ measure on LongBench, which these synthetic draws stand in for):
   same tokens drift in every head; the in-block K/V drift the same way;
 * needles (8B-class shapes): per sequence and KV head, 8 distinct pages whose
   keys are turned towards the direction of one random first-step query of that
-  KV head's group, at cosine 0.8 and with their norms kept.
+  KV head's group, at cosine 0.8 and with their norms kept;
+* tie cases (edge cases of the method's orderings, not a workload of the
+  pages): runs of pages that repeat one page's keys, and stable tokens with no
+  drift at all (stable_sigma = 0), so that bounds and localities tie exactly.
 
 Every array is float32 holding values exactly representable in the storage
 type (bf16 draws are rounded once, round-to-nearest-even), so both sides read
@@ -60,6 +63,7 @@ class Config:
     stable_sigma: float = 1e-3
     n_drift: Optional[int] = None   # drifting tokens per step (default: n_active)
     flags: int = 0                  # reading variants (row mask, shared active set, no write-back)
+    dup_pages: int = 1              # runs of this many pages share the keys of their first page
 
     @property
     def group(self) -> int:
@@ -176,6 +180,19 @@ def make_layer(cfg: Config, layer: int = 0, n_steps: Optional[int] = None,
                     k_cache[g, lo:hi] = to_storage(k_new.astype(np.float32), cfg.dtype)
                 lay.needles[(s, g)] = (pages.astype(np.int32), g * G + j, t)
 
+    if cfg.dup_pages > 1 and cache:
+        # ties: within each run of dup_pages whole pages, every page repeats the
+        # keys of the run's first page (so their per-page min/max, and every
+        # query's bound for them, are equal); partial last pages are left alone
+        r = cfg.dup_pages
+        for s in range(S):
+            full = int(lens[s]) // P
+            for p in range(full):
+                if p % r:
+                    src = int(kv_off[s]) + (p - p % r) * P
+                    dst = int(kv_off[s]) + p * P
+                    k_cache[:, dst:dst + P] = k_cache[:, src:src + P]
+
     q, kb, vb = q1, kb1, vb1
     for step in range(n_steps):
         if step == 0:
@@ -265,7 +282,8 @@ def trace_128k(layer: int = 0) -> Config:
 
 def small_case(cfg_id: int, *, n_seq=None, block=16, n_qhead=4, n_kvhead=1, head_dim=64,
                page_size=16, budget=64, n_active=4, dtype="f32", prefix_lens=(1024,),
-               n_steps=2, needles=False, n_drift=None, flags=0) -> Config:
+               n_steps=2, needles=False, n_drift=None, flags=0, stable_sigma=1e-3,
+               dup_pages=1) -> Config:
     """A free-form small workload for sweeps over shapes and edge cases; one
     sequence per prefix length."""
     if n_seq is None:
@@ -273,4 +291,5 @@ def small_case(cfg_id: int, *, n_seq=None, block=16, n_qhead=4, n_kvhead=1, head
     assert n_seq == len(prefix_lens), (n_seq, prefix_lens)
     return Config(f"small_{cfg_id}", 100 + cfg_id, n_seq, block, n_qhead, n_kvhead, head_dim,
                   page_size, budget, n_active, dtype, tuple(prefix_lens), n_steps,
-                  needles=needles, n_drift=n_drift, flags=flags)
+                  needles=needles, n_drift=n_drift, flags=flags, stable_sigma=stable_sigma,
+                  dup_pages=dup_pages)

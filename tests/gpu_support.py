@@ -8,15 +8,11 @@ import sys
 import numpy as np
 import torch
 
+from checks import TOL, check_lp, check_values
 from oracle import Oracle
 from sparse_attention_block_amd import binding as L
 from sparse_attention_block_amd import workloads as W
 from sparse_attention_block_amd.layer import LayerState, to_device
-
-# Output tolerances: bf16 outputs accumulated in fp32 against the double oracle
-# (max relative 2e-2, absolute 1e-2); fp32 inputs: fp32 accumulation over at
-# most a few thousand terms, errors ~1e-6 relative, bound set at 1e-4.
-TOL = {"bf16": dict(rtol=2e-2, atol=1e-2), "f32": dict(rtol=1e-4, atol=1e-5)}
 
 
 def say(*a):
@@ -25,19 +21,26 @@ def say(*a):
 
 
 def assert_close(got, ref, dtype, what):
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert got.shape == ref.shape, (what, got.shape, ref.shape)
-    both_inf = np.isneginf(got) & np.isneginf(ref)
-    g = np.where(both_inf, 0.0, got)
-    r = np.where(both_inf, 0.0, ref)
-    tol = TOL[dtype]
-    bad = ~(np.abs(g - r) <= tol["atol"] + tol["rtol"] * np.abs(r))
-    if bad.any():
-        idx = np.argwhere(bad)[:5].tolist()
-        worst = float(np.nanmax(np.abs(g - r)))
-        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
-                             f"first {idx}; max abs err {worst:.3g}")
+    """Values (last axis = one row) within the checks module's element and row bounds."""
+    say("  " + check_values(got, ref, dtype, what))
+
+
+def assert_lp(got, ref, dtype, what):
+    say("  " + check_lp(got, ref, dtype, what))
+
+
+def stratified_rows(cfg, per_group: int, seed: int):
+    """Rows (s, h, t) of a dense step: per_group rows in every (sequence, KV
+    head) group, each a random query head of the group and a random token,
+    distinct within the group."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for s in range(cfg.n_seq):
+        for g in range(cfg.n_kvhead):
+            picks = rng.choice(cfg.group * cfg.block, size=min(per_group, cfg.group * cfg.block),
+                               replace=False)
+            rows += [(s, g * cfg.group + int(x) // cfg.block, int(x) % cfg.block) for x in picks]
+    return rows
 
 
 def host(t: torch.Tensor) -> np.ndarray:
@@ -69,29 +72,29 @@ class Pair:
         self.gpu.op_cache.copy_(torch.from_numpy(op).to(self.gpu.op_cache.device))
         self.gpu.lp_cache.copy_(torch.from_numpy(lp).to(self.gpu.lp_cache.device))
 
-    def dense(self, step: int = 0, sample_rows=None):
+    def dense(self, step: int = 0, rows=None):
+        """The dense first step on the GPU against the oracle: every row (rows
+        None: the oracle's whole step, row-parallel over the host's cores), or
+        the given (s, h, t) rows only."""
         c = self.cfg
         say(f"[{self.name}] dense_first_step step={step}")
         out = self.gpu.dense_first_step(self.q[step], self.kb[step], self.vb[step])
         torch.cuda.synchronize()
         out, op, lp = host(out), host(self.gpu.op_cache), host(self.gpu.lp_cache)
-        if sample_rows is None:
-            ref = self.orc.dense_first_step(self.lay.q[step], self.lay.k_blk[step],
-                                            self.lay.v_blk[step])
+        args = (self.lay.q[step], self.lay.k_blk[step], self.lay.v_blk[step])
+        if rows is None:
+            ref = self.orc.dense_first_step_threaded(*args)
             assert_close(out, ref, c.dtype, f"{self.name} dense out")
             assert_close(op, self.orc.op, c.dtype, f"{self.name} dense o_p")
-            assert_close(lp, self.orc.lp, c.dtype, f"{self.name} dense L_p")
+            assert_lp(lp, self.orc.lp, c.dtype, f"{self.name} dense L_p")
         else:
-            rng = np.random.default_rng(1234)
-            for _ in range(sample_rows):
-                s = int(rng.integers(c.n_seq))
-                h = int(rng.integers(c.n_qhead))
-                t = int(rng.integers(c.block))
-                o_p, l_p, row = self.orc.dense_row(self.lay.q[step], self.lay.k_blk[step],
-                                                   self.lay.v_blk[step], s, h, t)
-                assert_close(out[s, t, h], row, c.dtype, f"{self.name} dense out {s},{h},{t}")
-                assert_close(op[s, h, t], o_p, c.dtype, f"{self.name} dense o_p {s},{h},{t}")
-                assert_close(lp[s, h, t], l_p, c.dtype, f"{self.name} dense L_p {s},{h},{t}")
+            o_p, l_p, o_rows = self.orc.dense_rows(*args, rows)
+            idx = tuple(np.array(rows).T)
+            s_, h_, t_ = idx
+            say(f"  {len(rows)} rows over {len(set(zip(s_, h_ // c.group)))} (sequence, KV head) groups")
+            assert_close(out[s_, t_, h_], o_rows, c.dtype, f"{self.name} dense out rows")
+            assert_close(op[s_, h_, t_], o_p, c.dtype, f"{self.name} dense o_p rows")
+            assert_lp(lp[s_, h_, t_], l_p, c.dtype, f"{self.name} dense L_p rows")
         return out
 
     def sparse(self, step: int, check_values=True):
@@ -120,5 +123,5 @@ class Pair:
         if check_values:
             assert_close(host(out), res["out"], c.dtype, f"{self.name} step {step} out")
             assert_close(host(self.gpu.op_cache), self.orc.op, c.dtype, f"{self.name} step {step} o_p")
-            assert_close(host(self.gpu.lp_cache), self.orc.lp, c.dtype, f"{self.name} step {step} L_p")
+            assert_lp(host(self.gpu.lp_cache), self.orc.lp, c.dtype, f"{self.name} step {step} L_p")
         return dict(out=host(out), res=res, union_cnt=ucnt)

@@ -490,7 +490,58 @@ def pin_no_writeback_keeps_cache(lib):
     assert np.array_equal(outs[0], outs[1])
 
 
+# ---------------------------------------------------------------------------
+# hand-worked values that only the ascending fp32 chains reproduce
+
+GOLDEN_DIR = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
+
+
+def chain_order_golden():
+    import json
+    with open(__import__("os").path.join(GOLDEN_DIR, "chain_order.json")) as f:
+        return json.load(f)
+
+
+def chain_order_layer(g):
+    """The golden's inputs placed into a small bf16 layer (every other value drawn)."""
+    sh = g["shape"]
+    cfg = W.small_case(390, dtype="bf16", head_dim=sh["head_dim"], block=sh["block"],
+                       n_active=sh["n_active"], budget=sh["budget"],
+                       prefix_lens=(sh["prefix_len"],), n_kvhead=1, n_qhead=sh["n_qhead"],
+                       n_steps=2)
+    lay = W.make_layer(cfg)
+    P, d = cfg.page_size, cfg.head_dim
+    for pg in (g["page_a"], g["page_b"]):
+        k = np.zeros(d, np.float32)
+        k[:len(pg["key"])] = pg["key"]
+        lay.k_cache[0, pg["page"] * P:(pg["page"] + 1) * P] = k
+    for row in (g["bound_row"], g["locality_row"]):
+        q = np.zeros(d, np.float32)
+        q[:len(row["q_t"])] = row["q_t"]
+        if row.get("fill_ones"):
+            q[len(row["q_t"]):] = 1.0
+        lay.q[1][0, row["token"], row["head"]] = q
+        lay.q[0][0, row["token"], row["head"]] = 0.0
+    return lay, cfg
+
+
+def pin_chain_order_golden(lib):
+    g = chain_order_golden()
+    lay, cfg = chain_order_layer(g)
+    orc = new_oracle(lib, lay)
+    orc.dense_first_step(lay.q[0], lay.k_blk[0], lay.v_blk[0])
+    res = orc.step(lay.q[1], lay.q[0], lay.k_blk[1], lay.v_blk[1])
+    e, lr, br = g["expected"], g["locality_row"], g["bound_row"]
+    got = float(res["locality"][0, lr["head"], lr["token"]])
+    assert got == e["locality"], f"locality chain {got} != {e['locality']}"
+    act = list(res["active"][0, br["head"]])
+    assert br["token"] in act, "the bound row must be active"
+    sel = res["page_sel"][0, br["head"], act.index(br["token"])].tolist()
+    assert sel == e["page_sel"], f"page bound chain selects {sel}, not {e['page_sel']}"
+
+
 ALL_PINS = [
+    pin_chain_order_golden,
     pin_page_meta, pin_locality_value, pin_locality_planted_drift, pin_active_set_order_and_ties,
     pin_page_bound_is_box_maximum, pin_topk_and_union, pin_needles_rank_high,
     pin_sparse_prefix_equals_sdpa, pin_dense_first_step_equals_attention,

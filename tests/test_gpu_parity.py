@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_support import Pair, assert_close, host, say
+from gpu_support import Pair, host, say, stratified_rows
+from oracle_pins import chain_order_golden, chain_order_layer
 from sparse_attention_block_amd import binding as L
 from sparse_attention_block_amd import workloads as W
 from sparse_attention_block_amd.build import SELFTEST_LIB
@@ -198,25 +199,107 @@ def test_determinism_and_lost_cache_recovery():
 
 
 # ---------------------------------------------------------------------------
+# ties: equal page bounds (runs of pages with identical keys) and equal
+# localities (stable tokens with no drift at all, more active slots than
+# drifting tokens), so that the lower-page and lower-token rules decide
+
+TIES = [
+    # runs of 3 equal pages, k = 8: the 8th and 9th best pages tie
+    ("ties_bf16_d128_k8", dict(dtype="bf16", head_dim=128, block=16, n_active=5, budget=128,
+                               prefix_lens=(3000, 700), n_kvhead=2, n_qhead=8, n_drift=2,
+                               stable_sigma=0.0, dup_pages=3)),
+    # k = 3 over runs of 2; one KV head, GQA 4
+    ("ties_bf16_d64_k3", dict(dtype="bf16", head_dim=64, block=16, n_active=3, budget=48,
+                              prefix_lens=(1040,), n_kvhead=1, n_qhead=4, n_drift=1,
+                              stable_sigma=0.0, dup_pages=2)),
+    ("ties_f32_d64_k4", dict(dtype="f32", head_dim=64, block=16, n_active=4, budget=64,
+                             prefix_lens=(999, 64), n_kvhead=1, n_qhead=4, n_drift=2,
+                             stable_sigma=0.0, dup_pages=3)),
+    # a long prefix: ties across many tiles and in the exact candidate ranking
+    ("ties_bf16_16k", dict(dtype="bf16", head_dim=128, block=16, n_active=4, budget=128,
+                           prefix_lens=(16384,), n_kvhead=8, n_qhead=32, n_drift=1,
+                           stable_sigma=0.0, dup_pages=3, needles=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", TIES, ids=[n for n, _ in TIES])
+def test_ties(name, kw):
+    cid = 300 + [n for n, _ in TIES].index(name)
+    cfg = W.small_case(cid, n_steps=3, **kw)
+    p = Pair(W.make_layer(cfg), name)
+    p.dense(0)
+    for step in (1, 2):
+        r = p.sparse(step)
+        # stable tokens did not move: their localities are exactly zero, and the
+        # active slots past the drifting tokens go to the lowest such tokens
+        loc = r["res"]["locality"]
+        drift = p.lay.drift_tokens[step]
+        for s in range(cfg.n_seq):
+            stable = np.setdiff1d(np.arange(cfg.block), drift[s])
+            assert (loc[s][:, stable] == 0).all()
+            n_extra = cfg.n_active - len(drift[s])
+            if n_extra > 0:
+                want = np.sort(np.concatenate([drift[s], stable[:n_extra]]))
+                assert (r["res"]["active"][s] == want).all(), f"{name}: ties of zero localities"
+
+
+# ---------------------------------------------------------------------------
+# the order of the index-deciding fp32 chains, pinned by hand-worked values
+# (tests/golden/chain_order.json) where any other summation order gives
+# another result
+
+def test_chain_order_hand_values():
+    g = chain_order_golden()
+    lay, cfg = chain_order_layer(g)
+    p = Pair(lay, "chain_order")
+    p.dense(0)
+    # indices only in the crafted step: its two crafted rows score 2^24/8 = 2^21
+    # nats against pages 3 and 7, where one fp32 unit of the score is 0.25 nats,
+    # beyond the bounded-score regime the value tolerances are derived for
+    r = p.sparse(1, check_values=False)
+    e = g["expected"]
+    h, t = g["bound_row"]["head"], g["bound_row"]["token"]
+    assert float(r["res"]["locality"][0, g["locality_row"]["head"], g["locality_row"]["token"]]) \
+        == e["locality"]
+    a = list(r["res"]["active"][0, h]).index(t)
+    assert r["res"]["page_sel"][0, h, a].tolist() == e["page_sel"]
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads (the long-context configuration the benchmark times)
 
 @pytest.mark.parametrize("budget,n_active", [(128, 4), (256, 8), (128, 2)])
 def test_long_64k(budget, n_active):
+    """Dense first step compared on every row, then LoSA steps from a planted cache."""
     cfg = W.long_64k(budget, n_active)
     lay = W.make_layer(cfg, n_steps=4)
     p = Pair(lay, cfg.name)
-    p.dense(0, sample_rows=12)
+    p.dense(0)
     op, lp = W.make_cache_state(cfg)
     p.set_cache(op, lp)
     for step in (1, 2, 3):
         p.sparse(step)
 
 
+@pytest.mark.parametrize("budget,n_active", [(256, 2), (256, 4), (128, 8), (128, 16), (256, 16)])
+def test_long_64k_more_configs(budget, n_active):
+    """The other budgets and active-set sizes the sweep times at 64K, including
+    every block token active (the QUEST-style step)."""
+    cfg = W.long_64k(budget, n_active)
+    lay = W.make_layer(cfg, n_steps=3)
+    p = Pair(lay, cfg.name)
+    op, lp = W.make_cache_state(cfg)
+    p.set_cache(op, lp)
+    for step in (1, 2):
+        p.sparse(step)
+
+
 def test_ragged_batch():
+    """Dense rows stratified over every (sequence, KV head) group, then LoSA steps."""
     cfg = W.ragged_batch()
     lay = W.make_layer(cfg, n_steps=3)
     p = Pair(lay, cfg.name)
-    p.dense(0, sample_rows=12)
+    p.dense(0, rows=stratified_rows(cfg, 4, seed=1234))
     op, lp = W.make_cache_state(cfg)
     p.set_cache(op, lp)
     for step in (1, 2):
@@ -228,7 +311,7 @@ def test_trace_128k_layer(layer):
     cfg = W.trace_128k(layer)
     lay = W.make_layer(cfg, layer=layer, n_steps=2)
     p = Pair(lay, cfg.name)
-    p.dense(0, sample_rows=6)
+    p.dense(0)
     op, lp = W.make_cache_state(cfg, layer)
     p.set_cache(op, lp)
     p.sparse(1)

@@ -55,6 +55,16 @@ MUTANTS = [
     ("shared_set_ignored", "if (sh->flags & ORACLE_SHARED_ACTIVE) {", "if (0) {", None),
     ("row_mask_ignored", "if (sh->flags & ORACLE_ROW_MASK) {", "if (0) {", None),
     ("no_writeback_ignored", "if (sh->flags & ORACLE_NO_WRITEBACK) {", "if (0) {", None),
+    ("locality_chain_reversed", "for (int i = 0; i < d; ++i) {\n                    float delta",
+     "for (int i = d - 1; i >= 0; --i) {\n                    float delta", None),
+    ("locality_chain_in_double",
+     "float acc = 0.0f;\n                for (int i = 0; i < d; ++i) {\n                    float delta",
+     "double acc = 0.0;\n                for (int i = 0; i < d; ++i) {\n                    float delta",
+     None),
+    ("bound_chain_reversed", "for (int i = 0; i < d; ++i) {\n        float sel",
+     "for (int i = d - 1; i >= 0; --i) {\n        float sel", None),
+    ("bound_chain_in_double", "    float acc = 0.0f;\n    for (int i = 0; i < d; ++i) {\n        float sel",
+     "    double acc = 0.0;\n    for (int i = 0; i < d; ++i) {\n        float sel", None),
 ]
 
 
