@@ -49,9 +49,9 @@
  *
  * Memory.  Every array argument is a device pointer (hipMalloc or
  * equivalent) owned by the caller, 16-byte aligned.  The library allocates,
- * frees and synchronises nothing and keeps no state between calls; the
- * workspace is scratch owned by the caller and must not be shared by calls
- * that may run concurrently.  All work is enqueued on `stream` (a
+ * frees and synchronises nothing and keeps no state between calls (except
+ * losa_step_noalloc's static scratch, below); the workspace is scratch owned
+ * by the caller and must not be shared by calls that may run concurrently.  All work is enqueued on `stream` (a
  * hipStream_t; NULL is the default stream).  Calls return after enqueueing.
  *
  * Layouts (row-major, innermost last; T = kv_tokens):
@@ -88,7 +88,8 @@ typedef enum losa_status {
     LOSA_ERR_INVALID_ARG = 1, /* a null/misaligned pointer or an inconsistent shape */
     LOSA_ERR_UNSUPPORTED = 2, /* a legal shape this build has no kernel for */
     LOSA_ERR_WORKSPACE = 3,   /* workspace smaller than losa_workspace_bytes() */
-    LOSA_ERR_HIP = 4          /* a HIP launch failed */
+    LOSA_ERR_HIP = 4,         /* a HIP launch failed */
+    LOSA_ERR_SCRATCH = 5      /* losa_step_noalloc: the shape needs more than its static scratch */
 } losa_status;
 
 typedef enum losa_dtype { LOSA_F32 = 0, LOSA_BF16 = 1 } losa_dtype;
@@ -225,6 +226,32 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
               const int32_t *kv_off, const int32_t *prefix_len, float *op_cache, float *lp_cache,
               void *out, const losa_debug *debug, void *workspace, size_t workspace_bytes,
               void *stream);
+
+/* Bytes of the static scratch that losa_step_noalloc uses on each GPU. */
+#define LOSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * losa_step for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels and results as losa_step, minus
+ * the workspace: the step's scratch (stacked query rows, page bounds, selected
+ * pages, split-K partials) lives in a static device array of
+ * LOSA_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held until
+ * the process ends.  The first call on a device, with that device current,
+ * looks up that device's copy (hipGetSymbolAddress); no call allocates or
+ * frees anything.  A shape whose scratch need exceeds the limit (it is at most
+ * losa_workspace_bytes(shape)) returns LOSA_ERR_SCRATCH with nothing enqueued;
+ * the headline shapes (64K or 128K prefix, B = 16, 32/8 heads, d = 128,
+ * budget <= 256) fit.  Every call on a GPU uses the same array, which keeps
+ * the last call's contents (nothing in it needs to start at zero): calls that
+ * may overlap on one GPU -- concurrent streams, or host threads -- race and
+ * must be serialised by the caller.
+ */
+int losa_step_noalloc(const losa_shape *shape, const void *q_t, const void *q_prev,
+                      const void *k_blk, const void *v_blk, const void *k_cache,
+                      const void *v_cache, const void *page_meta, const int32_t *kv_off,
+                      const int32_t *prefix_len, float *op_cache, float *lp_cache, void *out,
+                      const losa_debug *debug, void *stream);
 
 #ifdef __cplusplus
 }

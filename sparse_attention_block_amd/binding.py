@@ -22,7 +22,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblosa.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "losa.h")
 
-LOSA_OK, LOSA_ERR_INVALID_ARG, LOSA_ERR_UNSUPPORTED, LOSA_ERR_WORKSPACE, LOSA_ERR_HIP = range(5)
+(LOSA_OK, LOSA_ERR_INVALID_ARG, LOSA_ERR_UNSUPPORTED, LOSA_ERR_WORKSPACE, LOSA_ERR_HIP,
+ LOSA_ERR_SCRATCH) = range(6)
+LOSA_NOALLOC_SCRATCH_BYTES = 32 << 20
 LOSA_F32, LOSA_BF16 = 0, 1
 PAGE = 16
 
@@ -84,6 +86,8 @@ def load(path: str = LIB_PATH):
     lib.losa_step.argtypes = [S] + [c_void_p] * 12 + [POINTER(LosaDebug), c_void_p, c_size_t,
                                                        c_void_p]
     lib.losa_step.restype = c_int
+    lib.losa_step_noalloc.argtypes = [S] + [c_void_p] * 12 + [POINTER(LosaDebug), c_void_p]
+    lib.losa_step_noalloc.restype = c_int
     _lib = lib
     return lib
 
@@ -273,6 +277,27 @@ def losa_step(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_
     ws = _check(workspace, "workspace", torch.uint8, ws_need)
     _raise(load().losa_step(ctypes.byref(shape), *args, dbg, ws, workspace.numel(),
                             _stream(stream)), "losa_step")
+
+
+def losa_step_noalloc(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off,
+                      prefix_len, op_cache, lp_cache, out, debug: Optional[Debug] = None,
+                      stream=None):
+    """losa_step on the library's static per-GPU scratch (no workspace argument)."""
+    n, dt = _sizes(shape), _torch_dtype(shape)
+    args = [
+        _check(q_t, "q_t", dt, n["q"]), _check(q_prev, "q_prev", dt, n["q"]),
+        _check(k_blk, "k_blk", dt, n["blk"]), _check(v_blk, "v_blk", dt, n["blk"]),
+        _check(k_cache, "k_cache", dt, n["cache"]), _check(v_cache, "v_cache", dt, n["cache"]),
+        _check(page_meta, "page_meta", torch.uint8, page_meta_bytes(shape)),
+        _check(kv_off, "kv_off", torch.int32, shape.n_seq),
+        _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+        _check(op_cache, "op_cache", torch.float32, n["op"]),
+        _check(lp_cache, "lp_cache", torch.float32, n["lp"]),
+        _check(out, "out", dt, n["q"]),
+    ]
+    dbg = ctypes.byref(debug.struct(shape)) if debug is not None else None
+    _raise(load().losa_step_noalloc(ctypes.byref(shape), *args, dbg, _stream(stream)),
+           "losa_step_noalloc")
 
 
 # ---------------------------------------------------------------------------

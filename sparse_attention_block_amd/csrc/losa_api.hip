@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "losa_internal.h"
 
@@ -99,13 +100,15 @@ Dims make_dims(const losa_shape *sh) {
 }
 
 // Carve the workspace; with base == nullptr only the total size is computed.
-size_t carve(const Dims &D, char *base, Work *W) {
+// sparse_only: the layout losa_step alone needs (no dense first-step partials).
+size_t carve(const Dims &D, char *base, Work *W, bool sparse_only = false) {
     const size_t sT = D.bf16 ? 2 : 4;
     const size_t SG = (size_t)D.S * D.Hk;
     const size_t R1 = D.R > 0 ? D.R : 1;
     const size_t A1 = D.A > 0 ? D.A : 1;
     const size_t part_rows =
-        std::max((size_t)D.n_chunks_sparse * R1, (size_t)D.n_chunks_dense * D.Rd);
+        sparse_only ? (size_t)D.n_chunks_sparse * R1
+                    : std::max((size_t)D.n_chunks_sparse * R1, (size_t)D.n_chunks_dense * D.Rd);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         char *p = base ? base + off : nullptr;
@@ -145,6 +148,98 @@ hipError_t mark(void **events, int i, hipStream_t s) {
     return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
 }
 
+// Checks of losa_step's arguments (host only); fills the dims and the debug copy.
+int check_step_args(const losa_shape *shape, const void *const (&p16)[10], const int32_t *kv_off,
+                    const int32_t *prefix_len, const float *lp_cache, const losa_debug *debug,
+                    Dims *D, losa_debug *dbg) {
+    int st = check_shape(shape);
+    if (st != LOSA_OK) return st;
+    for (const void *p : p16)
+        if (!p || !aligned(p, 16)) return LOSA_ERR_INVALID_ARG;
+    if (!kv_off || !prefix_len || !lp_cache || !aligned(kv_off, 4) || !aligned(prefix_len, 4) ||
+        !aligned(lp_cache, 4))
+        return LOSA_ERR_INVALID_ARG;
+    *D = make_dims(shape);
+    memset(dbg, 0, sizeof *dbg);
+    if (debug) {
+        *dbg = *debug;
+        const void *pd[] = {dbg->locality, dbg->active, dbg->page_sel, dbg->union_idx,
+                            dbg->union_cnt};
+        for (const void *p : pd)
+            if (p && !aligned(p, 4)) return LOSA_ERR_INVALID_ARG;
+        if (dbg->union_idx && dbg->union_cap < D->union_cap) return LOSA_ERR_INVALID_ARG;
+    }
+    if (D->R > 0 && select_lds_bytes(*D) > 60 * 1024) return LOSA_ERR_UNSUPPORTED;
+    if (D->R > 0 && D->k > kMaxK && D->k < D->max_pages) return LOSA_ERR_UNSUPPORTED;
+    return LOSA_OK;
+}
+
+// The launches of one LoSA step on an already carved workspace.
+hipError_t launch_step(const Dims &D, const void *q_t, const void *q_prev, const void *k_blk,
+                       const void *v_blk, const void *k_cache, const void *v_cache,
+                       const void *page_meta, const int32_t *kv_off, const int32_t *prefix_len,
+                       float *op_cache, float *lp_cache, void *out, const losa_debug &dbg,
+                       const Work &W, hipStream_t s) {
+    void **ev = dbg.stage_events;
+    hipError_t e = mark(ev, 0, s);
+    if ((D.flags & LOSA_FLAG_SHARED_ACTIVE) && e == hipSuccess)
+        e = launch_shared_locality(D, q_t, q_prev, W, dbg.locality, s);
+    if (score_prep_fits(D)) {
+        // preparation and page scoring in one kernel (its time shows as scoring)
+        if (e == hipSuccess) e = mark(ev, 1, s);
+        if (e == hipSuccess)
+            e = launch_score_prep(D, q_t, q_prev, page_meta, kv_off, prefix_len, W, dbg.locality,
+                                  dbg.active, dbg.union_cnt, s);
+    } else {
+        if (e == hipSuccess)
+            e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active, dbg.union_cnt,
+                               s);
+        if (e == hipSuccess) e = mark(ev, 1, s);
+        if (D.R > 0 && e == hipSuccess) e = launch_score(D, page_meta, kv_off, prefix_len, W, s);
+    }
+    if (e == hipSuccess) e = mark(ev, 2, s);
+    // selection (active rows) and the in-block attention of every token
+    const BlockArgs blk{q_t, k_blk, v_blk, op_cache, lp_cache, out};
+    if (e == hipSuccess)
+        e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, blk, s);
+    if (e == hipSuccess) e = mark(ev, 3, s);
+    if (D.R > 0 && e == hipSuccess)
+        e = launch_prefix(D, false, q_t, k_cache, v_cache, kv_off, prefix_len, W, dbg.union_idx,
+                          dbg.union_cnt, dbg.union_cap, s);
+    if (e == hipSuccess) e = mark(ev, 4, s);
+    if (D.R > 0 && e == hipSuccess) e = launch_finish_active(D, W, op_cache, lp_cache, out, s);
+    if (e == hipSuccess) e = mark(ev, 5, s);
+    return e;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of losa_step_noalloc, for callers that cannot allocate.  In
+// host code `scratch` names a host-side stand-in, never device memory: the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[LOSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,6 +251,8 @@ const char *losa_status_string(int status) {
         case LOSA_ERR_UNSUPPORTED: return "unsupported shape";
         case LOSA_ERR_WORKSPACE: return "workspace too small";
         case LOSA_ERR_HIP: return "HIP launch failed";
+        case LOSA_ERR_SCRATCH:
+            return "shape needs more than the static scratch of losa_step_noalloc";
         default: return "unknown status";
     }
 }
@@ -245,61 +342,40 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
               const int32_t *kv_off, const int32_t *prefix_len, float *op_cache, float *lp_cache,
               void *out, const losa_debug *debug, void *workspace, size_t workspace_bytes,
               void *stream) {
-    int st = check_shape(shape);
-    if (st != LOSA_OK) return st;
-    const void *p16[] = {q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, op_cache, out,
-                         workspace};
-    for (const void *p : p16)
-        if (!p || !aligned(p, 16)) return LOSA_ERR_INVALID_ARG;
-    if (!kv_off || !prefix_len || !lp_cache || !aligned(kv_off, 4) || !aligned(prefix_len, 4) ||
-        !aligned(lp_cache, 4))
-        return LOSA_ERR_INVALID_ARG;
-    const Dims D = make_dims(shape);
+    const void *const p16[10] = {q_t,      q_prev,   k_blk, v_blk, k_cache,
+                                 v_cache,  page_meta, op_cache, out, workspace};
+    Dims D;
     losa_debug dbg;
-    memset(&dbg, 0, sizeof dbg);
-    if (debug) {
-        dbg = *debug;
-        const void *pd[] = {dbg.locality, dbg.active, dbg.page_sel, dbg.union_idx, dbg.union_cnt};
-        for (const void *p : pd)
-            if (p && !aligned(p, 4)) return LOSA_ERR_INVALID_ARG;
-        if (dbg.union_idx && dbg.union_cap < D.union_cap) return LOSA_ERR_INVALID_ARG;
-    }
+    int st = check_step_args(shape, p16, kv_off, prefix_len, lp_cache, debug, &D, &dbg);
+    if (st != LOSA_OK) return st;
     Work W;
     const size_t need = carve(D, static_cast<char *>(workspace), &W);
     if (workspace_bytes < need) return LOSA_ERR_WORKSPACE;
-    if (D.R > 0 && select_lds_bytes(D) > 60 * 1024) return LOSA_ERR_UNSUPPORTED;
-    if (D.R > 0 && D.k > kMaxK && D.k < D.max_pages) return LOSA_ERR_UNSUPPORTED;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    void **ev = dbg.stage_events;
-    hipError_t e = mark(ev, 0, s);
-    if ((D.flags & LOSA_FLAG_SHARED_ACTIVE) && e == hipSuccess)
-        e = launch_shared_locality(D, q_t, q_prev, W, dbg.locality, s);
-    if (score_prep_fits(D)) {
-        // preparation and page scoring in one kernel (its time shows as scoring)
-        if (e == hipSuccess) e = mark(ev, 1, s);
-        if (e == hipSuccess)
-            e = launch_score_prep(D, q_t, q_prev, page_meta, kv_off, prefix_len, W, dbg.locality,
-                                  dbg.active, dbg.union_cnt, s);
-    } else {
-        if (e == hipSuccess)
-            e = launch_prepare(D, false, q_t, q_prev, W, dbg.locality, dbg.active, dbg.union_cnt,
-                               s);
-        if (e == hipSuccess) e = mark(ev, 1, s);
-        if (D.R > 0 && e == hipSuccess) e = launch_score(D, page_meta, kv_off, prefix_len, W, s);
-    }
-    if (e == hipSuccess) e = mark(ev, 2, s);
-    // selection (active rows) and the in-block attention of every token
-    const BlockArgs blk{q_t, k_blk, v_blk, op_cache, lp_cache, out};
-    if (e == hipSuccess)
-        e = launch_select(D, page_meta, kv_off, prefix_len, W, dbg.page_sel, blk, s);
-    if (e == hipSuccess) e = mark(ev, 3, s);
-    if (D.R > 0 && e == hipSuccess)
-        e = launch_prefix(D, false, q_t, k_cache, v_cache, kv_off, prefix_len, W, dbg.union_idx,
-                          dbg.union_cnt, dbg.union_cap, s);
-    if (e == hipSuccess) e = mark(ev, 4, s);
-    if (D.R > 0 && e == hipSuccess) e = launch_finish_active(D, W, op_cache, lp_cache, out, s);
-    if (e == hipSuccess) e = mark(ev, 5, s);
-    return hip_status(e);
+    return hip_status(launch_step(D, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off,
+                                  prefix_len, op_cache, lp_cache, out, dbg, W,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int losa_step_noalloc(const losa_shape *shape, const void *q_t, const void *q_prev,
+                      const void *k_blk, const void *v_blk, const void *k_cache,
+                      const void *v_cache, const void *page_meta, const int32_t *kv_off,
+                      const int32_t *prefix_len, float *op_cache, float *lp_cache, void *out,
+                      const losa_debug *debug, void *stream) {
+    // (the scratch pointer stands in for the workspace in the pointer checks)
+    const void *const p16[10] = {q_t,     q_prev,    k_blk,    v_blk, k_cache,
+                                 v_cache, page_meta, op_cache, out,   q_t};
+    Dims D;
+    losa_debug dbg;
+    int st = check_step_args(shape, p16, kv_off, prefix_len, lp_cache, debug, &D, &dbg);
+    if (st != LOSA_OK) return st;
+    if (carve(D, nullptr, nullptr, true) > LOSA_NOALLOC_SCRATCH_BYTES) return LOSA_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (scratch_of_current_device(&ws) != hipSuccess) return LOSA_ERR_HIP;
+    Work W;
+    carve(D, static_cast<char *>(ws), &W, true);
+    return hip_status(launch_step(D, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off,
+                                  prefix_len, op_cache, lp_cache, out, dbg, W,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

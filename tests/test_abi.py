@@ -145,3 +145,14 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         L.losa_build_page_meta(sh, t, torch.zeros(1, dtype=torch.int32),
                                torch.zeros(1, dtype=torch.int32), torch.zeros(16, dtype=torch.uint8))
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """The ragged batch's step needs more than the static scratch: LOSA_ERR_SCRATCH
+    before any HIP call (the pointers below are never dereferenced)."""
+    cfg = W.ragged_batch()
+    sh = shape_of(cfg)
+    p = ctypes.c_void_p(1 << 20)
+    st = lib.losa_step_noalloc(ctypes.byref(sh), *([p] * 12), None, None)
+    assert st == L.LOSA_ERR_SCRATCH, L.status_string(st)
+    assert "static scratch" in L.status_string(L.LOSA_ERR_SCRATCH)
