@@ -12,12 +12,17 @@ prefix is built before timing (it changes once per committed block).
 
 Prints one JSON line: value = attention microseconds per (layer, denoising
 step), amortised over the block (dense first step included), from K timed
-replays of the block captured once as a HIP graph -- the same launches with no
-host launch overhead, checked bit for bit against an eager block (--no-graph
-times eager launches; the eager rate is reported beside); plus per-kernel
-durations from HIP events the library records between its launches during a
-second timed pass of K blocks, the roofline of the dominant kernel, and the CPU
-oracle timed on one layer-block of the same workload.
+replays of the block captured as two HIP graphs, its dense first steps and its
+LoSA steps -- the same launches with no host launch overhead, checked bit for
+bit against an eager block (--no-graph times eager launches; the eager rate is
+reported beside).  Events before, between and after the two graphs give
+dense_step_us and sparse_step_us, so value = (dense + 7 sparse) / 8 up to the
+events' own cost.  Per-kernel durations come from the committed rocprofv3
+summary of this workload (profiles/kernels_<workload>.json) wherever the
+digest of the kernel's sources matches, else from HIP events the library
+records between its launches in a second timed pass of K blocks (both are
+reported); then the roofline of the dominant kernel, and the CPU oracle timed
+on one layer-block of the same workload, on all host cores and on one.
 """
 from __future__ import annotations
 
@@ -56,21 +61,53 @@ def traffic_from_profile(kernel_tag: str):
 
 
 def cpu_baseline(cfg, lay):
-    """The oracle, as it stands, on one layer-block of the same workload."""
-    from oracle import Oracle
+    """The oracle, as it stands, on one layer-block of the same workload: once on
+    all host cores (row-parallel dense step, one thread per KV head in the LoSA
+    steps: the same per-row and per-head oracle calls, the same bits), once on
+    one thread."""
+    from oracle import Oracle, host_threads
 
-    orc = Oracle(cfg, lay.kv_off, lay.prefix_len, lay.kv_tokens, lay.k_cache, lay.v_cache)
-    orc.page_meta()
-    t0 = time.perf_counter()
-    orc.dense_first_step(lay.q[0], lay.k_blk[0], lay.v_blk[0])
-    for t in range(1, STEPS_PER_BLOCK):
-        orc.step(lay.q[t], lay.q[t - 1], lay.k_blk[t], lay.v_blk[t])
-    sec = time.perf_counter() - t0
-    return {"value": sec * 1e6 / STEPS_PER_BLOCK, "unit": "us per block-step", "cores": 1,
-            "kind": "oracle",
+    def run(threaded):
+        orc = Oracle(cfg, lay.kv_off, lay.prefix_len, lay.kv_tokens, lay.k_cache, lay.v_cache)
+        orc.page_meta()
+        t0 = time.perf_counter()
+        if threaded:
+            orc.dense_first_step_threaded(lay.q[0], lay.k_blk[0], lay.v_blk[0])
+        else:
+            orc.dense_first_step(lay.q[0], lay.k_blk[0], lay.v_blk[0])
+        for t in range(1, STEPS_PER_BLOCK):
+            step = orc.step_threaded if threaded else orc.step
+            step(lay.q[t], lay.q[t - 1], lay.k_blk[t], lay.v_blk[t])
+        return time.perf_counter() - t0
+
+    n = host_threads()
+    sec_all = run(True)
+    sec_one = run(False)
+    per = lambda sec: sec * 1e6 / STEPS_PER_BLOCK
+    return {"value": per(sec_all), "unit": "us per block-step", "cores": n, "kind": "oracle",
+            "value_1_thread": per(sec_one),
             "sample": f"one layer, one {STEPS_PER_BLOCK}-step block (1 dense + "
-                      f"{STEPS_PER_BLOCK - 1} LoSA steps) of the same 64K workload, single thread, "
-                      f"{sec:.1f} s"}
+                      f"{STEPS_PER_BLOCK - 1} LoSA steps) of the same 64K workload: {sec_all:.2f} s "
+                      f"on {n} threads (dense rows over {n} threads, LoSA steps one thread per "
+                      f"KV head, {cfg.n_kvhead}), {sec_one:.2f} s on one thread"}
+
+
+def rocprof_durations(workload: str):
+    """Average kernel durations from the committed rocprofv3 trace summary of this
+    workload, per kernel tag, kept only where the digest of the kernel's sources
+    still matches (else the summary describes other code)."""
+    from sparse_attention_block_amd.profiling import KERNEL_TAGS, source_digest
+
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.json")
+    if not os.path.exists(path):
+        return {}, None
+    with open(path) as f:
+        rec = json.load(f)
+    out = {}
+    for tag, k in rec.get("kernels", {}).items():
+        if tag in KERNEL_TAGS and k.get("source_digest") == source_digest(KERNEL_TAGS[tag][1]):
+            out[tag] = k["avg_us"]
+    return out, os.path.relpath(path, ROOT)
 
 
 # ---------------------------------------------------------------------------
@@ -499,7 +536,7 @@ def main():
     union_pages = np.array([u.sum() for u in union_cnt], dtype=np.float64)  # per step, all KV heads
 
     # one prepared call per (step, layer): checks and marshalling happen here,
-    # once; the same calls bound to a side stream are captured into a graph
+    # once; the same calls bound to a side stream are captured into graphs
     gstream = torch.cuda.Stream()
     calls, gcalls = {}, {}
     for t in range(STEPS_PER_BLOCK):
@@ -508,13 +545,19 @@ def main():
                 table[(t, li)] = (ls.prepare_dense_first_step(q[0], kb[0], vb[0], stream=st) if t == 0
                                   else ls.prepare_step(q[t], q[t - 1], kb[t], vb[t], stream=st))
 
-    def run_block(events, table=calls):
-        """One block for every layer; events[(t, l)] = stage events or None."""
-        for t in range(STEPS_PER_BLOCK):
+    def run_steps(steps, events=None, table=calls):
+        """Steps `steps` of the block for every layer, in model order (step-major,
+        layer-minor); events[(t, l)] = stage events or None."""
+        for t in steps:
             for li in range(len(layers)):
                 c = table[(t, li)]
                 c.set_events(events[(t, li)] if events is not None else None)
                 c()
+
+    dense_steps, sparse_steps = [0], list(range(1, STEPS_PER_BLOCK))
+
+    def run_block(events=None):
+        run_steps(dense_steps + sparse_steps, events)
 
     def new_events():
         return {(t, li): [hip.event() for _ in range(L.LOSA_STAGE_EVENTS)]
@@ -540,48 +583,63 @@ def main():
         log(f"[bench] copy calibration: {args.copy_calibration} MiB read + written once")
     log(f"[bench] warmup {args.warmup} blocks x {len(layers)} layers")
     for _ in range(args.warmup):
-        run_block(None)
+        run_block()
     torch.cuda.synchronize()
     eager_ref = block_outputs()
 
-    # the block captured once into a HIP graph (the same launches, replayed
-    # without host launch overhead); every check replay must reproduce the
-    # eager block bit for bit, with eager work and synchronisations between
-    graph = None
+    # the block captured into two HIP graphs, its dense first steps and its LoSA
+    # steps (the same launches, replayed without host launch overhead); every
+    # check replay must reproduce the eager block bit for bit, with eager work
+    # and synchronisations between
+    graphs = None
     if not args.no_graph:
         torch.cuda.synchronize()
-        graph = hip.capture(gstream.cuda_stream, lambda: run_block(None, gcalls))
+        g_dense = hip.capture(gstream.cuda_stream, lambda: run_steps(dense_steps, table=gcalls))
+        g_sparse = hip.capture(gstream.cuda_stream, lambda: run_steps(sparse_steps, table=gcalls))
+        graphs = (g_dense, g_sparse)
         for rep_i in range(3):
-            hip.launch(graph, gstream.cuda_stream)
+            hip.launch(g_dense, gstream.cuda_stream)
+            hip.launch(g_sparse, gstream.cuda_stream)
             torch.cuda.synchronize()
             got = block_outputs()
             for a, b in zip(got, eager_ref):
                 if not torch.equal(a, b):
                     raise SystemExit("graph replay differs from the eager block")
-            run_block(None)  # eager work between replays
+            run_block()  # eager work between replays
             torch.cuda.synchronize()
         log("[bench] graph replays match the eager block")
 
     # value: exactly K blocks with nothing but the library's launches in the
-    # timed region (an event between kernels costs GPU time of its own)
+    # timed region, plus one event before, between and after the block's two
+    # graphs (the dense first steps, then the LoSA steps), which splits the
+    # block time into the two kinds of step
     def timed(use_graph):
         st = gstream.cuda_stream if use_graph else stream
-        e0, e1 = hip.event(), hip.event()
+        evs = [[hip.event() for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         w0 = time.perf_counter()
-        hip.record(e0, st)
         for k in range(args.steps):
+            hip.record(evs[k][0], st)
             if use_graph:
-                hip.launch(graph, st)
+                hip.launch(graphs[0], st)
             else:
-                run_block(None)
-        hip.record(e1, st)
+                run_steps(dense_steps)
+            hip.record(evs[k][1], st)
+            if use_graph:
+                hip.launch(graphs[1], st)
+            else:
+                run_steps(sparse_steps)
+            hip.record(evs[k][2], st)
         torch.cuda.synchronize()
-        return hip.ms(e0, e1), time.perf_counter() - w0
+        wall = time.perf_counter() - w0
+        total = hip.ms(evs[0][0], evs[-1][2])
+        dense = sum(hip.ms(e[0], e[1]) for e in evs)
+        sparse = sum(hip.ms(e[1], e[2]) for e in evs)
+        return total, dense, sparse, wall
 
-    log(f"[bench] timing {args.steps} blocks ({'graph replay' if graph else 'eager launches'})")
-    total_ms, wall = timed(graph is not None)
-    eager_ms = timed(False)[0] if graph is not None else total_ms
+    log(f"[bench] timing {args.steps} blocks ({'graph replay' if graphs else 'eager launches'})")
+    total_ms, dense_ms, sparse_ms, wall = timed(graphs is not None)
+    eager_ms = timed(False)[0] if graphs is not None else total_ms
 
     # per-kernel durations: a second timed pass of K blocks with the library's
     # stage events recorded between its launches
@@ -598,18 +656,18 @@ def main():
     value_us = total_ms * 1e3 / n_calls
     ms_per_step = total_ms / args.steps
     eager_us = eager_ms * 1e3 / n_calls
+    dense_step_us = dense_ms * 1e3 / (args.steps * len(layers))
+    sparse_step_us = sparse_ms * 1e3 / (args.steps * (STEPS_PER_BLOCK - 1) * len(layers))
 
     # per-kernel durations from the library's stage events (one kernel per stage)
     names = ["prepare", "score", "select", "prefix", "finish"]
-    stages = {"dense": {n: [] for n in names + ["total"]},
-              "sparse": {n: [] for n in names + ["total"]}}
+    stages = {"dense": {n: [] for n in names}, "sparse": {n: [] for n in names}}
     if use_events:
         for evs in ev_blocks:
             for (t, li), e in evs.items():
                 kind = "dense" if t == 0 else "sparse"
                 for i, n in enumerate(names):
                     stages[kind][n].append(hip.ms(e[i], e[i + 1]) * 1e3)
-                stages[kind]["total"].append(hip.ms(e[0], e[5]) * 1e3)
     mean = lambda xs: float(np.mean(xs)) if xs else None
 
     # algorithmic bytes (bf16 storage)
@@ -629,41 +687,49 @@ def main():
     block_bytes = dense_step_bytes + (STEPS_PER_BLOCK - 1) * sparse_step_bytes
     hbm_gbps = block_bytes / (value_us * STEPS_PER_BLOCK * 1e-6) / 1e9
 
+    # kernels of this shape (bf16: the preparation is folded into scoring, and
+    # the dense pass reads the block queries itself, so neither has a stage of
+    # its own), with their algorithmic HBM bytes per launch and launches per
+    # layer-block; durations from the committed rocprofv3 summary of this
+    # workload where it describes the current sources, else from the events
+    # (which add the latency of an event record, about 1 us, to every kernel)
+    rp, rp_path = rocprof_durations(cfg.name)
+    spec = {
+        "page_score": (stages["sparse"]["score"], meta_bytes, STEPS_PER_BLOCK - 1),
+        "page_select": (stages["sparse"]["select"], 0, STEPS_PER_BLOCK - 1),
+        "sparse_prefix": (stages["sparse"]["prefix"], union_bytes, STEPS_PER_BLOCK - 1),
+        "sparse_finish": (stages["sparse"]["finish"], 0, STEPS_PER_BLOCK - 1),
+        "dense_prefix": (stages["dense"]["prefix"], dense_kv_bytes, 1),
+        "dense_finish": (stages["dense"]["finish"], 0, 1),
+    }
     kernels = {}
-    if use_events:
-        # name: (event durations, algorithmic HBM bytes per launch or 0, launches per block)
-        spec = {
-            "sparse_prefix": (stages["sparse"]["prefix"], union_bytes, STEPS_PER_BLOCK - 1),
-            "page_score": (stages["sparse"]["score"], meta_bytes, STEPS_PER_BLOCK - 1),
-            "page_select": (stages["sparse"]["select"], 0, STEPS_PER_BLOCK - 1),
-            "dense_prefix": (stages["dense"]["prefix"], dense_kv_bytes, 1),
-            "sparse_prepare": (stages["sparse"]["prepare"], 0, STEPS_PER_BLOCK - 1),
-            "sparse_finish": (stages["sparse"]["finish"], 0, STEPS_PER_BLOCK - 1),
-            "dense_prepare": (stages["dense"]["prepare"], 0, 1),
-            "dense_finish": (stages["dense"]["finish"], 0, 1),
-        }
-        for name, (xs, nbytes, per_block) in spec.items():
-            us = mean(xs)
-            kernels[name] = {"avg_us": us, "launches_per_layer_block": per_block,
-                             "us_per_layer_block": us * per_block if us else None}
-            if nbytes:
-                gbps = nbytes / (us * 1e-6) / 1e9
-                kernels[name].update({"bytes_per_launch": nbytes, "achieved_gbps": gbps,
-                                      "frac_of_peak": gbps / PEAK_HBM_GBPS})
+    for name, (xs, nbytes, per_block) in spec.items():
+        ev_us = mean(xs) if use_events else None
+        us = rp.get(name, ev_us)
+        if us is None:
+            continue
+        kernels[name] = {"avg_us": us, "avg_us_events": ev_us,
+                         "duration_source": "rocprofv3" if name in rp else "hip events",
+                         "launches_per_layer_block": per_block, "us_per_layer_block": us * per_block}
+        if nbytes:
+            gbps = nbytes / (us * 1e-6) / 1e9
+            kernels[name].update({"bytes_per_launch": nbytes, "achieved_gbps": gbps,
+                                  "frac_of_peak": gbps / PEAK_HBM_GBPS})
     dominant = max((k for k in kernels if "bytes_per_launch" in kernels[k]),
                    key=lambda k: kernels[k]["us_per_layer_block"], default=None)
 
     def roofline(name):
-        if name is None:
+        if name is None or name not in kernels:
             return None
         k = kernels[name]
         return {"kernel": name, "bound": "hbm", "achieved": k["achieved_gbps"],
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k["frac_of_peak"],
                 "traffic": traffic_from_profile(name),
-                "bytes_per_launch": k["bytes_per_launch"], "avg_launch_us": k["avg_us"]}
+                "bytes_per_launch": k["bytes_per_launch"], "avg_launch_us": k["avg_us"],
+                "avg_launch_us_events": k["avg_us_events"],
+                "duration_source": (f"rocprofv3 kernel trace, {rp_path}" if name in rp
+                                    else "hip events around the kernel")}
 
-    sparse_us = mean(stages["sparse"]["total"]) if use_events else None
-    dense_us = mean(stages["dense"]["total"]) if use_events else None
     rec = {
         "metric": METRIC,
         "value": value_us,
@@ -683,15 +749,16 @@ def main():
                    "layers": len(layers), "step": "one block of 8 denoising steps "
                    "(1 dense + 7 LoSA) for every layer"},
         "hbm_gbps": hbm_gbps,
-        "sparse_step_us": sparse_us,
-        "dense_step_us": dense_us,
-        "speedup_vs_dense": (dense_us / sparse_us) if (sparse_us and dense_us) else None,
+        "sparse_step_us": sparse_step_us,
+        "dense_step_us": dense_step_us,
+        "speedup_vs_dense": dense_step_us / sparse_step_us,
         "union_pages_per_kv_head": float(union_pages.mean()) / (cfg.n_seq * Hk),
         "density": float(union_pages.mean()) / (cfg.n_seq * Hk * n_pages),
         "roofline": roofline(dominant),
-        "roofline_sparse_prefix": roofline("sparse_prefix") if use_events else None,
+        "roofline_sparse_prefix": roofline("sparse_prefix"),
         "kernels": kernels,
-        "launch": "hip graph replay of the captured block" if graph else "eager launches",
+        "launch": ("hip graph replays of the captured block (dense first steps, then LoSA "
+                   "steps)" if graphs else "eager launches"),
         "value_eager_launch": eager_us,
         "wall_s": wall,
     }

@@ -166,6 +166,8 @@ def main(argv=None):
     s1 = sub.add_parser("stats")
     s1.add_argument("csv")
     s1.add_argument("--command", required=True)
+    s1.add_argument("--json", help="also write the tagged kernels' averages (with the digest "
+                                   "of their sources) to this file")
     s2 = sub.add_parser("counters")
     s2.add_argument("fetch_csv")
     s2.add_argument("write_csv")
@@ -196,8 +198,20 @@ def main(argv=None):
     if a.cmd == "stats":
         print(f"# rocprofv3 kernel statistics\n# command: {a.command}\n")
         print(f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'time%':>6s}")
-        for name, calls, avg, mn, mx, pct in stats_table(a.csv):
+        table = stats_table(a.csv)
+        for name, calls, avg, mn, mx, pct in table:
             print(f"{name[:64]:64s} {calls:6d} {avg:9.2f} {mn:9.2f} {mx:9.2f} {pct:6.2f}")
+        if a.json:
+            means = {name: (avg, calls) for name, calls, avg, *_ in table}
+            rec = {"command": a.command, "kernels": {}}
+            for tag, (pat, srcs) in KERNEL_TAGS.items():
+                hits = [k for k in means if re.search(pat, k)]
+                if len(hits) == 1:
+                    avg, calls = means[hits[0]]
+                    rec["kernels"][tag] = {"kernel": hits[0], "avg_us": avg, "calls": calls,
+                                           "source_digest": source_digest(srcs)}
+            with open(a.json, "w") as f:
+                json.dump(rec, f, indent=1)
         return 0
 
     fetch = counter_means(a.fetch_csv, "FETCH_SIZE")
