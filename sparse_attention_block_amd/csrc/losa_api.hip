@@ -69,7 +69,7 @@ Dims make_dims(const losa_shape *sh) {
     D.n_tiles_total = (D.T / kPage + kTile - 1) / kTile;
     D.meta_main_bytes = static_cast<int64_t>(meta_main_bytes(D));
     D.meta_pm_off = D.meta_main_bytes + D.Hk * D.n_tiles_total * kTile * 4;
-    D.n_tiles_grid = (D.max_pages + kTile - 1) / kTile + 1;
+    D.n_tiles_grid = std::max(1, (D.max_pages + kTile - 1) / kTile);
     D.R = D.G * D.A;
     D.Rs16 = (D.R + 15) / 16 * 16;
     D.Rd = D.G * D.B;

@@ -41,7 +41,7 @@ struct Dims {
     int64_t n_tiles_total;            // metadata tiles per KV head over the whole cache
     int64_t meta_main_bytes;          // bytes of the min/max part of the page metadata
     int64_t meta_pm_off;              // byte offset of its page-major copy
-    int n_tiles_grid;                 // tiles a sequence can touch
+    int n_tiles_grid;                 // 64-page groups of the longest sequence (from its first page)
     int union_cap;                    // min(max_pages, G*A*k)
     int R;                            // stacked active rows per KV head = G*A
     int Rs16;                         // R rounded up to 16 (selection MFMA row tiles)
@@ -60,7 +60,7 @@ struct Work {
     float *qsel32;       // [S][Hk][max(R,1)][d][2] fp32 (max(q,0), min(q,0)): exact chain operand
     float *qabs;         // [S][Hk][max(R,1)] upper bound of sum_i |q_i|
     float *hbound;       // [S][Hk][max(R,1)][hb_stride] upper bound of each page's exact bound
-    float *tmax;         // [S][Hk][max(R,1)][n_tiles_grid] per tile: max lower bound
+    float *tmax;         // [S][Hk][max(R,1)][n_tiles_grid] per page group: max lower bound
     int32_t *psel;       // [S][Hk][max(R,1)][k] each active row's selected pages
     int32_t *union_cnt;  // [S][Hk] union size, written by the sparse prefix kernel
     float *part_acc;     // [S][Hk][n_chunks][rows][d]
@@ -162,6 +162,15 @@ __device__ __forceinline__ float lane_xor16(float v) {
 __device__ __forceinline__ float lane_xor32(float v) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float((__lane_id() & 32) ? a[0] : a[1]);
+}
+
+// Workgroup barrier for LDS exchanges only: this wave's LDS (and scalar)
+// operations complete, then s_barrier.  Unlike __syncthreads, whose fences
+// also wait for the wave's global stores and loads to complete, it lets
+// stores for later kernels stay in flight.  (The memory clobber keeps the
+// compiler from moving memory accesses across it.)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Sequence geometry with out-of-range values clamped into the cache.

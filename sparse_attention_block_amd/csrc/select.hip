@@ -79,6 +79,23 @@ __device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {
     return __popcll(mask & ((1ull << lane) - 1ull));
 }
 
+// Page groups: the pages of a sequence are bounded in groups of 64 counted
+// from its first page (group x: pages 64x .. 64x + 63), whatever their place
+// in the metadata tiles, so a 64K prefix has exactly 64 groups.  The global
+// page gp's chunk c (of nch per page) in the tile layout of KV head g, and
+// the page's largest |key|; gp is clamped into the metadata.
+__device__ __forceinline__ const uint4 *meta_chunk(const uint4 *meta, const Dims &D, int g,
+                                                   int64_t gp, int c, int nch) {
+    gp = min(gp, D.n_tiles_total * kTile - 1);
+    return meta + ((size_t)g * D.n_tiles_total + gp / kTile) * nch * kTile + (size_t)c * kTile +
+           gp % kTile;
+}
+__device__ __forceinline__ float meta_amax(const uint4 *meta, const Dims &D, int g, int64_t gp) {
+    gp = min(gp, D.n_tiles_total * kTile - 1);
+    return reinterpret_cast<const float *>(reinterpret_cast<const char *>(meta) +
+                                           D.meta_main_bytes)[(size_t)g * D.n_tiles_total * kTile + gp];
+}
+
 // ---------------------------------------------------------------------------
 // Phase 1: bounds of every (row, page) of one tile, as an interval.
 
@@ -177,16 +194,10 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
     const int bx = (blockIdx.x / ng) * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
     const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
     if (D.k >= sg.pages) return;  // every page is selected; nothing to score
-    const int64_t tile0 = sg.gp0 / kTile;
-    const int n_t = static_cast<int>((sg.gp0 + sg.pages - 1) / kTile - tile0 + 1);
+    const int n_t = (sg.pages + kTile - 1) / kTile;  // page groups of the sequence
     if (bx >= n_t) return;
-    const int64_t tile = tile0 + bx;
-    const bool tile_full = tile * kTile >= sg.gp0 && tile * kTile + kTile <= sg.gp0 + sg.pages;
+    const bool tile_full = (bx + 1) * kTile <= sg.pages;
     const int R = D.R, R1 = R > 0 ? R : 1;
-    const float *aux = reinterpret_cast<const float *>(reinterpret_cast<const char *>(meta) +
-                                                       D.meta_main_bytes) +
-                       (size_t)g * D.n_tiles_total * kTile + tile * kTile;
-    const uint4 *mt = meta + (size_t)(g * D.n_tiles_total + tile) * NCH * kTile;
     float *hb = W.hbound + (size_t)sgi * R1 * D.hb_stride;
     float *tm = W.tmax + (size_t)sgi * R1 * D.n_tiles_grid;
     const float *qabs = W.qabs + (size_t)sgi * R1;
@@ -197,9 +208,8 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
         int pl[4];
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            const int in_tile = cb * 16 + l16;
-            pl[cb] = static_cast<int>(tile * kTile + in_tile - sg.gp0);
-            amax[cb] = aux[in_tile];
+            pl[cb] = bx * kTile + cb * 16 + l16;
+            amax[cb] = meta_amax(meta, D, g, sg.gp0 + pl[cb]);
         }
         const uint32_t *q16 = W.qsel16 + (size_t)sgi * D.Rs16 * DIM;
         constexpr int KS = DIM / 16;
@@ -223,7 +233,7 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) bop[kk][cb] = mt[(size_t)(4 * kk + lg) * kTile + cb * 16 + l16];
+            for (int cb = 0; cb < 4; ++cb) bop[kk][cb] = *meta_chunk(meta, D, g, sg.gp0 + pl[cb], 4 * kk + lg, NCH);
         __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
         const int n_rt = D.Rs16 / 16;
         for (int rt = 0; rt < n_rt; ++rt) {
@@ -239,16 +249,17 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
         }
     } else {
         // fp32 storage: lane = page, any summation order (the interval absorbs it)
-        const int p = static_cast<int>(tile * kTile + lane - sg.gp0);
-        const bool valid = p >= 0 && p < sg.pages;
-        const float am = aux[lane];
+        const int p = bx * kTile + lane;
+        const bool valid = p < sg.pages;
+        const float am = meta_amax(meta, D, g, sg.gp0 + p);
+        const uint4 *mt = meta_chunk(meta, D, g, sg.gp0 + p, 0, NCH);  // chunk c at mt[c * kTile]
         const float *q32 = W.qsel32 + (size_t)sgi * R1 * DIM * 2;
         for (int r = 0; r < R; ++r) {
             float u = 0.0f;
             const float *q = q32 + (size_t)r * DIM * 2;
 #pragma unroll 4
             for (int c = 0; c < NCH; ++c) {
-                const uint4 m4 = mt[(size_t)c * kTile + lane];
+                const uint4 m4 = mt[(size_t)c * kTile];
                 u = fmaf(q[4 * c + 0], __uint_as_float(m4.x), u);
                 u = fmaf(q[4 * c + 1], __uint_as_float(m4.y), u);
                 u = fmaf(q[4 * c + 2], __uint_as_float(m4.z), u);
@@ -264,32 +275,42 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
 
 // ---------------------------------------------------------------------------
 // Phase 1 with the step's preparation folded in (bf16, the group's block
-// queries fit in LDS).  Every workgroup of a (sequence, KV head) repeats the
-// preparation from the same inputs -- locality chain, active set, stacked rows
-// -- so all of them agree, and builds its MFMA row operands from LDS; the
-// workgroup of the first tiles also writes the active list and the stacked rows
-// for the later kernels and resets the union size.  The locality chain is the
-// one of prepare.hip: each rounded square added in ascending dimension order.
-// Each thread holds matching 16-byte vectors of both steps, so all threads
-// compute the rounded squares (into LDS), and one thread per row adds them.
+// queries fit in LDS).  One workgroup per (sequence, KV head) and TPW
+// consecutive 64-page tiles, four waves per tile, each wave bounding 16 pages,
+// so the metadata stream is spread over the whole chip.  Every workgroup of a
+// (sequence, KV head) repeats the preparation from the same inputs -- locality
+// chain, active set, stacked rows -- so all of them agree, and builds its MFMA
+// row operands from LDS; the workgroup of the first tiles also writes the
+// active list and the stacked rows for the later kernels and resets the union
+// size.  The locality chain is the one of prepare.hip: each rounded square
+// added in ascending dimension order.  Each thread holds matching 16-byte
+// vectors of both steps, so all threads compute the rounded squares (into
+// LDS), and one thread per row adds them.  The query rows reuse the squares'
+// LDS once the chains are done.  Barriers wait for LDS traffic only, so the
+// bounds' stores stay in flight.
 
 constexpr int kPrepPad = 4;  // words of padding per LDS row (bank spread)
+#ifndef LOSA_SCORE_TPW
+#define LOSA_SCORE_TPW 2
+#endif
+constexpr int kScoreTilesPerGroup = LOSA_SCORE_TPW;  // 64-page tiles per scoring workgroup
 
-template <int DIM, bool SHARED>
-__global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__restrict__ q_t,
-                                                    const uint16_t *__restrict__ q_prev,
-                                                    const uint4 *__restrict__ meta,
-                                                    const int32_t *__restrict__ kv_off,
-                                                    const int32_t *__restrict__ prefix_len,
-                                                    Work W, float *__restrict__ dbg_loc,
-                                                    int32_t *__restrict__ dbg_act,
-                                                    int32_t *__restrict__ dbg_ucnt) {
+template <int DIM, bool SHARED, int TPW>
+__global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t *__restrict__ q_t,
+                                                          const uint16_t *__restrict__ q_prev,
+                                                          const uint4 *__restrict__ meta,
+                                                          const int32_t *__restrict__ kv_off,
+                                                          const int32_t *__restrict__ prefix_len,
+                                                          Work W, float *__restrict__ dbg_loc,
+                                                          int32_t *__restrict__ dbg_act,
+                                                          int32_t *__restrict__ dbg_ucnt) {
+    constexpr int NT = 256 * TPW;            // threads
     constexpr int KS = DIM / 16, NCH = DIM / 4;
     constexpr int RWP = DIM / 2 + kPrepPad;  // words per LDS query row: bf16 pairs of dims 2w, 2w+1
     constexpr int RWS = DIM + kPrepPad;      // words per LDS row of squares
     constexpr int VPR = DIM / 8;             // 16-byte vectors per row
-    constexpr int NV = kPrepVecs / 2;        // vectors per thread and step
-    extern __shared__ uint32_t qsm[];        // [G*B][RWP] q_t rows, then [G*B][RWS] fp32 squares
+    constexpr int NV = kPrepVecs / 2 / TPW;  // vectors per thread and step
+    extern __shared__ uint32_t qsm[];        // [G*B][RWS] fp32 squares, then [G*B][RWP] q_t rows
     // localities as rank keys: the fp32 bits (localities are >= +0, so their
     // bits order as the values) above ~token, so that "greater key" is
     // "larger locality, or equal and earlier token"
@@ -298,22 +319,23 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
     __shared__ int act_s[kMaxRows];
     __shared__ int rbase_s[kMaxRows];        // stacked row r: word offset of its query row in qsm
     __shared__ float qabs_s[kMaxRows];
+    __shared__ uint32_t tmk_s[4 * TPW][16];   // per wave and row of a row tile: lower-end maxima
     __shared__ float shl_s[SHARED ? kMaxSharedPrep : 1];  // per-head localities [Hq][B]
     const int ng = D.S * D.Hk;
-    const int sgi = blockIdx.x % ng, blk = blockIdx.x / ng;
+    const int sgi = blockIdx.x % ng, bx = blockIdx.x / ng;  // tiles TPW*bx .. of the sequence
     const int s = sgi / D.Hk, g = sgi % D.Hk;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int bx = blk * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wt = TPW * bx + w / 4;  // the wave's tile, counted in the sequence
     const int G = D.G, B = D.B, A = D.A, GB = G * B, R = D.R, Hq = D.Hq;
-    const bool writer = blk == 0;
+    const bool writer = bx == 0;
 
     // 1. the group's query rows of both steps (clamped 16-byte vectors; a thread
-    //    holds the same vectors of q_t and q_prev), q_t into LDS, then the
-    //    tile's page operands are requested
+    //    holds the same vectors of q_t and q_prev)
     const int nvec = GB * VPR;
-    static_assert(NV * 2 == kPrepVecs, "vectors per thread");
+    static_assert(NV * 2 * TPW == kPrepVecs, "vectors per thread");
     auto qaddr = [&](const uint16_t *base, int i) {
-        const int v = min(tid + 256 * i, nvec - 1);
+        const int v = min(tid + NT * i, nvec - 1);
         const int row = v / VPR, c = v % VPR;
         return reinterpret_cast<const uint4 *>(
             base + ((size_t)(s * B + row % B) * Hq + g * G + row / B) * DIM + c * 8);
@@ -326,61 +348,39 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         for (int i = 0; i < NV; ++i) qb_v[i] = *qaddr(q_prev, i);
     }
     // shared active set: the sequence's per-head localities (clamped reads)
-    constexpr int kShl = SHARED ? kMaxSharedPrep / 256 : 1;
+    constexpr int kShl = SHARED ? (kMaxSharedPrep + NT - 1) / NT : 1;
     float shl[kShl];
     if constexpr (SHARED) {
         const float *e = W.shloc + (size_t)s * Hq * B;
 #pragma unroll
-        for (int i = 0; i < kShl; ++i) shl[i] = e[min(tid + 256 * i, Hq * B - 1)];
+        for (int i = 0; i < kShl; ++i) shl[i] = e[min(tid + NT * i, Hq * B - 1)];
     }
     __builtin_amdgcn_sched_barrier(0);  // the query vectors are requested first
+    // 2. the metadata of the wave's 16 pages: chunk 4*kk + lg of page
+    //    16*(w%4) + l16 of the wave's page group (clamped into the metadata
+    //    where the sequence has no such page, so that no load sits in a branch)
     const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
-    const int64_t tile0 = sg.gp0 / kTile;
-    const int n_t = static_cast<int>((sg.gp0 + sg.pages - 1) / kTile - tile0 + 1);
-    const bool tile_ok = D.k < sg.pages && bx < n_t;  // uniform over the wave
-    // a wave without a tile in range loads a clamped, in-bounds tile and never
-    // uses it, so that no load sits in a branch
-    const int64_t tile =
-        min(tile0 + max(0, min(bx, n_t - 1)), static_cast<int64_t>(D.n_tiles_total - 1));
-    const bool tile_full = tile * kTile >= sg.gp0 && tile * kTile + kTile <= sg.gp0 + sg.pages;
+    const int n_t = (sg.pages + kTile - 1) / kTile;       // page groups of the sequence
+    const bool wg_ok = D.k < sg.pages && TPW * bx < n_t;  // uniform over the workgroup
+    const bool wave_ok = D.k < sg.pages && wt < n_t;      // uniform over the wave
+    const bool tile_full = (wt + 1) * kTile <= sg.pages;   // every page of the group is live
     const int R1 = R > 0 ? R : 1;
     const int l16 = lane & 15, lg = lane >> 4;
-    const uint4 *mt = meta + (size_t)(g * D.n_tiles_total + tile) * NCH * kTile;
+    const int pl = wt * kTile + 16 * (w % 4) + l16;  // the lane's page in the sequence
+    uint4 bop[KS];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int v = min(tid + 256 * i, nvec - 1);
-        *reinterpret_cast<uint4 *>(&qsm[(v / VPR) * RWP + (v % VPR) * 4]) = qa_v[i];
-    }
+    for (int kk = 0; kk < KS; ++kk) bop[kk] = *meta_chunk(meta, D, g, sg.gp0 + pl, 4 * kk + lg, NCH);
+    const float amax = meta_amax(meta, D, g, sg.gp0 + pl);
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
     if constexpr (SHARED) {
 #pragma unroll
-        for (int i = 0; i < kShl; ++i) shl_s[tid + 256 * i] = shl[i];
-    }
-    // The tile is requested only now, after the query vectors have landed: the
-    // tiles of all workgroups together would otherwise queue ahead of them, and
-    // the preparation below waits for the queries, not for the tile.
-    __builtin_amdgcn_sched_barrier(0);
-    uint4 bop[KS][4];
-    float amax[4];
-    int pl[4];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) bop[kk][cb] = mt[(size_t)(4 * kk + lg) * kTile + cb * 16 + l16];
-    const float *aux = reinterpret_cast<const float *>(reinterpret_cast<const char *>(meta) +
-                                                       D.meta_main_bytes) +
-                       (size_t)g * D.n_tiles_total * kTile + tile * kTile;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        pl[cb] = static_cast<int>(tile * kTile + cb * 16 + l16 - sg.gp0);
-        amax[cb] = aux[cb * 16 + l16];
-    }
-    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
-    float *sq = reinterpret_cast<float *>(qsm + GB * RWP);
-    if constexpr (!SHARED) {
+        for (int i = 0; i < kShl; ++i)
+            if (tid + NT * i < kMaxSharedPrep) shl_s[tid + NT * i] = shl[i];
+    } else {
         // rounded squares of the change, dimensions c*8 .. c*8+7 of a row
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int v = min(tid + 256 * i, nvec - 1);
+            const int v = min(tid + NT * i, nvec - 1);
             const uint32_t aw[4] = {qa_v[i].x, qa_v[i].y, qa_v[i].z, qa_v[i].w};
             const uint32_t bw[4] = {qb_v[i].x, qb_v[i].y, qb_v[i].z, qb_v[i].w};
             float sv[8];
@@ -391,14 +391,15 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
                 const float d1 = bf16_hi(aw[e]) - bf16_hi(bw[e]);
                 sv[2 * e + 1] = d1 * d1;
             }
-            float4 *dst = reinterpret_cast<float4 *>(sq + (v / VPR) * RWS + (v % VPR) * 8);
+            float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(qsm) +
+                                                     (v / VPR) * RWS + (v % VPR) * 8);
             dst[0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
             dst[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // 2. locality chain per (query head, token), then the active set; with a
+    // 3. locality chain per (query head, token), then the active set; with a
     //    shared active set, the sum of the per-head localities over the query
     //    heads in ascending order, then one set for all of the group's heads
     if constexpr (SHARED) {
@@ -407,14 +408,14 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             for (int h = 0; h < Hq; ++h) acc = acc + shl_s[h * B + tid];
             ek_s[tid] = (static_cast<uint64_t>(__float_as_uint(acc)) << 32) | static_cast<uint32_t>(~tid);
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < B) {
             const uint64_t kt = ek_s[tid];
             int rank = 0;
             for (int u = 0; u < B; ++u) rank += ek_s[u] > kt;
             sel_s[tid] = rank < A;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < B && sel_s[tid]) {
             int pos = 0;
             for (int u = 0; u < tid; ++u) pos += sel_s[u];
@@ -423,10 +424,10 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
                 rbase_s[j * A + pos] = (j * B + tid) * RWP;
             }
         }
-        __syncthreads();
     } else {
         if (tid < GB) {
-            const float4 *sr = reinterpret_cast<const float4 *>(sq + tid * RWS);
+            const float4 *sr = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(qsm) +
+                                                                tid * RWS);
             float acc = 0.0f;
             // 16-byte reads in batches of RB, the next batch requested before
             // the adds of this one
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             if (writer && dbg_loc)
                 dbg_loc[((size_t)s * Hq + g * G + tid / B) * B + tid % B] = acc / static_cast<float>(DIM);
         }
-        __syncthreads();
+        lds_barrier();
         // rank inside the row's head (score desc, token asc); the |A| best are
         // active, listed in ascending token order
         const int j = tid / B, t = tid % B;
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             pos = __popcll(bal & below & ~before_head);
         } else {
             if (tid < GB) sel_s[tid] = sel;
-            __syncthreads();
+            lds_barrier();
             if (sel)
                 for (int u = 0; u < t; ++u) pos += sel_s[j * B + u];
         }
@@ -483,20 +484,26 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             act_s[j * A + pos] = t;
             rbase_s[j * A + pos] = tid * RWP;
         }
-        __syncthreads();
     }
+    lds_barrier();  // the squares have been read: their LDS takes the query rows
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int v = min(tid + NT * i, nvec - 1);
+        *reinterpret_cast<uint4 *>(&qsm[(v / VPR) * RWP + (v % VPR) * 4]) = qa_v[i];
+    }
+    lds_barrier();
 
-    // 3. stacked rows r = j*|A| + a: sum |q| bounds; the writer stores the rows
+    // 4. stacked rows r = j*|A| + a: sum |q| bounds; the writer stores the rows
     //    (bf16, rows up to the next multiple of 16 zeroed) for the later kernels
     // 16 lanes per row, each summing DIM/16 values; any order (an upper bound
     // with 1/256 of margin)
-    for (int r0 = 0; r0 < R; r0 += 16) {
+    for (int r0 = 0; r0 < R; r0 += NT / 16) {
         const int r = r0 + tid / 16, part = tid % 16;
         float ab = 0.0f;
         if (r < R) {
             const uint32_t *a = &qsm[rbase_s[r] + part * (DIM / 32)];
 #pragma unroll
-            for (int w = 0; w < DIM / 32; ++w) ab += fabsf(bf16_lo(a[w])) + fabsf(bf16_hi(a[w]));
+            for (int w2 = 0; w2 < DIM / 32; ++w2) ab += fabsf(bf16_lo(a[w2])) + fabsf(bf16_hi(a[w2]));
         }
         ab += lane_xor1(ab);  // then l^2, l^4, l^8: the row's sum in each of its lanes
         ab += lane_xor2(ab);
@@ -504,11 +511,10 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
         ab += lane_xor15(ab);
         if (r < R && part == 0) qabs_s[r] = ab * (1.0f + 1.0f / 256.0f);
     }
-    __syncthreads();
+    lds_barrier();
     // The writer's stores for the later kernels -- the active list, the stacked
     // rows (from LDS) and a zero union count, which the sparse prefix kernel
-    // overwrites -- go out after the wave's bounds (or before an early return):
-    // the wait for the metadata tile waits for every store issued before it.
+    // overwrites -- go out after the bounds (or before an early return).
     auto writer_stores = [&]() {
         if (!writer) return;
         if (tid == 0) {
@@ -516,27 +522,30 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             if (dbg_ucnt) dbg_ucnt[sgi] = 0;
         }
         int32_t *act = W.active + ((size_t)s * Hq + g * G) * A;  // [G][A], rows j*A + a
-        for (int i = tid; i < R; i += 256) {
+        for (int i = tid; i < R; i += NT) {
             act[i] = act_s[i];
             W.qabs[(size_t)sgi * R1 + i] = qabs_s[i];  // for the selection's short-sequence threshold
             if (dbg_act) dbg_act[((size_t)s * Hq + g * G) * A + i] = act_s[i];
         }
         uint16_t *qr = static_cast<uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
-        for (int i = tid; i < D.Rs16 * VPR; i += 256) {
+        for (int i = tid; i < D.Rs16 * VPR; i += NT) {
             const int r = i / VPR, c = i % VPR;
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
             if (r < R) v = *reinterpret_cast<const uint4 *>(&qsm[rbase_s[r] + c * 4]);
             *reinterpret_cast<uint4 *>(qr + (size_t)r * DIM + c * 8) = v;
         }
     };
-    if (!tile_ok) {
+    if (!wg_ok) {
         writer_stores();
         return;
     }
 
-    // 4. the tile's bounds, row tile by row tile, row operands built from LDS
+    // 5. the wave's 16 pages, row tile by row tile: each (row, page) upper end,
+    //    and each row's largest lower end over each tile's 64 pages (the four
+    //    waves' maxima meet in LDS); waves past the sequence's tiles store nothing
     float *hb = W.hbound + (size_t)sgi * R1 * D.hb_stride;
     float *tm = W.tmax + (size_t)sgi * R1 * D.n_tiles_grid;
+    const bool page_ok = wave_ok && pl < sg.pages;
     for (int rt = 0; rt < D.Rs16 / 16; ++rt) {
         const int row = rt * 16 + l16;
         const bool live = row < R;
@@ -558,16 +567,56 @@ __global__ __launch_bounds__(256) void k_score_prep(Dims D, const uint16_t *__re
             return make_uint2(__builtin_amdgcn_perm(x, x, (ml & lo_n) | (~ml & lo_p)),
                               __builtin_amdgcn_perm(x, x, (mh & hi_n) | (~mh & hi_p)));
         };
-        uint4 aop[KS];
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             const uint2 a = split(h2[kk].x), b = split(h2[kk].y);
-            aop[kk] = make_uint4(a.x, a.y, b.x, b.y);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y)),
+                __builtin_bit_cast(bf16x8_t, bop[kk]), acc, 0, 0, 0);
         }
-        float qa[4];
+        // lane holds rows rt*16 + 4*lg + j of page pl
+        uint32_t lk[4];
+        if (tile_full && (rt + 1) * 16 <= R) {
+            // every page of the tile and every row of the tile is live (uniform
+            // over the wave): no per-element guards
+            float *hr = hb + (size_t)(rt * 16 + 4 * lg) * D.hb_stride + pl;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qa[j] = qabs_s[min(rt * 16 + 4 * lg + j, R1 - 1)];
-        bound_rowtile<DIM>(D, rt, aop, qa, bop, amax, pl, sg.pages, bx, l16, lg, hb, tm, tile_full);
+            for (int j = 0; j < 4; ++j) {
+                const float e = kBoundRel * qabs_s[rt * 16 + 4 * lg + j] * amax + kBoundAbs;
+                hr[(size_t)j * D.hb_stride] = acc[j] + e;
+                lk[j] = ord_key(acc[j] - e);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = rt * 16 + 4 * lg + j;
+                const float e = kBoundRel * qabs_s[min(r, R1 - 1)] * amax + kBoundAbs;
+                lk[j] = 0u;
+                if (r < R && page_ok) {
+                    hb[(size_t)r * D.hb_stride + pl] = acc[j] + e;
+                    lk[j] = ord_key(acc[j] - e);
+                }
+            }
+        }
+        // the rows' maxima over the wave's 16 pages (lanes 16*lg + 15), then over
+        // each tile's four waves
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lk[j] = row16_max_u32(lk[j]);
+        if (l16 == 15) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tmk_s[w][4 * lg + j] = lk[j];
+        }
+        lds_barrier();
+        if (tid < 16 * TPW) {
+            const int tt = tid / 16, rr = rt * 16 + tid % 16;  // the tile of the workgroup, the row
+            if (rr < R && TPW * bx + tt < n_t) {
+                const uint32_t m = max(max(tmk_s[4 * tt][tid % 16], tmk_s[4 * tt + 1][tid % 16]),
+                                       max(tmk_s[4 * tt + 2][tid % 16], tmk_s[4 * tt + 3][tid % 16]));
+                tm[(size_t)rr * D.n_tiles_grid + TPW * bx + tt] = ord_to_f32(m);
+            }
+        }
+        lds_barrier();  // tmk_s is rewritten by the next row tile
     }
     writer_stores();
 }
@@ -683,8 +732,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
             for (int e = lane; e < k; e += 64)
                 dbg.page_sel[(((size_t)s * D.Hq + h) * D.A + a) * k + e] = e < sg.pages ? e : -1;
     } else {
-        const int64_t tile0 = sg.gp0 / kTile;
-        const int n_t = static_cast<int>((sg.gp0 + sg.pages - 1) / kTile - tile0 + 1);
+        const int n_t = (sg.pages + kTile - 1) / kTile;  // page groups of the sequence
         const float *tm = tmax + ((size_t)sgi * R1 + r) * D.n_tiles_grid;
         const float *hb = hbound + ((size_t)sgi * R1 + r) * D.hb_stride;
         // Requested together: the row's chain operands, the tile maxima of the
@@ -913,9 +961,10 @@ hipError_t launch_score(const Dims &D, const void *meta, const int32_t *kv_off,
 }
 
 size_t score_prep_lds_bytes(const Dims &D) {
+    // the squares, then (in the same place) the query rows
     const size_t rows = (size_t)D.G * D.B;
     const size_t squares = (D.flags & LOSA_FLAG_SHARED_ACTIVE) ? 0 : rows * (D.d + kPrepPad) * 4;
-    return rows * (D.d / 2 + kPrepPad) * 4 + squares;
+    return std::max(rows * (D.d / 2 + kPrepPad) * 4, squares);
 }
 
 bool score_prep_fits(const Dims &D) {
@@ -928,14 +977,15 @@ hipError_t launch_score_prep(const Dims &D, const void *q_t, const void *q_prev,
                              const int32_t *kv_off, const int32_t *prefix_len, const Work &W,
                              float *dbg_loc, int32_t *dbg_act, int32_t *dbg_ucnt, hipStream_t st) {
     const int ng = D.S * D.Hk;
-    const dim3 grid(((D.n_tiles_grid + 3) / 4) * ng);
+    constexpr int TPW = kScoreTilesPerGroup;
+    const dim3 grid(((D.n_tiles_grid + TPW - 1) / TPW) * ng);
     const size_t lds = score_prep_lds_bytes(D);
     auto *a = static_cast<const uint16_t *>(q_t);
     auto *b = static_cast<const uint16_t *>(q_prev);
     auto *m = static_cast<const uint4 *>(meta);
 #define LAUNCH_P(DIMV, SH)                                                                    \
-    hipLaunchKernelGGL((k_score_prep<DIMV, SH>), grid, dim3(256), lds, st, D, a, b, m, kv_off,  \
-                       prefix_len, W, dbg_loc, dbg_act, dbg_ucnt)
+    hipLaunchKernelGGL((k_score_prep<DIMV, SH, TPW>), grid, dim3(256 * TPW), lds, st, D, a, b, m, \
+                       kv_off, prefix_len, W, dbg_loc, dbg_act, dbg_ucnt)
     const bool shared = D.flags & LOSA_FLAG_SHARED_ACTIVE;
     if (D.d == 128) {
         if (shared) LAUNCH_P(128, true);
