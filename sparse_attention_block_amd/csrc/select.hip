@@ -306,18 +306,18 @@ __global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t
                                                           int32_t *__restrict__ dbg_ucnt) {
     constexpr int NT = 256 * TPW;            // threads
     constexpr int KS = DIM / 16, NCH = DIM / 4;
-    constexpr int RWP = DIM / 2 + kPrepPad;  // words per LDS query row: bf16 pairs of dims 2w, 2w+1
     constexpr int RWS = DIM + kPrepPad;      // words per LDS row of squares
     constexpr int VPR = DIM / 8;             // 16-byte vectors per row
     constexpr int NV = kPrepVecs / 2 / TPW;  // vectors per thread and step
-    extern __shared__ uint32_t qsm[];        // [G*B][RWS] fp32 squares, then [G*B][RWP] q_t rows
+    constexpr int OPS = DIM / 4 + 1;         // 16-byte chunks per LDS operand row (one of padding)
+    extern __shared__ uint32_t qsm[];        // [G*B][RWS] fp32 squares, then [Rs16][OPS] operand rows
     // localities as rank keys: the fp32 bits (localities are >= +0, so their
     // bits order as the values) above ~token, so that "greater key" is
     // "larger locality, or equal and earlier token"
     __shared__ uint64_t ek_s[kMaxRows];
     __shared__ int sel_s[kMaxRows];
     __shared__ int act_s[kMaxRows];
-    __shared__ int rbase_s[kMaxRows];        // stacked row r: word offset of its query row in qsm
+    __shared__ int rmap_s[kMaxRows];         // query row j*B + t: its stacked row, or -1
     __shared__ float qabs_s[kMaxRows];
     __shared__ uint32_t tmk_s[4 * TPW][16];   // per wave and row of a row tile: lower-end maxima
     __shared__ float shl_s[SHARED ? kMaxSharedPrep : 1];  // per-head localities [Hq][B]
@@ -416,12 +416,12 @@ __global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t
             sel_s[tid] = rank < A;
         }
         lds_barrier();
-        if (tid < B && sel_s[tid]) {
+        if (tid < B) {
             int pos = 0;
             for (int u = 0; u < tid; ++u) pos += sel_s[u];
             for (int j = 0; j < G; ++j) {
-                act_s[j * A + pos] = tid;
-                rbase_s[j * A + pos] = (j * B + tid) * RWP;
+                if (sel_s[tid]) act_s[j * A + pos] = tid;
+                rmap_s[j * B + tid] = sel_s[tid] ? j * A + pos : -1;
             }
         }
     } else {
@@ -480,30 +480,51 @@ __global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t
             if (sel)
                 for (int u = 0; u < t; ++u) pos += sel_s[j * B + u];
         }
-        if (sel) {
-            act_s[j * A + pos] = t;
-            rbase_s[j * A + pos] = tid * RWP;
-        }
+        if (sel) act_s[j * A + pos] = t;
+        if (tid < GB) rmap_s[tid] = sel ? j * A + pos : -1;
     }
-    lds_barrier();  // the squares have been read: their LDS takes the query rows
+    lds_barrier();  // the squares have been read: their LDS takes the operand rows
+    // 4. the stacked rows' MFMA operands, built once for all waves: the (q+, q-)
+    //    pairs of dims 4c .. 4c+3 as 16-byte chunk c of row r (a bf16 value goes
+    //    to the low half of its word when its sign bit is clear, else to the
+    //    high half, so -0 sits in the q- slot: a zero product either way), from
+    //    the query vectors each thread still holds (the writer stores the rows
+    //    themselves, bf16, for the later kernels at its end)
+    uint4 *opb = reinterpret_cast<uint4 *>(qsm);  // [Rs16][OPS]
+    uint16_t *qr = static_cast<uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
+    auto split = [](uint32_t x) {
+        const uint32_t ml = static_cast<uint32_t>(static_cast<int32_t>(x << 16) >> 31);  // sign of low
+        const uint32_t mh = static_cast<uint32_t>(static_cast<int32_t>(x) >> 31);        // sign of high
+        return make_uint2(__builtin_amdgcn_perm(x, x, (ml & 0x01000c0cu) | (~ml & 0x0c0c0100u)),
+                          __builtin_amdgcn_perm(x, x, (mh & 0x03020c0cu) | (~mh & 0x0c0c0302u)));
+    };
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int v = min(tid + NT * i, nvec - 1);
-        *reinterpret_cast<uint4 *>(&qsm[(v / VPR) * RWP + (v % VPR) * 4]) = qa_v[i];
+        const int v = tid + NT * i;
+        const int r = v < nvec ? rmap_s[v / VPR] : -1;
+        if (r >= 0) {
+            const int c = v % VPR;  // dims 8c .. 8c+7: operand chunks 2c, 2c+1
+            const uint2 a = split(qa_v[i].x), b = split(qa_v[i].y);
+            const uint2 c2 = split(qa_v[i].z), d2 = split(qa_v[i].w);
+            opb[r * OPS + 2 * c] = make_uint4(a.x, a.y, b.x, b.y);
+            opb[r * OPS + 2 * c + 1] = make_uint4(c2.x, c2.y, d2.x, d2.y);
+        }
     }
+    // padding rows of the last row tile: zero operands (their bounds are not stored)
+    for (int i = tid; i < (D.Rs16 - R) * (DIM / 4); i += NT)
+        opb[(R + i / (DIM / 4)) * OPS + i % (DIM / 4)] = make_uint4(0u, 0u, 0u, 0u);
     lds_barrier();
 
-    // 4. stacked rows r = j*|A| + a: sum |q| bounds; the writer stores the rows
-    //    (bf16, rows up to the next multiple of 16 zeroed) for the later kernels
-    // 16 lanes per row, each summing DIM/16 values; any order (an upper bound
-    // with 1/256 of margin)
+    // sum |q| bounds of the stacked rows: 16 lanes per row, each summing DIM/16
+    // values; any order (an upper bound with 1/256 of margin); a row's (q+, q-)
+    // pairs hold each value once and a zero
     for (int r0 = 0; r0 < R; r0 += NT / 16) {
         const int r = r0 + tid / 16, part = tid % 16;
         float ab = 0.0f;
         if (r < R) {
-            const uint32_t *a = &qsm[rbase_s[r] + part * (DIM / 32)];
+            const uint32_t *a = reinterpret_cast<const uint32_t *>(&opb[r * OPS]) + part * (DIM / 16);
 #pragma unroll
-            for (int w2 = 0; w2 < DIM / 32; ++w2) ab += fabsf(bf16_lo(a[w2])) + fabsf(bf16_hi(a[w2]));
+            for (int w2 = 0; w2 < DIM / 16; ++w2) ab += fabsf(bf16_lo(a[w2])) + fabsf(bf16_hi(a[w2]));
         }
         ab += lane_xor1(ab);  // then l^2, l^4, l^8: the row's sum in each of its lanes
         ab += lane_xor2(ab);
@@ -512,9 +533,10 @@ __global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t
         if (r < R && part == 0) qabs_s[r] = ab * (1.0f + 1.0f / 256.0f);
     }
     lds_barrier();
-    // The writer's stores for the later kernels -- the active list, the stacked
-    // rows (from LDS) and a zero union count, which the sparse prefix kernel
-    // overwrites -- go out after the bounds (or before an early return).
+    // The writer's stores for the later kernels -- the active list, the sum |q|
+    // bounds, the stacked rows with their zero padding and a zero union count,
+    // which the sparse prefix kernel overwrites -- go out after the bounds (or
+    // before an early return): a wait for the metadata would wait for them too.
     auto writer_stores = [&]() {
         if (!writer) return;
         if (tid == 0) {
@@ -527,13 +549,15 @@ __global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t
             W.qabs[(size_t)sgi * R1 + i] = qabs_s[i];  // for the selection's short-sequence threshold
             if (dbg_act) dbg_act[((size_t)s * Hq + g * G) * A + i] = act_s[i];
         }
-        uint16_t *qr = static_cast<uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
-        for (int i = tid; i < D.Rs16 * VPR; i += NT) {
-            const int r = i / VPR, c = i % VPR;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (r < R) v = *reinterpret_cast<const uint4 *>(&qsm[rbase_s[r] + c * 4]);
-            *reinterpret_cast<uint4 *>(qr + (size_t)r * DIM + c * 8) = v;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + NT * i;
+            const int r = v < nvec ? rmap_s[v / VPR] : -1;
+            if (r >= 0) *reinterpret_cast<uint4 *>(qr + (size_t)r * DIM + (v % VPR) * 8) = qa_v[i];
         }
+        for (int i = tid; i < (D.Rs16 - R) * VPR; i += NT)
+            *reinterpret_cast<uint4 *>(qr + (size_t)(R + i / VPR) * DIM + (i % VPR) * 8) =
+                make_uint4(0u, 0u, 0u, 0u);
     };
     if (!wg_ok) {
         writer_stores();
@@ -547,34 +571,12 @@ __global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t
     float *tm = W.tmax + (size_t)sgi * R1 * D.n_tiles_grid;
     const bool page_ok = wave_ok && pl < sg.pages;
     for (int rt = 0; rt < D.Rs16 / 16; ++rt) {
-        const int row = rt * 16 + l16;
-        const bool live = row < R;
-        // the row's query words (a clamped row for the padding rows, zeroed below)
-        const uint32_t *qrow = &qsm[rbase_s[min(row, R - 1)] + 2 * lg];
-        uint2 h2[KS];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) h2[kk] = *reinterpret_cast<const uint2 *>(qrow + 8 * kk);
-        // (q+, q-) pairs by byte permutes: a bf16 value goes to the low half of
-        // its word when its sign bit is clear, else to the high half (so -0 sits
-        // in the q- slot: a zero product either way); padding rows take the
-        // selector of four zero bytes
-        constexpr uint32_t kZero = 0x0c0c0c0cu;
-        const uint32_t lo_p = live ? 0x0c0c0100u : kZero, lo_n = live ? 0x01000c0cu : kZero;
-        const uint32_t hi_p = live ? 0x0c0c0302u : kZero, hi_n = live ? 0x03020c0cu : kZero;
-        auto split = [&](uint32_t x) {
-            const uint32_t ml = static_cast<uint32_t>(static_cast<int32_t>(x << 16) >> 31);  // sign of low
-            const uint32_t mh = static_cast<uint32_t>(static_cast<int32_t>(x) >> 31);        // sign of high
-            return make_uint2(__builtin_amdgcn_perm(x, x, (ml & lo_n) | (~ml & lo_p)),
-                              __builtin_amdgcn_perm(x, x, (mh & hi_n) | (~mh & hi_p)));
-        };
         float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const uint2 a = split(h2[kk].x), b = split(h2[kk].y);
+        for (int kk = 0; kk < KS; ++kk)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y)),
+                __builtin_bit_cast(bf16x8_t, opb[(rt * 16 + l16) * OPS + 4 * kk + lg]),
                 __builtin_bit_cast(bf16x8_t, bop[kk]), acc, 0, 0, 0);
-        }
         // lane holds rows rt*16 + 4*lg + j of page pl
         uint32_t lk[4];
         if (tile_full && (rt + 1) * 16 <= R) {
@@ -961,10 +963,10 @@ hipError_t launch_score(const Dims &D, const void *meta, const int32_t *kv_off,
 }
 
 size_t score_prep_lds_bytes(const Dims &D) {
-    // the squares, then (in the same place) the query rows
+    // the squares, then (in the same place) the stacked rows' MFMA operands
     const size_t rows = (size_t)D.G * D.B;
     const size_t squares = (D.flags & LOSA_FLAG_SHARED_ACTIVE) ? 0 : rows * (D.d + kPrepPad) * 4;
-    return std::max(rows * (D.d / 2 + kPrepPad) * 4, squares);
+    return std::max((size_t)D.Rs16 * (D.d + 4) * 4, squares);
 }
 
 bool score_prep_fits(const Dims &D) {
