@@ -58,20 +58,32 @@
  *   q_t, q_prev, out       [n_seq][B][n_qhead][head_dim]      dtype
  *   k_blk, v_blk           [n_seq][B][n_kvhead][head_dim]     dtype
  *   k_cache, v_cache       [n_kvhead][T][head_dim]            dtype
- *       sequence s holds tokens kv_off[s] .. kv_off[s]+prefix_len[s]-1;
- *       kv_off[s] is a multiple of page_size; sequences may not overlap.
- *   kv_off, prefix_len     [n_seq] int32 (device)
+ *       the cache rows of every KV head are grouped in physical pages of 16
+ *       tokens (page e: rows 16e .. 16e+15).  A sequence's prefix lies either
+ *       contiguously -- sequence s holds tokens kv_off[s] .. kv_off[s] +
+ *       prefix_len[s] - 1, kv_off[s] a multiple of page_size, sequences not
+ *       overlapping -- or, with a page table, in any pages of the pool: the
+ *       sequence's page p (its tokens 16p .. 16p+15) is physical page
+ *       page_table[s][p] (a paged KV pool: ragged sequences need no
+ *       contiguous room, and pages may be shared between sequences).
+ *   kv_off, prefix_len     [n_seq] int32 (device); kv_off may be NULL with a page table
+ *   page_table             NULL, or [n_seq][max(1, ceil(max_prefix_len / 16))] int32
+ *                          (device): physical pages in [0, T/16); entries at or
+ *                          past a sequence's page count are not used.  A page
+ *                          shared by sequences must hold the same valid tokens in
+ *                          each (whole pages, as shared prefixes give).
  *   op_cache               [n_seq][n_qhead][B][head_dim]      fp32 (o_p)
  *   lp_cache               [n_seq][n_qhead][B]                fp32 (L_p)
- *   page_meta              opaque, losa_page_meta_bytes() bytes
+ *   page_meta              opaque, losa_page_meta_bytes() bytes, indexed by physical page
  *
  * Errors.  Arguments are checked on the host before anything is enqueued;
  * a failed check returns its status and enqueues nothing.  A failed launch
  * returns LOSA_ERR_HIP.  Asynchronous device faults surface at the caller's
  * next synchronisation.  prefix_len[s] must lie in [0, max_prefix_len] and
- * kv_off[s] + prefix_len[s] <= kv_tokens; kernels clamp out-of-range values
- * into the cache instead of reading past it, so the results for such a
- * sequence are unspecified but memory-safe.  Inputs must be finite.
+ * kv_off[s] + prefix_len[s] <= kv_tokens (page-table entries in [0, T/16));
+ * kernels clamp out-of-range values into the cache instead of reading past
+ * it, so the results for such a sequence are unspecified but memory-safe.
+ * Inputs must be finite.
  */
 #ifndef LOSA_H_
 #define LOSA_H_
@@ -175,10 +187,13 @@ int32_t losa_union_capacity(const losa_shape *shape);
  * sequence and KV head, the element-wise minimum and maximum of the keys of
  * its tokens that lie below prefix_len[s].  Run once per committed block
  * (the prefix does not change between the denoising steps of a block).
- * Writes page_meta (losa_page_meta_bytes(shape) bytes, library layout).
+ * Writes page_meta (losa_page_meta_bytes(shape) bytes, library layout) at
+ * each page's physical index (with a page table, pages no sequence uses keep
+ * what they held; a page shared by sequences holds the same keys for each).
  */
 int losa_build_page_meta(const losa_shape *shape, const void *k_cache, const int32_t *kv_off,
-                         const int32_t *prefix_len, void *page_meta, void *stream);
+                         const int32_t *prefix_len, const int32_t *page_table, void *page_meta,
+                         void *stream);
 
 /*
  * Block commit: when the tokens first_token[s] .. prefix_len[s] - 1 of each
@@ -198,8 +213,9 @@ int losa_build_page_meta(const losa_shape *shape, const void *k_cache, const int
  * max, gist.science pt summary, "3. Metodologia", step 3).
  */
 int losa_update_page_meta(const losa_shape *shape, const void *k_cache, const int32_t *kv_off,
-                          const int32_t *prefix_len, const int32_t *first_token,
-                          int32_t max_new_tokens, void *page_meta, void *stream);
+                          const int32_t *prefix_len, const int32_t *page_table,
+                          const int32_t *first_token, int32_t max_new_tokens, void *page_meta,
+                          void *stream);
 
 /*
  * Forced dense first step of a block (agifrontier tutorial, limitations
@@ -210,9 +226,10 @@ int losa_update_page_meta(const losa_shape *shape, const void *k_cache, const in
  */
 int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *k_blk,
                           const void *v_blk, const void *k_cache, const void *v_cache,
-                          const int32_t *kv_off, const int32_t *prefix_len, float *op_cache,
-                          float *lp_cache, void *out, const losa_debug *debug, void *workspace,
-                          size_t workspace_bytes, void *stream);
+                          const int32_t *kv_off, const int32_t *prefix_len,
+                          const int32_t *page_table, float *op_cache, float *lp_cache, void *out,
+                          const losa_debug *debug, void *workspace, size_t workspace_bytes,
+                          void *stream);
 
 /*
  * One LoSA step (steps 1-8 above).  q_prev is the previous step's q_t.  Only
@@ -223,9 +240,9 @@ int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *
  */
 int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, const void *k_blk,
               const void *v_blk, const void *k_cache, const void *v_cache, const void *page_meta,
-              const int32_t *kv_off, const int32_t *prefix_len, float *op_cache, float *lp_cache,
-              void *out, const losa_debug *debug, void *workspace, size_t workspace_bytes,
-              void *stream);
+              const int32_t *kv_off, const int32_t *prefix_len, const int32_t *page_table,
+              float *op_cache, float *lp_cache, void *out, const losa_debug *debug,
+              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of the static scratch that losa_step_noalloc uses on each GPU. */
 #define LOSA_NOALLOC_SCRATCH_BYTES (32u << 20)
@@ -250,8 +267,8 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
 int losa_step_noalloc(const losa_shape *shape, const void *q_t, const void *q_prev,
                       const void *k_blk, const void *v_blk, const void *k_cache,
                       const void *v_cache, const void *page_meta, const int32_t *kv_off,
-                      const int32_t *prefix_len, float *op_cache, float *lp_cache, void *out,
-                      const losa_debug *debug, void *stream);
+                      const int32_t *prefix_len, const int32_t *page_table, float *op_cache,
+                      float *lp_cache, void *out, const losa_debug *debug, void *stream);
 
 #ifdef __cplusplus
 }

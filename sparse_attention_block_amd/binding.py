@@ -75,18 +75,19 @@ def load(path: str = LIB_PATH):
     lib.losa_workspace_bytes.restype = c_size_t
     lib.losa_union_capacity.argtypes = [S]
     lib.losa_union_capacity.restype = c_int32
-    lib.losa_build_page_meta.argtypes = [S, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.losa_build_page_meta.argtypes = [S, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p]
     lib.losa_build_page_meta.restype = c_int
-    lib.losa_update_page_meta.argtypes = [S, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
-                                          c_void_p, c_void_p]
+    lib.losa_update_page_meta.argtypes = [S, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_int32, c_void_p, c_void_p]
     lib.losa_update_page_meta.restype = c_int
-    lib.losa_dense_first_step.argtypes = [S] + [c_void_p] * 10 + [POINTER(LosaDebug), c_void_p,
+    lib.losa_dense_first_step.argtypes = [S] + [c_void_p] * 11 + [POINTER(LosaDebug), c_void_p,
                                                                    c_size_t, c_void_p]
     lib.losa_dense_first_step.restype = c_int
-    lib.losa_step.argtypes = [S] + [c_void_p] * 12 + [POINTER(LosaDebug), c_void_p, c_size_t,
+    lib.losa_step.argtypes = [S] + [c_void_p] * 13 + [POINTER(LosaDebug), c_void_p, c_size_t,
                                                        c_void_p]
     lib.losa_step.restype = c_int
-    lib.losa_step_noalloc.argtypes = [S] + [c_void_p] * 12 + [POINTER(LosaDebug), c_void_p]
+    lib.losa_step_noalloc.argtypes = [S] + [c_void_p] * 13 + [POINTER(LosaDebug), c_void_p]
     lib.losa_step_noalloc.restype = c_int
     _lib = lib
     return lib
@@ -164,18 +165,27 @@ def _raise(status: int, what: str):
 def _sizes(shape: LosaShape):
     S, B, Hq, Hk, d = shape.n_seq, shape.block, shape.n_qhead, shape.n_kvhead, shape.head_dim
     return dict(q=S * B * Hq * d, blk=S * B * Hk * d, cache=Hk * shape.kv_tokens * d,
-                op=S * Hq * B * d, lp=S * Hq * B)
+                op=S * Hq * B * d, lp=S * Hq * B,
+                pt=S * max(1, (shape.max_prefix_len + PAGE - 1) // PAGE))
+
+
+def _layout(shape, kv_off, prefix_len, page_table):
+    """kv_off (contiguous sequences) and prefix_len, or a page table (kv_off optional)."""
+    n = _sizes(shape)
+    return [_check(kv_off, "kv_off", torch.int32, shape.n_seq, optional=page_table is not None),
+            _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+            _check(page_table, "page_table", torch.int32, n["pt"], optional=True)]
 
 
 # ---------------------------------------------------------------------------
 # entry points
 
-def losa_build_page_meta(shape, k_cache, kv_off, prefix_len, page_meta, stream=None):
+def losa_build_page_meta(shape, k_cache, kv_off, prefix_len, page_meta, stream=None,
+                         page_table=None):
     n = _sizes(shape)
     args = [
         _check(k_cache, "k_cache", _torch_dtype(shape), n["cache"]),
-        _check(kv_off, "kv_off", torch.int32, shape.n_seq),
-        _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+        *_layout(shape, kv_off, prefix_len, page_table),
         _check(page_meta, "page_meta", torch.uint8, page_meta_bytes(shape)),
     ]
     _raise(load().losa_build_page_meta(ctypes.byref(shape), *args, _stream(stream)),
@@ -183,12 +193,11 @@ def losa_build_page_meta(shape, k_cache, kv_off, prefix_len, page_meta, stream=N
 
 
 def losa_update_page_meta(shape, k_cache, kv_off, prefix_len, first_token, max_new_tokens,
-                          page_meta, stream=None):
+                          page_meta, stream=None, page_table=None):
     n = _sizes(shape)
     args = [
         _check(k_cache, "k_cache", _torch_dtype(shape), n["cache"]),
-        _check(kv_off, "kv_off", torch.int32, shape.n_seq),
-        _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+        *_layout(shape, kv_off, prefix_len, page_table),
         _check(first_token, "first_token", torch.int32, shape.n_seq),
     ]
     meta = _check(page_meta, "page_meta", torch.uint8, page_meta_bytes(shape))
@@ -197,15 +206,15 @@ def losa_update_page_meta(shape, k_cache, kv_off, prefix_len, first_token, max_n
 
 
 def losa_dense_first_step(shape, q_t, k_blk, v_blk, k_cache, v_cache, kv_off, prefix_len,
-                          op_cache, lp_cache, out, workspace, debug=None, stream=None):
+                          op_cache, lp_cache, out, workspace, debug=None, stream=None,
+                          page_table=None):
     n, dt = _sizes(shape), _torch_dtype(shape)
     ws_need = workspace_bytes(shape)
     args = [
         _check(q_t, "q_t", dt, n["q"]), _check(k_blk, "k_blk", dt, n["blk"]),
         _check(v_blk, "v_blk", dt, n["blk"]), _check(k_cache, "k_cache", dt, n["cache"]),
         _check(v_cache, "v_cache", dt, n["cache"]),
-        _check(kv_off, "kv_off", torch.int32, shape.n_seq),
-        _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+        *_layout(shape, kv_off, prefix_len, page_table),
         _check(op_cache, "op_cache", torch.float32, n["op"]),
         _check(lp_cache, "lp_cache", torch.float32, n["lp"]),
         _check(out, "out", dt, n["q"]),
@@ -259,7 +268,8 @@ class Debug:
 
 
 def losa_step(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off, prefix_len,
-              op_cache, lp_cache, out, workspace, debug: Optional[Debug] = None, stream=None):
+              op_cache, lp_cache, out, workspace, debug: Optional[Debug] = None, stream=None,
+              page_table=None):
     n, dt = _sizes(shape), _torch_dtype(shape)
     ws_need = workspace_bytes(shape)
     args = [
@@ -267,8 +277,7 @@ def losa_step(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_
         _check(k_blk, "k_blk", dt, n["blk"]), _check(v_blk, "v_blk", dt, n["blk"]),
         _check(k_cache, "k_cache", dt, n["cache"]), _check(v_cache, "v_cache", dt, n["cache"]),
         _check(page_meta, "page_meta", torch.uint8, page_meta_bytes(shape)),
-        _check(kv_off, "kv_off", torch.int32, shape.n_seq),
-        _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+        *_layout(shape, kv_off, prefix_len, page_table),
         _check(op_cache, "op_cache", torch.float32, n["op"]),
         _check(lp_cache, "lp_cache", torch.float32, n["lp"]),
         _check(out, "out", dt, n["q"]),
@@ -281,7 +290,7 @@ def losa_step(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_
 
 def losa_step_noalloc(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off,
                       prefix_len, op_cache, lp_cache, out, debug: Optional[Debug] = None,
-                      stream=None):
+                      stream=None, page_table=None):
     """losa_step on the library's static per-GPU scratch (no workspace argument)."""
     n, dt = _sizes(shape), _torch_dtype(shape)
     args = [
@@ -289,8 +298,7 @@ def losa_step_noalloc(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_m
         _check(k_blk, "k_blk", dt, n["blk"]), _check(v_blk, "v_blk", dt, n["blk"]),
         _check(k_cache, "k_cache", dt, n["cache"]), _check(v_cache, "v_cache", dt, n["cache"]),
         _check(page_meta, "page_meta", torch.uint8, page_meta_bytes(shape)),
-        _check(kv_off, "kv_off", torch.int32, shape.n_seq),
-        _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+        *_layout(shape, kv_off, prefix_len, page_table),
         _check(op_cache, "op_cache", torch.float32, n["op"]),
         _check(lp_cache, "lp_cache", torch.float32, n["lp"]),
         _check(out, "out", dt, n["q"]),
@@ -329,21 +337,21 @@ class PreparedCall:
 
 
 def prepare_dense_first_step(shape, q_t, k_blk, v_blk, k_cache, v_cache, kv_off, prefix_len,
-                             op_cache, lp_cache, out, workspace, stream=None) -> PreparedCall:
+                             op_cache, lp_cache, out, workspace, stream=None,
+                             page_table=None) -> PreparedCall:
     n, dt = _sizes(shape), _torch_dtype(shape)
     head = [ctypes.byref(shape),
             _check(q_t, "q_t", dt, n["q"]), _check(k_blk, "k_blk", dt, n["blk"]),
             _check(v_blk, "v_blk", dt, n["blk"]), _check(k_cache, "k_cache", dt, n["cache"]),
             _check(v_cache, "v_cache", dt, n["cache"]),
-            _check(kv_off, "kv_off", torch.int32, shape.n_seq),
-            _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+            *_layout(shape, kv_off, prefix_len, page_table),
             _check(op_cache, "op_cache", torch.float32, n["op"]),
             _check(lp_cache, "lp_cache", torch.float32, n["lp"]),
             _check(out, "out", dt, n["q"])]
     tail = [_check(workspace, "workspace", torch.uint8, workspace_bytes(shape)),
             c_size_t(workspace.numel()), _stream(stream)]
-    keep = (q_t, k_blk, v_blk, k_cache, v_cache, kv_off, prefix_len, op_cache, lp_cache, out,
-            workspace)
+    keep = (q_t, k_blk, v_blk, k_cache, v_cache, kv_off, prefix_len, page_table, op_cache,
+            lp_cache, out, workspace)
     call = PreparedCall(load().losa_dense_first_step, head, LosaDebug(), tail,
                         "losa_dense_first_step")
     call._keep = keep
@@ -351,22 +359,22 @@ def prepare_dense_first_step(shape, q_t, k_blk, v_blk, k_cache, v_cache, kv_off,
 
 
 def prepare_step(shape, q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off,
-                 prefix_len, op_cache, lp_cache, out, workspace, stream=None) -> PreparedCall:
+                 prefix_len, op_cache, lp_cache, out, workspace, stream=None,
+                 page_table=None) -> PreparedCall:
     n, dt = _sizes(shape), _torch_dtype(shape)
     head = [ctypes.byref(shape),
             _check(q_t, "q_t", dt, n["q"]), _check(q_prev, "q_prev", dt, n["q"]),
             _check(k_blk, "k_blk", dt, n["blk"]), _check(v_blk, "v_blk", dt, n["blk"]),
             _check(k_cache, "k_cache", dt, n["cache"]), _check(v_cache, "v_cache", dt, n["cache"]),
             _check(page_meta, "page_meta", torch.uint8, page_meta_bytes(shape)),
-            _check(kv_off, "kv_off", torch.int32, shape.n_seq),
-            _check(prefix_len, "prefix_len", torch.int32, shape.n_seq),
+            *_layout(shape, kv_off, prefix_len, page_table),
             _check(op_cache, "op_cache", torch.float32, n["op"]),
             _check(lp_cache, "lp_cache", torch.float32, n["lp"]),
             _check(out, "out", dt, n["q"])]
     tail = [_check(workspace, "workspace", torch.uint8, workspace_bytes(shape)),
             c_size_t(workspace.numel()), _stream(stream)]
-    keep = (q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off, prefix_len, op_cache,
-            lp_cache, out, workspace)
+    keep = (q_t, q_prev, k_blk, v_blk, k_cache, v_cache, page_meta, kv_off, prefix_len, page_table,
+            op_cache, lp_cache, out, workspace)
     call = PreparedCall(load().losa_step, head, LosaDebug(), tail, "losa_step")
     call._keep = keep
     return call

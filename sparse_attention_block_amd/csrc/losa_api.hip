@@ -96,6 +96,7 @@ Dims make_dims(const losa_shape *sh) {
     const float scale = sh->softmax_scale > 0.0f ? sh->softmax_scale
                                                  : 1.0f / sqrtf(static_cast<float>(D.d));
     D.scale_log2 = scale * 1.44269504088896340736f;
+    D.page_table = nullptr;
     return D;
 }
 
@@ -148,18 +149,26 @@ hipError_t mark(void **events, int i, hipStream_t s) {
     return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
 }
 
+// The prefix cache's layout arguments: kv_off (contiguous sequences) or a page
+// table (then kv_off may be null); int32 arrays, 4-byte aligned.
+bool layout_ok(const int32_t *kv_off, const int32_t *prefix_len, const int32_t *page_table) {
+    if (!prefix_len || !aligned(prefix_len, 4)) return false;
+    if (page_table) return aligned(page_table, 4) && (!kv_off || aligned(kv_off, 4));
+    return kv_off && aligned(kv_off, 4);
+}
+
 // Checks of losa_step's arguments (host only); fills the dims and the debug copy.
 int check_step_args(const losa_shape *shape, const void *const (&p16)[10], const int32_t *kv_off,
-                    const int32_t *prefix_len, const float *lp_cache, const losa_debug *debug,
-                    Dims *D, losa_debug *dbg) {
+                    const int32_t *prefix_len, const int32_t *page_table, const float *lp_cache,
+                    const losa_debug *debug, Dims *D, losa_debug *dbg) {
     int st = check_shape(shape);
     if (st != LOSA_OK) return st;
     for (const void *p : p16)
         if (!p || !aligned(p, 16)) return LOSA_ERR_INVALID_ARG;
-    if (!kv_off || !prefix_len || !lp_cache || !aligned(kv_off, 4) || !aligned(prefix_len, 4) ||
-        !aligned(lp_cache, 4))
+    if (!layout_ok(kv_off, prefix_len, page_table) || !lp_cache || !aligned(lp_cache, 4))
         return LOSA_ERR_INVALID_ARG;
     *D = make_dims(shape);
+    D->page_table = page_table;
     memset(dbg, 0, sizeof *dbg);
     if (debug) {
         *dbg = *debug;
@@ -273,47 +282,51 @@ int32_t losa_union_capacity(const losa_shape *shape) {
 }
 
 int losa_build_page_meta(const losa_shape *shape, const void *k_cache, const int32_t *kv_off,
-                         const int32_t *prefix_len, void *page_meta, void *stream) {
+                         const int32_t *prefix_len, const int32_t *page_table, void *page_meta,
+                         void *stream) {
     int st = check_shape(shape);
     if (st != LOSA_OK) return st;
-    if (!k_cache || !kv_off || !prefix_len || !page_meta) return LOSA_ERR_INVALID_ARG;
-    if (!aligned(k_cache, 16) || !aligned(page_meta, 16) || !aligned(kv_off, 4) ||
-        !aligned(prefix_len, 4))
+    if (!k_cache || !page_meta || !layout_ok(kv_off, prefix_len, page_table))
         return LOSA_ERR_INVALID_ARG;
-    const Dims D = make_dims(shape);
+    if (!aligned(k_cache, 16) || !aligned(page_meta, 16)) return LOSA_ERR_INVALID_ARG;
+    Dims D = make_dims(shape);
+    D.page_table = page_table;
     return hip_status(launch_page_meta(D, k_cache, kv_off, prefix_len, nullptr, 0, page_meta,
                                        static_cast<hipStream_t>(stream)));
 }
 
 int losa_update_page_meta(const losa_shape *shape, const void *k_cache, const int32_t *kv_off,
-                          const int32_t *prefix_len, const int32_t *first_token,
-                          int32_t max_new_tokens, void *page_meta, void *stream) {
+                          const int32_t *prefix_len, const int32_t *page_table,
+                          const int32_t *first_token, int32_t max_new_tokens, void *page_meta,
+                          void *stream) {
     int st = check_shape(shape);
     if (st != LOSA_OK) return st;
-    if (!k_cache || !kv_off || !prefix_len || !first_token || !page_meta) return LOSA_ERR_INVALID_ARG;
-    if (!aligned(k_cache, 16) || !aligned(page_meta, 16) || !aligned(kv_off, 4) ||
-        !aligned(prefix_len, 4) || !aligned(first_token, 4))
+    if (!k_cache || !first_token || !page_meta || !layout_ok(kv_off, prefix_len, page_table))
+        return LOSA_ERR_INVALID_ARG;
+    if (!aligned(k_cache, 16) || !aligned(page_meta, 16) || !aligned(first_token, 4))
         return LOSA_ERR_INVALID_ARG;
     if (max_new_tokens < 0 || max_new_tokens > shape->max_prefix_len) return LOSA_ERR_INVALID_ARG;
-    const Dims D = make_dims(shape);
+    Dims D = make_dims(shape);
+    D.page_table = page_table;
     return hip_status(launch_page_meta(D, k_cache, kv_off, prefix_len, first_token, max_new_tokens,
                                        page_meta, static_cast<hipStream_t>(stream)));
 }
 
 int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *k_blk,
                           const void *v_blk, const void *k_cache, const void *v_cache,
-                          const int32_t *kv_off, const int32_t *prefix_len, float *op_cache,
-                          float *lp_cache, void *out, const losa_debug *debug, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+                          const int32_t *kv_off, const int32_t *prefix_len,
+                          const int32_t *page_table, float *op_cache, float *lp_cache, void *out,
+                          const losa_debug *debug, void *workspace, size_t workspace_bytes,
+                          void *stream) {
     int st = check_shape(shape);
     if (st != LOSA_OK) return st;
     const void *p16[] = {q_t, k_blk, v_blk, k_cache, v_cache, op_cache, out, workspace};
     for (const void *p : p16)
         if (!p || !aligned(p, 16)) return LOSA_ERR_INVALID_ARG;
-    if (!kv_off || !prefix_len || !lp_cache || !aligned(kv_off, 4) || !aligned(prefix_len, 4) ||
-        !aligned(lp_cache, 4))
+    if (!layout_ok(kv_off, prefix_len, page_table) || !lp_cache || !aligned(lp_cache, 4))
         return LOSA_ERR_INVALID_ARG;
     Dims D = make_dims(shape);
+    D.page_table = page_table;
     D.flags = 0;  // the dense first step has no reading variants
     Work W;
     const size_t need = carve(D, static_cast<char *>(workspace), &W);
@@ -339,14 +352,14 @@ int losa_dense_first_step(const losa_shape *shape, const void *q_t, const void *
 
 int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, const void *k_blk,
               const void *v_blk, const void *k_cache, const void *v_cache, const void *page_meta,
-              const int32_t *kv_off, const int32_t *prefix_len, float *op_cache, float *lp_cache,
-              void *out, const losa_debug *debug, void *workspace, size_t workspace_bytes,
-              void *stream) {
+              const int32_t *kv_off, const int32_t *prefix_len, const int32_t *page_table,
+              float *op_cache, float *lp_cache, void *out, const losa_debug *debug,
+              void *workspace, size_t workspace_bytes, void *stream) {
     const void *const p16[10] = {q_t,      q_prev,   k_blk, v_blk, k_cache,
                                  v_cache,  page_meta, op_cache, out, workspace};
     Dims D;
     losa_debug dbg;
-    int st = check_step_args(shape, p16, kv_off, prefix_len, lp_cache, debug, &D, &dbg);
+    int st = check_step_args(shape, p16, kv_off, prefix_len, page_table, lp_cache, debug, &D, &dbg);
     if (st != LOSA_OK) return st;
     Work W;
     const size_t need = carve(D, static_cast<char *>(workspace), &W);
@@ -359,14 +372,14 @@ int losa_step(const losa_shape *shape, const void *q_t, const void *q_prev, cons
 int losa_step_noalloc(const losa_shape *shape, const void *q_t, const void *q_prev,
                       const void *k_blk, const void *v_blk, const void *k_cache,
                       const void *v_cache, const void *page_meta, const int32_t *kv_off,
-                      const int32_t *prefix_len, float *op_cache, float *lp_cache, void *out,
-                      const losa_debug *debug, void *stream) {
+                      const int32_t *prefix_len, const int32_t *page_table, float *op_cache,
+                      float *lp_cache, void *out, const losa_debug *debug, void *stream) {
     // (the scratch pointer stands in for the workspace in the pointer checks)
     const void *const p16[10] = {q_t,     q_prev,    k_blk,    v_blk, k_cache,
                                  v_cache, page_meta, op_cache, out,   q_t};
     Dims D;
     losa_debug dbg;
-    int st = check_step_args(shape, p16, kv_off, prefix_len, lp_cache, debug, &D, &dbg);
+    int st = check_step_args(shape, p16, kv_off, prefix_len, page_table, lp_cache, debug, &D, &dbg);
     if (st != LOSA_OK) return st;
     if (carve(D, nullptr, nullptr, true) > LOSA_NOALLOC_SCRATCH_BYTES) return LOSA_ERR_SCRATCH;
     void *ws = nullptr;

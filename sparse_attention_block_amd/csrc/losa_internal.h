@@ -50,6 +50,8 @@ struct Dims {
     int sparse_chunk, dense_chunk;    // pages per prefix workgroup
     int n_chunks_sparse, n_chunks_dense;
     float scale_log2;                 // softmax scale * log2(e)
+    const int32_t *page_table;        // [S][max(max_pages,1)] physical page of each page of a
+                                      // sequence, or null: pages contiguous from kv_off[s]
 };
 
 // Device views into the workspace (all carved from one caller buffer).
@@ -175,28 +177,75 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Sequence geometry with out-of-range values clamped into the cache.
 struct SeqGeom {
-    int64_t off;   // first cache token
-    int len;       // prefix tokens
-    int pages;     // ceil(len / 16)
-    int64_t gp0;   // first global page
+    int64_t off;        // first cache token (contiguous layout)
+    int len;            // prefix tokens
+    int pages;          // ceil(len / 16)
+    int64_t gp0;        // first global page (contiguous layout)
+    const int32_t *pt;  // the sequence's row of the page table, or null
+    int64_t n_phys;     // pages in the cache (page-table entries are clamped below it)
 };
+
+// The geometry with the layout fixed at compile time (the hot kernels are
+// built for both layouts, so the contiguous layout's code is free of the
+// page table), and the runtime choice for the others.
+template <bool PAGED>
+__device__ __forceinline__ SeqGeom seq_geom_t(const Dims &D, const int32_t *kv_off,
+                                              const int32_t *prefix_len, int s) {
+    SeqGeom g;
+    g.n_phys = D.T / kPage;
+    if constexpr (PAGED) {
+        int len = prefix_len[s];
+        if (len < 0) len = 0;
+        if (len > D.max_pages * kPage) len = D.max_pages * kPage;
+        g.off = 0;
+        g.gp0 = 0;
+        g.pt = D.page_table + (size_t)s * (D.max_pages > 0 ? D.max_pages : 1);
+        g.len = len;
+    } else {
+        int64_t off = kv_off[s];
+        int len = prefix_len[s];
+        if (off < 0) off = 0;
+        off = off / kPage * kPage;
+        if (off > D.T) off = D.T;
+        if (len < 0) len = 0;
+        if (len > D.max_pages * kPage) len = D.max_pages * kPage;
+        if (off + len > D.T) len = static_cast<int>(D.T - off);
+        g.off = off;
+        g.gp0 = off / kPage;
+        g.pt = nullptr;
+        g.len = len;
+    }
+    g.pages = (g.len + kPage - 1) / kPage;
+    return g;
+}
 
 __device__ __forceinline__ SeqGeom seq_geom(const Dims &D, const int32_t *kv_off,
                                             const int32_t *prefix_len, int s) {
-    SeqGeom g;
-    int64_t off = kv_off[s];
-    int len = prefix_len[s];
-    if (off < 0) off = 0;
-    off = off / kPage * kPage;
-    if (off > D.T) off = D.T;
-    if (len < 0) len = 0;
-    if (len > D.max_pages * kPage) len = D.max_pages * kPage;
-    if (off + len > D.T) len = static_cast<int>(D.T - off);
-    g.off = off;
-    g.len = len;
-    g.pages = (len + kPage - 1) / kPage;
-    g.gp0 = off / kPage;
-    return g;
+    return D.page_table ? seq_geom_t<true>(D, kv_off, prefix_len, s)
+                        : seq_geom_t<false>(D, kv_off, prefix_len, s);
+}
+
+// Global (physical) page of the sequence's page p: the page-table entry, with
+// p clamped into the sequence's pages and the entry into the cache, or the
+// contiguous layout's first page + p.  Token t of a page is cache row
+// 16 * phys_page + t of every KV head.
+__device__ __forceinline__ int64_t phys_page(const SeqGeom &g, int p) {
+    if (g.pt) {
+        const int64_t e = g.pt[min(max(p, 0), max(g.pages - 1, 0))];
+        return e < 0 ? 0 : (e >= g.n_phys ? g.n_phys - 1 : e);
+    }
+    return g.gp0 + p;
+}
+// The same with the layout fixed at compile time (the hot kernels are built
+// for both, so the contiguous layout's code carries no page-table branch).
+template <bool PAGED>
+__device__ __forceinline__ int64_t phys_page_t(const SeqGeom &g, int p) {
+    if constexpr (PAGED) {
+        const int64_t e = g.pt[min(max(p, 0), max(g.pages - 1, 0))];
+        return e < 0 ? 0 : (e >= g.n_phys ? g.n_phys - 1 : e);
+    } else {
+        return g.gp0 + p;
+    }
 }
 
 }  // namespace losa

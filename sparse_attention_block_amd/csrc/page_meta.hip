@@ -55,11 +55,14 @@ __global__ __launch_bounds__(256) void k_page_meta(Dims D, const T *__restrict__
     // the page's 16 rows of this column chunk (clamped rows: tokens past the
     // prefix, and pages past the sequence, reread its last valid token)
     const int last = max(sg.len - 1, 0);
+    // (a page past the sequence rereads its last token, which lies in its last page)
+    const int plc = min(pl, max(sg.pages - 1, 0));
+    const int64_t prow = phys_page(sg, plc) * kPage;
     uint4 v[kPage];
 #pragma unroll
     for (int t = 0; t < kPage; ++t) {
-        const int64_t row = min(sg.off + min(pl * kPage + t, last), D.T - 1);  // inside the cache
-        v[t] = *reinterpret_cast<const uint4 *>(kc + ((size_t)g * D.T + row) * DIM + cc * EPC);
+        const int64_t row = min(prow + min(pl * kPage + t, last) - plc * kPage, D.T - 1);  // inside the cache
+        v[t] = *reinterpret_cast<const uint4 *>(kc + ((size_t)g * D.T + max(row, int64_t{0})) * DIM + cc * EPC);
     }
     __builtin_amdgcn_sched_barrier(0);
     float mn[EPC], mx[EPC];
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void k_page_meta(Dims D, const T *__restrict__
 #pragma unroll
     for (int o = 1; o < CPR; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
     if (!live) return;
-    const int64_t gp = sg.gp0 + pl;
+    const int64_t gp = phys_page(sg, pl);
     const int64_t tile = gp / kTile;
     const int lane = static_cast<int>(gp % kTile);
 #pragma unroll

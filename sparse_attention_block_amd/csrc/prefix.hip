@@ -425,7 +425,7 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
     }
 
     auto page_of = [&](int it) { return __builtin_amdgcn_readlane(my_page, it); };
-    auto base_of = [&](int p) { return ((size_t)g * D.T + sg.off + (size_t)p * kPage) * DIM; };
+    auto base_of = [&](int p) { return ((size_t)g * D.T + (size_t)phys_page(sg, p) * kPage) * DIM; };
     if (pg < n_pg && pg < n_here) {
         PageRegs<DIM> cur, nxt;
         {
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
 // wave 0 the (m, l).  The union slice, the arithmetic (log2-unit scores,
 // weights rounded to bf16, row sums of the rounded weights) and the partial
 // layout are those of k_prefix_bf16.
-template <int DIM, int RTW, bool MASK>
+template <int DIM, int RTW, bool MASK, bool PAGED>
 __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
                                                              const uint16_t *__restrict__ kc,
                                                              const uint16_t *__restrict__ vc,
@@ -588,7 +588,7 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
-    const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
+    const SeqGeom sg = seq_geom_t<PAGED>(D, kv_off, prefix_len, s);
     const int cp = D.sparse_chunk, first = chunk * cp;  // cp == NP
     const int rows = D.R, nch = D.n_chunks_sparse;
     const int n_rt = (rows + 15) / 16;
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
 #pragma unroll
     for (int n = 0; n < NP; ++n) {
         const int p = __builtin_amdgcn_readlane(my_page, min(n, n_here - 1));
-        base[n] = ((size_t)g * D.T + sg.off + (size_t)p * kPage) * DIM;
+        base[n] = ((size_t)g * D.T + (size_t)phys_page_t<PAGED>(sg, p) * kPage) * DIM;
         valid[n] = n < n_here ? min(kPage, sg.len - p * kPage) : 0;
     }
     const size_t kbase = base[min(w, n_here - 1)];
@@ -831,7 +831,7 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int DIM, int RTW, int NW>
+template <int DIM, int RTW, int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uint16_t *__restrict__ q_t,
                                                                const uint16_t *__restrict__ kc,
                                                                const uint16_t *__restrict__ vc,
@@ -856,7 +856,7 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
-    const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
+    const SeqGeom sg = seq_geom_t<PAGED>(D, kv_off, prefix_len, s);
     const int first = chunk * D.dense_chunk;
     const int n_here = min(D.dense_chunk, sg.pages - first);
     if (n_here <= 0) return;
@@ -888,13 +888,20 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     for (int h = 0; h < LPT; ++h) {
         const int L = (h * NW + w) * 64 + lane, cq = L % NCK;
         const int t = cq / CPT, c = (cq % CPT) ^ (t & (CPT - 1));
-        src_h[h] = (L < NCK ? kc : vc) + ((size_t)g * D.T + sg.off + (size_t)first * kPage) * DIM +
-                   t * DIM + c * 8;
+        src_h[h] = (L < NCK ? kc : vc) + (size_t)g * D.T * DIM + t * DIM + c * 8;
     }
+    // the cache row of each page of the chunk: lane i holds page first + i's
+    // (clamped to the chunk's last page; a page table is read once here)
+    const int64_t prow_lane = phys_page_t<PAGED>(sg, first + min(lane, n_here - 1)) * kPage;
     // (the builtin's arguments are passed as plain void pointers: with typed or
     // const ones the host pass silently drops the kernel's launch stub)
     auto issue = [&](int p, int slot) {  // page p of the chunk (clamped) into a slot
-        const size_t off = (size_t)min(p, n_here - 1) * kPage * DIM;
+        const int pc = min(p, n_here - 1);
+        const int64_t prow = static_cast<int64_t>(
+            (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(
+                 static_cast<int>(prow_lane >> 32), pc))) << 32) |
+            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(prow_lane), pc)));
+        const size_t off = (size_t)prow * DIM;
 #pragma unroll
         for (int h = 0; h < LPT; ++h)
             __builtin_amdgcn_global_load_lds(static_cast<void *>(const_cast<uint16_t *>(src_h[h] + off)),
@@ -1066,7 +1073,7 @@ __global__ __launch_bounds__(256) void k_prefix_f32(Dims D, const float *__restr
             const int pos = first + it;
             const int p = dense ? pos : s_pg[it];
             const int valid = min(kPage, sg.len - p * kPage);
-            const size_t base = ((size_t)g * D.T + sg.off + (size_t)p * kPage) * DIM;
+            const size_t base = ((size_t)g * D.T + (size_t)phys_page(sg, p) * kPage) * DIM;
             __syncthreads();
             for (int idx = tid; idx < 16 * DIM; idx += 256) {
                 const int t = idx / DIM, x = idx % DIM;
@@ -1119,6 +1126,7 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
                          hipStream_t st) {
     const int nch = dense ? D.n_chunks_dense : D.n_chunks_sparse;
     dim3 grid(nch * D.S * D.Hk);
+    const bool paged = D.page_table != nullptr;
     if (D.bf16) {
         auto *k = static_cast<const uint16_t *>(k_cache);
         auto *v = static_cast<const uint16_t *>(v_cache);
@@ -1137,8 +1145,16 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
         else LAUNCH_P(DIMV, 4, DN, false);                   \
     } while (0)
 #define LAUNCH_D(DIMV, RTWV, NWV)                                                                 \
-    hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV, NWV>), grid, dim3(64 * NWV), 0, st, D,    \
-                       static_cast<const uint16_t *>(q_t), k, v, kv_off, prefix_len, W)
+    do {                                                                                          \
+        if (paged)                                                                                \
+            hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV, NWV, true>), grid, dim3(64 * NWV),   \
+                               0, st, D, static_cast<const uint16_t *>(q_t), k, v, kv_off,        \
+                               prefix_len, W);                                                    \
+        else                                                                                      \
+            hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV, NWV, false>), grid, dim3(64 * NWV),  \
+                               0, st, D, static_cast<const uint16_t *>(q_t), k, v, kv_off,        \
+                               prefix_len, W);                                                    \
+    } while (0)
         // dense pass: wave w of NW takes row tiles w, w + NW, ...; head_dim 128
         // uses eight waves (one page of K and V is one 16-byte piece per thread)
         // once there are more than four row tiles
@@ -1151,8 +1167,14 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
                 // chunks of 4 pages, at most 32 rows: waves split the dimensions
                 const bool mk = D.flags & LOSA_FLAG_ROW_MASK;
 #define LAUNCH_Q(RTWV, MK)                                                                          \
-    hipLaunchKernelGGL((k_prefix_quarter_bf16<128, RTWV, MK>), grid, dim3(256), 0, st, D, k, v,     \
-                       kv_off, prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap)
+    do {                                                                                            \
+        if (paged)                                                                                  \
+            hipLaunchKernelGGL((k_prefix_quarter_bf16<128, RTWV, MK, true>), grid, dim3(256), 0, st, \
+                               D, k, v, kv_off, prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap);      \
+        else                                                                                        \
+            hipLaunchKernelGGL((k_prefix_quarter_bf16<128, RTWV, MK, false>), grid, dim3(256), 0,   \
+                               st, D, k, v, kv_off, prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap);  \
+    } while (0)
                 if (n_rt == 1) {
                     if (mk) LAUNCH_Q(1, true);
                     else LAUNCH_Q(1, false);

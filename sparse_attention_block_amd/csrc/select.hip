@@ -206,10 +206,12 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
         const int l16 = lane & 15, lg = lane >> 4;
         float amax[4];
         int pl[4];
+        int64_t gpl[4];
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             pl[cb] = bx * kTile + cb * 16 + l16;
-            amax[cb] = meta_amax(meta, D, g, sg.gp0 + pl[cb]);
+            gpl[cb] = phys_page(sg, pl[cb]);
+            amax[cb] = meta_amax(meta, D, g, gpl[cb]);
         }
         const uint32_t *q16 = W.qsel16 + (size_t)sgi * D.Rs16 * DIM;
         constexpr int KS = DIM / 16;
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) bop[kk][cb] = *meta_chunk(meta, D, g, sg.gp0 + pl[cb], 4 * kk + lg, NCH);
+            for (int cb = 0; cb < 4; ++cb) bop[kk][cb] = *meta_chunk(meta, D, g, gpl[cb], 4 * kk + lg, NCH);
         __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
         const int n_rt = D.Rs16 / 16;
         for (int rt = 0; rt < n_rt; ++rt) {
@@ -251,8 +253,9 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
         // fp32 storage: lane = page, any summation order (the interval absorbs it)
         const int p = bx * kTile + lane;
         const bool valid = p < sg.pages;
-        const float am = meta_amax(meta, D, g, sg.gp0 + p);
-        const uint4 *mt = meta_chunk(meta, D, g, sg.gp0 + p, 0, NCH);  // chunk c at mt[c * kTile]
+        const int64_t gp = phys_page(sg, p);
+        const float am = meta_amax(meta, D, g, gp);
+        const uint4 *mt = meta_chunk(meta, D, g, gp, 0, NCH);  // chunk c at mt[c * kTile]
         const float *q32 = W.qsel32 + (size_t)sgi * R1 * DIM * 2;
         for (int r = 0; r < R; ++r) {
             float u = 0.0f;
@@ -295,7 +298,7 @@ constexpr int kPrepPad = 4;  // words of padding per LDS row (bank spread)
 #endif
 constexpr int kScoreTilesPerGroup = LOSA_SCORE_TPW;  // 64-page tiles per scoring workgroup
 
-template <int DIM, bool SHARED, int TPW>
+template <int DIM, bool SHARED, int TPW, bool PAGED>
 __global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t *__restrict__ q_t,
                                                           const uint16_t *__restrict__ q_prev,
                                                           const uint4 *__restrict__ meta,
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t
     // 2. the metadata of the wave's 16 pages: chunk 4*kk + lg of page
     //    16*(w%4) + l16 of the wave's page group (clamped into the metadata
     //    where the sequence has no such page, so that no load sits in a branch)
-    const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
+    const SeqGeom sg = seq_geom_t<PAGED>(D, kv_off, prefix_len, s);
     const int n_t = (sg.pages + kTile - 1) / kTile;       // page groups of the sequence
     const bool wg_ok = D.k < sg.pages && TPW * bx < n_t;  // uniform over the workgroup
     const bool wave_ok = D.k < sg.pages && wt < n_t;      // uniform over the wave
@@ -368,9 +371,10 @@ __global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t
     const int l16 = lane & 15, lg = lane >> 4;
     const int pl = wt * kTile + 16 * (w % 4) + l16;  // the lane's page in the sequence
     uint4 bop[KS];
+    const int64_t gpl = phys_page_t<PAGED>(sg, pl);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) bop[kk] = *meta_chunk(meta, D, g, sg.gp0 + pl, 4 * kk + lg, NCH);
-    const float amax = meta_amax(meta, D, g, sg.gp0 + pl);
+    for (int kk = 0; kk < KS; ++kk) bop[kk] = *meta_chunk(meta, D, g, gpl, 4 * kk + lg, NCH);
+    const float amax = meta_amax(meta, D, g, gpl);
     __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
     if constexpr (SHARED) {
 #pragma unroll
@@ -689,7 +693,7 @@ __device__ __forceinline__ float exact_bound(const uint4 *meta, const Dims &D, i
 // MAXB: the block-size bound of the in-block attention workgroups (16, 32 or
 // 64), a template parameter so that the larger blocks' registers do not lower
 // the occupancy of launches with small blocks.
-template <int DIM, bool BF, int MAXB>
+template <int DIM, bool BF, int MAXB, bool PAGED>
 __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__ meta,
                                                const int32_t *__restrict__ kv_off,
                                                const int32_t *__restrict__ prefix_len, Work W,
@@ -720,7 +724,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
     const int r = blockIdx.x / ng;
     const int s = sgi / D.Hk, g = sgi % D.Hk;
     const int lane = threadIdx.x;
-    const SeqGeom sg = seq_geom(D, kv_off, prefix_len, s);
+    const SeqGeom sg = seq_geom_t<PAGED>(D, kv_off, prefix_len, s);
     const int R = D.R, R1 = R > 0 ? R : 1, k = D.k;
     const int h = g * D.G + r / D.A, a = r % D.A;
     const bool all_pages = k >= sg.pages;
@@ -801,9 +805,6 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         const bool short_seq = min(n_t, 64) < k && sg.pages >= 4 * k;  // uniform
         if (short_seq) {
             const float qa = W.qabs[(size_t)sgi * R1 + r];
-            const float *am = reinterpret_cast<const float *>(reinterpret_cast<const char *>(meta) +
-                                                              D.meta_main_bytes) +
-                              (size_t)g * D.n_tiles_total * kTile + sg.gp0;
             float lmax = -__builtin_huge_valf();
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
@@ -812,7 +813,8 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
 #pragma unroll
                     for (int e4 = 0; e4 < 4; ++e4) {
                         const int p = 256 * jj + 4 * lane + e4;
-                        const float e = kBoundRel * qa * am[min(p, sg.pages - 1)] + kBoundAbs;
+                        const float e =
+                            kBoundRel * qa * meta_amax(meta, D, g, phys_page_t<PAGED>(sg, min(p, sg.pages - 1))) + kBoundAbs;
                         const float lo = (hx[e4] - 2.0f * e) - (fabsf(hx[e4]) + 2.0f * e) * (1.0f / 2097152.0f);
                         if (p < sg.pages) lmax = fmaxf(lmax, lo);
                     }
@@ -844,7 +846,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
             uint64_t cand = 0ull;
             if (lane < n) {
                 const int pc = pend[c0 + lane];
-                const float u = exact_bound<DIM, BF>(meta, D, g, sg.gp0 + pc, qw);
+                const float u = exact_bound<DIM, BF>(meta, D, g, phys_page_t<PAGED>(sg, pc), qw);
                 cand = (static_cast<uint64_t>(ord_key(u)) << 32) |
                        static_cast<uint32_t>(~static_cast<uint32_t>(pc));
             }
@@ -985,9 +987,15 @@ hipError_t launch_score_prep(const Dims &D, const void *q_t, const void *q_prev,
     auto *a = static_cast<const uint16_t *>(q_t);
     auto *b = static_cast<const uint16_t *>(q_prev);
     auto *m = static_cast<const uint4 *>(meta);
-#define LAUNCH_P(DIMV, SH)                                                                    \
-    hipLaunchKernelGGL((k_score_prep<DIMV, SH, TPW>), grid, dim3(256 * TPW), lds, st, D, a, b, m, \
-                       kv_off, prefix_len, W, dbg_loc, dbg_act, dbg_ucnt)
+#define LAUNCH_P(DIMV, SH)                                                                       \
+    do {                                                                                         \
+        if (D.page_table)                                                                        \
+            hipLaunchKernelGGL((k_score_prep<DIMV, SH, TPW, true>), grid, dim3(256 * TPW), lds, st, \
+                               D, a, b, m, kv_off, prefix_len, W, dbg_loc, dbg_act, dbg_ucnt);   \
+        else                                                                                     \
+            hipLaunchKernelGGL((k_score_prep<DIMV, SH, TPW, false>), grid, dim3(256 * TPW), lds,   \
+                               st, D, a, b, m, kv_off, prefix_len, W, dbg_loc, dbg_act, dbg_ucnt); \
+    } while (0)
     const bool shared = D.flags & LOSA_FLAG_SHARED_ACTIVE;
     if (D.d == 128) {
         if (shared) LAUNCH_P(128, true);
@@ -1014,8 +1022,16 @@ hipError_t launch_select(const Dims &D, const void *meta, const int32_t *kv_off,
     SelectDbg dbg{dbg_page_sel};
     auto *m = static_cast<const uint4 *>(meta);
 #define LAUNCH_S(DIMV, BFV, MB)                                                                  \
-    hipLaunchKernelGGL((k_select<DIMV, BFV, MB>), grid, dim3(64), lds, st, D, m, kv_off,         \
-                       prefix_len, W, W.qrows, W.qsel32, W.hbound, W.tmax, dbg, blk)
+    do {                                                                                         \
+        if (D.page_table)                                                                        \
+            hipLaunchKernelGGL((k_select<DIMV, BFV, MB, true>), grid, dim3(64), lds, st, D, m,      \
+                               kv_off, prefix_len, W, W.qrows, W.qsel32, W.hbound, W.tmax, dbg,  \
+                               blk);                                                             \
+        else                                                                                     \
+            hipLaunchKernelGGL((k_select<DIMV, BFV, MB, false>), grid, dim3(64), lds, st, D, m,     \
+                               kv_off, prefix_len, W, W.qrows, W.qsel32, W.hbound, W.tmax, dbg,  \
+                               blk);                                                             \
+    } while (0)
 #define PICK_S(DIMV, BFV)                           \
     do {                                            \
         if (maxb == 16) LAUNCH_S(DIMV, BFV, 16);    \

@@ -24,7 +24,7 @@ class LayerState:
     def __init__(self, *, n_seq, block, n_qhead, n_kvhead, head_dim, budget_tokens, n_active,
                  dtype, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_off, prefix_len,
                  max_prefix_len: Optional[int] = None, softmax_scale=0.0, flags=0,
-                 device="cuda"):
+                 device="cuda", page_table=None):
         self.device = device
         kv_off = torch.as_tensor(np.asarray(kv_off, np.int32)).to(device)
         prefix_len_t = torch.as_tensor(np.asarray(prefix_len, np.int32)).to(device)
@@ -38,6 +38,9 @@ class LayerState:
         self.dtype = dtype
         self.k_cache, self.v_cache = k_cache, v_cache
         self.kv_off, self.prefix_len = kv_off, prefix_len_t
+        # paged KV pool: [n_seq][pages of the longest prefix] physical pages (or None)
+        self.page_table = (None if page_table is None else
+                           torch.as_tensor(np.asarray(page_table, np.int32)).contiguous().to(device))
         self.page_meta = torch.zeros(max(1, L.page_meta_bytes(self.shape)), dtype=torch.uint8,
                                      device=device)
         self.workspace = torch.zeros(max(1, L.workspace_bytes(self.shape)), dtype=torch.uint8,
@@ -62,21 +65,21 @@ class LayerState:
 
     def build_page_meta(self, stream=None):
         L.losa_build_page_meta(self.shape, self.k_cache, self.kv_off, self.prefix_len,
-                               self.page_meta, stream)
+                               self.page_meta, stream, page_table=self.page_table)
 
     def update_page_meta(self, first_token, max_new_tokens: int, stream=None):
         """After a committed block: the new prefix lengths are already in
         self.prefix_len; first_token[s] is each sequence's first new token."""
         ft = torch.as_tensor(np.asarray(first_token, np.int32)).to(self.device)
         L.losa_update_page_meta(self.shape, self.k_cache, self.kv_off, self.prefix_len, ft,
-                                max_new_tokens, self.page_meta, stream)
+                                max_new_tokens, self.page_meta, stream, page_table=self.page_table)
 
     def dense_first_step(self, q_t, k_blk, v_blk, out=None, debug: Optional[L.Debug] = None,
                          stream=None):
         out = self.out if out is None else out
         L.losa_dense_first_step(self.shape, q_t, k_blk, v_blk, self.k_cache, self.v_cache,
                                 self.kv_off, self.prefix_len, self.op_cache, self.lp_cache, out,
-                                self.workspace, debug, stream)
+                                self.workspace, debug, stream, page_table=self.page_table)
         return out
 
     def prepare_dense_first_step(self, q_t, k_blk, v_blk, out=None, stream=None):
@@ -84,18 +87,19 @@ class LayerState:
         return L.prepare_dense_first_step(self.shape, q_t, k_blk, v_blk, self.k_cache,
                                           self.v_cache, self.kv_off, self.prefix_len,
                                           self.op_cache, self.lp_cache, out, self.workspace,
-                                          stream)
+                                          stream, page_table=self.page_table)
 
     def prepare_step(self, q_t, q_prev, k_blk, v_blk, out=None, stream=None):
         out = self.out if out is None else out
         return L.prepare_step(self.shape, q_t, q_prev, k_blk, v_blk, self.k_cache, self.v_cache,
                               self.page_meta, self.kv_off, self.prefix_len, self.op_cache,
-                              self.lp_cache, out, self.workspace, stream)
+                              self.lp_cache, out, self.workspace, stream,
+                              page_table=self.page_table)
 
     def step(self, q_t, q_prev, k_blk, v_blk, debug: Optional[L.Debug] = None, out=None,
              stream=None):
         out = self.out if out is None else out
         L.losa_step(self.shape, q_t, q_prev, k_blk, v_blk, self.k_cache, self.v_cache,
                     self.page_meta, self.kv_off, self.prefix_len, self.op_cache, self.lp_cache,
-                    out, self.workspace, debug, stream)
+                    out, self.workspace, debug, stream, page_table=self.page_table)
         return out

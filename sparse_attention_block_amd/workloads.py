@@ -221,6 +221,53 @@ def make_layer(cfg: Config, layer: int = 0, n_steps: Optional[int] = None,
     return lay
 
 
+def paged_pool(lay: Layer, seed: int = 0, spare: float = 0.25, share_pages: int = 0):
+    """The layer's prefix scattered over a pool of physical pages (a paged KV
+    cache): returns (k_pool, v_pool, page_table) with k_pool, v_pool
+    [H_kv][16 * n_pool][d] and page_table [n_seq][max(1, pages of the longest
+    prefix)] int32, where page p of sequence s is pool page page_table[s][p].
+    The pool has ``spare`` more pages than the prefixes use, filled with N(0, 1)
+    noise, and the pages are placed in a seeded random order.  With share_pages
+    = n, every sequence after the first reuses the first sequence's first n
+    whole pages: their keys and values are first copied into ``lay``'s own
+    cache (so a contiguous reading sees the same prefix), then mapped to the
+    same pool pages.  Data movement only."""
+    c = lay.cfg
+    P, S = c.page_size, c.n_seq
+    lens = [int(x) for x in lay.prefix_len]
+    pages = [(L + P - 1) // P for L in lens]
+    if share_pages:
+        full0 = lens[0] // P
+        for s in range(1, S):
+            n = min(share_pages, full0, lens[s] // P)
+            a, b = int(lay.kv_off[0]), int(lay.kv_off[s])
+            lay.k_cache[:, b:b + n * P] = lay.k_cache[:, a:a + n * P]
+            lay.v_cache[:, b:b + n * P] = lay.v_cache[:, a:a + n * P]
+    own = [pages[0]] + [pages[s] - (min(share_pages, lens[0] // P, lens[s] // P) if share_pages else 0)
+                        for s in range(1, S)]
+    used = sum(own)
+    n_pool = max(1, used + int(np.ceil(used * spare)))
+    rng = _rng(c.cfg_id, lay.layer, 30, 0, seed)
+    order = rng.permutation(n_pool)
+    k_pool = to_storage(_normal(rng, (c.n_kvhead, n_pool * P, c.head_dim)), c.dtype)
+    v_pool = to_storage(_normal(rng, (c.n_kvhead, n_pool * P, c.head_dim)), c.dtype)
+    max_pages = max(1, max(pages) if pages else 1)
+    pt = np.zeros((S, max_pages), np.int32)
+    nxt = 0
+    for s in range(S):
+        for p in range(pages[s]):
+            if s > 0 and share_pages and p < min(share_pages, lens[0] // P, lens[s] // P):
+                pt[s, p] = pt[0, p]
+                continue
+            e = int(order[nxt])
+            nxt += 1
+            pt[s, p] = e
+            src = int(lay.kv_off[s]) + p * P
+            k_pool[:, e * P:(e + 1) * P] = lay.k_cache[:, src:src + P]
+            v_pool[:, e * P:(e + 1) * P] = lay.v_cache[:, src:src + P]
+    return k_pool, v_pool, pt
+
+
 def make_cache_state(cfg: Config, layer: int = 0, stream: int = 20):
     """A seeded (o_p, L_p) cache state: the prefix statistics a previous step left
     behind, for starting a step without running the dense pass first.

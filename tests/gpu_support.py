@@ -48,15 +48,27 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 class Pair:
-    """The HIP path and the oracle on one layer's inputs."""
+    """The HIP path and the oracle on one layer's inputs.  With ``paged`` =
+    (k_pool, v_pool, page_table) the GPU reads the prefix from a paged pool
+    (workloads.paged_pool) while the oracle reads the layer's contiguous cache."""
 
-    def __init__(self, lay: W.Layer, name: str):
+    def __init__(self, lay: W.Layer, name: str, paged=None):
         self.lay, self.cfg, self.name = lay, lay.cfg, name
         c = lay.cfg
         self.orc = Oracle(c, lay.kv_off, lay.prefix_len, lay.kv_tokens, lay.k_cache, lay.v_cache)
         say(f"[{name}] upload S={c.n_seq} L={list(c.prefix_lens)[:4]} B={c.block} "
-            f"Hq={c.n_qhead} Hkv={c.n_kvhead} d={c.head_dim} budget={c.budget} A={c.n_active} {c.dtype}")
-        self.gpu = LayerState.from_layer(lay)
+            f"Hq={c.n_qhead} Hkv={c.n_kvhead} d={c.head_dim} budget={c.budget} A={c.n_active} {c.dtype}"
+            + (f" paged pool of {paged[0].shape[1] // c.page_size} pages" if paged else ""))
+        if paged is None:
+            self.gpu = LayerState.from_layer(lay)
+        else:
+            k_pool, v_pool, pt = paged
+            self.gpu = LayerState(n_seq=c.n_seq, block=c.block, n_qhead=c.n_qhead,
+                                  n_kvhead=c.n_kvhead, head_dim=c.head_dim, budget_tokens=c.budget,
+                                  n_active=c.n_active, dtype=c.dtype,
+                                  k_cache=to_device(k_pool, c.dtype), v_cache=to_device(v_pool, c.dtype),
+                                  kv_off=lay.kv_off, prefix_len=lay.prefix_len,
+                                  flags=getattr(c, "flags", 0), page_table=pt)
         self.dev = lambda x: to_device(x, c.dtype)
         self.q = [self.dev(x) for x in lay.q]
         self.kb = [self.dev(x) for x in lay.k_blk]

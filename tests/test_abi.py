@@ -82,13 +82,13 @@ def test_bad_shape_rejected(lib, kw, status):
     assert L.workspace_bytes(sh) == 0 and L.page_meta_bytes(sh) == 0
     assert L.union_capacity(sh) == -1
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
-    r = lib.losa_step(ctypes.byref(sh), *([fake] * 12), None, fake, 1 << 30, None)
+    r = lib.losa_step(ctypes.byref(sh), *([fake] * 13), None, fake, 1 << 30, None)
     assert r == status
-    r = lib.losa_dense_first_step(ctypes.byref(sh), *([fake] * 10), None, fake, 1 << 30, None)
+    r = lib.losa_dense_first_step(ctypes.byref(sh), *([fake] * 11), None, fake, 1 << 30, None)
     assert r == status
-    r = lib.losa_build_page_meta(ctypes.byref(sh), fake, fake, fake, fake, None)
+    r = lib.losa_build_page_meta(ctypes.byref(sh), fake, fake, fake, None, fake, None)
     assert r == status
-    r = lib.losa_update_page_meta(ctypes.byref(sh), fake, fake, fake, fake, 16, fake, None)
+    r = lib.losa_update_page_meta(ctypes.byref(sh), fake, fake, fake, None, fake, 16, fake, None)
     assert r == status
 
 
@@ -98,14 +98,17 @@ def test_update_page_meta_checks(lib):
     sh = shape_of(W.gqa_16k())
     fake = ctypes.c_void_p(1 << 20)
     odd = ctypes.c_void_p((1 << 20) + 2)
-    ok = [fake] * 4
-    for i in range(4):
+    ok = [fake, fake, fake, None, fake]  # k_cache, kv_off, prefix_len, page_table, first_token
+    for i in (0, 1, 2, 4):
         bad = list(ok)
         bad[i] = None
         assert lib.losa_update_page_meta(ctypes.byref(sh), *bad, 16, fake, None) == L.LOSA_ERR_INVALID_ARG
     assert lib.losa_update_page_meta(ctypes.byref(sh), *ok, 16, None, None) == L.LOSA_ERR_INVALID_ARG
-    assert lib.losa_update_page_meta(ctypes.byref(sh), fake, fake, fake, odd, 16, fake,
-                                     None) == L.LOSA_ERR_INVALID_ARG
+    for i in (0, 1, 2, 3, 4):
+        bad = list(ok)
+        bad[i] = odd
+        assert lib.losa_update_page_meta(ctypes.byref(sh), *bad, 16, fake, None) == \
+            L.LOSA_ERR_INVALID_ARG
     assert lib.losa_update_page_meta(ctypes.byref(sh), *ok, -1, fake, None) == L.LOSA_ERR_INVALID_ARG
     assert lib.losa_update_page_meta(ctypes.byref(sh), *ok, sh.max_prefix_len + 1, fake,
                                      None) == L.LOSA_ERR_INVALID_ARG
@@ -116,20 +119,31 @@ def test_pointer_and_workspace_checks(lib):
     fake = ctypes.c_void_p(1 << 20)
     odd = ctypes.c_void_p((1 << 20) + 2)
     need = L.workspace_bytes(sh)
-    args = [fake] * 12
-    # null and misaligned tensors
-    for i in range(12):
+    # q_t q_prev k_blk v_blk k_cache v_cache page_meta kv_off prefix_len page_table op lp out
+    args = [fake] * 9 + [None] + [fake] * 3
+    KV_OFF, PREFIX_LEN, PAGE_TABLE, LP = 7, 8, 9, 11
+    # null and misaligned tensors (a null page table is the contiguous layout)
+    for i in range(13):
         bad = list(args)
-        bad[i] = None
-        assert lib.losa_step(ctypes.byref(sh), *bad, None, fake, need, None) == L.LOSA_ERR_INVALID_ARG
-        if i not in (7, 8, 10):  # kv_off, prefix_len, lp_cache need only 4-byte alignment
+        if i != PAGE_TABLE:
+            bad[i] = None
+            assert lib.losa_step(ctypes.byref(sh), *bad, None, fake, need, None) == L.LOSA_ERR_INVALID_ARG
+        if i not in (KV_OFF, PREFIX_LEN, PAGE_TABLE, LP):  # int32 / fp32 arrays: 4-byte alignment
             bad[i] = odd
             assert lib.losa_step(ctypes.byref(sh), *bad, None, fake, need, None) == \
                 L.LOSA_ERR_INVALID_ARG
+    # a misaligned page table; a page table with a misaligned kv_off
+    bad = list(args)
+    bad[PAGE_TABLE] = odd
+    assert lib.losa_step(ctypes.byref(sh), *bad, None, fake, need, None) == L.LOSA_ERR_INVALID_ARG
+    bad = list(args)
+    bad[PAGE_TABLE], bad[KV_OFF] = fake, odd
+    assert lib.losa_step(ctypes.byref(sh), *bad, None, fake, need, None) == L.LOSA_ERR_INVALID_ARG
     assert lib.losa_step(ctypes.byref(sh), *args, None, None, need, None) == L.LOSA_ERR_INVALID_ARG
     # workspace one byte short
     assert lib.losa_step(ctypes.byref(sh), *args, None, fake, need - 1, None) == L.LOSA_ERR_WORKSPACE
-    assert lib.losa_dense_first_step(ctypes.byref(sh), *([fake] * 10), None, fake, need - 1,
+    dense = [fake] * 7 + [None] + [fake] * 3
+    assert lib.losa_dense_first_step(ctypes.byref(sh), *dense, None, fake, need - 1,
                                      None) == L.LOSA_ERR_WORKSPACE
     # debug union list shorter than the union capacity
     dbg = L.LosaDebug(None, None, None, fake, None, L.union_capacity(sh) - 1, None)
@@ -153,6 +167,6 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
     cfg = W.ragged_batch()
     sh = shape_of(cfg)
     p = ctypes.c_void_p(1 << 20)
-    st = lib.losa_step_noalloc(ctypes.byref(sh), *([p] * 12), None, None)
+    st = lib.losa_step_noalloc(ctypes.byref(sh), *([p] * 9), None, *([p] * 3), None, None)
     assert st == L.LOSA_ERR_SCRATCH, L.status_string(st)
     assert "static scratch" in L.status_string(L.LOSA_ERR_SCRATCH)
