@@ -239,7 +239,7 @@ def page_meta_times(hip, lay, kv, reps):
 
 
 def measure_case(hip, lay_kv, inputs_of, *, cfg, budget, active_of, dense_every_step, reps,
-                 union_layers=(0,), flags=0):
+                 union_layers=(0,), flags=0, page_table=None):
     """Time one case over the device KV replicas ``lay_kv`` = (layer, [(k, v), ...]).
 
     inputs_of(li) -> (q, k_blk, v_blk) device tensor lists per step for layer li.
@@ -259,7 +259,8 @@ def measure_case(hip, lay_kv, inputs_of, *, cfg, budget, active_of, dense_every_
         ls = LayerState(n_seq=cfg.n_seq, block=cfg.block, n_qhead=cfg.n_qhead,
                         n_kvhead=cfg.n_kvhead, head_dim=cfg.head_dim, budget_tokens=budget,
                         n_active=active_of(li), dtype=cfg.dtype, k_cache=k, v_cache=v,
-                        kv_off=lay.kv_off, prefix_len=lay.prefix_len, flags=flags)
+                        kv_off=lay.kv_off, prefix_len=lay.prefix_len, flags=flags,
+                        page_table=page_table)
         ls.build_page_meta()
         layers.append(ls)
     # union sizes over the block (from the library's debug outputs)
@@ -401,6 +402,13 @@ def sweep(args):
                            active_of=lambda i: base.block, dense_every_step=False, reps=args.steps)
         add_row("64K", "QUEST-style (all 16 tokens active, |A|=4 inputs)", base, budget,
                 base.block, SWEEP_LAYERS, res, False)
+        # naive per-query sparse attention: every token its own pages (row masks),
+        # no reuse; the union of all 16 tokens' pages is what it loads
+        res = measure_case(hip, kv, lambda i: inp4, cfg=base, budget=budget,
+                           active_of=lambda i: base.block, dense_every_step=False, reps=args.steps,
+                           flags=1)
+        add_row("64K", "naive per-query (all 16 tokens active, own pages)", base, budget,
+                base.block, SWEEP_LAYERS, res, False)
     inp4 = dev_inputs(lay, base.dtype)
     res = measure_case(hip, kv, lambda i: inp4, cfg=base, budget=128, active_of=lambda i: 4,
                        dense_every_step=True, reps=args.steps)
@@ -420,12 +428,29 @@ def sweep(args):
         lay = W.make_layer(c, n_steps=c.n_steps)
         kv = (lay, replicas(lay, n_layers))
         inp = dev_inputs(lay, c.dtype)
-        for label, a, dense_mode in ((f"LoSA |A|={c.n_active}", c.n_active, False),
-                                     (f"QUEST-style (all {c.block} tokens active)", c.block, False),
-                                     ("dense every step", c.n_active, True)):
+        cases = [(f"LoSA |A|={c.n_active}", c.n_active, False, 0),
+                 (f"QUEST-style (all {c.block} tokens active)", c.block, False, 0),
+                 ("dense every step", c.n_active, True, 0)]
+        if c.group * c.block <= 64:  # row masks take at most 64 stacked rows per KV head
+            cases.append((f"naive per-query (all {c.block} tokens active, own pages)", c.block,
+                          False, 1))
+        for label, a, dense_mode, fl in cases:
             res = measure_case(hip, kv, lambda i: inp, cfg=c, budget=c.budget,
-                               active_of=lambda i: a, dense_every_step=dense_mode, reps=args.steps)
+                               active_of=lambda i: a, dense_every_step=dense_mode, reps=args.steps,
+                               flags=fl)
             add_row(c.name, label, c, c.budget, a, n_layers, res, dense_mode)
+        if c.n_seq > 1:
+            # the same batch read through a page table from a shuffled pool
+            kp, vp, pt = W.paged_pool(lay, seed=5)
+            kvp = (lay, [(to_device(kp, c.dtype), to_device(vp, c.dtype))] +
+                   [(to_device(kp, c.dtype), to_device(vp, c.dtype)) for _ in range(n_layers - 1)])
+            for label, a, dense_mode in ((f"LoSA |A|={c.n_active}, paged pool", c.n_active, False),
+                                         ("dense every step, paged pool", c.n_active, True)):
+                res = measure_case(hip, kvp, lambda i: inp, cfg=c, budget=c.budget,
+                                   active_of=lambda i: a, dense_every_step=dense_mode,
+                                   reps=args.steps, page_table=pt)
+                add_row(c.name, label, c, c.budget, a, n_layers, res, dense_mode)
+            del kvp
         del kv, lay, inp
         torch.cuda.empty_cache()
 
