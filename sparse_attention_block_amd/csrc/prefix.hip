@@ -593,8 +593,11 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
     const int rows = D.R, nch = D.n_chunks_sparse;
     const int n_rt = (rows + 15) / 16;
 
-    // the rows' page lists (one entry per thread, clamped) and the Q operands
-    // (row tiles past the rows read the last one and are zeroed), requested first
+    // the rows' page lists (one entry per thread, clamped) and the Q operands,
+    // requested first.  Row tiles past the rows read the last one again: their
+    // scores go to LDS slots that are never read, so no load is conditional
+    // (a zeroing select would be compiled as a branch around each load, with a
+    // wait for all loads in flight before it)
     const int32_t *psel_g = W.psel + (size_t)sgi * rows * D.k;
     const int n_sel = rows * D.k;
     const int pre0 = psel_g[min(tid, max(n_sel - 1, 0))];
@@ -602,13 +605,11 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
     const uint16_t *qr = static_cast<const uint16_t *>(W.qrows) + (size_t)sgi * D.R16 * DIM;
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
-        const int rtc = min(i, n_rt - 1);
+        const int rtc = min(i, max(n_rt - 1, 0));
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(qr + (size_t)(rtc * 16 + l16) * DIM +
-                                                             32 * kk + 8 * lg);
-            qop[i][kk] = i < n_rt ? v : make_uint4(0, 0, 0, 0);
-        }
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            qop[i][kk] = *reinterpret_cast<const uint4 *>(qr + (size_t)(rtc * 16 + l16) * DIM +
+                                                          32 * kk + 8 * lg);
     }
     const int n_items = union_slice(psel_g, pre0, n_sel, sg.pages, D.k >= sg.pages, first, cp,
                                     s_bm, s_wsum, s_pg,

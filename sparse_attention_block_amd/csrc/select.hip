@@ -634,37 +634,56 @@ struct SelectDbg {
     int32_t *page_sel;   // [S][Hq][A][k]
 };
 
-// The exact chain for global page gp (contract of include/losa.h); the page's
-// metadata chunks are loaded, from the page-major copy, before the chain
-// starts.  bf16: qw holds the row's query values as fp32 (DIM words), then per
-// dimension the byte selector that turns the metadata word (max | min << 16)
-// into the fp32 bits of max_i (q >= 0, -0 included) or of min_i (q < 0); per
-// dimension one fused
-// multiply-add with that value -- the same value as the pair q+ * max then
-// q- * min, whose other product is an exact zero.  fp32: qw holds (max(q,0),
-// min(q,0)) per dimension, each product rounded, then added.
+// The selection workgroup is one wave: its LDS writes are seen by its later
+// LDS reads once they have completed, so it needs the wait and no s_barrier
+// (which is not free even for a lone wave).
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// The exact chain for global page gp (contract of include/losa.h), computed
+// by a group of LPC consecutive lanes: lane j of the group loads chunks
+// j*NCH/LPC .. of the page's metadata (from the page-major copy) before the
+// chain starts, and the chain runs through the group in LPC phases -- in phase
+// p lane p carries on from lane p-1's value (a quad permute) over its own
+// chunks -- so the group's last lane ends with the one ascending chain, while
+// each lane holds only 1/LPC of the page.  bf16: qw holds the row's query
+// values as fp32 (DIM words), then per dimension the byte selector that turns
+// the metadata word (max | min << 16) into the fp32 bits of max_i (q >= 0, -0
+// included) or of min_i (q < 0); per dimension one fused multiply-add with
+// that value -- the same value as the pair q+ * max then q- * min, whose
+// other product is an exact zero.  fp32: qw holds (max(q,0), min(q,0)) per
+// dimension, each product rounded, then added.
 constexpr uint32_t kSelMax = 0x01000c0cu;  // v_perm_b32: bytes 1,0 of the word to 3,2; zeros below
 constexpr uint32_t kSelMin = 0x03020c0cu;  // bytes 3,2 to 3,2; zeros below
+template <bool BF>
+constexpr int chain_lanes() { return BF ? 2 : 4; }  // 16 chunks (64 VGPRs) per lane at d = 128
+constexpr int kPendRing = 128;  // candidate pages waiting for their chains (a ring in LDS)
+
 template <int DIM, bool BF>
 __device__ __forceinline__ float exact_bound(const uint4 *meta, const Dims &D, int g, int64_t gp,
-                                             const uint32_t *qw) {
-    constexpr int DPC = BF ? 4 : 2;
+                                             const uint32_t *qw, int lane) {
+    constexpr int DPC = BF ? 4 : 2;  // dimensions per 16-byte chunk
     constexpr int NCH = DIM / DPC;
-    // the page-major copy: the page's chunks are contiguous
+    constexpr int LPC = chain_lanes<BF>();
+    constexpr int NQ = NCH / LPC;    // chunks per lane
+    const int j = lane % LPC;
     const uint4 *m =
         reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(meta) + D.meta_pm_off) +
-        ((size_t)g * D.n_tiles_total * kTile + gp) * NCH;
+        ((size_t)g * D.n_tiles_total * kTile + gp) * NCH + j * NQ;
+    uint4 mv[NQ];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) mv[c] = m[c];
     float acc = 0.0f;
-    constexpr int BATCH = NCH < 32 ? NCH : 32;
+#pragma unroll 1
+    for (int ph = 0; ph < LPC; ++ph) {
+        // lane j of each quad takes lane j-1's value (lane 0 its own): in
+        // phase ph the value of lane ph is the chain up to its chunks
+        if (ph > 0) acc = dpp_f32<0x90>(acc);  // quad_perm [0,0,1,2]
+        int cq = j * NQ;                // the lane's first chunk, opaque to the
+        asm volatile("" : "+v"(cq));   // compiler so that the query reads stay in the loop
 #pragma unroll
-    for (int c0 = 0; c0 < NCH; c0 += BATCH) {
-        uint4 mv[BATCH];
-#pragma unroll
-        for (int c = 0; c < BATCH; ++c) mv[c] = m[c0 + c];
-#pragma unroll
-        for (int c = 0; c < BATCH; ++c) {
+        for (int c = 0; c < NQ; ++c) {
             const uint4 m4 = mv[c];
-            const int cc = c0 + c;
+            const int cc = cq + c;
             if constexpr (BF) {
                 const float4 q4 = *reinterpret_cast<const float4 *>(qw + 4 * cc);
                 const uint4 sl = *reinterpret_cast<const uint4 *>(qw + DIM + 4 * cc);
@@ -675,14 +694,14 @@ __device__ __forceinline__ float exact_bound(const uint4 *meta, const Dims &D, i
                     acc = __builtin_fmaf(qd[e], __uint_as_float(__builtin_amdgcn_perm(0u, wd[e], sd[e])),
                                          acc);
             } else {
-                const float *q = reinterpret_cast<const float *>(qw);
-                const float p0 = q[4 * cc + 0] * __uint_as_float(m4.x);
+                const float4 q4 = *reinterpret_cast<const float4 *>(qw + 4 * cc);
+                const float p0 = q4.x * __uint_as_float(m4.x);
                 acc = acc + p0;
-                const float p1 = q[4 * cc + 1] * __uint_as_float(m4.y);
+                const float p1 = q4.y * __uint_as_float(m4.y);
                 acc = acc + p1;
-                const float p2 = q[4 * cc + 2] * __uint_as_float(m4.z);
+                const float p2 = q4.z * __uint_as_float(m4.z);
                 acc = acc + p2;
-                const float p3 = q[4 * cc + 3] * __uint_as_float(m4.w);
+                const float p3 = q4.w * __uint_as_float(m4.w);
                 acc = acc + p3;
             }
         }
@@ -730,7 +749,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
     const bool all_pages = k >= sg.pages;
     uint64_t *mk = reinterpret_cast<uint64_t *>(smem);  // [128] keys being merged
     uint32_t *qw = smem + 256;                           // [2*DIM] the row's chain operands
-    int32_t *pend = reinterpret_cast<int32_t *>(smem + 256 + 2 * DIM);  // [4096] candidate pages
+    int32_t *pend = reinterpret_cast<int32_t *>(smem + 256 + 2 * DIM);  // [kPendRing] candidate pages
     int32_t *psel = W.psel + ((size_t)sgi * R1 + r) * k;
 
     if (all_pages) {
@@ -761,11 +780,14 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
 #pragma unroll
         for (int i = 0; i < TMR; ++i) tmv[i] = tm[min(lane + 64 * i, n_t - 1)];
         // upper ends of pages base + 256*jj + 4*lane + e, jj < 16, e < 4
+        // (the lane's offset is recomputed per call, opaque to the compiler:
+        // else the 16 offsets stay in registers through the whole selection)
         auto load_h = [&](int base, float4 (&hv)[16]) {
+            int o = base + 4 * lane;
+            asm volatile("" : "+v"(o));
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj)
-                hv[jj] = *reinterpret_cast<const float4 *>(
-                    hb + min(base + 256 * jj + 4 * lane, D.hb_stride - 4));
+                hv[jj] = *reinterpret_cast<const float4 *>(hb + min(o + 256 * jj, D.hb_stride - 4));
         };
         float4 hv0[16];
         load_h(0, hv0);
@@ -819,6 +841,9 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                         if (p < sg.pages) lmax = fmaxf(lmax, lo);
                     }
                 }
+                // at most 16 of the page maxima in flight: the upper ends
+                // already take 64 registers
+                if (jj % 4 == 3) __builtin_amdgcn_sched_barrier(0);
             }
             gm = lmax == -__builtin_huge_valf() ? 0u : ord_key(lmax);
         }
@@ -830,26 +855,31 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                 if (__popcll(__ballot(gm >= c)) >= k) lam = c;
             }
         }
-        __syncthreads();  // qw visible to the chains
-        // 2. candidates: upper end >= threshold; exact chain in batches of 64
+        wave_lds_fence();  // qw visible to the chains
+        // 2. candidates: upper end >= threshold; exact chains, CPP at a time
         uint64_t lst = 0ull;  // lane e < k: e-th best (score key << 32 | ~page)
         // the threshold as a float: ord_key preserves the order of floats (-0
         // and +0 alike), so ord_key(x) >= lam is x >= lamf; key 0 (every page
         // qualifies) is below every finite value
         const float lamf = lam == 0u ? -__builtin_huge_valf() : ord_to_f32(lam);
-        // exact chains of the pending pages pend[c0 .. c0 + n), n <= 64, merged
-        // into the list: a key's rank is the number of greater keys among the
-        // chains' (lanes < n) and the list's (lanes < nlst), read lane by lane
-        // into scalar registers (keys are distinct: one per page); the key of
-        // rank e < k goes to lane e through LDS
+        // Exact chains of the pending pages c0 .. c0 + n - 1 of the ring, n <=
+        // CPP, one per group of LPC lanes (candidate i on lanes LPC*i ..; its
+        // value on the group's last lane), merged into the list: a key's rank
+        // is the number of greater keys among the chains' and the list's
+        // (lanes < nlst), read lane by lane into scalar registers (keys are
+        // distinct: one per page); the key of rank e < k goes to lane e
+        // through LDS.
+        constexpr int LPC = chain_lanes<BF>(), CPP = 64 / LPC;
         auto chains = [&](int c0, int n) {
-            uint64_t cand = 0ull;
-            if (lane < n) {
-                const int pc = pend[c0 + lane];
-                const float u = exact_bound<DIM, BF>(meta, D, g, phys_page_t<PAGED>(sg, pc), qw);
-                cand = (static_cast<uint64_t>(ord_key(u)) << 32) |
-                       static_cast<uint32_t>(~static_cast<uint32_t>(pc));
-            }
+            const int pc = pend[(c0 + min(lane / LPC, n - 1)) & (kPendRing - 1)];
+            // (lanes past the groups stay idle: a load's cost grows with its active lanes)
+            float u = 0.0f;
+            if (lane < LPC * n)
+                u = exact_bound<DIM, BF>(meta, D, g, phys_page_t<PAGED>(sg, pc), qw, lane);
+            const bool mine = lane % LPC == LPC - 1 && lane / LPC < n;
+            const uint64_t cand = mine ? (static_cast<uint64_t>(ord_key(u)) << 32) |
+                                             static_cast<uint32_t>(~static_cast<uint32_t>(pc))
+                                       : 0ull;
             const int nlst = __popcll(__ballot(lane < k && lst != 0ull));
             auto lane_key = [](uint64_t v, int i) {
                 const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), i);
@@ -858,7 +888,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
             };
             int rc = 0, rl = 0;
             for (int i = 0; i < n; ++i) {
-                const uint64_t y = lane_key(cand, i);
+                const uint64_t y = lane_key(cand, LPC * i + LPC - 1);
                 rc += y > cand;
                 rl += y > lst;
             }
@@ -867,10 +897,10 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                 rc += y > cand;
                 rl += y > lst;
             }
-            __syncthreads();  // the previous list has been read from mk
-            if (lane < n && rc < k) mk[rc] = cand;
+            wave_lds_fence();  // the previous list has been read from mk
+            if (mine && rc < k) mk[rc] = cand;
             if (lane < nlst && rl < k) mk[rl] = lst;
-            __syncthreads();
+            wave_lds_fence();
             lst = lane < min(n + nlst, k) ? mk[lane] : 0ull;
         };
         // The largest float below lamf: hx >= lamf is then lamb - hx < 0, the
@@ -880,12 +910,16 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
         const float lamb = lam == 0u ? -__builtin_huge_valf()
                                      : __uint_as_float(lb == 0u ? 0x80000001u
                                                                 : ((lb & 0x80000000u) ? lb + 1u : lb - 1u));
+        // Pending candidates: ring entries done .. listed - 1 (at most CPP - 1
+        // left after each listing round, plus the round's 64 new ones)
+        static_assert(CPP - 1 + 64 <= kPendRing, "candidate ring");
+        int listed = 0, done = 0;
         // One batch of 4096 pages.  Candidate bits: element i = 4*jj + e4 (page
         // base + 256*jj + 4*lane + e4) at bit 31 - i%32 of cm[i/32], shifted in
         // with v_alignbit (two instructions per upper end, no branch).  Each
-        // lane then lists its candidates in pend, lowest bit first, while any
-        // lane has some; their chains go 64 at a time.  The first batch uses
-        // the upper ends requested above; later ones load theirs.
+        // lane then lists its candidates, lowest bit first, while any lane has
+        // some; whenever CPP are pending their chains run.  The first batch
+        // uses the upper ends requested above; later ones load theirs.
         auto batch = [&](int base, const float4 (&hv)[16]) {
             uint32_t cm[2] = {0u, 0u};
             if (sg.pages - base >= 4096) {  // uniform: every page of the batch is in the sequence
@@ -897,7 +931,8 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                         cm[jj >> 3] = __builtin_amdgcn_alignbit(cm[jj >> 3], __float_as_uint(lamb - hx[e4]), 31);
                 }
             } else {
-                const int lim = sg.pages - base - 4 * lane;  // in the sequence: 256*jj + e4 < lim
+                int lim = sg.pages - base - 4 * lane;  // in the sequence: 256*jj + e4 < lim
+                asm volatile("" : "+v"(lim));
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) {
                     const float hx[4] = {hv[jj].x, hv[jj].y, hv[jj].z, hv[jj].w};
@@ -908,7 +943,6 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                 }
             }
             uint64_t cmask = (static_cast<uint64_t>(cm[1]) << 32) | cm[0];
-            int npend = 0;
             for (;;) {
                 const bool c = cmask != 0ull;
                 const uint64_t bal = __ballot(c);
@@ -916,20 +950,29 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                 if (c) {
                     const int b = __ffsll(static_cast<unsigned long long>(cmask)) - 1;
                     const int e = (b & 32) + 31 - (b & 31);  // the element
-                    pend[npend + lanes_below(bal, lane)] = base + 256 * (e >> 2) + 4 * lane + (e & 3);
+                    pend[(listed + lanes_below(bal, lane)) & (kPendRing - 1)] =
+                        base + 256 * (e >> 2) + 4 * lane + (e & 3);
                     cmask &= cmask - 1ull;
                 }
-                npend += __popcll(bal);
+                listed += __popcll(bal);
+                if (listed - done >= CPP) {  // uniform
+                    wave_lds_fence();  // the listed pages visible to every lane
+                    do {
+                        chains(done, CPP);
+                        done += CPP;
+                    } while (listed - done >= CPP);
+                }
             }
-            __syncthreads();  // pend visible to every lane
-            for (int c0 = 0; c0 < npend; c0 += 64) chains(c0, min(npend - c0, 64));
         };
         batch(0, hv0);
         for (int base = 4096; base < sg.pages; base += 4096) {
             float4 hv[16];
             load_h(base, hv);
-            __syncthreads();  // the previous batch has read pend
             batch(base, hv);
+        }
+        if (listed > done) {
+            wave_lds_fence();
+            chains(done, listed - done);
         }
         // 3. the row's pages (k of them: every page of the exact top-k is a candidate)
         const bool has = lane < k && lst != 0ull;
@@ -944,7 +987,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
     }
 }
 
-size_t select_lds_bytes(const Dims &D) { return (256 + 2 * (size_t)D.d + 4096) * 4; }
+size_t select_lds_bytes(const Dims &D) { return (256 + 2 * (size_t)D.d + kPendRing) * 4; }
 
 hipError_t launch_score(const Dims &D, const void *meta, const int32_t *kv_off,
                         const int32_t *prefix_len, const Work &W, hipStream_t st) {
