@@ -110,6 +110,20 @@ def rocprof_durations(workload: str):
     return out, os.path.relpath(path, ROOT)
 
 
+def floors_record(floors, rp):
+    """The floors of this run (event-bracketed), with the probe kernels' own
+    durations from the committed rocprofv3 summary where its digest matches."""
+    rec = dict(floors)
+    rec["empty_kernel_us_rocprof"] = rp.get("probe_empty")
+    for mib, _ in FLOOR_READS:
+        r = rec["read"][f"{mib}MiB"]
+        us = rp.get(f"probe_read_{mib}MiB")
+        r["us_rocprof"] = us
+        r["gbps_rocprof"] = (mib << 20) / (us * 1e-6) / 1e9 if us else None
+        r["frac_rocprof"] = r["gbps_rocprof"] / PEAK_HBM_GBPS if us else None
+    return rec
+
+
 # ---------------------------------------------------------------------------
 # --sweep: the |A| x budget sweep, the KV-union density study against a
 # QUEST-style step (every block token active, same inputs) and a dense step
@@ -125,12 +139,24 @@ def _selftest():
     st.losa_selftest_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_int, ctypes.c_void_p]
     st.losa_selftest_empty.argtypes = [ctypes.c_void_p]
+    st.losa_selftest_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
     return st
 
 
-def latency_floors(hip, stream, reps=200):
-    """Back-to-back empty kernels, one event-bracketed empty kernel, and plain copies
-    of 1/8/64 MiB rotated over >= 512 MiB of buffers (so none is served from the MALL)."""
+FLOOR_READS = ((1, 256), (8, 512), (16, 1024), (64, 2048))  # (MiB, workgroups)
+FLOOR_REPS = 8
+
+
+def latency_floors(hip, stream, reps=50):
+    """Floors for reading the kernels' durations: an empty kernel (back to back,
+    and between two events), an empty event pair, and pure reads of 1/8/16/64 MiB
+    (the selftest library's k_probe_read, FLOOR_REPS of each).  Every read takes a
+    region of a pool that no kernel has touched since the pool was filled, at
+    least 1 GiB of writes earlier, so none is served from the 256 MB MALL or an
+    L2.  Durations here are event-bracketed (about 1 us more than the kernel);
+    the committed rocprofv3 summary of the bench command holds the same
+    kernels' own durations (k_empty, k_probe_read<MiB>)."""
     import torch
 
     st = _selftest()
@@ -160,25 +186,35 @@ def latency_floors(hip, stream, reps=200):
     torch.cuda.synchronize()
     out["empty_event_pair_us"] = float(sorted(
         hip.ms(evs[2 * i], evs[2 * i + 1]) * 1e3 for i in range(50))[25])
-    copies = {}
-    for mib in (1, 8, 64):
+    # a 2 GiB pool, filled; then 512 MiB between 1 and 1.5 GiB are read (in
+    # 32 MiB pieces, k_probe_read<0>), which evicts the fill's dirty tail from
+    # the MALL, so that no write-back runs beside the timed reads; those read
+    # the first GiB, each byte once
+    pool_bytes = 2048 << 20
+    pool = torch.ones(pool_bytes // 4, dtype=torch.float32, device="cuda")
+    for i in range(16):
+        assert st.losa_selftest_read(pool.data_ptr() + (1024 << 20) + (i << 25), 32 << 20, 1024, 0,
+                                     None, stream) == 0
+    need = sum(m << 20 for m, _ in FLOOR_READS) * FLOOR_REPS
+    assert need <= 1024 << 20
+    off = 0
+    reads = {}
+    for mib, blocks in FLOOR_READS:
         nb = mib << 20
-        n_buf = max(2, (512 << 20) // nb)
-        bufs = [torch.empty(nb // 4, dtype=torch.float32, device="cuda") for _ in range(n_buf + 1)]
-        blocks = max(1, min(4096, nb // (16 * 256)))
-        evs = [hip.event() for _ in range(2 * n_buf)]
+        evs = [hip.event() for _ in range(2 * FLOOR_REPS)]
         torch.cuda.synchronize()
-        for i in range(n_buf):
-            hip.record(evs[2 * i], stream)
-            assert st.losa_selftest_copy(bufs[i].data_ptr(), bufs[i + 1].data_ptr(), nb, blocks,
-                                         stream) == 0
-            hip.record(evs[2 * i + 1], stream)
+        for r in range(FLOOR_REPS):
+            hip.record(evs[2 * r], stream)
+            assert st.losa_selftest_read(pool.data_ptr() + off, nb, blocks, 0, None, stream) == 0
+            hip.record(evs[2 * r + 1], stream)
+            off += nb
         torch.cuda.synchronize()
-        us = sorted(hip.ms(evs[2 * i], evs[2 * i + 1]) * 1e3 for i in range(1, n_buf))
+        us = sorted(hip.ms(evs[2 * r], evs[2 * r + 1]) * 1e3 for r in range(FLOOR_REPS))
         med = float(us[len(us) // 2])
-        copies[f"{mib}MiB"] = {"us": med, "gbps": 2 * nb / (med * 1e-6) / 1e9}
-        del bufs
-    out["copy"] = copies
+        reads[f"{mib}MiB"] = {"workgroups": blocks, "us_events": med,
+                              "gbps_events": nb / (med * 1e-6) / 1e9}
+    out["read"] = reads
+    del pool
     torch.cuda.empty_cache()
     return out
 
@@ -677,6 +713,11 @@ def main():
             run_block(ev_blocks[k])
         torch.cuda.synchronize()
 
+    # launch and streaming floors, outside the timed region (their kernels also
+    # appear in the rocprofv3 summary of this command)
+    log("[bench] latency floors")
+    floors = latency_floors(hip, stream)
+
     n_calls = args.steps * STEPS_PER_BLOCK * len(layers)
     value_us = total_ms * 1e3 / n_calls
     ms_per_step = total_ms / args.steps
@@ -786,6 +827,7 @@ def main():
                    "steps)" if graphs else "eager launches"),
         "value_eager_launch": eager_us,
         "wall_s": wall,
+        "floors": floors_record(floors, rp),
     }
     hip.close()
     if not args.no_cpu_baseline:

@@ -2,9 +2,9 @@
 // called only by the GPU tests (not part of the LoSA computation).
 //  * one page-bound step, fma(q+, max, acc) then fma(q-, min, acc) with bf16
 //    operands, must equal the IEEE round-to-nearest-even sum acc + q*sel;
-//  * a plain copy kernel (HBM traffic calibration of the profiler counters,
-//    and the bandwidth a short streaming kernel reaches) and an empty kernel
-//    (the launch floor);
+//  * a plain copy kernel (HBM traffic calibration of the profiler counters),
+//    a pure read kernel (the rate a short streaming read reaches) and an
+//    empty kernel (the launch floor);
 //  * the operand/result lane layouts assumed for v_mfma_f32_16x16x32_bf16
 //    and v_mfma_f32_16x16x16_bf16: lane l supplies row (or column) l%16 and
 //    k-elements K*(l/16) .. K*(l/16)+K-1, and holds result rows
@@ -64,12 +64,57 @@ __global__ __launch_bounds__(256) void k_copy(const uint4 *__restrict__ src, uin
 
 __global__ void k_empty() {}
 
+// Pure read of n16 16-byte elements: workgroup b reads a contiguous slice,
+// each thread 8 loads in flight, and folds them with XOR; the fold is stored
+// only when the caller sets `sink` (the reads must stay live), so the kernel
+// moves no other bytes.  TAG (the size in MiB) only names the instantiation,
+// so that a profiler's per-kernel statistics keep the sizes apart.
+template <int TAG>
+__global__ __launch_bounds__(256) void k_probe_read(const uint4 *__restrict__ src, size_t n16,
+                                                    int sink, uint32_t *out) {
+    constexpr int U = 8;
+    const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const size_t b0 = blockIdx.x * per;
+    const size_t b1 = b0 + per < n16 ? b0 + per : n16;
+    uint32_t acc = 0;
+    for (size_t i = b0 + threadIdx.x; i < b1; i += 256 * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t j = i + (size_t)u * 256;
+            v[u] = src[j < b1 ? j : b1 - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (sink) out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 extern "C" {
 
 int losa_selftest_copy(const void *src, void *dst, size_t bytes, int blocks, void *stream) {
     if (bytes % 16 || blocks <= 0) return 1;
     hipLaunchKernelGGL(k_copy, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// bytes: a multiple of 16; out: blocks * 256 words when sink is set (else unused)
+int losa_selftest_read(const void *src, size_t bytes, int blocks, int sink, void *out, void *stream) {
+    if (bytes % 16 || bytes == 0 || blocks <= 0 || (sink && !out)) return 1;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint4 *p = static_cast<const uint4 *>(src);
+    uint32_t *o = static_cast<uint32_t *>(out);
+    const size_t n16 = bytes / 16;
+#define PROBE(TAGV) hipLaunchKernelGGL(k_probe_read<TAGV>, dim3(blocks), dim3(256), 0, st, p, n16, sink, o)
+    switch (bytes >> 20) {
+        case 1: PROBE(1); break;
+        case 8: PROBE(8); break;
+        case 16: PROBE(16); break;
+        case 64: PROBE(64); break;
+        default: PROBE(0); break;
+    }
+#undef PROBE
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

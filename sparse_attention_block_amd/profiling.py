@@ -29,13 +29,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 # tag -> (kernel-name pattern, sources whose digest identifies the build)
 KERNEL_TAGS = {
-    "dense_prefix": (r"k_prefix_dense_bf16<\d+, \d+, \d+>", ["prefix.hip", "losa_internal.h"]),
-    "sparse_prefix": (r"k_prefix_quarter_bf16<\d+, \d+, false>", ["prefix.hip", "losa_internal.h"]),
-    "page_score": (r"k_score_prep<\d+, false>", ["select.hip", "block_attn.h", "losa_internal.h"]),
-    "page_select": (r"k_select<\d+, true, \d+>", ["select.hip", "block_attn.h", "losa_internal.h"]),
+    "dense_prefix": (r"k_prefix_dense_bf16<\d+, \d+, \d+, false>", ["prefix.hip", "losa_internal.h"]),
+    "sparse_prefix": (r"k_prefix_quarter_bf16<\d+, \d+, false, false>", ["prefix.hip", "losa_internal.h"]),
+    "page_score": (r"k_score_prep<\d+, false, \d+, false>", ["select.hip", "block_attn.h", "losa_internal.h"]),
+    "page_select": (r"k_select<\d+, true, \d+, false>", ["select.hip", "block_attn.h", "losa_internal.h"]),
     "sparse_finish": (r"k_finish_active<unsigned short, \d+>", ["finish.hip", "losa_internal.h"]),
     "dense_finish": (r"k_finish<unsigned short, \d+>", ["finish.hip", "losa_internal.h"]),
     "page_meta": (r"k_page_meta<unsigned short, \d+>", ["page_meta.hip", "losa_internal.h"]),
+    # floors: an empty kernel and pure reads of cold buffers (selftest library)
+    "probe_empty": (r"(^|\W)k_empty($|\W)", ["selftest.hip"]),
+    "probe_read_1MiB": (r"k_probe_read<1>", ["selftest.hip"]),
+    "probe_read_8MiB": (r"k_probe_read<8>", ["selftest.hip"]),
+    "probe_read_16MiB": (r"k_probe_read<16>", ["selftest.hip"]),
+    "probe_read_64MiB": (r"k_probe_read<64>", ["selftest.hip"]),
 }
 COPY_KERNEL = r"(^|\W)k_copy($|\W)"
 
@@ -86,11 +92,12 @@ def print_sweep(path: str, command: str):
     print("Times are per (layer, step) from HIP-graph replays over the layer replicas; stage "
           "times are medians of the library's stage events, each including one event pair "
           f"({fl['empty_event_pair_us']:.2f} us for an empty pair).\n")
-    print("Latency floors: empty kernel back to back "
+    print("Latency floors (event-bracketed: the rocprofv3 summary of the bench command has the "
+          "kernels' own durations): empty kernel back to back "
           f"{fl['empty_kernel_back_to_back_us']:.2f} us, between two events "
-          f"{fl['empty_kernel_between_events_us']:.2f} us; plain copy (read + write): " +
-          ", ".join(f"{k} {v['us']:.1f} us ({v['gbps']:.0f} GB/s)" for k, v in fl["copy"].items())
-          + ".\n")
+          f"{fl['empty_kernel_between_events_us']:.2f} us; pure read of a cold buffer: " +
+          ", ".join(f"{k} {v['us_events']:.1f} us ({v['gbps_events']:.0f} GB/s)"
+                    for k, v in fl["read"].items()) + ".\n")
     if "page_meta" in fl:
         pm = fl["page_meta"]
         print(f"Page metadata of a 64K layer (8 KV heads): full build {pm['full_build_us']:.1f} us "
