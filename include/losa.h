@@ -74,7 +74,10 @@
  *                          each (whole pages, as shared prefixes give).
  *   op_cache               [n_seq][n_qhead][B][head_dim]      fp32 (o_p)
  *   lp_cache               [n_seq][n_qhead][B]                fp32 (L_p)
- *   page_meta              opaque, losa_page_meta_bytes() bytes, indexed by physical page
+ *   page_meta              opaque, losa_page_meta_bytes() bytes, kept per (sequence,
+ *                          page of the sequence): at the page's cache position in
+ *                          the contiguous layout, from s * ceil(max_prefix_len / 16)
+ *                          for sequence s with a page table
  *
  * Errors.  Arguments are checked on the host before anything is enqueued;
  * a failed check returns its status and enqueues nothing.  A failed launch
@@ -169,8 +172,9 @@ typedef struct losa_debug {
 /* Human-readable name of a status code (static string). */
 const char *losa_status_string(int status);
 
-/* Bytes of the page metadata for this shape's cache (0 if the shape is invalid):
- * per KV head and page of the whole cache, the page's per-dimension min and
+/* Bytes of the page metadata for this shape (0 if the shape is invalid): per
+ * KV head and metadata page -- max(kv_tokens / 16, n_seq * ceil(max_prefix_len
+ * / 16)) of them, enough for either layout -- the page's per-dimension min and
  * max twice (two layouts: one for scoring, one for the exact bounds of
  * selection), 4 * head_dim element sizes, plus one fp32 (the largest |key|). */
 size_t losa_page_meta_bytes(const losa_shape *shape);
@@ -187,9 +191,12 @@ int32_t losa_union_capacity(const losa_shape *shape);
  * sequence and KV head, the element-wise minimum and maximum of the keys of
  * its tokens that lie below prefix_len[s].  Run once per committed block
  * (the prefix does not change between the denoising steps of a block).
- * Writes page_meta (losa_page_meta_bytes(shape) bytes, library layout) at
- * each page's physical index (with a page table, pages no sequence uses keep
- * what they held; a page shared by sequences holds the same keys for each).
+ * Writes page_meta (losa_page_meta_bytes(shape) bytes, library layout) per
+ * (sequence, page): with a page table the keys are read through it and a page
+ * shared by sequences gets its metadata once per sequence, so the metadata of
+ * a sequence's consecutive pages stays contiguous however the table scatters
+ * them.  Metadata must be built and used with the same layout (page table or
+ * not).
  */
 int losa_build_page_meta(const losa_shape *shape, const void *k_cache, const int32_t *kv_off,
                          const int32_t *prefix_len, const int32_t *page_table, void *page_meta,

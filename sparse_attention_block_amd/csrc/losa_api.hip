@@ -66,7 +66,10 @@ Dims make_dims(const losa_shape *sh) {
     D.max_pages = (sh->max_prefix_len + kPage - 1) / kPage;
     D.hb_stride = (std::max(D.max_pages, 1) + 3) / 4 * 4;
     D.T = sh->kv_tokens;
-    D.n_tiles_total = (D.T / kPage + kTile - 1) / kTile;
+    // metadata pages per KV head: the cache's pages (contiguous layout) or
+    // max_pages per sequence (page table), whichever is more
+    const int64_t meta_pages = std::max<int64_t>(D.T / kPage, (int64_t)D.S * D.max_pages);
+    D.n_tiles_total = (meta_pages + kTile - 1) / kTile;
     D.meta_main_bytes = static_cast<int64_t>(meta_main_bytes(D));
     D.meta_pm_off = D.meta_main_bytes + D.Hk * D.n_tiles_total * kTile * 4;
     D.n_tiles_grid = std::max(1, (D.max_pages + kTile - 1) / kTile);

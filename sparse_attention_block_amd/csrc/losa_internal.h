@@ -181,6 +181,7 @@ struct SeqGeom {
     int len;            // prefix tokens
     int pages;          // ceil(len / 16)
     int64_t gp0;        // first global page (contiguous layout)
+    int64_t mp0;        // first metadata page of the sequence
     const int32_t *pt;  // the sequence's row of the page table, or null
     int64_t n_phys;     // pages in the cache (page-table entries are clamped below it)
 };
@@ -199,6 +200,7 @@ __device__ __forceinline__ SeqGeom seq_geom_t(const Dims &D, const int32_t *kv_o
         if (len > D.max_pages * kPage) len = D.max_pages * kPage;
         g.off = 0;
         g.gp0 = 0;
+        g.mp0 = (int64_t)s * (D.max_pages > 0 ? D.max_pages : 1);
         g.pt = D.page_table + (size_t)s * (D.max_pages > 0 ? D.max_pages : 1);
         g.len = len;
     } else {
@@ -212,6 +214,7 @@ __device__ __forceinline__ SeqGeom seq_geom_t(const Dims &D, const int32_t *kv_o
         if (off + len > D.T) len = static_cast<int>(D.T - off);
         g.off = off;
         g.gp0 = off / kPage;
+        g.mp0 = g.gp0;
         g.pt = nullptr;
         g.len = len;
     }
@@ -236,6 +239,13 @@ __device__ __forceinline__ int64_t phys_page(const SeqGeom &g, int p) {
     }
     return g.gp0 + p;
 }
+// Metadata page of the sequence's page p.  Page metadata is kept per
+// (sequence, page): at the page's cache position in the contiguous layout,
+// from s * max_pages for sequence s with a page table -- so the metadata of a
+// run of a sequence's pages lies side by side in either layout, however the
+// table scatters the pages themselves.
+__device__ __forceinline__ int64_t meta_page(const SeqGeom &g, int p) { return g.mp0 + p; }
+
 // The same with the layout fixed at compile time (the hot kernels are built
 // for both, so the contiguous layout's code carries no page-table branch).
 template <bool PAGED>

@@ -4,7 +4,10 @@
 // reading of it).
 //
 // Layout (library-owned).  Pages are grouped per KV head into tiles of 64
-// consecutive global pages (global page = kv_off/16 + local page).  Inside a
+// consecutive metadata pages: sequence s's page p is metadata page kv_off/16
+// + p in the contiguous layout and s * max_pages + p with a page table (which
+// reads the keys through the table but keeps the metadata of a sequence's
+// pages side by side, so scoring reads whole tiles either way).  Inside a
 // tile, the metadata of chunk c of every page's dimensions is stored for the
 // 64 pages back to back, 16 bytes per page, so a wave whose lane = page reads
 // one chunk with one fully coalesced 1 KiB load:
@@ -12,9 +15,9 @@
 //   fp32: chunk = 2 dimensions, (max_0, min_0, max_1, min_1)
 // That chunk is also exactly the B operand a lane supplies to
 // v_mfma_f32_16x16x32_bf16 for 8 consecutive k-slots (max_i, min_i pairs).
-// After the min/max part follows, per KV head and global page, the largest
+// After the min/max part follows, per KV head and metadata page, the largest
 // |key| element of the page (fp32), which bounds the error of MFMA scoring.
-// Last comes a page-major copy of the min/max part: per KV head and global
+// Last comes a page-major copy of the min/max part: per KV head and metadata
 // page, the page's chunks 0 .. DIM/DPC - 1 back to back (DIM*2 element sizes
 // contiguous), for the exact bound of selection, whose lanes each take one
 // page scattered over the prefix: one page then fills whole cache lines
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(256) void k_page_meta(Dims D, const T *__restrict__
 #pragma unroll
     for (int o = 1; o < CPR; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
     if (!live) return;
-    const int64_t gp = phys_page(sg, pl);
+    const int64_t gp = meta_page(sg, pl);
     const int64_t tile = gp / kTile;
     const int lane = static_cast<int>(gp % kTile);
 #pragma unroll

@@ -81,7 +81,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {
 
 // Page groups: the pages of a sequence are bounded in groups of 64 counted
 // from its first page (group x: pages 64x .. 64x + 63), whatever their place
-// in the metadata tiles, so a 64K prefix has exactly 64 groups.  The global
+// in the metadata tiles, so a 64K prefix has exactly 64 groups.  Metadata
 // page gp's chunk c (of nch per page) in the tile layout of KV head g, and
 // the page's largest |key|; gp is clamped into the metadata.
 __device__ __forceinline__ const uint4 *meta_chunk(const uint4 *meta, const Dims &D, int g,
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             pl[cb] = bx * kTile + cb * 16 + l16;
-            gpl[cb] = phys_page(sg, pl[cb]);
+            gpl[cb] = meta_page(sg, pl[cb]);
             amax[cb] = meta_amax(meta, D, g, gpl[cb]);
         }
         const uint32_t *q16 = W.qsel16 + (size_t)sgi * D.Rs16 * DIM;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void k_score(Dims D, const uint4 *__restrict__
         // fp32 storage: lane = page, any summation order (the interval absorbs it)
         const int p = bx * kTile + lane;
         const bool valid = p < sg.pages;
-        const int64_t gp = phys_page(sg, p);
+        const int64_t gp = meta_page(sg, p);
         const float am = meta_amax(meta, D, g, gp);
         const uint4 *mt = meta_chunk(meta, D, g, gp, 0, NCH);  // chunk c at mt[c * kTile]
         const float *q32 = W.qsel32 + (size_t)sgi * R1 * DIM * 2;
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256 * TPW) void k_score_prep(Dims D, const uint16_t
     const int l16 = lane & 15, lg = lane >> 4;
     const int pl = wt * kTile + 16 * (w % 4) + l16;  // the lane's page in the sequence
     uint4 bop[KS];
-    const int64_t gpl = phys_page_t<PAGED>(sg, pl);
+    const int64_t gpl = meta_page(sg, pl);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) bop[kk] = *meta_chunk(meta, D, g, gpl, 4 * kk + lg, NCH);
     const float amax = meta_amax(meta, D, g, gpl);
@@ -639,7 +639,7 @@ struct SelectDbg {
 // (which is not free even for a lone wave).
 __device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// The exact chain for global page gp (contract of include/losa.h), computed
+// The exact chain for metadata page gp (contract of include/losa.h), computed
 // by a group of LPC consecutive lanes: lane j of the group loads chunks
 // j*NCH/LPC .. of the page's metadata (from the page-major copy) before the
 // chain starts, and the chain runs through the group in LPC phases -- in phase
@@ -836,7 +836,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                     for (int e4 = 0; e4 < 4; ++e4) {
                         const int p = 256 * jj + 4 * lane + e4;
                         const float e =
-                            kBoundRel * qa * meta_amax(meta, D, g, phys_page_t<PAGED>(sg, min(p, sg.pages - 1))) + kBoundAbs;
+                            kBoundRel * qa * meta_amax(meta, D, g, meta_page(sg, min(p, sg.pages - 1))) + kBoundAbs;
                         const float lo = (hx[e4] - 2.0f * e) - (fabsf(hx[e4]) + 2.0f * e) * (1.0f / 2097152.0f);
                         if (p < sg.pages) lmax = fmaxf(lmax, lo);
                     }
@@ -875,7 +875,7 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
             // (lanes past the groups stay idle: a load's cost grows with its active lanes)
             float u = 0.0f;
             if (lane < LPC * n)
-                u = exact_bound<DIM, BF>(meta, D, g, phys_page_t<PAGED>(sg, pc), qw, lane);
+                u = exact_bound<DIM, BF>(meta, D, g, meta_page(sg, pc), qw, lane);
             const bool mine = lane % LPC == LPC - 1 && lane / LPC < n;
             const uint64_t cand = mine ? (static_cast<uint64_t>(ord_key(u)) << 32) |
                                              static_cast<uint32_t>(~static_cast<uint32_t>(pc))

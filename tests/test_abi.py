@@ -50,7 +50,8 @@ def test_sizes(cfg):
     cap = min(max_pages, cfg.group * cfg.n_active * (cfg.budget // 16))
     assert L.union_capacity(sh) == max(cap, 1)
     s_t = 2 if cfg.dtype == "bf16" else 4
-    tiles = (T // 16 + 63) // 64
+    # metadata pages: the cache's pages or max_pages per sequence, whichever is more
+    tiles = (max(T // 16, cfg.n_seq * max_pages) + 63) // 64
     # min/max pairs per (page, dimension), then one fp32 max |key| per page
     assert L.page_meta_bytes(sh) == cfg.n_kvhead * tiles * 64 * (2 * cfg.head_dim * 2 * s_t + 4)
     ws = L.workspace_bytes(sh)

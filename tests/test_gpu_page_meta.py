@@ -24,10 +24,13 @@ def _gpu():
     L.load()
 
 
-def decode(meta: np.ndarray, cfg, kv_tokens: int):
-    """(kmin, kmax) [Hk][T/16][d] and the largest |key| [Hk][T/16] of every global page."""
+def decode(meta: np.ndarray, cfg, kv_tokens: int, max_prefix_len: int):
+    """(kmin, kmax) [Hk][M][d] and the largest |key| [Hk][M] of every metadata
+    page, M = max(T/16, n_seq * max_pages): a sequence's page p is metadata page
+    kv_off/16 + p (contiguous layout) or s * max_pages + p (page table)."""
     Hk, d = cfg.n_kvhead, cfg.head_dim
-    TP = kv_tokens // cfg.page_size
+    max_pages = (max_prefix_len + cfg.page_size - 1) // cfg.page_size
+    TP = max(kv_tokens // cfg.page_size, cfg.n_seq * max_pages)
     n_tiles = (TP + 63) // 64
     bf = cfg.dtype == "bf16"
     nch = d // (4 if bf else 2)
@@ -70,7 +73,8 @@ def test_page_meta_matches_oracle(name, kw):
     ls = LayerState.from_layer(lay)
     ls.build_page_meta()
     torch.cuda.synchronize()
-    kmin, kmax, amax = decode(ls.page_meta.cpu().numpy(), cfg, lay.kv_tokens)
+    kmin, kmax, amax = decode(ls.page_meta.cpu().numpy(), cfg, lay.kv_tokens,
+                              int(ls.shape.max_prefix_len))
     orc = Oracle(cfg, lay.kv_off, lay.prefix_len, lay.kv_tokens, lay.k_cache, lay.v_cache)
     omin, omax = orc.page_meta()
     for s, (gp0, n) in enumerate(seq_pages(lay)):

@@ -83,16 +83,20 @@ def test_paged_page_meta_matches_oracle():
                     prefix_len=lay.prefix_len, page_table=pt)
     ls.build_page_meta()
     torch.cuda.synchronize()
-    kmin, kmax, amax = decode(ls.page_meta.cpu().numpy(), cfg, k_pool.shape[1])
+    maxp_len = int(ls.shape.max_prefix_len)
+    kmin, kmax, amax = decode(ls.page_meta.cpu().numpy(), cfg, k_pool.shape[1], maxp_len)
     orc = Oracle(cfg, lay.kv_off, lay.prefix_len, lay.kv_tokens, lay.k_cache, lay.v_cache)
     omin, omax = orc.page_meta()
     P = cfg.page_size
+    max_pages = (maxp_len + P - 1) // P
     for s in range(cfg.n_seq):
         n = (int(lay.prefix_len[s]) + P - 1) // P
         gp0 = int(lay.kv_off[s]) // P
-        phys = pt[s, :n]
-        assert np.array_equal(kmin[:, phys].view(np.uint32), omin[:, gp0:gp0 + n].view(np.uint32)), s
-        assert np.array_equal(kmax[:, phys].view(np.uint32), omax[:, gp0:gp0 + n].view(np.uint32)), s
+        mp = slice(s * max_pages, s * max_pages + n)  # the sequence's metadata pages
+        assert np.array_equal(kmin[:, mp].view(np.uint32), omin[:, gp0:gp0 + n].view(np.uint32)), s
+        assert np.array_equal(kmax[:, mp].view(np.uint32), omax[:, gp0:gp0 + n].view(np.uint32)), s
+        want = np.maximum(np.abs(omin[:, gp0:gp0 + n]), np.abs(omax[:, gp0:gp0 + n])).max(axis=2)
+        assert np.array_equal(amax[:, mp], want), s
 
 
 def test_paged_update_after_commit():
