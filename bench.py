@@ -784,17 +784,34 @@ def main():
     dominant = max((k for k in kernels if "bytes_per_launch" in kernels[k]),
                    key=lambda k: kernels[k]["us_per_layer_block"], default=None)
 
+    def read_floor(nbytes):
+        """The pure-read probe of the nearest size at or above nbytes (rocprofv3
+        duration where the committed summary matches, else its events)."""
+        for mib, _ in FLOOR_READS:
+            if (mib << 20) >= nbytes:
+                us = rp.get(f"probe_read_{mib}MiB")
+                src = "rocprofv3" if us is not None else "hip events"
+                if us is None:
+                    us = floors["read"][f"{mib}MiB"]["us_events"]
+                return {"probe": f"pure read of {mib} MiB (cold)", "us": us, "duration_source": src,
+                        "kernel_over_probe": None}
+        return None
+
     def roofline(name):
         if name is None or name not in kernels:
             return None
         k = kernels[name]
+        fl = read_floor(k["bytes_per_launch"])
+        if fl is not None:
+            fl["kernel_over_probe"] = k["avg_us"] / fl["us"]
         return {"kernel": name, "bound": "hbm", "achieved": k["achieved_gbps"],
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k["frac_of_peak"],
                 "traffic": traffic_from_profile(name),
                 "bytes_per_launch": k["bytes_per_launch"], "avg_launch_us": k["avg_us"],
                 "avg_launch_us_events": k["avg_us_events"],
                 "duration_source": (f"rocprofv3 kernel trace, {rp_path}" if name in rp
-                                    else "hip events around the kernel")}
+                                    else "hip events around the kernel"),
+                "read_floor": fl}
 
     rec = {
         "metric": METRIC,
