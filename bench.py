@@ -18,7 +18,7 @@ bit against an eager block (--no-graph times eager launches; the eager rate is
 reported beside).  Events before, between and after the two graphs give
 dense_step_us and sparse_step_us, so value = (dense + 7 sparse) / 8 up to the
 events' own cost.  Per-kernel durations come from the committed rocprofv3
-summary of this workload (profiles/kernels_<workload>.json) wherever the
+summary of this workload (profiles/kernels_long_64k_b<budget>_a<|A|>.json) wherever the
 digest of the kernel's sources matches, else from HIP events the library
 records between its launches in a second timed pass of K blocks (both are
 reported); then the roofline of the dominant kernel, and the CPU oracle timed
@@ -759,7 +759,8 @@ def main():
     # layer-block; durations from the committed rocprofv3 summary of this
     # workload where it describes the current sources, else from the events
     # (which add the latency of an event record, about 1 us, to every kernel)
-    rp, rp_path = rocprof_durations(cfg.name)
+    # (the summaries are named for the workload: long_64k_b<budget>_a<|A|>)
+    rp, rp_path = rocprof_durations(f"long_64k_b{cfg.budget}_a{cfg.n_active}")
     spec = {
         "page_score": (stages["sparse"]["score"], meta_bytes, STEPS_PER_BLOCK - 1),
         "page_select": (stages["sparse"]["select"], 0, STEPS_PER_BLOCK - 1),
