@@ -64,7 +64,7 @@ def load(path: str = LIB_PATH):
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+        raise RuntimeError(f"{path} is missing: build it with python -m sparse_attention_block_amd.build")
     lib = ctypes.CDLL(path)
     S = POINTER(LosaShape)
     lib.losa_status_string.argtypes = [c_int]
