@@ -841,9 +841,6 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
                         if (p < sg.pages) lmax = fmaxf(lmax, lo);
                     }
                 }
-                // at most 16 of the page maxima in flight: the upper ends
-                // already take 64 registers
-                if (jj % 4 == 3) __builtin_amdgcn_sched_barrier(0);
             }
             gm = lmax == -__builtin_huge_valf() ? 0u : ord_key(lmax);
         }
