@@ -99,6 +99,126 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // from any overflow in the fp32 sums.
 constexpr float kLazyRescale = 8.0f;
 
+// The attention of the wave's row tiles over NP pages given the V^T operands
+// in MFMA layout: vpair[n/2][e] for page pairs (NP even; the A operand of
+// v_mfma_f32_16x16x32_bf16 for output block e), vop[n][e] for single pages
+// (v_mfma_f32_16x16x16bf16_1k); the output layout of block e is the caller's.
+// MSUM (page pairs only): the row sums of the rounded weights come from one
+// more MFMA with an all-ones A operand, accumulated in l4[i] (every element
+// the row's sum over all lanes' tokens; l_run is then unused), and the scale
+// is applied inside the exponent's fused multiply-add -- fewer vector
+// instructions per page pair.
+template <int DIM, int RTW, int NP, bool MASK = false, bool MSUM = false>
+__device__ __forceinline__ void attend_core(const uint4 (&kop)[NP][DIM / 32],
+                                            const u32x4_t (&vpair)[NP % 2 == 0 ? NP / 2 : 1][DIM / 16],
+                                            const short4_t (&vop)[NP % 2 == 0 ? 1 : NP][DIM / 16],
+                                            const int (&valid)[NP],
+                                            const uint4 (&qop)[RTW][DIM / 32],
+                                            const bool (&rt_ok)[RTW], float scale_log2,
+                                            float4_t (&oacc)[RTW][DIM / 16], float (&m_run)[RTW],
+                                            float (&l_run)[RTW], int lg,
+                                            const uint64_t (&rmask)[NP] = {},
+                                            const int (&row0)[RTW] = {}, float4_t *l4 = nullptr) {
+    constexpr int KSTEPS = DIM / 32, DPL = DIM / 16;
+    static_assert(!MSUM || NP % 2 == 0, "MFMA row sums are written for page pairs");
+    bool full[NP];
+#pragma unroll
+    for (int n = 0; n < NP; ++n) full[n] = valid[n] >= kPage;  // uniform
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        if (!rt_ok[i]) break;
+        float sv[NP][4];
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, kop[n][kk]), __builtin_bit_cast(bf16x8_t, qop[i][kk]),
+                    sacc, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[n][j] = MSUM ? sacc[j] : sacc[j] * scale_log2;
+            if (!full[n]) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (4 * lg + j >= valid[n]) sv[n][j] = -__builtin_huge_valf();
+            }
+            if constexpr (MASK) {  // rows that did not select the page attend none of it
+                const int l16 = __lane_id() & 15;
+                if (!((rmask[n] >> (row0[i] + l16)) & 1ull)) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sv[n][j] = -__builtin_huge_valf();
+                }
+            }
+        }
+        float mp = -__builtin_huge_valf();
+#pragma unroll
+        for (int n = 0; n < NP; ++n) mp = fmaxf(mp, fmaxf(fmaxf(sv[n][0], sv[n][1]), fmaxf(sv[n][2], sv[n][3])));
+        mp = shfl_max32(mp);
+        if constexpr (MSUM) mp *= scale_log2;  // (a positive scale keeps the maximum)
+        // Lazy reference: a row's reference m_run moves to its running maximum
+        // only once a score exceeds it by more than kLazyRescale (log2 units), so
+        // weights stay below 2^kLazyRescale and the output is rescaled rarely
+        // (softmax does not depend on the reference; the partial keeps it).
+        const float mx = fmaxf(m_run[i], mp);
+        if (__ballot(mx > m_run[i] + kLazyRescale) != 0ull) {  // uniform branch
+            const float mn = mx > m_run[i] + kLazyRescale ? mx : m_run[i];
+            // (with masks a row's reference may still be -inf: it keeps factor 1)
+            const float alpha = MASK && mn == m_run[i] ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - mn);
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) oacc[i][e] *= alpha;
+            if constexpr (MSUM) l4[i] *= alpha;
+            else l_run[i] *= alpha;
+            m_run[i] = mn;
+        }
+        // (with masks a row may have seen no score yet: its weights are zero)
+        const float mn = MASK && m_run[i] == -__builtin_huge_valf() ? 0.0f : m_run[i];
+        u32x2_t pw[NP];  // the lane's weights of page n (tokens 4*lg .. +3), bf16
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                x[j] = MSUM ? __builtin_fmaf(sv[n][j], scale_log2, -mn) : sv[n][j] - mn;
+            const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(x[0])),
+                                  static_cast<__bf16>(__builtin_amdgcn_exp2f(x[1]))};
+            const bf16x2_t p23 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(x[2])),
+                                  static_cast<__bf16>(__builtin_amdgcn_exp2f(x[3]))};
+            const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
+            if constexpr (!MSUM)
+                l_run[i] += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
+            pw[n] = u32x2_t{w01, w23};
+        }
+        if constexpr (NP % 2 == 0) {
+            // pages n and n+1 in one v_mfma_f32_16x16x32_bf16: its k index
+            // 8*lg + c stands for token 4*lg + c%4 of page n + c/4, in both
+            // operands (the sum over k does not depend on the order)
+#pragma unroll
+            for (int n = 0; n < NP; n += 2) {
+                const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[n].x, pw[n].y, pw[n + 1].x, pw[n + 1].y});
+#pragma unroll
+                for (int e = 0; e < DPL; ++e)
+                    oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, vpair[n / 2][e]), pop, oacc[i][e], 0, 0, 0);
+                if constexpr (MSUM) {  // bf16 1.0 in every k slot: the weights' sum per row
+                    constexpr uint32_t kOnes = 0x3f803f80u;
+                    l4[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, u32x4_t{kOnes, kOnes, kOnes, kOnes}), pop, l4[i], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NP; ++n) {
+                const short4_t pop = __builtin_bit_cast(short4_t, pw[n]);
+#pragma unroll
+                for (int e = 0; e < DPL; ++e)
+                    oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[n][e], pop, oacc[i][e], 0, 0, 0);
+            }
+        }
+    }
+}
+
+
 // NP pages of 16 tokens for the wave's row tiles i (those with rt_ok[i]):
 // S^T = K.Q^T with v_mfma_f32_16x16x32_bf16, online softmax in log2 units over
 // the NP pages together, then O^T += V^T.P: two pages per
@@ -170,86 +290,8 @@ __device__ __forceinline__ void attend_pages(const uint4 (&kop)[NP][DIM / 32],
                 vop[n][e] = __builtin_bit_cast(short4_t, u32x2_t{tok2(n, 0, e) & m0, tok2(n, 2, e) & m1});
         }
     }
-#pragma unroll
-    for (int i = 0; i < RTW; ++i) {
-        if (!rt_ok[i]) break;
-        float sv[NP][4];
-#pragma unroll
-        for (int n = 0; n < NP; ++n) {
-            float4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk)
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, kop[n][kk]), __builtin_bit_cast(bf16x8_t, qop[i][kk]),
-                    sacc, 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sv[n][j] = sacc[j] * scale_log2;
-            if (!full[n]) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (4 * lg + j >= valid[n]) sv[n][j] = -__builtin_huge_valf();
-            }
-            if constexpr (MASK) {  // rows that did not select the page attend none of it
-                const int l16 = __lane_id() & 15;
-                if (!((rmask[n] >> (row0[i] + l16)) & 1ull)) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sv[n][j] = -__builtin_huge_valf();
-                }
-            }
-        }
-        float mp = -__builtin_huge_valf();
-#pragma unroll
-        for (int n = 0; n < NP; ++n) mp = fmaxf(mp, fmaxf(fmaxf(sv[n][0], sv[n][1]), fmaxf(sv[n][2], sv[n][3])));
-        mp = shfl_max32(mp);
-        // Lazy reference: a row's reference m_run moves to its running maximum
-        // only once a score exceeds it by more than kLazyRescale (log2 units), so
-        // weights stay below 2^kLazyRescale and the output is rescaled rarely
-        // (softmax does not depend on the reference; the partial keeps it).
-        const float mx = fmaxf(m_run[i], mp);
-        if (__ballot(mx > m_run[i] + kLazyRescale) != 0ull) {  // uniform branch
-            const float mn = mx > m_run[i] + kLazyRescale ? mx : m_run[i];
-            // (with masks a row's reference may still be -inf: it keeps factor 1)
-            const float alpha = MASK && mn == m_run[i] ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - mn);
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) oacc[i][e] *= alpha;
-            l_run[i] *= alpha;
-            m_run[i] = mn;
-        }
-        // (with masks a row may have seen no score yet: its weights are zero)
-        const float mn = MASK && m_run[i] == -__builtin_huge_valf() ? 0.0f : m_run[i];
-        u32x2_t pw[NP];  // the lane's weights of page n (tokens 4*lg .. +3), bf16
-#pragma unroll
-        for (int n = 0; n < NP; ++n) {
-            const bf16x2_t p01 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][0] - mn)),
-                                  static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][1] - mn))};
-            const bf16x2_t p23 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][2] - mn)),
-                                  static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][3] - mn))};
-            const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
-            l_run[i] += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
-            pw[n] = u32x2_t{w01, w23};
-        }
-        if constexpr (NP % 2 == 0) {
-            // pages n and n+1 in one v_mfma_f32_16x16x32_bf16: its k index
-            // 8*lg + c stands for token 4*lg + c%4 of page n + c/4, in both
-            // operands (the sum over k does not depend on the order)
-#pragma unroll
-            for (int n = 0; n < NP; n += 2) {
-                const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[n].x, pw[n].y, pw[n + 1].x, pw[n + 1].y});
-#pragma unroll
-                for (int e = 0; e < DPL; ++e)
-                    oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, vpair[n / 2][e]), pop, oacc[i][e], 0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int n = 0; n < NP; ++n) {
-                const short4_t pop = __builtin_bit_cast(short4_t, pw[n]);
-#pragma unroll
-                for (int e = 0; e < DPL; ++e)
-                    oacc[i][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[n][e], pop, oacc[i][e], 0, 0, 0);
-            }
-        }
-    }
+    attend_core<DIM, RTW, NP, MASK>(kop, vpair, vop, valid, qop, rt_ok, scale_log2, oacc, m_run, l_run,
+                                    lg, rmask, row0);
 }
 
 // Union of the selected pages of one (sequence, KV head) -- the rows' lists
@@ -805,6 +847,55 @@ struct GroupReads<128> {
     }
 };
 
+// The K operands of two LDS page slots as GroupReads<128> reads them, and
+// the V^T operands with gfx950's transposing read ds_read_b64_tr_b16: in each
+// group of 16 lanes, lane a + 4k points at 4 consecutive dims of row k of the
+// group's 4 token rows, and lane 4a + e receives dim e of the vectors of lanes
+// a, a + 4, a + 8, a + 12.  So lane l gets one dim of tokens 4*(l/16) .. +3,
+// the A operand of the PV product for its output dims: no byte permutes.
+// av[f]: the lane's byte address for output block f (dims 16 f ..) in the
+// first slot; the second slot is 8192 bytes on.
+struct GroupReadsTr128 {
+    static __device__ __forceinline__ void read(const uint32_t (&ak)[4], const uint32_t (&av)[8],
+                                                u32x4_t (&k)[2][4], u32x2_t (&v)[2][8]) {
+        asm volatile(
+            "ds_read_b128 %0, %24\n\t"
+            "ds_read_b128 %1, %25\n\t"
+            "ds_read_b128 %2, %26\n\t"
+            "ds_read_b128 %3, %27\n\t"
+            "ds_read_b128 %4, %24 offset:8192\n\t"
+            "ds_read_b128 %5, %25 offset:8192\n\t"
+            "ds_read_b128 %6, %26 offset:8192\n\t"
+            "ds_read_b128 %7, %27 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %8, %28\n\t"
+            "ds_read_b64_tr_b16 %9, %29\n\t"
+            "ds_read_b64_tr_b16 %10, %30\n\t"
+            "ds_read_b64_tr_b16 %11, %31\n\t"
+            "ds_read_b64_tr_b16 %12, %32\n\t"
+            "ds_read_b64_tr_b16 %13, %33\n\t"
+            "ds_read_b64_tr_b16 %14, %34\n\t"
+            "ds_read_b64_tr_b16 %15, %35\n\t"
+            "ds_read_b64_tr_b16 %16, %28 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %17, %29 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %18, %30 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %19, %31 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %20, %32 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %21, %33 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %22, %34 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %23, %35 offset:8192\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[0][2]), "=&v"(k[0][3]),
+              "=&v"(k[1][0]), "=&v"(k[1][1]), "=&v"(k[1][2]), "=&v"(k[1][3]),
+              "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
+              "=&v"(v[0][4]), "=&v"(v[0][5]), "=&v"(v[0][6]), "=&v"(v[0][7]),
+              "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]),
+              "=&v"(v[1][4]), "=&v"(v[1][5]), "=&v"(v[1][6]), "=&v"(v[1][7])
+            : "v"(ak[0]), "v"(ak[1]), "v"(ak[2]), "v"(ak[3]),
+              "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]), "v"(av[4]), "v"(av[5]), "v"(av[6]), "v"(av[7])
+            : "memory");
+    }
+};
+
 template <>
 struct GroupReads<64> {
     static __device__ __forceinline__ void read(const uint32_t (&ak)[2], const uint32_t (&av)[4],
@@ -840,6 +931,7 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
                                                                const int32_t *__restrict__ prefix_len,
                                                                Work W) {
     constexpr int KSTEPS = DIM / 32, DPL = DIM / 16, CPT = DIM / 8;
+    constexpr bool TR = DIM == 128;          // V^T operands by transposing LDS reads
     constexpr int NCK = 16 * CPT;            // 16-byte chunks per page and tensor
     constexpr int NT = 64 * NW;              // threads
     constexpr int LPT = 2 * NCK / NT;        // direct loads per thread per page (K and V)
@@ -888,7 +980,11 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
 #pragma unroll
     for (int h = 0; h < LPT; ++h) {
         const int L = (h * NW + w) * 64 + lane, cq = L % NCK;
-        const int t = cq / CPT, c = (cq % CPT) ^ (t & (CPT - 1));
+        // K: chunks XOR-swizzled by the token row; V with the transposing
+        // reads (d = 128): chunk pairs (32 bytes) XOR-swizzled by the row's
+        // low 3 bits
+        const int t = cq / CPT;
+        const int c = (L < NCK || !TR) ? (cq % CPT) ^ (t & (CPT - 1)) : (cq % CPT) ^ ((t & 7) << 1);
         src_h[h] = (L < NCK ? kc : vc) + (size_t)g * D.T * DIM + t * DIM + c * 8;
     }
     // the cache row of each page of the chunk: lane i holds page first + i's
@@ -926,6 +1022,9 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     bool rt_ok[RTW];
 #pragma unroll
     for (int i = 0; i < RTW; ++i) rt_ok[i] = w + NW * i < n_rt;
+    float4_t l4[RTW];  // (transposing reads) the rows' weight sums from the MFMA
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) l4[i] = float4_t{0.f, 0.f, 0.f, 0.f};
     // the lane's operand chunks inside a slot (bytes): K chunk (token l%16,
     // dims 32*kk + 8*(l/16) ..) and V chunk (token 4*(l/16) + j, dims DPL*(l%16) ..)
     static_assert(NG == 2, "operand reads are written for page pairs");
@@ -936,6 +1035,15 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     for (int kk = 0; kk < KSTEPS; ++kk) ak[kk] = ring + 16u * swz<DIM>(l16, 4 * kk + lg);
 #pragma unroll
     for (int j = 0; j < 4; ++j) av[j] = ring + 16u * (NCK + swz<DIM>(4 * lg + j, (DPL * l16) / 8));
+    // (transposing reads) the lane's V address per output block f: token row
+    // 4*lg + l16/4, dims 16 f + 4*(l16 % 4) .. +3, in the pair-swizzled layout
+    uint32_t avt[TR ? 8 : 1];
+    if constexpr (TR) {
+        const int t = 4 * lg + (l16 >> 2), a = l16 & 3;
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+            avt[f] = ring + 16u * NCK + 256u * t + 32u * static_cast<uint32_t>(f ^ (t & 7)) + 8u * a;
+    }
 
     // Group at pages pi .. pi+NG-1 (slots pi % NS ..): loads are issued in page
     // order and complete in order, and when the group is due the pages issued
@@ -955,9 +1063,45 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
         }
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t sbase = static_cast<uint32_t>((pi % NS) * SLOT_BYTES);
-        uint32_t akk[KSTEPS], avv[4];
+        uint32_t akk[KSTEPS];
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) akk[kk] = ak[kk] + sbase;
+        if constexpr (TR) {
+            uint32_t avv[8];
+#pragma unroll
+            for (int f = 0; f < 8; ++f) avv[f] = avt[f] + sbase;
+            u32x4_t kraw[NG][KSTEPS];
+            u32x2_t vtr[NG][8];
+            GroupReadsTr128::read(akk, avv, kraw, vtr);
+            uint4 kop[NG][KSTEPS];
+            int valid[NG];
+            u32x2_t vm[NG];  // token masks (tokens 4*lg .. +3 past the prefix zeroed)
+#pragma unroll
+            for (int n = 0; n < NG; ++n) {
+                valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + pi + n) * kPage) : 0;
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk) kop[n][kk] = __builtin_bit_cast(uint4, kraw[n][kk]);
+                vm[n] = u32x2_t{(4 * lg + 0 < valid[n] ? 0x0000ffffu : 0u) | (4 * lg + 1 < valid[n] ? 0xffff0000u : 0u),
+                                (4 * lg + 2 < valid[n] ? 0x0000ffffu : 0u) | (4 * lg + 3 < valid[n] ? 0xffff0000u : 0u)};
+            }
+            // the PV operand of block f: page pi's tokens, then page pi + 1's
+            u32x4_t vpair[1][DPL];
+            const bool full2 = valid[0] >= kPage && valid[1] >= kPage;  // uniform
+#pragma unroll
+            for (int f = 0; f < DPL; ++f) {
+                u32x2_t a0 = vtr[0][f], a1 = vtr[1][f];
+                if (!full2) {
+                    a0 &= vm[0];
+                    a1 &= vm[1];
+                }
+                vpair[0][f] = u32x4_t{a0.x, a0.y, a1.x, a1.y};
+            }
+            short4_t vop_none[1][DPL];
+            attend_core<DIM, RTW, NG, false, true>(kop, vpair, vop_none, valid, qop, rt_ok, D.scale_log2,
+                                                   oacc, m_run, l_run, lg, {}, {}, l4);
+            continue;
+        }
+        uint32_t avv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) avv[j] = av[j] + sbase;
         u32x4_t kraw[NG][KSTEPS], vraw[NG][4];
@@ -990,9 +1134,10 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     // no direct load may still be writing LDS when the workgroup ends
     wait_vmcnt<0>();
 #pragma unroll
-    for (int i = 0; i < RTW; ++i) l_run[i] = shfl_sum32(l_run[i]);
+    for (int i = 0; i < RTW; ++i) l_run[i] = TR ? l4[i][0] : shfl_sum32(l_run[i]);
 
-    // Lane l holds, for row l%16, dims DPL*(4*lg + j) + e.
+    // Lane l holds, for row l%16, dims DPL*(4*lg + j) + e (transposing reads:
+    // dims 16 e + 4*lg + j).
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
         const int rt = w + NW * i;
@@ -1005,6 +1150,13 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
             W.part_ml[pb * 2 + 1] = l_run[i];
         }
         float *dst = W.part_acc + pb * DIM;
+        if constexpr (TR) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                *reinterpret_cast<float4 *>(dst + 16 * e + 4 * lg) =
+                    make_float4(oacc[i][e][0], oacc[i][e][1], oacc[i][e][2], oacc[i][e][3]);
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float tmp[DPL];
