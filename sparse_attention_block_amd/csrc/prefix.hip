@@ -814,9 +814,10 @@ __device__ __forceinline__ int swz(int t, int c) {
     return t * CPT + (c ^ (t & (CPT - 1)));
 }
 
-// The K and V operands of two LDS page slots (slot stride PS bytes) in one
-// block of ds_read_b128: ak[kk] / av[j] are the lane's byte addresses of K
-// chunk kk and V chunk j in the first slot.  Written as one asm block that
+// The K and V operands of two adjacent LDS page slots in one block of
+// ds_read_b128: ak[kk] / av[j] are the lane's byte addresses of K chunk kk and
+// V chunk j in the ring's first slot, and the pair starts SB bytes into the
+// ring (an immediate offset, so no address arithmetic per pair).  Written as one asm block that
 // waits for its own reads, so that the compiler, which cannot tell the ring's
 // slots apart, does not make the reads wait for every direct load in flight.
 // (The low 32 bits of a generic pointer into LDS are its LDS address.)
@@ -825,24 +826,25 @@ struct GroupReads;
 
 template <>
 struct GroupReads<128> {
+    template <uint32_t SB>
     static __device__ __forceinline__ void read(const uint32_t (&ak)[4], const uint32_t (&av)[4],
                                                 u32x4_t (&k)[2][4], u32x4_t (&v)[2][4]) {
         asm volatile(
-            "ds_read_b128 %0, %16\n\tds_read_b128 %1, %17\n\t"
-            "ds_read_b128 %2, %18\n\tds_read_b128 %3, %19\n\t"
-            "ds_read_b128 %4, %16 offset:8192\n\tds_read_b128 %5, %17 offset:8192\n\t"
-            "ds_read_b128 %6, %18 offset:8192\n\tds_read_b128 %7, %19 offset:8192\n\t"
-            "ds_read_b128 %8, %20\n\tds_read_b128 %9, %21\n\t"
-            "ds_read_b128 %10, %22\n\tds_read_b128 %11, %23\n\t"
-            "ds_read_b128 %12, %20 offset:8192\n\tds_read_b128 %13, %21 offset:8192\n\t"
-            "ds_read_b128 %14, %22 offset:8192\n\tds_read_b128 %15, %23 offset:8192\n\t"
+            "ds_read_b128 %0, %16 offset:%24\n\tds_read_b128 %1, %17 offset:%24\n\t"
+            "ds_read_b128 %2, %18 offset:%24\n\tds_read_b128 %3, %19 offset:%24\n\t"
+            "ds_read_b128 %4, %16 offset:%25\n\tds_read_b128 %5, %17 offset:%25\n\t"
+            "ds_read_b128 %6, %18 offset:%25\n\tds_read_b128 %7, %19 offset:%25\n\t"
+            "ds_read_b128 %8, %20 offset:%24\n\tds_read_b128 %9, %21 offset:%24\n\t"
+            "ds_read_b128 %10, %22 offset:%24\n\tds_read_b128 %11, %23 offset:%24\n\t"
+            "ds_read_b128 %12, %20 offset:%25\n\tds_read_b128 %13, %21 offset:%25\n\t"
+            "ds_read_b128 %14, %22 offset:%25\n\tds_read_b128 %15, %23 offset:%25\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[0][2]), "=&v"(k[0][3]),
               "=&v"(k[1][0]), "=&v"(k[1][1]), "=&v"(k[1][2]), "=&v"(k[1][3]),
               "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
               "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
             : "v"(ak[0]), "v"(ak[1]), "v"(ak[2]), "v"(ak[3]),
-              "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3])
+              "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]), "i"(SB), "i"(SB + 8192u)
             : "memory");
     }
 };
@@ -854,35 +856,36 @@ struct GroupReads<128> {
 // a, a + 4, a + 8, a + 12.  So lane l gets one dim of tokens 4*(l/16) .. +3,
 // the A operand of the PV product for its output dims: no byte permutes.
 // av[f]: the lane's byte address for output block f (dims 16 f ..) in the
-// first slot; the second slot is 8192 bytes on.
+// ring's first slot; the pair's slots start SB and SB + 8192 bytes on.
 struct GroupReadsTr128 {
+    template <uint32_t SB>
     static __device__ __forceinline__ void read(const uint32_t (&ak)[4], const uint32_t (&av)[8],
                                                 u32x4_t (&k)[2][4], u32x2_t (&v)[2][8]) {
         asm volatile(
-            "ds_read_b128 %0, %24\n\t"
-            "ds_read_b128 %1, %25\n\t"
-            "ds_read_b128 %2, %26\n\t"
-            "ds_read_b128 %3, %27\n\t"
-            "ds_read_b128 %4, %24 offset:8192\n\t"
-            "ds_read_b128 %5, %25 offset:8192\n\t"
-            "ds_read_b128 %6, %26 offset:8192\n\t"
-            "ds_read_b128 %7, %27 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %8, %28\n\t"
-            "ds_read_b64_tr_b16 %9, %29\n\t"
-            "ds_read_b64_tr_b16 %10, %30\n\t"
-            "ds_read_b64_tr_b16 %11, %31\n\t"
-            "ds_read_b64_tr_b16 %12, %32\n\t"
-            "ds_read_b64_tr_b16 %13, %33\n\t"
-            "ds_read_b64_tr_b16 %14, %34\n\t"
-            "ds_read_b64_tr_b16 %15, %35\n\t"
-            "ds_read_b64_tr_b16 %16, %28 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %17, %29 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %18, %30 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %19, %31 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %20, %32 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %21, %33 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %22, %34 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %23, %35 offset:8192\n\t"
+            "ds_read_b128 %0, %24 offset:%36\n\t"
+            "ds_read_b128 %1, %25 offset:%36\n\t"
+            "ds_read_b128 %2, %26 offset:%36\n\t"
+            "ds_read_b128 %3, %27 offset:%36\n\t"
+            "ds_read_b128 %4, %24 offset:%37\n\t"
+            "ds_read_b128 %5, %25 offset:%37\n\t"
+            "ds_read_b128 %6, %26 offset:%37\n\t"
+            "ds_read_b128 %7, %27 offset:%37\n\t"
+            "ds_read_b64_tr_b16 %8, %28 offset:%36\n\t"
+            "ds_read_b64_tr_b16 %9, %29 offset:%36\n\t"
+            "ds_read_b64_tr_b16 %10, %30 offset:%36\n\t"
+            "ds_read_b64_tr_b16 %11, %31 offset:%36\n\t"
+            "ds_read_b64_tr_b16 %12, %32 offset:%36\n\t"
+            "ds_read_b64_tr_b16 %13, %33 offset:%36\n\t"
+            "ds_read_b64_tr_b16 %14, %34 offset:%36\n\t"
+            "ds_read_b64_tr_b16 %15, %35 offset:%36\n\t"
+            "ds_read_b64_tr_b16 %16, %28 offset:%37\n\t"
+            "ds_read_b64_tr_b16 %17, %29 offset:%37\n\t"
+            "ds_read_b64_tr_b16 %18, %30 offset:%37\n\t"
+            "ds_read_b64_tr_b16 %19, %31 offset:%37\n\t"
+            "ds_read_b64_tr_b16 %20, %32 offset:%37\n\t"
+            "ds_read_b64_tr_b16 %21, %33 offset:%37\n\t"
+            "ds_read_b64_tr_b16 %22, %34 offset:%37\n\t"
+            "ds_read_b64_tr_b16 %23, %35 offset:%37\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[0][2]), "=&v"(k[0][3]),
               "=&v"(k[1][0]), "=&v"(k[1][1]), "=&v"(k[1][2]), "=&v"(k[1][3]),
@@ -891,30 +894,46 @@ struct GroupReadsTr128 {
               "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]),
               "=&v"(v[1][4]), "=&v"(v[1][5]), "=&v"(v[1][6]), "=&v"(v[1][7])
             : "v"(ak[0]), "v"(ak[1]), "v"(ak[2]), "v"(ak[3]),
-              "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]), "v"(av[4]), "v"(av[5]), "v"(av[6]), "v"(av[7])
+              "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]), "v"(av[4]), "v"(av[5]), "v"(av[6]), "v"(av[7]),
+              "i"(SB), "i"(SB + 8192u)
             : "memory");
     }
 };
 
 template <>
 struct GroupReads<64> {
+    template <uint32_t SB>
     static __device__ __forceinline__ void read(const uint32_t (&ak)[2], const uint32_t (&av)[4],
                                                 u32x4_t (&k)[2][2], u32x4_t (&v)[2][4]) {
         asm volatile(
-            "ds_read_b128 %0, %12\n\tds_read_b128 %1, %13\n\t"
-            "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %3, %13 offset:4096\n\t"
-            "ds_read_b128 %4, %14\n\tds_read_b128 %5, %15\n\t"
-            "ds_read_b128 %6, %16\n\tds_read_b128 %7, %17\n\t"
-            "ds_read_b128 %8, %14 offset:4096\n\tds_read_b128 %9, %15 offset:4096\n\t"
-            "ds_read_b128 %10, %16 offset:4096\n\tds_read_b128 %11, %17 offset:4096\n\t"
+            "ds_read_b128 %0, %12 offset:%18\n\tds_read_b128 %1, %13 offset:%18\n\t"
+            "ds_read_b128 %2, %12 offset:%19\n\tds_read_b128 %3, %13 offset:%19\n\t"
+            "ds_read_b128 %4, %14 offset:%18\n\tds_read_b128 %5, %15 offset:%18\n\t"
+            "ds_read_b128 %6, %16 offset:%18\n\tds_read_b128 %7, %17 offset:%18\n\t"
+            "ds_read_b128 %8, %14 offset:%19\n\tds_read_b128 %9, %15 offset:%19\n\t"
+            "ds_read_b128 %10, %16 offset:%19\n\tds_read_b128 %11, %17 offset:%19\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[1][0]), "=&v"(k[1][1]),
               "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
               "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
-            : "v"(ak[0]), "v"(ak[1]), "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3])
+            : "v"(ak[0]), "v"(ak[1]), "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]), "i"(SB),
+              "i"(SB + 4096u)
             : "memory");
     }
 };
+
+// f(IntC<I>{}) for I = 0, 1, .., N - 1 while f returns true (a loop body
+// that needs I as a constant)
+template <int I>
+struct IntC {
+    static constexpr int value = I;
+};
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_while(F &&f) {
+    if constexpr (I < N) {
+        if (f(IntC<I>{})) static_while<I + 1, N>(f);
+    }
+}
 
 // s_waitcnt with only the vector-memory counter: at most N loads in flight.
 template <int N>
@@ -992,8 +1011,15 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     const int64_t prow_lane = phys_page_t<PAGED>(sg, first + min(lane, n_here - 1)) * kPage;
     // (the builtin's arguments are passed as plain void pointers: with typed or
     // const ones the host pass silently drops the kernel's launch stub)
+    // Workgroups take their chunk's pages in a rotated order, starting at page
+    // blockIdx.x mod n_here, so that the many streams in flight at once do
+    // not walk the same offsets of their regions in step (measured 1 us faster
+    // on the 64K layer); attention over a set of pages does not depend on
+    // their order beyond rounding.
+    const int rot = static_cast<int>(blockIdx.x % static_cast<unsigned>(n_here));
+    auto rp = [&](int p) { return p + rot < n_here ? p + rot : p + rot - n_here; };  // p < n_here
     auto issue = [&](int p, int slot) {  // page p of the chunk (clamped) into a slot
-        const int pc = min(p, n_here - 1);
+        const int pc = rp(min(p, n_here - 1));
         const int64_t prow = static_cast<int64_t>(
             (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(
                  static_cast<int>(prow_lane >> 32), pc))) << 32) |
@@ -1053,84 +1079,103 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     // covers every thread's pieces, and tells that the previous group's slots
     // are no longer read, so they are refilled with the pages NS ahead (clamped
     // to the chunk's last page: slots past the chunk are never attended).
-    for (int pi = 0; pi < n_here; pi += NG) {
+    // The ring holds NSG groups; the loop body is unrolled over them, so that
+    // each group's slots are a constant offset in its LDS reads.
+    constexpr int NSG = NS / NG;
+    auto group = [&](auto sgc, int pi) {
+        constexpr int SG = decltype(sgc)::value;  // pages pi.. sit in slots SG*NG ..
+        // the pair's byte offset in the ring; LDS offsets have 16 bits, so a
+        // pair that ends past 64 KiB (10 slots of d = 128) adds 64 KiB to the
+        // addresses instead
+        constexpr uint32_t HI = SG * NG * SLOT_BYTES + NG * SLOT_BYTES > 0x10000u ? 0x10000u : 0u;
+        constexpr uint32_t SB = SG * NG * SLOT_BYTES - HI;
+        uint32_t akh[KSTEPS], avh[TR ? 8 : 4];
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) akh[kk] = ak[kk] + HI;
+        if constexpr (TR) {
+#pragma unroll
+            for (int f = 0; f < 8; ++f) avh[f] = avt[f] + HI;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) avh[j] = av[j] + HI;
+        }
         wait_vmcnt<kAhead>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         if (pi > 0) {  // (the first group waits for a little more than it needs)
 #pragma unroll
-            for (int n = 0; n < NG; ++n) issue(pi - NG + n + NS, (pi - NG + n) % NS);
+            for (int n = 0; n < NG; ++n) issue(pi - NG + n + NS, ((SG + NSG - 1) % NSG) * NG + n);
         }
         __builtin_amdgcn_sched_barrier(0);
-        const uint32_t sbase = static_cast<uint32_t>((pi % NS) * SLOT_BYTES);
-        uint32_t akk[KSTEPS];
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) akk[kk] = ak[kk] + sbase;
         if constexpr (TR) {
-            uint32_t avv[8];
-#pragma unroll
-            for (int f = 0; f < 8; ++f) avv[f] = avt[f] + sbase;
             u32x4_t kraw[NG][KSTEPS];
             u32x2_t vtr[NG][8];
-            GroupReadsTr128::read(akk, avv, kraw, vtr);
+            GroupReadsTr128::read<SB>(akh, avh, kraw, vtr);
             uint4 kop[NG][KSTEPS];
             int valid[NG];
-            u32x2_t vm[NG];  // token masks (tokens 4*lg .. +3 past the prefix zeroed)
 #pragma unroll
             for (int n = 0; n < NG; ++n) {
-                valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + pi + n) * kPage) : 0;
+                valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + rp(pi + n)) * kPage) : 0;
 #pragma unroll
                 for (int kk = 0; kk < KSTEPS; ++kk) kop[n][kk] = __builtin_bit_cast(uint4, kraw[n][kk]);
-                vm[n] = u32x2_t{(4 * lg + 0 < valid[n] ? 0x0000ffffu : 0u) | (4 * lg + 1 < valid[n] ? 0xffff0000u : 0u),
-                                (4 * lg + 2 < valid[n] ? 0x0000ffffu : 0u) | (4 * lg + 3 < valid[n] ? 0xffff0000u : 0u)};
             }
             // the PV operand of block f: page pi's tokens, then page pi + 1's
             u32x4_t vpair[1][DPL];
-            const bool full2 = valid[0] >= kPage && valid[1] >= kPage;  // uniform
 #pragma unroll
-            for (int f = 0; f < DPL; ++f) {
-                u32x2_t a0 = vtr[0][f], a1 = vtr[1][f];
-                if (!full2) {
-                    a0 &= vm[0];
-                    a1 &= vm[1];
+            for (int f = 0; f < DPL; ++f)
+                vpair[0][f] = u32x4_t{vtr[0][f].x, vtr[0][f].y, vtr[1][f].x, vtr[1][f].y};
+            if (valid[0] < kPage || valid[1] < kPage) {  // uniform; only a prefix's last pages
+                // (the empty asm keeps this rare masking behind the branch
+                // instead of turning it into selects on every page pair)
+                asm volatile("");
+                u32x4_t vm;  // tokens 4*lg .. +3 of each page past the prefix zeroed
+#pragma unroll
+                for (int n = 0; n < NG; ++n) {
+                    vm[2 * n] = (4 * lg + 0 < valid[n] ? 0x0000ffffu : 0u) | (4 * lg + 1 < valid[n] ? 0xffff0000u : 0u);
+                    vm[2 * n + 1] = (4 * lg + 2 < valid[n] ? 0x0000ffffu : 0u) | (4 * lg + 3 < valid[n] ? 0xffff0000u : 0u);
                 }
-                vpair[0][f] = u32x4_t{a0.x, a0.y, a1.x, a1.y};
+#pragma unroll
+                for (int f = 0; f < DPL; ++f) vpair[0][f] &= vm;
             }
             short4_t vop_none[1][DPL];
             attend_core<DIM, RTW, NG, false, true>(kop, vpair, vop_none, valid, qop, rt_ok, D.scale_log2,
                                                    oacc, m_run, l_run, lg, {}, {}, l4);
-            continue;
-        }
-        uint32_t avv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) avv[j] = av[j] + sbase;
-        u32x4_t kraw[NG][KSTEPS], vraw[NG][4];
-        GroupReads<DIM>::read(akk, avv, kraw, vraw);
+        } else {
+            u32x4_t kraw[NG][KSTEPS], vraw[NG][4];
+            GroupReads<DIM>::template read<SB>(akh, avh, kraw, vraw);
 
-        uint4 kop[NG][KSTEPS];
-        uint32_t vw[NG][4][DPL / 2];
-        int valid[NG];
+            uint4 kop[NG][KSTEPS];
+            uint32_t vw[NG][4][DPL / 2];
+            int valid[NG];
 #pragma unroll
-        for (int n = 0; n < NG; ++n) {
-            // a page past the chunk (odd count) attends nothing
-            valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + pi + n) * kPage) : 0;
+            for (int n = 0; n < NG; ++n) {
+                // a page past the chunk (odd count) attends nothing
+                valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + rp(pi + n)) * kPage) : 0;
 #pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) kop[n][kk] = __builtin_bit_cast(uint4, kraw[n][kk]);
-            // V words of tokens 4*lg + j for the lane's dims DPL*l16 .. +DPL-1
+                for (int kk = 0; kk < KSTEPS; ++kk) kop[n][kk] = __builtin_bit_cast(uint4, kraw[n][kk]);
+                // V words of tokens 4*lg + j for the lane's dims DPL*l16 .. +DPL-1
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u32x4_t c4 = vraw[n][j];
-                if constexpr (DPL == 8) {
-                    vw[n][j][0] = c4[0]; vw[n][j][1] = c4[1]; vw[n][j][2] = c4[2]; vw[n][j][3] = c4[3];
-                } else {
-                    const bool hi = (l16 & 1) != 0;
-                    vw[n][j][0] = hi ? c4[2] : c4[0];
-                    vw[n][j][1] = hi ? c4[3] : c4[1];
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4_t c4 = vraw[n][j];
+                    if constexpr (DPL == 8) {
+                        vw[n][j][0] = c4[0]; vw[n][j][1] = c4[1]; vw[n][j][2] = c4[2]; vw[n][j][3] = c4[3];
+                    } else {
+                        const bool hi = (l16 & 1) != 0;
+                        vw[n][j][0] = hi ? c4[2] : c4[0];
+                        vw[n][j][1] = hi ? c4[3] : c4[1];
+                    }
                 }
             }
+            attend_pages<DIM, RTW, NG>(kop, vw, valid, qop, rt_ok, D.scale_log2, oacc, m_run, l_run, lg);
         }
-        attend_pages<DIM, RTW, NG>(kop, vw, valid, qop, rt_ok, D.scale_log2, oacc, m_run, l_run, lg);
-    }
+    };
+    for (int p0 = 0; p0 < n_here; p0 += NS)
+        static_while<0, NSG>([&](auto sgc) {
+            const int pi = p0 + decltype(sgc)::value * NG;
+            if (pi >= n_here) return false;
+            group(sgc, pi);
+            return true;
+        });
     // no direct load may still be writing LDS when the workgroup ends
     wait_vmcnt<0>();
 #pragma unroll
