@@ -1182,7 +1182,14 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     for (int i = 0; i < RTW; ++i) l_run[i] = TR ? l4[i][0] : shfl_sum32(l_run[i]);
 
     // Lane l holds, for row l%16, dims DPL*(4*lg + j) + e (transposing reads:
-    // dims 16 e + 4*lg + j).
+    // dims 16 e + 4*lg + j).  The partials are stored non-temporally: every
+    // workgroup stores at about the same time, at the end, and stores that
+    // skip the L2 leave no dirty lines for the kernel's end to write back
+    // (measured 2.4 us shorter on the 64K layer; the finishing kernel then
+    // reads them 0.4 us more slowly).
+    auto st4 = [](float *p, float a, float b, float c, float d) {
+        __builtin_nontemporal_store(float4_t{a, b, c, d}, reinterpret_cast<float4_t *>(p));
+    };
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
         const int rt = w + NW * i;
@@ -1191,15 +1198,14 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
         if (r >= rows) continue;
         const size_t pb = ((size_t)sgi * nch + chunk) * rows + r;
         if (lg == 0) {
-            W.part_ml[pb * 2 + 0] = m_run[i];
-            W.part_ml[pb * 2 + 1] = l_run[i];
+            __builtin_nontemporal_store(m_run[i], &W.part_ml[pb * 2 + 0]);
+            __builtin_nontemporal_store(l_run[i], &W.part_ml[pb * 2 + 1]);
         }
         float *dst = W.part_acc + pb * DIM;
         if constexpr (TR) {
 #pragma unroll
             for (int e = 0; e < DPL; ++e)
-                *reinterpret_cast<float4 *>(dst + 16 * e + 4 * lg) =
-                    make_float4(oacc[i][e][0], oacc[i][e][1], oacc[i][e][2], oacc[i][e][3]);
+                st4(dst + 16 * e + 4 * lg, oacc[i][e][0], oacc[i][e][1], oacc[i][e][2], oacc[i][e][3]);
             continue;
         }
 #pragma unroll
@@ -1209,8 +1215,7 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
             for (int e = 0; e < DPL; ++e) tmp[e] = oacc[i][e][j];
             float *d0 = dst + DPL * (4 * lg + j);
 #pragma unroll
-            for (int e = 0; e < DPL; e += 4)
-                *reinterpret_cast<float4 *>(d0 + e) = make_float4(tmp[e], tmp[e + 1], tmp[e + 2], tmp[e + 3]);
+            for (int e = 0; e < DPL; e += 4) st4(d0 + e, tmp[e], tmp[e + 1], tmp[e + 2], tmp[e + 3]);
         }
     }
 }
