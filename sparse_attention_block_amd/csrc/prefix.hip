@@ -798,10 +798,13 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
 // global_load_lds_dwordx4 (no register staging), so NS - 2*kDenseGroup
 // pages stay in flight while a group is attended.  The NW waves (row tiles w,
 // w + NW, ...) read their K and V^T operands from LDS and attend kDenseGroup
-// pages together.  Chunks of 8 elements are XOR-swizzled per token row, which
-// makes both operand reads free of bank conflicts; a direct load writes lane
-// i's 16 bytes to LDS position i, so each lane fetches the global chunk that
-// belongs at its swizzled position.  Same arithmetic as k_prefix_bf16.
+// pages together.  Chunks of 8 elements are XOR-swizzled per token row (for
+// d = 128, V's chunk pairs, for the transposing reads), which makes the
+// operand reads free of bank conflicts; a direct load writes lane i's 16 bytes
+// to LDS position i, so each lane fetches the global chunk that belongs at its
+// swizzled position.  The arithmetic is k_prefix_bf16's (log2-unit scores,
+// weights rounded to bf16, row sums of the rounded weights); for d = 128 the
+// row sums come from an MFMA, so they are added in another order.
 // LDS page slots per workgroup (ring): 6 with 4 waves (measured 2-3% faster
 // than 8 or 10 on the 64K layer), 10 with 8 waves (one load per thread and page)
 template <int NW>
