@@ -1362,12 +1362,15 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
                                prefix_len, W);                                                    \
     } while (0)
         // dense pass: wave w of NW takes row tiles w, w + NW, ...; head_dim 128
-        // uses eight waves (one page of K and V is one 16-byte piece per thread)
-        // once there are more than four row tiles
+        // with up to 8 row tiles takes 4 waves of two row tiles each (two
+        // independent chains per wave at 210 VGPRs, two workgroups per CU,
+        // where 8 waves of one row tile at 164 VGPRs fit one per CU: the ragged
+        // batch's dense first step takes 409 us instead of 496), beyond that 8
+        // waves of two (one page of K and V is one 16-byte piece per thread)
         if (D.d == 128) {
             if (dense) {
                 if (n_rt <= 4) LAUNCH_D(128, 1, 4);
-                else if (n_rt <= 8) LAUNCH_D(128, 1, 8);
+                else if (n_rt <= 8) LAUNCH_D(128, 2, 4);
                 else LAUNCH_D(128, 2, 8);
             } else if (D.sparse_chunk == 4 && n_rt <= 2) {
                 // chunks of 4 pages, at most 32 rows: waves split the dimensions
