@@ -945,13 +945,14 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int DIM, int RTW, int NW, bool PAGED>
-__global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uint16_t *__restrict__ q_t,
-                                                               const uint16_t *__restrict__ kc,
-                                                               const uint16_t *__restrict__ vc,
-                                                               const int32_t *__restrict__ kv_off,
-                                                               const int32_t *__restrict__ prefix_len,
-                                                               Work W) {
+template <int DIM, int RTW, int NW, bool SPARSE, bool PAGED>
+__global__ __launch_bounds__(64 * NW) void k_prefix_ring_bf16(Dims D, const uint16_t *__restrict__ q_t,
+                                                              const uint16_t *__restrict__ kc,
+                                                              const uint16_t *__restrict__ vc,
+                                                              const int32_t *__restrict__ kv_off,
+                                                              const int32_t *__restrict__ prefix_len,
+                                                              Work W, int32_t *dbg_uidx,
+                                                              int32_t *dbg_ucnt, int dbg_cap) {
     constexpr int KSTEPS = DIM / 32, DPL = DIM / 16, CPT = DIM / 8;
     constexpr bool TR = DIM == 128;          // V^T operands by transposing LDS reads
     constexpr int NCK = 16 * CPT;            // 16-byte chunks per page and tensor
@@ -963,7 +964,13 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     // loads each thread may leave in flight when a group must have landed: the
     // pages of the groups after it that have been issued
     constexpr int kAhead = LPT * (NS - 2 * NG);
+    static_assert(!SPARSE || NW == 4, "the union slice is built by 256 threads");
     __shared__ uint4 s_page[NS][2 * NCK];  // [slot][K chunks, then V chunks], swizzled
+    // the union bitmap (sparse pass) lives in the ring where it fits: the ring
+    // is first written after the union slice's last barrier
+    constexpr bool kBmInRing = sizeof(uint4) * NS * 2 * NCK >= 4 * kMaxBitmapWords;
+    __shared__ uint32_t s_bm[SPARSE && !kBmInRing ? kMaxBitmapWords : 1];
+    __shared__ int s_wsum[4], s_pg[SPARSE ? kMaxSparseChunk : 1];
     const int ng = D.S * D.Hk;
     const int sgi = blockIdx.x % ng;
     const int chunk = blockIdx.x / ng;
@@ -972,28 +979,53 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
     const SeqGeom sg = seq_geom_t<PAGED>(D, kv_off, prefix_len, s);
-    const int first = chunk * D.dense_chunk;
-    const int n_here = min(D.dense_chunk, sg.pages - first);
-    if (n_here <= 0) return;
-    const int rows = D.Rd, nch = D.n_chunks_dense;
+    const int cp = SPARSE ? D.sparse_chunk : D.dense_chunk;
+    const int first = chunk * cp;
+    if (!SPARSE && first >= sg.pages) return;
+    const int rows = SPARSE ? D.R : D.Rd, nch = SPARSE ? D.n_chunks_sparse : D.n_chunks_dense;
     const int n_rt = (rows + 15) / 16;
 
-    // Q operands (B of QK^T) of row tiles w + NW*i, read straight from the
-    // block queries: row r = j*B + t of the group is head g*G + j, token t.  Lane
-    // l holds row l%16, dims 32*kk + 8*(l/16) .. +7; rows past the group read
-    // its last row (their outputs are not stored).  Issued before any page so
-    // that waiting for them never waits for a page.
+    // Sparse pass: the rows' page lists (one entry per thread, clamped),
+    // requested first, for the union slice below
+    const int32_t *psel_g = W.psel + (size_t)sgi * (rows > 0 ? rows : 1) * D.k;
+    const int n_sel = rows * D.k;
+    const int pre0 = SPARSE ? psel_g[min(tid, max(n_sel - 1, 0))] : 0;
+    // Q operands (B of QK^T) of row tiles w + NW*i.  Dense pass: straight from
+    // the block queries, row r = j*B + t of the group being head g*G + j, token
+    // t (rows past the group read its last row; their outputs are not stored).
+    // Sparse pass: the stacked active rows of the group, zero-padded to whole
+    // tiles.  Lane l holds row l%16, dims 32*kk + 8*(l/16) .. +7.  Issued
+    // before any page so that waiting for them never waits for a page.
     uint4 qop[RTW][KSTEPS];
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
         const int rt = min(w + NW * i, n_rt - 1);
-        const int r = min(rt * 16 + l16, rows - 1);
-        const uint16_t *qrow = q_t + ((size_t)(s * D.B + r % D.B) * D.Hq + g * D.G + r / D.B) * DIM;
+        const uint16_t *qrow;
+        if constexpr (SPARSE) {
+            qrow = static_cast<const uint16_t *>(W.qrows) + ((size_t)sgi * D.R16 + rt * 16 + l16) * DIM;
+        } else {
+            const int r = min(rt * 16 + l16, rows - 1);
+            qrow = q_t + ((size_t)(s * D.B + r % D.B) * D.Hq + g * D.G + r / D.B) * DIM;
+        }
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
             qop[i][kk] = *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * lg);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // the chunk's pages: the dense pass's consecutive ones, or the sparse
+    // pass's slice of the group's union (chunk 0 records the union size)
+    int n_items = sg.pages;
+    if constexpr (SPARSE) {
+        uint32_t *bm = kBmInRing ? reinterpret_cast<uint32_t *>(&s_page[0][0]) : s_bm;
+        n_items = union_slice(psel_g, pre0, n_sel, sg.pages, D.k >= sg.pages, first, cp, bm, s_wsum,
+                              s_pg, dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr, dbg_cap, D.k);
+        if (chunk == 0 && tid == 0) {
+            W.union_cnt[sgi] = min(n_items, D.union_cap);
+            if (dbg_ucnt) dbg_ucnt[sgi] = n_items;
+        }
+        if (first >= n_items) return;
+    }
+    const int n_here = min(cp, n_items - first);
 
     // Direct load h of a page: wave w writes LDS chunks (h*NW + w)*64 .. +63 of
     // the slot; lane i's chunk L holds token t = (L % NCK) / CPT, swizzled column
@@ -1009,9 +1041,14 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
         const int c = (L < NCK || !TR) ? (cq % CPT) ^ (t & (CPT - 1)) : (cq % CPT) ^ ((t & 7) << 1);
         src_h[h] = (L < NCK ? kc : vc) + (size_t)g * D.T * DIM + t * DIM + c * 8;
     }
-    // the cache row of each page of the chunk: lane i holds page first + i's
-    // (clamped to the chunk's last page; a page table is read once here)
-    const int64_t prow_lane = phys_page_t<PAGED>(sg, first + min(lane, n_here - 1)) * kPage;
+    // the sequence page and the cache row of each page of the chunk: lane i
+    // holds the chunk's page i (clamped to its last page; a page table is read
+    // once here)
+    const int my_page = SPARSE ? s_pg[min(lane, n_here - 1)] : first + min(lane, n_here - 1);
+    const int64_t prow_lane = phys_page_t<PAGED>(sg, my_page) * kPage;
+    auto seq_page = [&](int q) {  // the chunk's page q (uniform)
+        return SPARSE ? __builtin_amdgcn_readlane(my_page, q) : first + q;
+    };
     // (the builtin's arguments are passed as plain void pointers: with typed or
     // const ones the host pass silently drops the kernel's launch stub)
     // Workgroups take their chunk's pages in a rotated order, starting at page
@@ -1118,7 +1155,7 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
             int valid[NG];
 #pragma unroll
             for (int n = 0; n < NG; ++n) {
-                valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + rp(pi + n)) * kPage) : 0;
+                valid[n] = pi + n < n_here ? min(kPage, sg.len - seq_page(rp(pi + n)) * kPage) : 0;
 #pragma unroll
                 for (int kk = 0; kk < KSTEPS; ++kk) kop[n][kk] = __builtin_bit_cast(uint4, kraw[n][kk]);
             }
@@ -1153,7 +1190,7 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
 #pragma unroll
             for (int n = 0; n < NG; ++n) {
                 // a page past the chunk (odd count) attends nothing
-                valid[n] = pi + n < n_here ? min(kPage, sg.len - (first + rp(pi + n)) * kPage) : 0;
+                valid[n] = pi + n < n_here ? min(kPage, sg.len - seq_page(rp(pi + n)) * kPage) : 0;
 #pragma unroll
                 for (int kk = 0; kk < KSTEPS; ++kk) kop[n][kk] = __builtin_bit_cast(uint4, kraw[n][kk]);
                 // V words of tokens 4*lg + j for the lane's dims DPL*l16 .. +DPL-1
@@ -1185,13 +1222,16 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
     for (int i = 0; i < RTW; ++i) l_run[i] = TR ? l4[i][0] : shfl_sum32(l_run[i]);
 
     // Lane l holds, for row l%16, dims DPL*(4*lg + j) + e (transposing reads:
-    // dims 16 e + 4*lg + j).  The partials are stored non-temporally: every
-    // workgroup stores at about the same time, at the end, and stores that
-    // skip the L2 leave no dirty lines for the kernel's end to write back
-    // (measured 2.4 us shorter on the 64K layer; the finishing kernel then
-    // reads them 0.4 us more slowly).
+    // dims 16 e + 4*lg + j).  The dense pass stores its partials
+    // non-temporally: every workgroup stores at about the same time, at the
+    // end, and stores that skip the L2 leave no dirty lines for the kernel's
+    // end to write back (measured 2.4 us shorter on the 64K layer; the
+    // finishing kernel then reads them 0.4 us more slowly).  The sparse pass's
+    // few partials are read sooner from the L2 (its finish took 0.9 us longer
+    // with non-temporal stores).
     auto st4 = [](float *p, float a, float b, float c, float d) {
-        __builtin_nontemporal_store(float4_t{a, b, c, d}, reinterpret_cast<float4_t *>(p));
+        if constexpr (SPARSE) *reinterpret_cast<float4_t *>(p) = float4_t{a, b, c, d};
+        else __builtin_nontemporal_store(float4_t{a, b, c, d}, reinterpret_cast<float4_t *>(p));
     };
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
@@ -1201,8 +1241,13 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_dense_bf16(Dims D, const uin
         if (r >= rows) continue;
         const size_t pb = ((size_t)sgi * nch + chunk) * rows + r;
         if (lg == 0) {
-            __builtin_nontemporal_store(m_run[i], &W.part_ml[pb * 2 + 0]);
-            __builtin_nontemporal_store(l_run[i], &W.part_ml[pb * 2 + 1]);
+            if constexpr (SPARSE) {
+                W.part_ml[pb * 2 + 0] = m_run[i];
+                W.part_ml[pb * 2 + 1] = l_run[i];
+            } else {
+                __builtin_nontemporal_store(m_run[i], &W.part_ml[pb * 2 + 0]);
+                __builtin_nontemporal_store(l_run[i], &W.part_ml[pb * 2 + 1]);
+            }
         }
         float *dst = W.part_acc + pb * DIM;
         if constexpr (TR) {
@@ -1350,17 +1395,18 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
         else if (rtw == 2) LAUNCH_P(DIMV, 2, DN, false);     \
         else LAUNCH_P(DIMV, 4, DN, false);                   \
     } while (0)
-#define LAUNCH_D(DIMV, RTWV, NWV)                                                                 \
+#define LAUNCH_R(DIMV, RTWV, NWV, SP)                                                             \
     do {                                                                                          \
         if (paged)                                                                                \
-            hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV, NWV, true>), grid, dim3(64 * NWV),   \
-                               0, st, D, static_cast<const uint16_t *>(q_t), k, v, kv_off,        \
-                               prefix_len, W);                                                    \
+            hipLaunchKernelGGL((k_prefix_ring_bf16<DIMV, RTWV, NWV, SP, true>), grid,               \
+                               dim3(64 * NWV), 0, st, D, static_cast<const uint16_t *>(q_t), k, v, \
+                               kv_off, prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap);             \
         else                                                                                      \
-            hipLaunchKernelGGL((k_prefix_dense_bf16<DIMV, RTWV, NWV, false>), grid, dim3(64 * NWV),  \
-                               0, st, D, static_cast<const uint16_t *>(q_t), k, v, kv_off,        \
-                               prefix_len, W);                                                    \
+            hipLaunchKernelGGL((k_prefix_ring_bf16<DIMV, RTWV, NWV, SP, false>), grid,              \
+                               dim3(64 * NWV), 0, st, D, static_cast<const uint16_t *>(q_t), k, v, \
+                               kv_off, prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap);             \
     } while (0)
+#define LAUNCH_D(DIMV, RTWV, NWV) LAUNCH_R(DIMV, RTWV, NWV, false)
         // dense pass: wave w of NW takes row tiles w, w + NW, ...; head_dim 128
         // with up to 8 row tiles takes 4 waves of two row tiles each (two
         // independent chains per wave at 210 VGPRs, two workgroups per CU,
@@ -1392,6 +1438,10 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
                     else LAUNCH_Q(2, false);
                 }
 #undef LAUNCH_Q
+            } else if (!(D.flags & LOSA_FLAG_ROW_MASK) && n_rt <= 8) {
+                // larger union slices stream through the dense pass's LDS ring
+                if (n_rt <= 4) LAUNCH_R(128, 1, 4, true);
+                else LAUNCH_R(128, 2, 4, true);
             } else {
                 PICK_P(128, false);
             }
@@ -1400,11 +1450,15 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
                 if (n_rt <= 4) LAUNCH_D(64, 1, 4);
                 else if (n_rt <= 8) LAUNCH_D(64, 2, 4);
                 else LAUNCH_D(64, 4, 4);
+            } else if (!(D.flags & LOSA_FLAG_ROW_MASK) && n_rt <= 8) {
+                if (n_rt <= 4) LAUNCH_R(64, 1, 4, true);
+                else LAUNCH_R(64, 2, 4, true);
             } else {
                 PICK_P(64, false);
             }
         }
 #undef LAUNCH_D
+#undef LAUNCH_R
 #undef PICK_P
 #undef LAUNCH_P
     } else {
