@@ -945,7 +945,7 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int DIM, int RTW, int NW, bool SPARSE, bool PAGED>
+template <int DIM, int RTW, int NW, bool SPARSE, bool MASK, bool PAGED>
 __global__ __launch_bounds__(64 * NW) void k_prefix_ring_bf16(Dims D, const uint16_t *__restrict__ q_t,
                                                               const uint16_t *__restrict__ kc,
                                                               const uint16_t *__restrict__ vc,
@@ -965,12 +965,14 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_ring_bf16(Dims D, const uint
     // pages of the groups after it that have been issued
     constexpr int kAhead = LPT * (NS - 2 * NG);
     static_assert(!SPARSE || NW == 4, "the union slice is built by 256 threads");
+    static_assert(!MASK || (SPARSE && RTW == 1), "row masks: sparse pass, at most 64 rows");
     __shared__ uint4 s_page[NS][2 * NCK];  // [slot][K chunks, then V chunks], swizzled
     // the union bitmap (sparse pass) lives in the ring where it fits: the ring
     // is first written after the union slice's last barrier
     constexpr bool kBmInRing = sizeof(uint4) * NS * 2 * NCK >= 4 * kMaxBitmapWords;
     __shared__ uint32_t s_bm[SPARSE && !kBmInRing ? kMaxBitmapWords : 1];
     __shared__ int s_wsum[4], s_pg[SPARSE ? kMaxSparseChunk : 1];
+    __shared__ uint64_t s_rmask[MASK ? kMaxSparseChunk : 1];  // rows that selected each page
     const int ng = D.S * D.Hk;
     const int sgi = blockIdx.x % ng;
     const int chunk = blockIdx.x / ng;
@@ -1018,7 +1020,8 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_ring_bf16(Dims D, const uint
     if constexpr (SPARSE) {
         uint32_t *bm = kBmInRing ? reinterpret_cast<uint32_t *>(&s_page[0][0]) : s_bm;
         n_items = union_slice(psel_g, pre0, n_sel, sg.pages, D.k >= sg.pages, first, cp, bm, s_wsum,
-                              s_pg, dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr, dbg_cap, D.k);
+                              s_pg, dbg_uidx ? dbg_uidx + (size_t)sgi * dbg_cap : nullptr, dbg_cap, D.k,
+                              MASK ? s_rmask : nullptr);
         if (chunk == 0 && tid == 0) {
             W.union_cnt[sgi] = min(n_items, D.union_cap);
             if (dbg_ucnt) dbg_ucnt[sgi] = n_items;
@@ -1147,6 +1150,14 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_ring_bf16(Dims D, const uint
             for (int n = 0; n < NG; ++n) issue(pi - NG + n + NS, ((SG + NSG - 1) % NSG) * NG + n);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // (row masks) the rows that selected each page of the pair, and the
+        // first row of the wave's row tile
+        uint64_t rm[NG];
+#pragma unroll
+        for (int n = 0; n < NG; ++n) rm[n] = MASK && pi + n < n_here ? s_rmask[rp(pi + n)] : 0ull;
+        int row0[RTW];
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) row0[i] = (w + NW * i) * 16;
         if constexpr (TR) {
             u32x4_t kraw[NG][KSTEPS];
             u32x2_t vtr[NG][8];
@@ -1178,8 +1189,8 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_ring_bf16(Dims D, const uint
                 for (int f = 0; f < DPL; ++f) vpair[0][f] &= vm;
             }
             short4_t vop_none[1][DPL];
-            attend_core<DIM, RTW, NG, false, true>(kop, vpair, vop_none, valid, qop, rt_ok, D.scale_log2,
-                                                   oacc, m_run, l_run, lg, {}, {}, l4);
+            attend_core<DIM, RTW, NG, MASK, true>(kop, vpair, vop_none, valid, qop, rt_ok, D.scale_log2,
+                                                  oacc, m_run, l_run, lg, rm, row0, l4);
         } else {
             u32x4_t kraw[NG][KSTEPS], vraw[NG][4];
             GroupReads<DIM>::template read<SB>(akh, avh, kraw, vraw);
@@ -1206,7 +1217,8 @@ __global__ __launch_bounds__(64 * NW) void k_prefix_ring_bf16(Dims D, const uint
                     }
                 }
             }
-            attend_pages<DIM, RTW, NG>(kop, vw, valid, qop, rt_ok, D.scale_log2, oacc, m_run, l_run, lg);
+            attend_pages<DIM, RTW, NG, MASK>(kop, vw, valid, qop, rt_ok, D.scale_log2, oacc, m_run, l_run,
+                                             lg, rm, row0);
         }
     };
     for (int p0 = 0; p0 < n_here; p0 += NS)
@@ -1395,18 +1407,18 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
         else if (rtw == 2) LAUNCH_P(DIMV, 2, DN, false);     \
         else LAUNCH_P(DIMV, 4, DN, false);                   \
     } while (0)
-#define LAUNCH_R(DIMV, RTWV, NWV, SP)                                                             \
+#define LAUNCH_R(DIMV, RTWV, NWV, SP, MK)                                                         \
     do {                                                                                          \
         if (paged)                                                                                \
-            hipLaunchKernelGGL((k_prefix_ring_bf16<DIMV, RTWV, NWV, SP, true>), grid,               \
+            hipLaunchKernelGGL((k_prefix_ring_bf16<DIMV, RTWV, NWV, SP, MK, true>), grid,           \
                                dim3(64 * NWV), 0, st, D, static_cast<const uint16_t *>(q_t), k, v, \
                                kv_off, prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap);             \
         else                                                                                      \
-            hipLaunchKernelGGL((k_prefix_ring_bf16<DIMV, RTWV, NWV, SP, false>), grid,              \
+            hipLaunchKernelGGL((k_prefix_ring_bf16<DIMV, RTWV, NWV, SP, MK, false>), grid,          \
                                dim3(64 * NWV), 0, st, D, static_cast<const uint16_t *>(q_t), k, v, \
                                kv_off, prefix_len, W, dbg_uidx, dbg_ucnt, dbg_cap);             \
     } while (0)
-#define LAUNCH_D(DIMV, RTWV, NWV) LAUNCH_R(DIMV, RTWV, NWV, false)
+#define LAUNCH_D(DIMV, RTWV, NWV) LAUNCH_R(DIMV, RTWV, NWV, false, false)
         // dense pass: wave w of NW takes row tiles w, w + NW, ...; head_dim 128
         // with up to 8 row tiles takes 4 waves of two row tiles each (two
         // independent chains per wave at 210 VGPRs, two workgroups per CU,
@@ -1438,10 +1450,11 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
                     else LAUNCH_Q(2, false);
                 }
 #undef LAUNCH_Q
-            } else if (!(D.flags & LOSA_FLAG_ROW_MASK) && n_rt <= 8) {
+            } else if (D.flags & LOSA_FLAG_ROW_MASK ? n_rt <= 4 : n_rt <= 8) {
                 // larger union slices stream through the dense pass's LDS ring
-                if (n_rt <= 4) LAUNCH_R(128, 1, 4, true);
-                else LAUNCH_R(128, 2, 4, true);
+                if (D.flags & LOSA_FLAG_ROW_MASK) LAUNCH_R(128, 1, 4, true, true);
+                else if (n_rt <= 4) LAUNCH_R(128, 1, 4, true, false);
+                else LAUNCH_R(128, 2, 4, true, false);
             } else {
                 PICK_P(128, false);
             }
@@ -1450,9 +1463,10 @@ hipError_t launch_prefix(const Dims &D, bool dense, const void *q_t, const void 
                 if (n_rt <= 4) LAUNCH_D(64, 1, 4);
                 else if (n_rt <= 8) LAUNCH_D(64, 2, 4);
                 else LAUNCH_D(64, 4, 4);
-            } else if (!(D.flags & LOSA_FLAG_ROW_MASK) && n_rt <= 8) {
-                if (n_rt <= 4) LAUNCH_R(64, 1, 4, true);
-                else LAUNCH_R(64, 2, 4, true);
+            } else if (D.flags & LOSA_FLAG_ROW_MASK ? n_rt <= 4 : n_rt <= 8) {
+                if (D.flags & LOSA_FLAG_ROW_MASK) LAUNCH_R(64, 1, 4, true, true);
+                else if (n_rt <= 4) LAUNCH_R(64, 1, 4, true, false);
+                else LAUNCH_R(64, 2, 4, true, false);
             } else {
                 PICK_P(64, false);
             }

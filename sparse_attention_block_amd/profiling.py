@@ -29,7 +29,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 # tag -> (kernel-name pattern, sources whose digest identifies the build)
 KERNEL_TAGS = {
-    "dense_prefix": (r"k_prefix_ring_bf16<\d+, \d+, \d+, false, false>", ["prefix.hip", "losa_api.hip", "losa_internal.h"]),
+    "dense_prefix": (r"k_prefix_ring_bf16<\d+, \d+, \d+, false, false, false>", ["prefix.hip", "losa_api.hip", "losa_internal.h"]),
     "sparse_prefix": (r"k_prefix_quarter_bf16<\d+, \d+, false, false>", ["prefix.hip", "losa_api.hip", "losa_internal.h"]),
     "page_score": (r"k_score_prep<\d+, false, \d+, false>", ["select.hip", "block_attn.h", "losa_internal.h"]),
     "page_select": (r"k_select<\d+, true, \d+, false>", ["select.hip", "block_attn.h", "losa_internal.h"]),
