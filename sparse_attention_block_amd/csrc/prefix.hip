@@ -793,7 +793,10 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
     store_count();  // after the waits for the pages, which would wait for it too
 }
 
-// Dense first-step pass, bf16.  Each page of the workgroup's chunk is read
+// Prefix pass over a page list streamed through LDS, bf16: the dense first
+// step's chunk of consecutive pages, or (SPARSE) a sparse step's slice of the
+// group's union with the stacked active rows as queries, optionally with row
+// masks.  Each page of the workgroup's list is read
 // from HBM once, straight into a ring of NS LDS page slots with
 // global_load_lds_dwordx4 (no register staging), so NS - 2*kDenseGroup
 // pages stay in flight while a group is attended.  The NW waves (row tiles w,
