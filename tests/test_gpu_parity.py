@@ -315,3 +315,17 @@ def test_trace_128k_layer(layer):
     op, lp = W.make_cache_state(cfg, layer)
     p.set_cache(op, lp)
     p.sparse(1)
+
+
+def test_long_single_head_prefixes():
+    """Prefixes of 15626 and 8750 pages (ragged last pages) with one KV head and
+    16 active rows: union bitmaps of 489 and 274 words, two per thread of the
+    4-page sparse pass, and tile maxima of 245 and 137 page groups per row."""
+    cfg = W.small_case(262, dtype="bf16", head_dim=128, block=16, n_qhead=4, n_kvhead=1,
+                       budget=128, n_active=4, prefix_lens=(250008, 139990), n_steps=3,
+                       needles=True)
+    lay = W.make_layer(cfg)
+    p = Pair(lay, "long_single_head_prefixes")
+    p.dense(0)
+    for step in (1, 2):
+        p.sparse(step)
