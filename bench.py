@@ -121,6 +121,10 @@ def floors_record(floors, rp):
         r["us_rocprof"] = us
         r["gbps_rocprof"] = (mib << 20) / (us * 1e-6) / 1e9 if us else None
         r["frac_rocprof"] = r["gbps_rocprof"] / PEAK_HBM_GBPS if us else None
+    if "gather" in rec:
+        us = rp.get("probe_gather")
+        rec["gather"] = dict(rec["gather"], us_rocprof=us,
+                             gbps_rocprof=rec["gather"]["bytes"] / (us * 1e-6) / 1e9 if us else None)
     return rec
 
 
@@ -141,11 +145,18 @@ def _selftest():
     st.losa_selftest_empty.argtypes = [ctypes.c_void_p]
     st.losa_selftest_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p]
+    st.losa_selftest_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     return st
 
 
 FLOOR_READS = ((1, 256), (8, 512), (16, 1024), (64, 2048))  # (MiB, workgroups)
 FLOOR_REPS = 8
+# the sparse prefix pass's memory pattern on the headline layer: 28 chunks of
+# 4 union pages for each of 8 KV heads, every page 8 KiB (keys and values),
+# drawn without repeats from a cold 32 MiB window per repetition
+FLOOR_GATHER_BLOCKS = 224
+FLOOR_GATHER_WINDOW = 32 << 20
 
 
 def latency_floors(hip, stream, reps=50):
@@ -214,6 +225,33 @@ def latency_floors(hip, stream, reps=50):
         reads[f"{mib}MiB"] = {"workgroups": blocks, "us_events": med,
                               "gbps_events": nb / (med * 1e-6) / 1e9}
     out["read"] = reads
+    # gathers (k_probe_gather): a page list copied into place just before (as
+    # the selection kernel writes the rows' page lists), then the
+    # pages, then partial-sized stores; each repetition in a window no kernel
+    # has touched
+    import numpy as np
+    rng = np.random.default_rng(20260)
+    n_pg = 4 * FLOOR_GATHER_BLOCKS
+    win_pages = FLOOR_GATHER_WINDOW // 8192
+    assert off + FLOOR_REPS * FLOOR_GATHER_WINDOW <= 1024 << 20
+    lists = np.stack([np.sort(rng.choice(win_pages, n_pg, replace=False)) +
+                      (off + r * FLOOR_GATHER_WINDOW) // 8192 for r in range(FLOOR_REPS)])
+    assert lists.max() < pool_bytes // 8192
+    list_src = torch.from_numpy(lists.astype(np.int32)).cuda()
+    list_dst = torch.empty(n_pg, dtype=torch.int32, device="cuda")
+    part = torch.empty(FLOOR_GATHER_BLOCKS * 16 * 130, dtype=torch.float32, device="cuda")
+    evs = [hip.event() for _ in range(2 * FLOOR_REPS)]
+    torch.cuda.synchronize()
+    for r in range(FLOOR_REPS):
+        list_dst.copy_(list_src[r])  # a device copy on the same (current) stream
+        hip.record(evs[2 * r], stream)
+        assert st.losa_selftest_gather(list_dst.data_ptr(), pool.data_ptr(), pool_bytes,
+                                       part.data_ptr(), FLOOR_GATHER_BLOCKS, stream) == 0
+        hip.record(evs[2 * r + 1], stream)
+    torch.cuda.synchronize()
+    us = sorted(hip.ms(evs[2 * r], evs[2 * r + 1]) * 1e3 for r in range(FLOOR_REPS))
+    out["gather"] = {"workgroups": FLOOR_GATHER_BLOCKS, "pages": n_pg, "bytes": n_pg * 8192,
+                     "us_events": float(us[len(us) // 2])}
     del pool
     torch.cuda.empty_cache()
     return out
@@ -798,6 +836,20 @@ def main():
                         "kernel_over_probe": None}
         return None
 
+    def gather_floor():
+        """The gather probe with the sparse prefix pass's memory pattern and no
+        arithmetic (rocprofv3 duration where the committed summary matches)."""
+        g = floors.get("gather")
+        if not g:
+            return None
+        us = rp.get("probe_gather")
+        src = "rocprofv3" if us is not None else "hip events"
+        if us is None:
+            us = g["us_events"]
+        return {"probe": f"page lists then {g['pages']} cold pages of 8 KiB, 4 per workgroup "
+                         f"({g['workgroups']} workgroups), then partial-sized stores",
+                "us": us, "duration_source": src, "kernel_over_probe": None}
+
     def roofline(name):
         if name is None or name not in kernels:
             return None
@@ -805,6 +857,9 @@ def main():
         fl = read_floor(k["bytes_per_launch"])
         if fl is not None:
             fl["kernel_over_probe"] = k["avg_us"] / fl["us"]
+        pf = gather_floor() if name == "sparse_prefix" else None
+        if pf is not None:
+            pf["kernel_over_probe"] = k["avg_us"] / pf["us"]
         return {"kernel": name, "bound": "hbm", "achieved": k["achieved_gbps"],
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k["frac_of_peak"],
                 "traffic": traffic_from_profile(name),
@@ -812,7 +867,7 @@ def main():
                 "avg_launch_us_events": k["avg_us_events"],
                 "duration_source": (f"rocprofv3 kernel trace, {rp_path}" if name in rp
                                     else "hip events around the kernel"),
-                "read_floor": fl}
+                "read_floor": fl, **({"pattern_floor": pf} if pf is not None else {})}
 
     rec = {
         "metric": METRIC,

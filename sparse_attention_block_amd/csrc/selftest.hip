@@ -3,8 +3,9 @@
 //  * one page-bound step, fma(q+, max, acc) then fma(q-, min, acc) with bf16
 //    operands, must equal the IEEE round-to-nearest-even sum acc + q*sel;
 //  * a plain copy kernel (HBM traffic calibration of the profiler counters),
-//    a pure read kernel (the rate a short streaming read reaches) and an
-//    empty kernel (the launch floor);
+//    a pure read kernel (the rate a short streaming read reaches), a gather
+//    kernel with the sparse prefix pass's memory pattern and no arithmetic,
+//    and an empty kernel (the launch floor);
 //  * the operand/result lane layouts assumed for v_mfma_f32_16x16x32_bf16
 //    and v_mfma_f32_16x16x16_bf16: lane l supplies row (or column) l%16 and
 //    k-elements K*(l/16) .. K*(l/16)+K-1, and holds result rows
@@ -90,7 +91,42 @@ __global__ __launch_bounds__(256) void k_probe_read(const uint4 *__restrict__ sr
     if (sink) out[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// The sparse prefix pass's memory pattern without its arithmetic: workgroup b
+// (4 waves) reads its 4 page indexes from `list` (written by the kernel before
+// it: one dependent round trip), wave w then reads page list[4b + w] of the
+// pool (8 KiB: a page's keys and values), 8 loads of 16 bytes per lane in
+// flight, folds them with XOR, and the workgroup stores as many bytes as the
+// pass's split-K partial of 16 rows (16 x 130 floats).
+constexpr int kGatherPageBytes = 8192;
+constexpr int kGatherPartF4 = 16 * 130 / 4;
+__global__ __launch_bounds__(256) void k_probe_gather(const int32_t *__restrict__ list,
+                                                      const uint4 *__restrict__ pool,
+                                                      float4 *__restrict__ part) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int pg = list[blockIdx.x * 4 + w];
+    const uint4 *src = pool + (size_t)pg * (kGatherPageBytes / 16);
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[u * 64 + lane];
+    uint32_t acc = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    const float f = __uint_as_float(acc & 0x3f7fffffu);  // finite
+    float4 *dst = part + (size_t)blockIdx.x * kGatherPartF4;
+    for (int i = threadIdx.x; i < kGatherPartF4; i += 256) dst[i] = make_float4(f, f, f, f);
+}
+
 extern "C" {
+
+// list: 4 * blocks page indexes, each below pool_bytes / 8192 (the caller's
+// guarantee: the list is device memory); part: blocks * 8320 bytes
+int losa_selftest_gather(const int32_t *list, const void *pool, size_t pool_bytes, void *part,
+                         int blocks, void *stream) {
+    if (!list || !pool || !part || blocks <= 0 || pool_bytes < (size_t)kGatherPageBytes) return 1;
+    hipLaunchKernelGGL(k_probe_gather, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       list, static_cast<const uint4 *>(pool), static_cast<float4 *>(part));
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 int losa_selftest_copy(const void *src, void *dst, size_t bytes, int blocks, void *stream) {
     if (bytes % 16 || blocks <= 0) return 1;

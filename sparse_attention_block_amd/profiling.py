@@ -42,6 +42,7 @@ KERNEL_TAGS = {
     "probe_read_8MiB": (r"k_probe_read<8>", ["selftest.hip"]),
     "probe_read_16MiB": (r"k_probe_read<16>", ["selftest.hip"]),
     "probe_read_64MiB": (r"k_probe_read<64>", ["selftest.hip"]),
+    "probe_gather": (r"(^|\W)k_probe_gather($|\W)", ["selftest.hip"]),
 }
 COPY_KERNEL = r"(^|\W)k_copy($|\W)"
 
@@ -69,12 +70,16 @@ def stats_table(path: str) -> list:
 
 
 def counter_means(path: str, counter: str) -> dict:
+    """Per kernel name: (mean over its dispatches, dispatch count); for the copy
+    kernel the largest dispatch only (the calibration copy; any other copy in
+    the run is small)."""
     vals = collections.defaultdict(list)
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] == counter:
                 vals[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
-    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+    return {k: ((max(v), 1) if re.search(COPY_KERNEL, k) else (sum(v) / len(v), len(v)))
+            for k, v in vals.items()}
 
 
 def find(means: dict, pattern: str):
@@ -97,7 +102,10 @@ def print_sweep(path: str, command: str):
           f"{fl['empty_kernel_back_to_back_us']:.2f} us, between two events "
           f"{fl['empty_kernel_between_events_us']:.2f} us; pure read of a cold buffer: " +
           ", ".join(f"{k} {v['us_events']:.1f} us ({v['gbps_events']:.0f} GB/s)"
-                    for k, v in fl["read"].items()) + ".\n")
+                    for k, v in fl["read"].items()) +
+          (f"; gather of {fl['gather']['pages']} cold 8 KiB pages after a dependent page-list "
+           f"read, with partial-sized stores: {fl['gather']['us_events']:.1f} us"
+           if "gather" in fl else "") + ".\n")
     if "page_meta" in fl:
         pm = fl["page_meta"]
         print(f"Page metadata of a 64K layer (8 KV heads): full build {pm['full_build_us']:.1f} us "
