@@ -851,7 +851,7 @@ def main():
                 "us": us, "duration_source": src, "kernel_over_probe": None}
 
     def roofline(name):
-        if name is None or name not in kernels:
+        if name is None or "bytes_per_launch" not in kernels.get(name, {}):
             return None
         k = kernels[name]
         fl = read_floor(k["bytes_per_launch"])

@@ -187,6 +187,15 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
 
     // -- 2. this token's prefix row; its first batch of partials is requested
     //       before the block scores are computed -------------------------------
+    // The first kDenseBatch chunks stay in flight until the merge (the
+    // barriers up to it wait on LDS only): (m, l) of chunk x by thread x of
+    // the token (shared through LDS), and 8-byte pieces of the chunks' outputs
+    // -- lanes x and x^1 both read dimensions 2*(x/2) and 2*(x/2) + 1, lane x
+    // of chunks 32*(x%2) .. + 31, and swap one sum at the end -- so that a
+    // thread has 33 loads in flight (a wave tracks at most 63: 65 loads would
+    // hold the last ones back a round trip).  Chunk indexes are clamped, so
+    // that no load is conditional; entries past the chunk count are ignored.
+    // Later chunks (long prefixes) are read in batches of kPartBatch.
     const int rho = live ? t : -1;
     const size_t pr0 = (size_t)sgi * nch * rows + row0 + (rho < 0 ? 0 : rho);
     const float *mlp = part_ml + pr0 * 2;
@@ -194,18 +203,15 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     // chunk strides in elements: a row's partials span < 2^31 bytes (at most
     // 4096 chunks x 256 rows x DIM floats), so 32-bit offsets suffice
     const int cs = rows * 2, as = rows * DIM;
-    // The first kDenseBatch chunks: (m, l) of chunk x by thread x of the token
-    // (shared through LDS), this thread's dimension of each chunk's output; the
-    // chunk index is clamped so that no load is conditional, and entries past
-    // the chunk count are ignored.  Later chunks (long prefixes) are read in
-    // batches of kPartBatch.
     const int clast = max(nchu - 1, 0);
+    const int h32 = (kDenseBatch / 2) * (x & 1);  // this lane's half of the first batch
     const float2 ml0 = *reinterpret_cast<const float2 *>(mlp + min(min(x, kDenseBatch - 1), clast) * cs);
-    float av0[kDenseBatch];
+    const float *acp2 = part_acc + pr0 * DIM + (x & ~1);
+    float2 av0[kDenseBatch / 2];
 #pragma unroll
-    for (int i = 0; i < kDenseBatch; ++i) av0[i] = acp[min(i, clast) * as];
+    for (int i = 0; i < kDenseBatch / 2; ++i)
+        av0[i] = *reinterpret_cast<const float2 *>(acp2 + (size_t)min(h32 + i, clast) * as);
     __builtin_amdgcn_sched_barrier(0);  // the partials stay in flight during the block scores
-
     // block scores q.k (scaled, log2 units): 8 threads per (token, key) pair
     {
         constexpr int SEG = DIM / 8;
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
         s_m0[t][x] = ml0.x;
         s_l0[t][x] = ml0.y;
     }
-    __syncthreads();
+    lds_barrier();
     // the first batch's chunk weights, once per (token, chunk): lane c of the
     // token's first wave takes chunk c, after the batch maximum by lane
     // butterflies (published by the barriers of the block softmax below)
@@ -282,11 +288,11 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
         const float m = seg_max(v);
         const float p = on ? __builtin_amdgcn_exp2f(v - m) : 0.0f;
         const float l = seg_sum(p);
-        __syncthreads();  // every score has been read
+        lds_barrier();  // every score has been read
         if (on) ps[tt * B + u] = p / l;
         if (on && u == 0) ls2[tt] = m + __log2f(l);
     }
-    __syncthreads();
+    lds_barrier();
     if (!live) return;
 
     // -- 3. output ---------------------------------------------------------------
@@ -303,16 +309,22 @@ __global__ __launch_bounds__(kFinishMaxThreads) void k_finish(
     PartAcc pa;
     if (nchu > 0) {
         const int nb = min(nchu, kDenseBatch);
-        float ls = 0.0f, oa = 0.0f;
+        float ls = 0.0f, sx = 0.0f, sy = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kDenseBatch; ++i) {
-            const float w = s_w0[t][i];
-            ls = fmaf(w, s_l0[t][i], ls);
-            oa = fmaf(w, i < nb ? av0[i] : 0.0f, oa);
+        for (int i = 0; i < kDenseBatch; ++i) ls = fmaf(s_w0[t][i], s_l0[t][i], ls);
+        // this lane's half of the chunks for both dimensions of its pair, in
+        // chunk order; then the sum over the other half from lane x^1
+#pragma unroll
+        for (int i = 0; i < kDenseBatch / 2; ++i) {
+            const float w = s_w0[t][h32 + i];
+            const bool on = h32 + i < nb;
+            sx = fmaf(w, on ? av0[i].x : 0.0f, sx);
+            sy = fmaf(w, on ? av0[i].y : 0.0f, sy);
         }
+        const float other = lane_xor1((x & 1) ? sx : sy);  // lane x^1's sum for dimension x
         pa.mx = s_mx0[t];
         pa.ls = ls;
-        pa.oa = oa;
+        pa.oa = ((x & 1) ? sy : sx) + other;  // (halves added in either order: the same sum)
     }
     for (int c0 = kDenseBatch; c0 < nchu; c0 += kPartBatch) {
         float mv[kPartBatch], lv[kPartBatch], av[kPartBatch];
