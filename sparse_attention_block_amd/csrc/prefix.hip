@@ -604,7 +604,9 @@ __global__ __launch_bounds__(256) void k_prefix_bf16(Dims D,
 // no combine of outputs: each writes its dimensions of the chunk's partial,
 // wave 0 the (m, l).  The union slice, the arithmetic (log2-unit scores,
 // weights rounded to bf16, row sums of the rounded weights) and the partial
-// layout are those of k_prefix_bf16.
+// layout are those of k_prefix_bf16; the row sums come from an MFMA, so they
+// are added in another order.  Token masks (a prefix's partial last page, the
+// union's last chunk) sit behind a uniform branch.
 template <int DIM, int RTW, bool MASK, bool PAGED>
 __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
                                                              const uint16_t *__restrict__ kc,
@@ -683,6 +685,9 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
     }
     const size_t kbase = base[min(w, n_here - 1)];
     const int kvalid = w < n_here ? valid[min(w, NP - 1)] : 0;
+    // every slot a whole page (uniform): only a prefix's last page is partial,
+    // and only the union's last chunk has fewer than NP pages
+    const bool full = n_here == NP && valid[NP - 1] >= kPage;
     uint4 kop[KSTEPS];
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
@@ -709,9 +714,16 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
                                                            sacc, 0, 0, 0);
         float sv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sv[j] = 4 * lg + j < kvalid ? sacc[j] * D.scale_log2 : -__builtin_huge_valf();
-            if (MASK && !((rmw >> (i * 16 + l16)) & 1ull)) sv[j] = -__builtin_huge_valf();
+        for (int j = 0; j < 4; ++j) sv[j] = sacc[j] * D.scale_log2;
+        if (!full) {  // uniform branch
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (4 * lg + j >= kvalid) sv[j] = -__builtin_huge_valf();
+        }
+        if constexpr (MASK) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!((rmw >> (i * 16 + l16)) & 1ull)) sv[j] = -__builtin_huge_valf();
         }
         s_sc[i][w][lane] = make_float4(sv[0], sv[1], sv[2], sv[3]);
     }
@@ -723,19 +735,35 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
         for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(vw[n][j]));
     __syncthreads();
 
-    // V^T operands of the wave's quarter: dim 2*(l%16) + e, tokens 4*lg .. +3
-    // (tokens past the prefix zeroed)
-    short4_t vop[NP][DPLQ];
+    // V^T operands of the wave's quarter: dim 2*(l%16) + e, tokens 4*lg .. +3,
+    // one byte permute per pair of tokens (tokens past the prefix zeroed, behind
+    // a uniform branch)
+    u32x2_t vop2[NP][DPLQ];
 #pragma unroll
     for (int n = 0; n < NP; ++n)
 #pragma unroll
         for (int e = 0; e < DPLQ; ++e) {
-            short4_t x;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                x[j] = 4 * lg + j < valid[n] ? static_cast<short>(vw[n][j] >> (16 * e)) : short(0);
-            vop[n][e] = x;
+            const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+            vop2[n][e] = u32x2_t{__builtin_amdgcn_perm(vw[n][1], vw[n][0], sel),
+                                 __builtin_amdgcn_perm(vw[n][3], vw[n][2], sel)};
         }
+    if (!full) {  // uniform branch
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            const uint32_t m0 = (4 * lg + 0 < valid[n] ? 0x0000ffffu : 0u) | (4 * lg + 1 < valid[n] ? 0xffff0000u : 0u);
+            const uint32_t m1 = (4 * lg + 2 < valid[n] ? 0x0000ffffu : 0u) | (4 * lg + 3 < valid[n] ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int e = 0; e < DPLQ; ++e) {
+                vop2[n][e][0] &= m0;
+                vop2[n][e][1] &= m1;
+            }
+        }
+    }
+    short4_t vop[NP][DPLQ];
+#pragma unroll
+    for (int n = 0; n < NP; ++n)
+#pragma unroll
+        for (int e = 0; e < DPLQ; ++e) vop[n][e] = __builtin_bit_cast(short4_t, vop2[n][e]);
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
         if (i >= n_rt) break;
@@ -751,7 +779,6 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
         mp = shfl_max32(mp);
         // (with row masks a row may have no score in the chunk: zero weights)
         const float mref = MASK && mp == -__builtin_huge_valf() ? 0.0f : mp;
-        float lsum = 0.0f;
         uint2 pw[NP];
 #pragma unroll
         for (int n = 0; n < NP; ++n) {
@@ -759,19 +786,22 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
                                   static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][1] - mref))};
             const bf16x2_t p23 = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][2] - mref)),
                                   static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[n][3] - mref))};
-            const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
-            lsum += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
-            pw[n] = make_uint2(w01, w23);
+            pw[n] = make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
         }
-        lsum = shfl_sum32(lsum);
         // O^T += V^T.P, pages n and n+1 in one v_mfma_f32_16x16x32_bf16 (its k
-        // index 8*lg + c: token 4*lg + c%4 of page n + c/4, in both operands)
-        float4_t oacc[DPLQ];
+        // index 8*lg + c: token 4*lg + c%4 of page n + c/4, in both operands);
+        // wave 0, which stores the (m, l), takes the rows' sums of the rounded
+        // weights with one more MFMA against an all-ones operand: every output
+        // row of it is the row sum, in the output's lane layout
+        float4_t oacc[DPLQ], lacc = {0.f, 0.f, 0.f, 0.f};
+        const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u,
+                                                                      0x3f803f80u, 0x3f803f80u));
 #pragma unroll
         for (int e = 0; e < DPLQ; ++e) oacc[e] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int n = 0; n < NP; n += 2) {
             const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[n].x, pw[n].y, pw[n + 1].x, pw[n + 1].y));
+            if (w == 0) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, lacc, 0, 0, 0);  // uniform
 #pragma unroll
             for (int e = 0; e < DPLQ; ++e) {
                 const uint2 v0 = __builtin_bit_cast(uint2, vop[n][e]), v1 = __builtin_bit_cast(uint2, vop[n + 1][e]);
@@ -784,7 +814,7 @@ __global__ __launch_bounds__(256) void k_prefix_quarter_bf16(Dims D,
         const int r = i * 16 + l16;
         if (r < rows) {
             const size_t pb = ((size_t)sgi * nch + chunk) * rows + r;
-            if (w == 0 && lg == 0) *reinterpret_cast<float2 *>(&W.part_ml[pb * 2]) = make_float2(mp, lsum);
+            if (w == 0 && lg == 0) *reinterpret_cast<float2 *>(&W.part_ml[pb * 2]) = make_float2(mp, lacc[0]);
             float *dst = W.part_acc + pb * DIM + DQ * w + DPLQ * 4 * lg;
             *reinterpret_cast<float4 *>(dst) = make_float4(oacc[0][0], oacc[1][0], oacc[0][1], oacc[1][1]);
             *reinterpret_cast<float4 *>(dst + 4) = make_float4(oacc[0][2], oacc[1][2], oacc[0][3], oacc[1][3]);
