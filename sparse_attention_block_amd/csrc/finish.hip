@@ -392,14 +392,22 @@ __global__ __launch_bounds__(DIM) void k_finish_active(
     __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
     const int nchu = (ucnt + D.sparse_chunk - 1) / D.sparse_chunk;  // chunks that wrote partials
     float mx = -__builtin_huge_valf(), ls = 0.0f, oa = 0.0f;  // running max, sum, output
-    for (int c0 = 0; c0 < nchu; c0 += kActBatch) {
+    // The first batch is always combined (with no chunk it changes nothing), so
+    // that its loads are needed on every path: if they were used only when the
+    // union is not empty, the compiler would move them behind the union size's
+    // read, a round trip later.
+    int c0 = 0;
+    do {
         if (c0 > 0) {
             ml = load_ml(c0);
             load_acc(c0);
             __syncthreads();  // the previous batch's weights have been read
         }
         const int n = min(kActBatch, nchu - c0);
-        if (x < 64) {
+        {
+            // every wave runs this (lanes past the batch see no chunk and store
+            // nothing), so that the (m, l) loads above are not moved into a
+            // branch behind the union size's read
             const bool v = x < n;
             const float m = v ? ml.x : -__builtin_huge_valf();
             float bm = m;  // maximum over the batch: butterflies over the wave
@@ -432,7 +440,8 @@ __global__ __launch_bounds__(DIM) void k_finish_active(
             ls = fmaf(w, s_l[i], ls);
             oa = fmaf(w, i < n ? av[i] : 0.0f, oa);  // (chunks past the batch: clamped reads)
         }
-    }
+        c0 += kActBatch;
+    } while (c0 < nchu);
     float op = 0.0f, lp2 = -__builtin_huge_valf();
     if (nchu > 0) {
         op = oa / ls;
