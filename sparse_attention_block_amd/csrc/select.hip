@@ -743,55 +743,66 @@ __global__ __launch_bounds__(64) void k_select(Dims D, const uint4 *__restrict__
     const int r = blockIdx.x / ng;
     const int s = sgi / D.Hk, g = sgi % D.Hk;
     const int lane = threadIdx.x;
-    const SeqGeom sg = seq_geom_t<PAGED>(D, kv_off, prefix_len, s);
     const int R = D.R, R1 = R > 0 ? R : 1, k = D.k;
     const int h = g * D.G + r / D.A, a = r % D.A;
-    const bool all_pages = k >= sg.pages;
     uint64_t *mk = reinterpret_cast<uint64_t *>(smem);  // [128] keys being merged
     uint32_t *qw = smem + 256;                           // [2*DIM] the row's chain operands
     int32_t *pend = reinterpret_cast<int32_t *>(smem + 256 + 2 * DIM);  // [kPendRing] candidate pages
     int32_t *psel = W.psel + ((size_t)sgi * R1 + r) * k;
+    const float *tm = tmax + ((size_t)sgi * R1 + r) * D.n_tiles_grid;
+    const float *hb = hbound + ((size_t)sgi * R1 + r) * D.hb_stride;
+    // Requested together, before the sequence's geometry is read (the
+    // addresses need only the grid's shape, so no load waits for it): the
+    // row's chain operands, the tile maxima of the first 256 tiles and the
+    // first 4096 upper ends.  Indexes are clamped into the buffers; entries
+    // past the sequence's pages are masked where the values are used, and a
+    // row whose budget covers every page does not use them.
+    constexpr int QPL = BF ? DIM / 128 : 2 * DIM / 64;  // operand words per lane (0: half a wave)
+    uint32_t qv[QPL > 0 ? QPL : 1];
+    if constexpr (BF) {
+        const uint32_t *qg = reinterpret_cast<const uint32_t *>(
+            static_cast<const uint16_t *>(qrows) + ((size_t)sgi * D.R16 + r) * DIM);
+        qv[0] = qg[lane % (DIM / 2)];
+    } else {
+        const float *qg = qsel32 + ((size_t)sgi * R1 + r) * DIM * 2;
+#pragma unroll
+        for (int i = 0; i < QPL; ++i) qv[i] = __float_as_uint(qg[lane + 64 * i]);
+    }
+    constexpr int TMR = 4;
+    float tmv[TMR];
+#pragma unroll
+    for (int i = 0; i < TMR; ++i) tmv[i] = tm[min(lane + 64 * i, D.n_tiles_grid - 1)];
+    // upper ends of pages base + 256*jj + 4*lane + e, jj < 16, e < 4
+    // (the lane's offset is recomputed per call, opaque to the compiler:
+    // else the 16 offsets stay in registers through the whole selection)
+    auto load_h = [&](int base, float4 (&hv)[16]) {
+        int o = base + 4 * lane;
+        asm volatile("" : "+v"(o));
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            hv[jj] = *reinterpret_cast<const float4 *>(hb + min(o + 256 * jj, D.hb_stride - 4));
+    };
+    float4 hv0[16];
+    load_h(0, hv0);
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
+    const SeqGeom sg = seq_geom_t<PAGED>(D, kv_off, prefix_len, s);
+    const bool all_pages = k >= sg.pages;
 
     if (all_pages) {
+        // (the values loaded above are used on this path too, so that the
+        // compiler does not move their loads into the other path, behind the
+        // read of the sequence's geometry)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) asm volatile("" ::"v"(hv0[jj].x));
+#pragma unroll
+        for (int i = 0; i < TMR; ++i) asm volatile("" ::"v"(tmv[i]));
+#pragma unroll
+        for (int i = 0; i < (QPL > 0 ? QPL : 1); ++i) asm volatile("" ::"v"(qv[i]));
         if (dbg.page_sel)
             for (int e = lane; e < k; e += 64)
                 dbg.page_sel[(((size_t)s * D.Hq + h) * D.A + a) * k + e] = e < sg.pages ? e : -1;
     } else {
         const int n_t = (sg.pages + kTile - 1) / kTile;  // page groups of the sequence
-        const float *tm = tmax + ((size_t)sgi * R1 + r) * D.n_tiles_grid;
-        const float *hb = hbound + ((size_t)sgi * R1 + r) * D.hb_stride;
-        // Requested together: the row's chain operands, the tile maxima of the
-        // first 256 tiles and the first 4096 upper ends.  Indexes are clamped
-        // into the buffers; lanes past the end are masked where the values
-        // are used.
-        constexpr int QPL = BF ? DIM / 128 : 2 * DIM / 64;  // operand words per lane (0: half a wave)
-        uint32_t qv[QPL > 0 ? QPL : 1];
-        if constexpr (BF) {
-            const uint32_t *qg = reinterpret_cast<const uint32_t *>(
-                static_cast<const uint16_t *>(qrows) + ((size_t)sgi * D.R16 + r) * DIM);
-            qv[0] = qg[lane % (DIM / 2)];
-        } else {
-            const float *qg = qsel32 + ((size_t)sgi * R1 + r) * DIM * 2;
-#pragma unroll
-            for (int i = 0; i < QPL; ++i) qv[i] = __float_as_uint(qg[lane + 64 * i]);
-        }
-        constexpr int TMR = 4;
-        float tmv[TMR];
-#pragma unroll
-        for (int i = 0; i < TMR; ++i) tmv[i] = tm[min(lane + 64 * i, n_t - 1)];
-        // upper ends of pages base + 256*jj + 4*lane + e, jj < 16, e < 4
-        // (the lane's offset is recomputed per call, opaque to the compiler:
-        // else the 16 offsets stay in registers through the whole selection)
-        auto load_h = [&](int base, float4 (&hv)[16]) {
-            int o = base + 4 * lane;
-            asm volatile("" : "+v"(o));
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj)
-                hv[jj] = *reinterpret_cast<const float4 *>(hb + min(o + 256 * jj, D.hb_stride - 4));
-        };
-        float4 hv0[16];
-        load_h(0, hv0);
-        __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
         if constexpr (BF) {
             // every lane stores (lanes past DIM/2 repeat a word with its own value),
             // so that the query word's load is not sunk into a branch
